@@ -1,0 +1,207 @@
+"""Python binding of libspecache: the four C-ABI calls on torch tensors.
+
+Argument marshalling only -- every step of the path runs in the HIP kernels
+behind include/specache.h.  torch provides device memory (outputs and
+workspaces are torch allocations) and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class LowBitCache:
+    """C' of one layer: the four device buffers written by quantize_pack."""
+    k_codes: torch.Tensor   # uint32 [B, Hkv, N, bits, D/32]   (stored as int32)
+    k_meta: torch.Tensor    # float16 [B, Hkv, N/32, 2, D]
+    v_codes: torch.Tensor   # uint32 [B, Hkv, N/32, bits, D]
+    v_meta: torch.Tensor    # float16 [B, Hkv, N/32, 2, D/32, 32]
+    batch: int
+    n_kv_heads: int
+    seq_len: int
+    head_dim: int
+    bits: int
+    group: int = 32
+
+    def c_struct(self) -> _lib.LowBit:
+        return _lib.LowBit(self.k_codes.data_ptr(), self.k_meta.data_ptr(),
+                           self.v_codes.data_ptr(), self.v_meta.data_ptr())
+
+    def shape(self, n_q_heads: int | None = None) -> _lib.Shape:
+        return _lib.Shape(self.batch, n_q_heads or self.n_kv_heads, self.n_kv_heads, self.head_dim,
+                          self.seq_len, self.bits, self.group)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_meta, self.v_codes, self.v_meta))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int, cuda: bool = True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def lowbit_sizes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, bits: int, group: int = 32):
+    """(k_codes, k_meta, v_codes, v_meta) element shapes of C' (see include/specache.h)."""
+    W = head_dim // 32
+    nblk = seq_len // group
+    return ((batch, n_kv_heads, seq_len, bits, W), (batch, n_kv_heads, nblk, 2, head_dim),
+            (batch, n_kv_heads, nblk, bits, head_dim), (batch, n_kv_heads, nblk, 2, W, 32))
+
+
+def empty_cache(batch, n_kv_heads, seq_len, head_dim, bits, device="cuda") -> LowBitCache:
+    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, seq_len, head_dim, bits)
+    return LowBitCache(torch.empty(kc, dtype=torch.int32, device=device),
+                       torch.empty(km, dtype=torch.float16, device=device),
+                       torch.empty(vc, dtype=torch.int32, device=device),
+                       torch.empty(vm, dtype=torch.float16, device=device),
+                       batch, n_kv_heads, seq_len, head_dim, bits)
+
+
+def quantize_pack(k16: torch.Tensor, v16: torch.Tensor, bits: int, out: LowBitCache | None = None,
+                  stream=None) -> LowBitCache:
+    """specache_quantize_pack: K, V [B, Hkv, N, D] float16 (device) -> C'."""
+    _need(k16, "k16", torch.float16, 4)
+    _need(v16, "v16", torch.float16, 4)
+    if k16.shape != v16.shape:
+        raise ValueError("k16 and v16 must have the same shape")
+    B, Hkv, N, D = k16.shape
+    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device)
+    lib = _lib.load()
+    shape = cache.shape()
+    if (cache.batch, cache.n_kv_heads, cache.seq_len, cache.head_dim, cache.bits) != (B, Hkv, N, D, bits):
+        raise ValueError("out cache shape does not match the inputs")
+    _lib.check(lib.specache_quantize_pack(ctypes.byref(shape), k16.data_ptr(), v16.data_ptr(),
+                                          ctypes.byref(cache.c_struct()), _stream(stream)),
+               "specache_quantize_pack")
+    return cache
+
+
+def score_topk_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int) -> int:
+    shape = cache.shape(n_q_heads)
+    return int(_lib.load().specache_score_topk_workspace_size(ctypes.byref(shape), n_tokens, k))
+
+
+def score_topk(q16: torch.Tensor, cache: LowBitCache, k: int, rank_row: int = 1, sm_scale: float | None = None,
+               idx_out: torch.Tensor | None = None, rank_key_out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """specache_score_topk: idx [B, Hkv, k] int32 (ascending) of the top-k positions
+    by the rank row's attention over C'.  rank_key_out, if given ([B, Hkv, N]
+    float32), receives r(p)."""
+    _need(q16, "q16", torch.float16, 4)
+    B, Hq, T, D = q16.shape
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    lib = _lib.load()
+    shape = cache.shape(Hq)
+    need = lib.specache_score_topk_workspace_size(ctypes.byref(shape), T, k)
+    if need == 0:
+        raise ValueError("invalid score_topk arguments (shape, n_tokens or k)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    if idx_out is None:
+        idx_out = torch.empty((B, cache.n_kv_heads, k), dtype=torch.int32, device=q16.device)
+    _need(idx_out, "idx_out", torch.int32, 3)
+    rk = 0
+    if rank_key_out is not None:
+        _need(rank_key_out, "rank_key_out", torch.float32, 3)
+        rk = rank_key_out.data_ptr()
+    _lib.check(lib.specache_score_topk(ctypes.byref(shape), q16.data_ptr(), T, rank_row,
+                                       ctypes.byref(cache.c_struct()), sm_scale, k, idx_out.data_ptr(), rk,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)),
+               "specache_score_topk")
+    return idx_out
+
+
+def gather_fp16(idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor, bits: int = 1,
+                k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None, stream=None):
+    """specache_gather_fp16: rows idx of the 16-bit cache (pinned host or device,
+    [B, Hkv, N, D]) -> (k_sel, v_sel) [B, Hkv, k, D] on the device."""
+    _need(idx, "idx", torch.int32, 3)
+    _need(k16_src, "k16_src", torch.float16, 4, cuda=False)
+    _need(v16_src, "v16_src", torch.float16, 4, cuda=False)
+    for name, t in (("k16_src", k16_src), ("v16_src", v16_src)):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    B, Hkv, N, D = k16_src.shape
+    k = idx.shape[2]
+    dev = idx.device
+    if k_sel is None:
+        k_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
+    if v_sel is None:
+        v_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
+    shape = _lib.Shape(B, Hkv, Hkv, D, N, bits, 32)
+    _lib.check(_lib.load().specache_gather_fp16(ctypes.byref(shape), idx.data_ptr(), k, k16_src.data_ptr(),
+                                                v16_src.data_ptr(), k_sel.data_ptr(), v_sel.data_ptr(),
+                                                _stream(stream)),
+               "specache_gather_fp16")
+    return k_sel, v_sel
+
+
+def decode_attn_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int, tail_len: int = 0) -> int:
+    shape = cache.shape(n_q_heads)
+    return int(_lib.load().specache_decode_attn_workspace_size(ctypes.byref(shape), n_tokens, k, tail_len))
+
+
+def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None = None,
+                k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None,
+                k_tail: torch.Tensor | None = None, v_tail: torch.Tensor | None = None,
+                sm_scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """specache_decode_attn: O [B, Hq, T, D] float16 = Attn(q, C' with rows idx replaced by
+    k_sel / v_sel, then the optional tail)."""
+    _need(q16, "q16", torch.float16, 4)
+    B, Hq, T, D = q16.shape
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    k = 0
+    ip = kp = vp = 0
+    if idx is not None:
+        _need(idx, "idx", torch.int32, 3)
+        k = idx.shape[2]
+        if k > 0:
+            _need(k_sel, "k_sel", torch.float16, 4)
+            _need(v_sel, "v_sel", torch.float16, 4)
+            ip, kp, vp = idx.data_ptr(), k_sel.data_ptr(), v_sel.data_ptr()
+    R = 0
+    ktp = vtp = 0
+    if k_tail is not None:
+        _need(k_tail, "k_tail", torch.float16, 4)
+        _need(v_tail, "v_tail", torch.float16, 4)
+        R = k_tail.shape[2]
+        ktp, vtp = k_tail.data_ptr(), v_tail.data_ptr()
+    lib = _lib.load()
+    shape = cache.shape(Hq)
+    need = lib.specache_decode_attn_workspace_size(ctypes.byref(shape), T, k, R)
+    if need == 0:
+        raise ValueError("invalid decode_attn arguments (shape, n_tokens, k or tail length)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    if out is None:
+        out = torch.empty_like(q16)
+    _lib.check(lib.specache_decode_attn(ctypes.byref(shape), q16.data_ptr(), T, ctypes.byref(cache.c_struct()),
+                                        ip, k, kp, vp, ktp, vtp, R, sm_scale, out.data_ptr(),
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)),
+               "specache_decode_attn")
+    return out

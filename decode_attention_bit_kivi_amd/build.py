@@ -1,0 +1,78 @@
+"""Build libspecache.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m decode_attention_bit_kivi_amd.build  [--jobs N]
+
+Every .hip file under csrc/ is compiled to an object for gfx950 and linked
+into decode_attention_bit_kivi_amd/libspecache.so.  Packed-FP32 VALU
+instructions are disabled for all device code (-packed-fp32-ops).
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+OUT = os.path.join(PKG, "libspecache.so")
+BUILD_DIR = os.path.join(os.path.dirname(PKG), "_build")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found (ROCm is required to build libspecache)")
+    return exe
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    if r.stderr.strip():
+        # hipcc's host pass warns about the device-only target feature; keep other warnings visible
+        lines = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+        if lines:
+            print("\n".join(lines), file=sys.stderr)
+    return obj
+
+
+def build(jobs: int = 8, verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(sources)))) as ex:
+        objs = list(ex.map(_compile, sources))
+    tmp = OUT + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT} from {len(sources)} sources")
+    return OUT
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=8)
+    args = ap.parse_args()
+    build(args.jobs)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,110 @@
+// Shared definitions of libspecache's HIP sources (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specache {
+
+constexpr int kGroup = 32;        // quantization group (tokens for keys, channels for values)
+constexpr int kMaxRows = 16;      // G * T query rows per KV head handled by one workgroup
+constexpr int kMaxTail = 64;
+
+// Problem dimensions after validation.
+struct Dims {
+  int B, Hq, Hkv, D, bits, G, W;
+  int64_t N, nblk;   // positions and 32-position blocks per slice
+  int64_t slices() const { return (int64_t)B * Hkv; }
+};
+
+// Bit i of a packed word stands for element 2*(i mod 16) + (i div 16):
+// even elements in the low half-word, odd elements in the high half-word.
+__host__ __device__ __forceinline__ int bit_to_elem(int i) { return 2 * (i & 15) + (i >> 4); }
+__host__ __device__ __forceinline__ int elem_to_bit(int e) { return (e >> 1) + ((e & 1) << 4); }
+
+__host__ __device__ __forceinline__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// ---- split plans (pure functions of the shape; used for workspace sizing and launch) ----
+
+struct ScorePlan {
+  int64_t L;       // positions per split (multiple of 128)
+  int S;           // splits per slice
+};
+
+inline ScorePlan score_plan(const Dims& d) {
+  const int64_t target = 2048;  // workgroups to aim for
+  int64_t L = ceil_div(d.N * d.slices(), target);
+  L = round_up(L, 128);
+  if (L < 128) L = 128;
+  if (L > 4096) L = 4096;
+  ScorePlan p;
+  p.L = L;
+  p.S = (int)ceil_div(d.N, L);
+  return p;
+}
+
+struct AttnPlan {
+  int64_t L;       // low-bit positions per split (multiple of 32)
+  int S_lb;        // low-bit splits
+  int Lsel;        // 16-bit rows per split
+  int S_sel;       // 16-bit row splits
+  int S_tail;      // 0 or 1
+  int S;           // total splits per slice
+};
+
+inline AttnPlan attn_plan(const Dims& d, int k, int tail) {
+  const int64_t target = 2048;
+  int64_t L = ceil_div(d.N * d.slices(), target);
+  L = round_up(L, 32);
+  if (L < 64) L = 64;
+  if (L > 2048) L = 2048;
+  AttnPlan p;
+  p.L = L;
+  p.S_lb = (int)ceil_div(d.N, L);
+  p.Lsel = 64;
+  p.S_sel = (int)ceil_div(k, p.Lsel);
+  p.S_tail = tail > 0 ? 1 : 0;
+  p.S = p.S_lb + p.S_sel + p.S_tail;
+  return p;
+}
+
+// ---- launchers (defined in the .hip files) ----
+
+hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v16, uint32_t* k_codes,
+                           _Float16* k_meta, uint32_t* v_codes, _Float16* v_meta, hipStream_t s);
+
+hipError_t launch_score(const Dims& d, const ScorePlan& plan, const _Float16* q16, int n_tokens,
+                        int rank_row, const uint32_t* k_codes, const _Float16* k_meta, float sm_scale,
+                        float* logits, float* part_m, float* part_l, hipStream_t s);
+
+hipError_t launch_rank_select(const Dims& d, const ScorePlan& plan, const float* logits,
+                              const float* part_m, const float* part_l, int k, float* keys,
+                              int32_t* idx_out, hipStream_t s);
+
+hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,
+                         const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, hipStream_t s);
+
+struct AttnArgs {
+  const _Float16* q16;
+  int T;
+  const uint32_t* k_codes;
+  const _Float16* k_meta;
+  const uint32_t* v_codes;
+  const _Float16* v_meta;
+  const int32_t* idx;
+  int k;
+  const _Float16* k_sel;
+  const _Float16* v_sel;
+  const _Float16* k_tail;
+  const _Float16* v_tail;
+  int tail;
+  float sm_scale;
+  _Float16* out16;
+  float* part_ml;    // [B][Hq][T][S][2]  (running max in log2 units, sum of exp2)
+  float* part_acc;   // [B][Hq][T][S][D]
+};
+
+hipError_t launch_decode_attn(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
+
+}  // namespace specache

@@ -1,0 +1,220 @@
+/*
+ * specache.h -- C ABI of libspecache: decode-step attention over a 1/2-bit
+ * KIVI-style KV cache with speculative top-k prefetch of 16-bit rows, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is SpeCache ("SpeCache: Speculative Key-Value Caching for
+ * Efficient Generation of LLMs", papercache.org summary of arXiv:2503.16163):
+ * the GPU keeps only a low-bit copy C' of the KV cache, the 16-bit cache C
+ * lives in host memory, each decode step runs two query tokens (the real T_t
+ * and a speculative T'_{t+1}), ranks positions by the speculative token's
+ * attention over C', prefetches the top-k 16-bit rows, and attends over
+ * C' with those rows substituted.  The four calls below map onto the
+ * operations of the summary's appendix algorithms:
+ *
+ *   Quant(K), Quant(V)     (Algorithm 1)      -> specache_quantize_pack
+ *   ArgTopK(A_{1,:})       (Algorithms 2, 3)  -> specache_score_topk
+ *   Pre-fetch(C_kappa)     (Algorithms 2, 3)  -> specache_gather_fp16
+ *   Attn(.., C' U C_kappa) (Algorithm 3)      -> specache_decode_attn
+ *   Offload(C)             is the caller's own device-to-host copy.
+ *
+ * ------------------------------------------------------------------------
+ * Conventions (every call)
+ * ------------------------------------------------------------------------
+ *  - Plain pointers.  Unless a parameter says otherwise, a pointer is device
+ *    memory of the current HIP device, caller-allocated and caller-owned; the
+ *    library never frees or retains it.  Inputs are read only; outputs are
+ *    fully overwritten.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *    only enqueue work and return; results are ready when the stream reaches
+ *    them.  Ordering across streams is the caller's job (HIP events).
+ *  - The library keeps no state and allocates nothing: scratch space comes
+ *    from a caller-provided workspace whose size the *_workspace_size
+ *    functions return.
+ *  - Return value: a specache_status.  Argument errors are detected on the
+ *    host before anything is enqueued; SPECACHE_ERR_HIP means a HIP runtime
+ *    call or a kernel launch failed (faults inside kernels surface at the
+ *    caller's next synchronization, as with any HIP kernel).  No C++
+ *    exception crosses this boundary.
+ *  - All tensors are dense, row-major (last index fastest), with the shapes
+ *    given below.  float16 is IEEE binary16.
+ *
+ * ------------------------------------------------------------------------
+ * Shapes and symbols
+ * ------------------------------------------------------------------------
+ *  B = batch, Hq = query heads, Hkv = KV heads, G = Hq / Hkv (query head hq
+ *  reads KV head hq / G), D = head_dim (64 or 128), N = cached positions
+ *  (a positive multiple of 32), T = query tokens per step (1 or 2; row 0 is
+ *  the real token T_t, row 1 the speculative token T'_{t+1}), b = bits per
+ *  code (1 or 2), g = quantization group = 32, W = D / 32.  G * T <= 16.
+ *
+ * ------------------------------------------------------------------------
+ * Low-bit cache C' (written by specache_quantize_pack)
+ * ------------------------------------------------------------------------
+ *  Quantizer: the summary's §3.  Keys are grouped per channel over 32
+ *  consecutive tokens, values per token over 32 consecutive channels (KIVI's
+ *  grouping, as restated in the SemKV page, §2.1).  For a group with minimum
+ *  mn and maximum mx (computed in float32 from the float16 inputs):
+ *    b = 1 (§3 "improved 1-bit quantization"): z = (3*mn + mx)/4,
+ *          s = (mx - mn)/2, evaluated as z = (3*mn + mx) * 0.25 and
+ *          s = (mx - mn) * 0.5 in float32;
+ *    b = 2 (§3 "original KIVI quantization"): z = mn, s = (mx - mn)/3 with a
+ *          correctly rounded float32 division;
+ *  z and s are stored as float16 (round to nearest even; -0 stored as +0).
+ *  code(x) = clamp(floor(q + 1/2), 0, 2^b - 1) with q = (x - z16) / s16 in
+ *  float32 (round half up, the summary's rounding), and code 0 when s16 == 0.
+ *  Dequantized value: code * s16 + z16.
+ *
+ *  Bit planes: a code's bit j (j = 0 least significant) lives in plane j.
+ *  Within every 32-bit word, bit i (i = 0..31) stands for element
+ *  e(i) = 2*(i mod 16) + (i div 16): even elements in the low half-word, odd
+ *  elements in the high half-word (element e is a channel for keys, a token
+ *  for values).
+ *
+ *  k_codes  uint32 [B][Hkv][N][b][W]       word (p, j, w) holds plane j of the
+ *                                          codes of token p, channels 32w+e(i).
+ *  k_meta   float16[B][Hkv][N/32][2][D]    [blk][0][c] = z, [blk][1][c] = s of the
+ *                                          key group (tokens 32blk..32blk+31, channel c).
+ *  v_codes  uint32 [B][Hkv][N/32][b][D]    word (blk, j, c) holds plane j of the
+ *                                          codes of channel c, tokens 32blk+e(i).
+ *  v_meta   float16[B][Hkv][N/32][2][W][32] [blk][0][w][t] = z, [blk][1][w][t] = s of
+ *                                          the value group (token 32blk+t, channels
+ *                                          32w..32w+31).
+ *  Bytes per position per KV head: (b*D/8 + 4*D/32) for keys and the same for
+ *  values -- 64 B at D = 128, b = 1 (one eighth of float16), 96 B at b = 2.
+ *
+ * ------------------------------------------------------------------------
+ * Other tensors
+ * ------------------------------------------------------------------------
+ *  q16, out16      float16 [B][Hq][T][D]
+ *  k16, v16        float16 [B][Hkv][N][D]      the full 16-bit cache C
+ *  idx             int32   [B][Hkv][k]         strictly ascending, each in [0, N)
+ *  k_sel, v_sel    float16 [B][Hkv][k][D]      row i = 16-bit row idx[i]
+ *  k_tail, v_tail  float16 [B][Hkv][R][D]      optional 16-bit positions after the
+ *                                              cache (the step's own new KV)
+ *  rank_key        float32 [B][Hkv][N]         r(p), see specache_score_topk
+ */
+#ifndef SPECACHE_H_
+#define SPECACHE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPECACHE_ABI_VERSION 1
+
+typedef enum specache_status {
+  SPECACHE_OK = 0,
+  SPECACHE_ERR_INVALID = 1,     /* bad argument: null pointer, size out of range, inconsistent shape */
+  SPECACHE_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128, group != 32, G*T > 16 */
+  SPECACHE_ERR_WORKSPACE = 3,   /* workspace null or smaller than the *_workspace_size value */
+  SPECACHE_ERR_NOT_PINNED = 4,  /* gather source is neither device memory nor pinned host memory */
+  SPECACHE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} specache_status;
+
+/* Shape of one layer's cache.  group must be 32. */
+typedef struct specache_shape {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int64_t seq_len;
+  int32_t bits;
+  int32_t group;
+} specache_shape;
+
+/* The four device buffers of C' (layouts above). */
+typedef struct specache_lowbit {
+  void* k_codes;
+  void* k_meta;
+  void* v_codes;
+  void* v_meta;
+} specache_lowbit;
+
+/* Byte sizes of the four C' buffers for `shape` (0 for an invalid shape). */
+size_t specache_lowbit_bytes(const specache_shape* shape, size_t* k_codes, size_t* k_meta,
+                             size_t* v_codes, size_t* v_meta);
+
+/*
+ * Quant(K), Quant(V) of the summary's Algorithm 1 (prefill), with the §3
+ * quantizer described above: reads k16, v16 [B][Hkv][N][D] (device float16)
+ * and writes the four buffers of `out`.  Bit-exact by definition (no
+ * floating-point freedom).  Inputs must be finite.
+ */
+int specache_quantize_pack(const specache_shape* shape, const void* k16, const void* v16,
+                           const specache_lowbit* out, void* stream);
+
+/*
+ * ArgTopK over the speculative row (the summary's quick read, second
+ * mechanism; §3 "prefetch and offload during decoding"; Algorithm 3's
+ * ArgTopK(A_{1,:}), Algorithm 2 with n_tokens = 1).
+ *
+ * For every slice (b, h) and each of its G query heads hq = h*G + gi, the
+ * logits of row `rank_row` against C' are s_gi(p) = sm_scale * q . Khat(p)
+ * (Khat dequantized; the 16-bit rows play no part).  With LSE_gi the
+ * log-sum-exp of s_gi over p, the rank of position p is
+ *     r(p) = log sum_gi exp(s_gi(p) - LSE_gi),
+ * the log of the attention mass the G heads put on p.  idx_out [B][Hkv][k]
+ * receives the k positions of largest r in ascending order (ties -> lower
+ * position).  rank_key_out, if not NULL, receives r [B][Hkv][N] (float32).
+ *
+ * n_tokens in {1, 2}; 0 <= rank_row < n_tokens; 1 <= k <= N.
+ * Workspace: specache_score_topk_workspace_size bytes, device memory,
+ * 256-byte aligned.
+ */
+size_t specache_score_topk_workspace_size(const specache_shape* shape, int n_tokens, int k);
+int specache_score_topk(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
+                        const specache_lowbit* cache, float sm_scale, int k, int32_t* idx_out,
+                        float* rank_key_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Pre-fetch(C_kappa) of Algorithm 3: k_sel[b][h][i][:] = k16_src[b][h][idx[b][h][i]][:]
+ * and the same for values -- a byte copy.  k16_src / v16_src may be pinned
+ * host memory (hipHostMalloc, or torch pin_memory) read directly by the
+ * kernel over the host link, or device memory; anything else returns
+ * SPECACHE_ERR_NOT_PINNED.  An idx entry outside [0, N) is not dereferenced:
+ * its output row is filled with float16 NaN.  0 <= k <= N (k = 0 is a no-op).
+ * Typically enqueued on a side stream after an event recorded behind
+ * specache_score_topk.
+ */
+int specache_gather_fp16(const specache_shape* shape, const int32_t* idx, int k,
+                         const void* k16_src, const void* v16_src, void* k_sel, void* v_sel,
+                         void* stream);
+
+/*
+ * O = Attn([T_t, T'_{t+1}], C' U C_kappa) (the summary's quick read, third
+ * mechanism; §3 "decoding"; Algorithm 3): softmax attention of every query
+ * row over the N cached positions, where the k positions listed in idx use
+ * the 16-bit rows k_sel / v_sel in place of their dequantized low-bit rows,
+ * followed by the tail_len positions of k_tail / v_tail; tail position j is
+ * visible to query row t iff j <= tail_len - n_tokens + t (the masked
+ * softmax of Algorithm 3: the real token does not see the speculative
+ * token's entry).  Logits are sm_scale * q . k.  out16 [B][Hq][T][D] float16.
+ *
+ * 0 <= k <= N (k = 0: pure low-bit attention; idx, k_sel, v_sel may be NULL);
+ * idx must be strictly ascending within [0, N) per slice (not checked on the
+ * device); 0 <= tail_len <= 64 (k_tail / v_tail may be NULL when 0).
+ * Workspace: specache_decode_attn_workspace_size bytes, device memory.
+ */
+size_t specache_decode_attn_workspace_size(const specache_shape* shape, int n_tokens, int k,
+                                           int tail_len);
+int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tokens,
+                         const specache_lowbit* cache, const int32_t* idx, int k,
+                         const void* k_sel, const void* v_sel, const void* k_tail,
+                         const void* v_tail, int tail_len, float sm_scale, void* out16,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* specache_status_string(int status);
+
+/* SPECACHE_ABI_VERSION of the built library. */
+int specache_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECACHE_H_ */

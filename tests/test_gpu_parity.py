@@ -1,0 +1,315 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (fixed before the kernels were written):
+  * quantize_pack: codes and float16 zero-points / scales bit-exact;
+  * score_topk: same count, unique, ascending; every position in the symmetric
+    difference with the oracle's set has an oracle rank within 1e-5 of the k-th
+    largest (ties go to the lower position);
+  * gather_fp16: bitwise copy;
+  * decode_attn: max |O_gpu - O_ref| / max |O_ref| <= 2e-3 (float16 output).
+Small cases are checked in full; the large workloads run at full size in the
+launch configuration the benchmark uses, with a few seeded slices filled and
+checked against the oracle (the other slices are left zero).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_attention_bit_kivi_amd import (
+    quantize_pack, score_topk, gather_fp16, decode_attn, SpecacheError,
+)
+from tests.layout import unpack_keys, unpack_values
+from workloads import get_config, generate_all
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-3
+TIE_BAND = 1e-5
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _sampled(cfg, n=4, seed=123):
+    rng = np.random.default_rng(seed)
+    allp = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads)]
+    if len(allp) <= n:
+        return allp
+    pick = rng.choice(len(allp), size=n, replace=False)
+    return [allp[i] for i in sorted(pick)]
+
+
+def _reference_cache(K, V, bits):
+    kc, kz, ks = oracle.quantize_keys(K, bits)
+    vc, vz, vs = oracle.quantize_values(V, bits)
+    return (kc, kz, ks, vc, vz, vs), oracle.dequantize_keys(kc, kz, ks), oracle.dequantize_values(vc, vz, vs)
+
+
+def _assert_quantize_exact(cache, ref, bits, slices=None):
+    kc, kz, ks, vc, vz, vs = ref
+    gk, gkz, gks = unpack_keys(_np(cache.k_codes), _np(cache.k_meta), bits)
+    gv, gvz, gvs = unpack_values(_np(cache.v_codes), _np(cache.v_meta), bits)
+    sel = (slice(None),) if slices is None else (tuple(b for b, _ in slices), tuple(h for _, h in slices))
+    pairs = [(gk, kc), (gv, vc)]
+    for got, want in pairs:
+        assert np.array_equal(got[sel], want[sel]), "codes differ"
+    for got, want in ((gkz, kz), (gks, ks), (gvz, vz), (gvs, vs)):
+        assert np.array_equal(got[sel].view(np.uint16), want[sel].view(np.uint16)), "metadata differs"
+
+
+def _assert_topk(idx_gpu, r_ref, k, slices):
+    for (b, h) in slices:
+        got = idx_gpu[b, h]
+        assert len(got) == k and np.all(np.diff(got) > 0), "not strictly ascending"
+        want = oracle.topk_positions(r_ref[b:b + 1, h:h + 1], k)[0, 0]
+        kth = np.sort(r_ref[b, h])[::-1][k - 1]
+        diff = np.setxor1d(got, want)
+        bad = [p for p in diff if abs(r_ref[b, h, p] - kth) >= TIE_BAND]
+        assert not bad, f"slice {(b, h)}: positions {bad[:8]} outside the tie band"
+
+
+def _attn_err(o_gpu, o_ref):
+    return float(np.max(np.abs(o_gpu.astype(np.float64) - o_ref)) / np.max(np.abs(o_ref)))
+
+
+# ---------------------------------------------------------------- quantize_pack
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("tiny", dict(bits=2)),
+    ("tiny", dict(head_dim=128, seq_len=96, batch=2)),
+    ("llama8k", {}),
+    ("llama8k", dict(bits=1, seed=1)),
+    ("llama8k", dict(head_dim=64, seq_len=32, seed=2)),
+])
+def test_quantize_bit_exact(gpu, name, over):
+    cfg = get_config(name).with_(**over)
+    K, V, _, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    torch.cuda.synchronize()
+    ref, _, _ = _reference_cache(K, V, cfg.bits)
+    _assert_quantize_exact(cache, ref, cfg.bits)
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_quantize_adversarial_values(gpu, bits):
+    """Exact ties, constant groups, signed zeros, float16 extremes and subnormals."""
+    rng = np.random.default_rng(77 + bits)
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 0.5, -0.5, 0.25, 65504.0, -65504.0, 6e-8, -6e-8,
+                         1e-4, 3.0, 1.5, 2.0, -2.0], dtype=np.float16)
+    B, H, N, D = 2, 2, 256, 64
+    K = rng.choice(specials, size=(B, H, N, D))
+    V = rng.choice(specials, size=(B, H, N, D))
+    K[0, 0, :32] = np.float16(0.75)                                   # constant key groups
+    V[0, 1, 5] = np.float16(-3.0)                                     # constant value groups
+    t = rng.integers(0, 7, size=(N, D)) / 2                           # exact half-way 2-bit codes
+    K[1, 1] = (np.float16(-1.0) + np.float16(0.25) * t).astype(np.float16)
+    K[1, 1, ::32] = np.float16(-1.0)
+    K[1, 1, 1::32] = np.float16(-0.25)
+    cache = quantize_pack(_dev(K), _dev(V), bits)
+    torch.cuda.synchronize()
+    ref, _, _ = _reference_cache(K, V, bits)
+    _assert_quantize_exact(cache, ref, bits)
+
+
+@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
+def test_quantize_full_size_sampled(gpu, name):
+    cfg = get_config(name)
+    sl = _sampled(cfg, 3)
+    K, V, _, _, _, _ = generate_all(cfg, slices=sl)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    torch.cuda.synchronize()
+    for (b, h) in sl:
+        ref, _, _ = _reference_cache(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], cfg.bits)
+        sub = type(cache)(*(t[b:b + 1, h:h + 1] for t in (cache.k_codes, cache.k_meta, cache.v_codes, cache.v_meta)),
+                          1, 1, cfg.seq_len, cfg.head_dim, cfg.bits)
+        _assert_quantize_exact(sub, ref, cfg.bits)
+
+
+# ---------------------------------------------------------------- score_topk
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("tiny", dict(bits=2, seed=1, top_k=1)),
+    ("tiny", dict(seq_len=96, top_k=96)),                   # k = N
+    ("llama8k", {}),
+    ("llama8k", dict(bits=1, seed=2)),
+    ("llama8k", dict(seq_len=8192 + 160, seed=3)),           # ragged last split
+    ("llama8k", dict(n_tokens=1)),                           # pre-decoding: one token, row 0
+])
+def test_score_topk_matches_oracle(gpu, name, over):
+    cfg = get_config(name).with_(**over)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    row = 1 if cfg.n_tokens == 2 else 0
+    rk = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    idx = score_topk(_dev(Q), cache, cfg.top_k, rank_row=row, rank_key_out=rk)
+    torch.cuda.synchronize()
+    _, kh, _ = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores(Q, kh, row, cfg.sm_scale)
+    slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads)]
+    _assert_topk(_np(idx), r_ref, cfg.top_k, slices)
+    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+
+
+@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
+def test_score_topk_full_size_sampled(gpu, name):
+    cfg = get_config(name)
+    sl = _sampled(cfg, 3)
+    K, V, Q, planted, _, _ = generate_all(cfg, slices=sl)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    idx = _np(score_topk(_dev(Q), cache, cfg.top_k))
+    for (b, h) in sl:
+        G = cfg.gqa
+        q = Q[b:b + 1, h * G:(h + 1) * G]
+        _, kh, _ = _reference_cache(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], cfg.bits)
+        r_ref = oracle.rank_scores(q, kh, 1, cfg.sm_scale)
+        _assert_topk(idx[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)])
+        if cfg.n_planted:
+            assert np.isin(planted[b, h], idx[b, h]).mean() >= 0.9
+
+
+# ---------------------------------------------------------------- gather_fp16
+
+@pytest.mark.parametrize("pinned", [True, False])
+def test_gather_bitwise(gpu, pinned):
+    cfg = get_config("llama8k").with_(seq_len=2048, batch=2)
+    K, V, _, _, _, _ = generate_all(cfg)
+    rng = np.random.default_rng(5)
+    k = 37
+    idx = np.stack([np.stack([np.sort(rng.choice(cfg.seq_len, k, replace=False)) for _ in range(cfg.n_kv_heads)])
+                    for _ in range(cfg.batch)]).astype(np.int32)
+    src_k = torch.from_numpy(K).pin_memory() if pinned else _dev(K)
+    src_v = torch.from_numpy(V).pin_memory() if pinned else _dev(V)
+    ks, vs = gather_fp16(_dev(idx), src_k, src_v)
+    torch.cuda.synchronize()
+    wk, wv = oracle.gather_rows(K, V, idx)
+    assert np.array_equal(_np(ks).view(np.uint16), wk.view(np.uint16))
+    assert np.array_equal(_np(vs).view(np.uint16), wv.view(np.uint16))
+
+
+def test_gather_rejects_pageable_source_and_flags_bad_rows(gpu):
+    import ctypes
+    from decode_attention_bit_kivi_amd import _lib
+    K = np.ones((1, 1, 64, 64), dtype=np.float16)
+    idx = _dev(np.array([[[0, 63, 64, -1]]], dtype=np.int32))
+    dk = _dev(K)
+    out_k = torch.empty((1, 1, 4, 64), dtype=torch.float16, device="cuda")
+    out_v = torch.empty_like(out_k)
+    shape = _lib.Shape(1, 1, 1, 64, 64, 1, 32)
+    pageable = K.ctypes.data                      # plain host memory: not readable by the GPU
+    st = _lib.load().specache_gather_fp16(ctypes.byref(shape), idx.data_ptr(), 4, pageable, dk.data_ptr(),
+                                          out_k.data_ptr(), out_v.data_ptr(), None)
+    assert st == _lib.SPECACHE_ERR_NOT_PINNED
+    ks, vs = gather_fp16(idx, dk, dk)
+    torch.cuda.synchronize()
+    out = _np(ks)[0, 0]
+    assert np.all(out[:2] == 1) and np.all(np.isnan(out[2:]))
+
+
+# ---------------------------------------------------------------- decode_attn
+
+def _random_idx(rng, B, H, N, k):
+    return np.stack([np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(H)])
+                     for _ in range(B)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("name,over,mode", [
+    ("tiny", {}, "none"),
+    ("tiny", {}, "random"),
+    ("tiny", dict(bits=2), "all"),
+    ("tiny", {}, "tail"),
+    ("tiny", dict(n_tokens=1), "random"),
+    ("llama8k", {}, "topk"),
+    ("llama8k", dict(bits=1, seed=1), "none"),
+    ("llama8k", dict(seq_len=8192 + 96), "random"),
+    ("llama8k", dict(n_q_heads=64, n_kv_heads=8), "random"),     # G = 8: 16 rows
+])
+def test_decode_attn_matches_oracle(gpu, name, over, mode):
+    cfg = get_config(name).with_(**over)
+    if mode == "tail":
+        cfg = cfg.with_(tail_len=2)
+    K, V, Q, _, KT, VT = generate_all(cfg)
+    B, Hkv, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    _, kh, vh = _reference_cache(K, V, cfg.bits)
+    rng = np.random.default_rng(9)
+    idx = None
+    if mode == "random" or mode == "tail":
+        idx = _random_idx(rng, B, Hkv, N, cfg.top_k)
+    elif mode == "all":
+        idx = np.broadcast_to(np.arange(N, dtype=np.int32), (B, Hkv, N)).copy()
+    elif mode == "topk":
+        idx = _np(score_topk(_dev(Q), cache, cfg.top_k))
+    ks = vs = None
+    if idx is not None:
+        ks, vs = oracle.gather_rows(K, V, idx)
+    out = decode_attn(_dev(Q), cache, None if idx is None else _dev(idx),
+                      None if ks is None else _dev(ks), None if vs is None else _dev(vs),
+                      None if KT is None else _dev(KT), None if VT is None else _dev(VT))
+    torch.cuda.synchronize()
+    ref = oracle.mixed_attention(Q, kh, vh, idx, ks, vs, KT, VT, sm_scale=cfg.sm_scale)
+    err = _attn_err(_np(out), ref)
+    assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
+def test_decode_step_full_size_sampled(gpu, name):
+    """The whole step at full size: score_topk -> gather from pinned host -> decode_attn."""
+    cfg = get_config(name)
+    sl = _sampled(cfg, 3)
+    K, V, Q, _, _, _ = generate_all(cfg, slices=sl)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    idx = score_topk(_dev(Q), cache, cfg.top_k)
+    hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
+    ks, vs = gather_fp16(idx, hk, hv)
+    out = _np(decode_attn(_dev(Q), cache, idx, ks, vs))
+    idx = _np(idx)
+    G = cfg.gqa
+    for (b, h) in sl:
+        q = Q[b:b + 1, h * G:(h + 1) * G]
+        _, kh, vh = _reference_cache(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], cfg.bits)
+        i = idx[b:b + 1, h:h + 1]
+        rks, rvs = oracle.gather_rows(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], i)
+        ref = oracle.mixed_attention(q, kh, vh, i, rks, rvs, sm_scale=cfg.sm_scale)
+        assert _attn_err(out[b:b + 1, h * G:(h + 1) * G], ref) <= ATTN_TOL
+
+
+def test_overlapped_streams_match_serial(gpu):
+    """score_topk on the compute stream, gather on a side stream after an event,
+    attention after the gather's event: bitwise equal to the serialized run."""
+    cfg = get_config("llama8k").with_(batch=2)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    q = _dev(Q)
+    hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
+    idx0 = score_topk(q, cache, cfg.top_k)
+    ks0, vs0 = gather_fp16(idx0, hk, hv)
+    o0 = decode_attn(q, cache, idx0, ks0, vs0)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    ks = torch.full_like(ks0, float("nan"))
+    vs = torch.full_like(vs0, float("nan"))
+    idx = score_topk(q, cache, cfg.top_k)
+    ev = torch.cuda.Event()
+    ev.record()
+    side.wait_event(ev)
+    gather_fp16(idx, hk, hv, k_sel=ks, v_sel=vs, stream=side)
+    ev2 = torch.cuda.Event()
+    ev2.record(side)
+    torch.cuda.current_stream().wait_event(ev2)
+    o1 = decode_attn(q, cache, idx, ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx0)
+    assert torch.equal(o1.view(torch.int16), o0.view(torch.int16))
