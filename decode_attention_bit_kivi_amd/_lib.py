@@ -1,6 +1,7 @@
 """ctypes loader for libspecache.so (the C ABI in include/specache.h).
 
-The library is built in-tree by `python -m decode_attention_bit_kivi_amd.build`.
+The library is built in-tree by `python -m decode_attention_bit_kivi_amd.build`
+(SPECACHE_LIB may point at another build of the same library).
 There is no fallback: if the shared object is missing or does not load, every
 call raises.
 """
@@ -10,7 +11,8 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecache.so")
+LIB_PATH = os.environ.get("SPECACHE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libspecache.so")
 
 ABI_VERSION = 1
 

@@ -46,7 +46,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct ScoreWs {
-  size_t logits, part_m, part_l, keys, total;
+  size_t logits, part_m, part_l, keys, hist, total;
 };
 
 ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
@@ -59,6 +59,8 @@ ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
   off += align256(sizeof(float) * (size_t)d.slices() * d.G * p.S);
   w.keys = off;
   off += align256(sizeof(float) * (size_t)d.slices() * d.N);
+  w.hist = off;
+  off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
   w.total = off;
   return w;
 }
@@ -160,12 +162,13 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
   float* part_m = reinterpret_cast<float*>(base + ws.part_m);
   float* part_l = reinterpret_cast<float*>(base + ws.part_l);
   float* keys = rank_key_out ? rank_key_out : reinterpret_cast<float*>(base + ws.keys);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + ws.hist);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_score(d, plan, static_cast<const _Float16*>(q16), n_tokens, rank_row,
                               static_cast<const uint32_t*>(cache->k_codes), static_cast<const _Float16*>(cache->k_meta),
-                              sm_scale, logits, part_m, part_l, s);
+                              sm_scale, logits, part_m, part_l, hist, s);
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
-  e = launch_rank_select(d, plan, logits, part_m, part_l, k, keys, idx_out, s);
+  e = launch_rank_select(d, plan, logits, part_m, part_l, k, keys, hist, idx_out, s);
   return hip_status(e);
 }
 
@@ -189,7 +192,7 @@ size_t specache_decode_attn_workspace_size(const specache_shape* shape, int n_to
   Dims d;
   int err;
   if (!make_dims(shape, &d, &err) || n_tokens < 1 || n_tokens > 2 || k < 0 || k > d.N || tail_len < 0 ||
-      tail_len > kMaxTail || d.G * n_tokens > kMaxRows)
+      tail_len > kMaxTail || d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen)
     return 0;
   return attn_ws(d, attn_plan(d, k, tail_len), n_tokens).total;
 }
@@ -204,7 +207,7 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
   if (n_tokens < 1 || n_tokens > 2 || k < 0 || k > d.N || tail_len < 0 || tail_len > kMaxTail || !q16 ||
       !lowbit_ok(cache) || !out16 || !(sm_scale > 0.0f) || sm_scale == INFINITY)
     return SPECACHE_ERR_INVALID;
-  if (d.G * n_tokens > kMaxRows) return SPECACHE_ERR_UNSUPPORTED;
+  if (d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen) return SPECACHE_ERR_UNSUPPORTED;
   if (k > 0 && (!idx || !k_sel || !v_sel)) return SPECACHE_ERR_INVALID;
   if (tail_len > 0 && (!k_tail || !v_tail)) return SPECACHE_ERR_INVALID;
   const AttnPlan plan = attn_plan(d, k, tail_len);

@@ -9,6 +9,7 @@ namespace specache {
 constexpr int kGroup = 32;        // quantization group (tokens for keys, channels for values)
 constexpr int kMaxRows = 16;      // G * T query rows per KV head handled by one workgroup
 constexpr int kMaxTail = 64;
+constexpr int64_t kMaxAttnSeqLen = int64_t(4096) * 1024;  // 1024 splits of at most 4096 positions
 
 // Problem dimensions after validation.
 struct Dims {
@@ -45,27 +46,20 @@ inline ScorePlan score_plan(const Dims& d) {
 }
 
 struct AttnPlan {
-  int64_t L;       // low-bit positions per split (multiple of 32)
-  int S_lb;        // low-bit splits
-  int Lsel;        // 16-bit rows per split
-  int S_sel;       // 16-bit row splits
-  int S_tail;      // 0 or 1
-  int S;           // total splits per slice
+  int64_t L;       // positions per split (multiple of 32, at most 4096)
+  int S;           // splits per slice; a split also handles the fetched rows of its
+                   // positions, and the last split handles the tail
 };
 
-inline AttnPlan attn_plan(const Dims& d, int k, int tail) {
-  const int64_t target = 2048;
+inline AttnPlan attn_plan(const Dims& d, int /*k*/, int /*tail*/) {
+  const int64_t target = 1024;  // workgroups to aim for
   int64_t L = ceil_div(d.N * d.slices(), target);
-  L = round_up(L, 32);
-  if (L < 64) L = 64;
-  if (L > 2048) L = 2048;
+  L = round_up(L, 128);
+  if (L < 128) L = 128;
+  if (L > 4096) L = 4096;
   AttnPlan p;
   p.L = L;
-  p.S_lb = (int)ceil_div(d.N, L);
-  p.Lsel = 64;
-  p.S_sel = (int)ceil_div(k, p.Lsel);
-  p.S_tail = tail > 0 ? 1 : 0;
-  p.S = p.S_lb + p.S_sel + p.S_tail;
+  p.S = (int)ceil_div(d.N, L);
   return p;
 }
 
@@ -74,12 +68,13 @@ inline AttnPlan attn_plan(const Dims& d, int k, int tail) {
 hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v16, uint32_t* k_codes,
                            _Float16* k_meta, uint32_t* v_codes, _Float16* v_meta, hipStream_t s);
 
+// Also zeroes `hist` ([slices][2048]) for the rank kernels that follow on the same stream.
 hipError_t launch_score(const Dims& d, const ScorePlan& plan, const _Float16* q16, int n_tokens,
                         int rank_row, const uint32_t* k_codes, const _Float16* k_meta, float sm_scale,
-                        float* logits, float* part_m, float* part_l, hipStream_t s);
+                        float* logits, float* part_m, float* part_l, uint32_t* hist, hipStream_t s);
 
 hipError_t launch_rank_select(const Dims& d, const ScorePlan& plan, const float* logits,
-                              const float* part_m, const float* part_l, int k, float* keys,
+                              const float* part_m, const float* part_l, int k, float* keys, uint32_t* hist,
                               int32_t* idx_out, hipStream_t s);
 
 hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,

@@ -6,14 +6,26 @@
 // layers' compute (quick read, second mechanism).
 //
 // The source is pinned host memory read directly by the kernel (zero copy
-// over the host link) or device memory.  D*2/16 lanes per row, one 16-byte
-// load per lane, consecutive lanes on consecutive bytes of a row; 256
-// threads move 256*16 bytes of K and as much of V per round.
+// over the host link) or device memory.  The copy is bound by the host link,
+// not by the GPU, so the kernel runs on a small fixed grid (kGatherBlocks
+// workgroups) that leaves almost every CU to the compute stream it overlaps
+// with; each thread keeps kUnroll 16-byte host reads in flight to cover the
+// link's latency.  D*2/16 lanes cover one row, consecutive lanes on
+// consecutive bytes.
 #include "common.h"
 
 namespace specache {
 
 namespace {
+
+#ifndef SPECACHE_GATHER_BLOCKS
+#define SPECACHE_GATHER_BLOCKS 32
+#endif
+#ifndef SPECACHE_GATHER_UNROLL
+#define SPECACHE_GATHER_UNROLL 1
+#endif
+constexpr int kGatherBlocks = SPECACHE_GATHER_BLOCKS;
+constexpr int kUnroll = SPECACHE_GATHER_UNROLL;
 
 template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx, int k, int64_t N,
@@ -22,24 +34,37 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
                                                      uint4* __restrict__ k_sel, uint4* __restrict__ v_sel,
                                                      int64_t total_rows) {
   constexpr int kLanesPerRow = D * 2 / 16;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  constexpr int kRowsPerPass = 256 / kLanesPerRow;
   const int part = threadIdx.x % kLanesPerRow;
-  if (row >= total_rows) return;
-  const int64_t slice = row / k;
-  const int32_t p = idx[row];
-  uint4 kv, vv;
-  if (p >= 0 && p < N) {
-    const int64_t src = (slice * N + p) * kLanesPerRow + part;
-    kv = k_src[src];
-    vv = v_src[src];
-  } else {
-    const uint32_t nan2 = 0x7e007e00u;  // two float16 quiet NaNs
-    kv = make_uint4(nan2, nan2, nan2, nan2);
-    vv = kv;
+  const int64_t stride = (int64_t)gridDim.x * kRowsPerPass;
+  const uint32_t nan2 = 0x7e007e00u;  // two float16 quiet NaNs
+  for (int64_t base = (int64_t)blockIdx.x * kRowsPerPass + threadIdx.x / kLanesPerRow; base < total_rows;
+       base += stride * kUnroll) {
+    uint4 kv[kUnroll], vv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = base + u * stride;
+      kv[u] = make_uint4(nan2, nan2, nan2, nan2);
+      vv[u] = kv[u];
+      if (row < total_rows) {
+        const int64_t slice = row / k;
+        const int32_t p = idx[row];
+        if (p >= 0 && p < N) {
+          const int64_t src = (slice * N + p) * kLanesPerRow + part;
+          kv[u] = k_src[src];
+          vv[u] = v_src[src];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t row = base + u * stride;
+      if (row < total_rows) {
+        k_sel[row * kLanesPerRow + part] = kv[u];
+        v_sel[row * kLanesPerRow + part] = vv[u];
+      }
+    }
   }
-  k_sel[row * kLanesPerRow + part] = kv;
-  v_sel[row * kLanesPerRow + part] = vv;
 }
 
 }  // namespace
@@ -48,9 +73,9 @@ hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float1
                          const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, hipStream_t s) {
   const int64_t rows = d.slices() * k;
   if (rows == 0) return hipSuccess;
-  const int lanes = d.D * 2 / 16;
-  const int rows_per_block = 256 / lanes;
-  const unsigned grid = (unsigned)ceil_div(rows, rows_per_block);
+  const int rows_per_pass = 256 / (d.D * 2 / 16);
+  const int64_t need = ceil_div(rows, rows_per_pass);
+  const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
   if (d.D == 128)
     gather_kernel<128><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
                                             reinterpret_cast<const uint4*>(v_src), reinterpret_cast<uint4*>(k_sel),

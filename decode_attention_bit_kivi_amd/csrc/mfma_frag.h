@@ -1,0 +1,90 @@
+// MFMA fragments for gfx950's v_mfma_f32_16x16x32_f16 and the bit-to-operand
+// expansion shared by the score and attention kernels.
+//
+// Operand layout of the 16x16x32 instruction (wave64): lane l holds 8 float16
+// of A for row l % 16 and 8 float16 of B for column l % 16, both in k-group
+// l / 16; A's slot j in a k-group multiplies B's slot j of the same k-group.
+// The 16x16 float32 result puts element (m, n) in lane n + 16 * (m / 4),
+// register m % 4.
+//
+// A 1-bit code b of an element with scale s contributes s * (2b - 1) / 2
+// around the group's midpoint, so the operand value is +-s: the code bit
+// becomes the float16 sign bit of s (a set bit gives -s, so the operand is
+// -(2b - 1) s and the kernels scale its products by -1/2).  The packed layout keeps the two
+// elements of an operand dword 16 bit positions apart, so one shift moves
+// both bits into the two sign positions and one and-or attaches the
+// magnitudes -- two VALU operations per two elements, and every product with
+// a float16 query element is exact in the float32 accumulator.
+#pragma once
+
+#include "common.h"
+
+namespace specache {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+union Frag {
+  half8_t h;
+  uint4 v;
+  uint32_t u[4];
+};
+
+__device__ __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.h, b.h, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// Elements whose bits sit at positions p and p + 16 of `word`, with
+// shift = 15 - p: returns the float16 pair (+-mag.lo, +-mag.hi).
+__device__ __forceinline__ uint32_t signed_pair(uint32_t word, int shift, uint32_t mag) {
+  return ((word << shift) & 0x80008000u) | mag;
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int NW>
+struct Words {
+  uint32_t w[NW];
+};
+
+// NW consecutive 32-bit words from a 4*NW-byte aligned address.
+template <int NW>
+__device__ __forceinline__ Words<NW> load_words(const uint32_t* p) {
+  Words<NW> r;
+  if constexpr (NW == 8) {
+    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  } else if constexpr (NW == 4) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  } else if constexpr (NW == 2) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = a.x; r.w[1] = a.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) r.w[i] = p[i];
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint2 load_u2(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint4 load_u4(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Reductions over the four k-groups of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace specache

@@ -1,155 +1,240 @@
-// Low-bit scoring for the speculative ranking: logits of the rank row's G
+// Low-bit scoring for the speculative ranking: the logits of the rank row's G
 // query heads against the dequantized keys of C', plus per-split softmax
-// statistics (running max and sum of exponentials) per head.
+// statistics per head.
 //
 // SpeCache summary, quick read (second mechanism) and §3 "prefetch and offload
 // during decoding": the speculative token's attention over the low-bit copy
 // decides which 16-bit pairs to fetch.
 //
-// Within a 32-token key block the zero-point and scale are per channel, so
-//   q . Khat(p) = sum_c q_c z_c + sum_c (q_c s_c) code(p, c):
-// the first sum is one number per (block, head) and the second is a dot
-// product of a per-block table a_c = q_c s_c with the codes.
+// Within a 32-token key block the zero-point z and scale s are per channel:
+//   q . Khat(p) = sum_c q_c (z_c + h s_c) - (1/2) sum_c q_c (-(2b - 1) s_c)   (1 bit, h = 1/2)
+// The first sum is one number per (block, head) and comes from a small MFMA
+// prepass (zero-points and scales of 16 blocks against the queries); the
+// second is a matrix product of the expanded codes (mfma_frag.h) with the
+// float16 queries on the matrix cores.  Every product is exact, so the
+// logits carry only float32 accumulation error (the ranking tie band is 1e-5).
+// Two bits: h = 3/2 and plane 1 enters with weight 1.
 //
-// Layout: grid (splits, slices), 128 threads; a split is L positions (a
-// multiple of 128) walked in rounds of 128 positions = 4 key blocks, one
-// position per thread.
-#include "common.h"
+// Layout: grid (splits, slices), 256 threads = 4 waves; a wave owns every
+// 4th 32-position block of its split.  With at most 8 heads the two 16-token
+// tiles of a block share one accumulator (heads in columns 0-7 for tile 0,
+// 8-15 for tile 1).  Logits go to [slice][head][position] as float32; the
+// per-split statistics are (max, sum of 2^(x - max)) in log2 units.
+#include "mfma_frag.h"
 
 namespace specache {
 
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(128) void score_kernel(const _Float16* __restrict__ q16, int T, int rank_row,
-                                                    const uint32_t* __restrict__ k_codes,
-                                                    const _Float16* __restrict__ k_meta, int64_t N,
-                                                    int bits, int G, int Hkv, float sm_scale, int64_t L,
-                                                    int S, float* __restrict__ logits,
-                                                    float* __restrict__ part_m, float* __restrict__ part_l) {
-  constexpr int W = D / 32;
-  __shared__ float qs[kMaxRows][D];
-  __shared__ float zs[4][2][D];
-  __shared__ float atab[4][D][kMaxRows];
-  __shared__ float ctab[4][kMaxRows];
-  __shared__ float red_m[2][kMaxRows];
-  __shared__ float red_l[2][kMaxRows];
+constexpr float kLog2e = 1.4426950408889634f;
 
-  const int t = threadIdx.x;
+template <int D, int BITS, int PACK>
+__global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restrict__ q16, int T, int rank_row,
+                                                       const uint32_t* __restrict__ k_codes,
+                                                       const _Float16* __restrict__ k_meta, int64_t N, int G,
+                                                       int Hkv, float sm_scale, int64_t L, int S,
+                                                       float* __restrict__ logits, float* __restrict__ part_m,
+                                                       float* __restrict__ part_l, uint32_t* __restrict__ hist) {
+  constexpr int W = D / 32;
+  constexpr float hK = BITS == 1 ? 0.5f : 1.5f;
+  constexpr int NX = PACK == 2 ? 4 : 8;
+  __shared__ float cst[4][16][16];
+  __shared__ float red_m[4][16], red_l[4][16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
   const int64_t slice = blockIdx.y;
   const int64_t b = slice / Hkv, h = slice % Hkv;
-  const int64_t nblk = N / 32;
   const int Hq = Hkv * G;
+  const int64_t nblk = N / 32;
+  const int64_t p0 = (int64_t)split * L;
+  const int64_t p1 = p0 + L < N ? p0 + L : N;
+  const int nb = (int)((p1 - p0) / 32);
+  const int64_t blk0 = p0 / 32;
+  if (split == 0)  // the rank kernels accumulate a per-slice histogram here
+    for (int i = tid; i < 2048; i += 256) hist[slice * 2048 + i] = 0u;
 
-  for (int e = t; e < G * D; e += 128) {
-    const int g = e / D, c = e % D;
-    qs[g][c] = (float)q16[((b * Hq + h * G + g) * T + rank_row) * D + c];
+  // query fragments of the rank row: B[k-slot (g, j)][column] = q[head][32w + 8g + j]
+  Frag B0[W], B1[W];
+  {
+    const int r0 = PACK == 2 ? (n16 < 8 ? n16 : -1) : n16;
+    const int r1 = PACK == 2 ? (n16 >= 8 ? n16 - 8 : -1) : -1;
+    const int ra = r0 >= 0 && r0 < G ? r0 : 0, rb = r1 >= 0 && r1 < G ? r1 : 0;
+    const _Float16* qa = q16 + ((b * Hq + h * G + ra) * T + rank_row) * D;
+    const _Float16* qb = q16 + ((b * Hq + h * G + rb) * T + rank_row) * D;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const uint4 va = load_u4(qa + 32 * w + 8 * g), vb = load_u4(qb + 32 * w + 8 * g);
+      B0[w].v = (r0 >= 0 && r0 < G) ? va : make_uint4(0, 0, 0, 0);
+      B1[w].v = (r1 >= 0 && r1 < G) ? vb : make_uint4(0, 0, 0, 0);
+    }
   }
 
-  float m_run[kMaxRows], l_run[kMaxRows];
+  struct BlockData {
+    Words<W> kw[2][BITS];
+    uint4 ks[W];
+  };
+  auto load_block = [&](int jj) {
+    BlockData bd;
+    const int64_t blk = blk0 + jj;
+    const uint32_t* kc = k_codes + (slice * N + blk * 32) * BITS * W;
 #pragma unroll
-  for (int g = 0; g < kMaxRows; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.0f;
-  }
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int pl = 0; pl < BITS; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * BITS + pl) * W);
+    const _Float16* kms = k_meta + ((slice * nblk + blk) * 2 + 1) * D;
+#pragma unroll
+    for (int w = 0; w < W; ++w) bd.ks[w] = load_u4(kms + 32 * w + 8 * g);
+    return bd;
+  };
 
-  const int64_t p_begin = (int64_t)split * L;
-  const int64_t p_end = p_begin + L < N ? p_begin + L : N;
-  for (int64_t p0 = p_begin; p0 < p_end; p0 += 128) {
-    const int nb = (int)((p_end - p0) / 32 < 4 ? (p_end - p0) / 32 : 4);
-    const int64_t blk0 = p0 / 32;
-    __syncthreads();  // previous round's tables are no longer read
-    for (int e = t; e < nb * 2 * D; e += 128)
-      zs[e / (2 * D)][(e / D) & 1][e % D] = (float)k_meta[(slice * nblk + blk0) * 2 * D + e];
-    __syncthreads();
-    for (int e = t; e < nb * D * G; e += 128) {
-      const int bb = e / (D * G), r = e % (D * G);
-      const int cp = r / G, g = r % G;
-      const int c = 32 * (cp / 32) + bit_to_elem(cp % 32);
-      atab[bb][cp][g] = qs[g][c] * zs[bb][1][c];
-    }
-    for (int pr = t; pr < nb * G; pr += 128) {
-      const int bb = pr / G, g = pr % G;
-      float acc = 0.0f;
-      for (int c = 0; c < D; ++c) acc = fmaf(qs[g][c], zs[bb][0][c], acc);
-      ctab[bb][g] = acc;
-    }
-    __syncthreads();
+  float m2 = -INFINITY, l2 = 0.0f;   // this lane's running (max, sum 2^(x - max)) in log2 units
+  const int head = PACK == 2 ? (n16 & 7) : n16;
+  const bool writer = head < G;
 
-    const int64_t p = p0 + t;
-    if (p < p_end) {
-      const int bb = t / 32;
-      uint32_t wd[2][W];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int w = 0; w < W; ++w) wd[j][w] = (j < bits) ? k_codes[((slice * N + p) * bits + j) * W + w] : 0u;
-      float acc[kMaxRows];
-#pragma unroll
-      for (int g = 0; g < kMaxRows; ++g) acc[g] = 0.0f;
+  BlockData cur;
+  if (wave < nb) cur = load_block(wave);
+  for (int jj = wave; jj < nb; jj += 4) {
+    const int step = (jj - wave) >> 2;
+    const bool prepass = (step & 15) == 0;
+    Frag az[W], as[W];
+    if (prepass) {
+      const int bi = jj + 4 * n16;
+      const _Float16* km = k_meta + (slice * nblk + blk0 + (bi < nb ? bi : jj)) * 2 * D;
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        for (int i = 0; i < 32; ++i) {
-          const float cf = (float)(((wd[0][w] >> i) & 1u) + 2u * ((wd[1][w] >> i) & 1u));
-          const float* a = &atab[bb][32 * w + i][0];
+        az[w].v = load_u4(km + 32 * w + 8 * g);
+        as[w].v = load_u4(km + D + 32 * w + 8 * g);
+      }
+    }
+    const BlockData nxt = load_block(jj + 4 < nb ? jj + 4 : jj);
+    if (prepass) {
+      f32x4 accZ = zero4(), accS = zero4();
 #pragma unroll
-          for (int g = 0; g < kMaxRows; ++g)
-            if (g < G) acc[g] = fmaf(cf, a[g], acc[g]);
-        }
+      for (int w = 0; w < W; ++w) {
+        accZ = mma(az[w], B0[w], accZ);
+        accS = mma(as[w], B0[w], accS);
       }
 #pragma unroll
-      for (int g = 0; g < kMaxRows; ++g) {
-        if (g < G) {
-          const float x = sm_scale * (ctab[bb][g] + acc[g]);
-          logits[(slice * G + g) * N + p] = x;
-          const float mn = fmaxf(m_run[g], x);
-          l_run[g] = l_run[g] * __expf(m_run[g] - mn) + __expf(x - mn);
-          m_run[g] = mn;
+      for (int i = 0; i < 4; ++i) cst[wave][4 * g + i][n16] = accZ[i] + hK * accS[i];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+
+    f32x4 acc[2][BITS];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int pl = 0; pl < BITS; ++pl) acc[tau][pl] = zero4();
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const uint32_t* mag = reinterpret_cast<const uint32_t*>(&cur.ks[w]);
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+        for (int pl = 0; pl < BITS; ++pl) {
+          Frag A;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(cur.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
+          if constexpr (PACK == 2)
+            acc[0][pl] = mma(A, tau == 0 ? B0[w] : B1[w], acc[0][pl]);
+          else
+            acc[tau][pl] = mma(A, B0[w], acc[tau][pl]);
         }
       }
     }
+    const float c0 = cst[wave][step & 15][head];
+    float x[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int tau = PACK == 2 ? 0 : i / 4;
+      const float s = BITS == 1 ? -0.5f * acc[tau][0][i & 3] : -0.5f * acc[tau][0][i & 3] - acc[tau][BITS - 1][i & 3];
+      x[i] = sm_scale * (c0 + s);
+    }
+    const int64_t pos = (blk0 + jj) * 32;
+    if (writer) {
+      float* dst = logits + (slice * G + head) * N + pos;
+      if constexpr (PACK == 2) {
+        *reinterpret_cast<float4*>(dst + 16 * (n16 >> 3) + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+      } else {
+        *reinterpret_cast<float4*>(dst + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(dst + 16 + 4 * g) = make_float4(x[4], x[5], x[6], x[7]);
+      }
+    }
+    float bm = x[0];
+#pragma unroll
+    for (int i = 1; i < NX; ++i) bm = fmaxf(bm, x[i]);
+    const float mn = fmaxf(m2, bm * kLog2e);
+    float add = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) add += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mn));
+    l2 = l2 * __builtin_amdgcn_exp2f(m2 - mn) + add;
+    m2 = mn;
+    cur = nxt;
   }
 
-  // Reduce (m, l) per head over the 128 threads: within each wave, then across the two waves.
-  const int lane = t & 63, wv = t >> 6;
-#pragma unroll
-  for (int g = 0; g < kMaxRows; ++g) {
-    float m = m_run[g], l = l_run[g];
-    for (int off = 32; off > 0; off >>= 1) {
-      const float mo = __shfl_xor(m, off);
-      const float lo = __shfl_xor(l, off);
-      const float mn = fmaxf(m, mo);
-      l = (mn == -INFINITY) ? 0.0f : l * __expf(m - mn) + lo * __expf(mo - mn);
-      m = mn;
+  // per head: combine the lanes of the head (k-groups and, with PACK == 2, both tiles), then the waves
+  auto combine = [](float& m, float& l, float mo, float lo) {
+    const float mn = fmaxf(m, mo);
+    l = (mn == -INFINITY) ? 0.0f : l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+    m = mn;
+  };
+  {
+    float mo = __shfl_xor(m2, 16), lo = __shfl_xor(l2, 16);
+    combine(m2, l2, mo, lo);
+    mo = __shfl_xor(m2, 32);
+    lo = __shfl_xor(l2, 32);
+    combine(m2, l2, mo, lo);
+    if constexpr (PACK == 2) {
+      mo = __shfl_xor(m2, 8);
+      lo = __shfl_xor(l2, 8);
+      combine(m2, l2, mo, lo);
     }
-    if (lane == 0) {
-      red_m[wv][g] = m;
-      red_l[wv][g] = l;
-    }
+  }
+  if (lane < 16) {
+    red_m[wave][lane] = m2;
+    red_l[wave][lane] = l2;
   }
   __syncthreads();
-  if (t < G) {
-    const float m0 = red_m[0][t], m1 = red_m[1][t];
-    const float mn = fmaxf(m0, m1);
-    const float l = (mn == -INFINITY) ? 0.0f : red_l[0][t] * __expf(m0 - mn) + red_l[1][t] * __expf(m1 - mn);
-    part_m[(slice * G + t) * S + split] = mn;
-    part_l[(slice * G + t) * S + split] = l;
+  if (tid < G) {
+    float m = red_m[0][tid], l = red_l[0][tid];
+#pragma unroll
+    for (int w4 = 1; w4 < 4; ++w4) combine(m, l, red_m[w4][tid], red_l[w4][tid]);
+    part_m[(slice * G + tid) * S + split] = m;
+    part_l[(slice * G + tid) * S + split] = l;
   }
+}
+
+template <int D, int BITS>
+void launch_score_t(const Dims& d, const ScorePlan& plan, const _Float16* q16, int n_tokens, int rank_row,
+                    const uint32_t* k_codes, const _Float16* k_meta, float sm_scale, float* logits, float* part_m,
+                    float* part_l, uint32_t* hist, hipStream_t s) {
+  const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
+  if (d.G <= 8)
+    score_kernel<D, BITS, 2><<<grid, 256, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.G, d.Hkv,
+                                                  sm_scale, plan.L, plan.S, logits, part_m, part_l, hist);
+  else
+    score_kernel<D, BITS, 1><<<grid, 256, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.G, d.Hkv,
+                                                  sm_scale, plan.L, plan.S, logits, part_m, part_l, hist);
 }
 
 }  // namespace
 
 hipError_t launch_score(const Dims& d, const ScorePlan& plan, const _Float16* q16, int n_tokens,
                         int rank_row, const uint32_t* k_codes, const _Float16* k_meta, float sm_scale,
-                        float* logits, float* part_m, float* part_l, hipStream_t s) {
-  const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
-  if (d.D == 128)
-    score_kernel<128><<<grid, 128, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.bits, d.G, d.Hkv,
-                                           sm_scale, plan.L, plan.S, logits, part_m, part_l);
-  else
-    score_kernel<64><<<grid, 128, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.bits, d.G, d.Hkv,
-                                          sm_scale, plan.L, plan.S, logits, part_m, part_l);
+                        float* logits, float* part_m, float* part_l, uint32_t* hist, hipStream_t s) {
+  if (d.D == 128) {
+    if (d.bits == 1)
+      launch_score_t<128, 1>(d, plan, q16, n_tokens, rank_row, k_codes, k_meta, sm_scale, logits, part_m, part_l, hist, s);
+    else
+      launch_score_t<128, 2>(d, plan, q16, n_tokens, rank_row, k_codes, k_meta, sm_scale, logits, part_m, part_l, hist, s);
+  } else {
+    if (d.bits == 1)
+      launch_score_t<64, 1>(d, plan, q16, n_tokens, rank_row, k_codes, k_meta, sm_scale, logits, part_m, part_l, hist, s);
+    else
+      launch_score_t<64, 2>(d, plan, q16, n_tokens, rank_row, k_codes, k_meta, sm_scale, logits, part_m, part_l, hist, s);
+  }
   return hipGetLastError();
 }
 

@@ -194,6 +194,7 @@ int specache_gather_fp16(const specache_shape* shape, const int32_t* idx, int k,
  * softmax of Algorithm 3: the real token does not see the speculative
  * token's entry).  Logits are sm_scale * q . k.  out16 [B][Hq][T][D] float16.
  *
+ * N <= 4194304 (SPECACHE_ERR_UNSUPPORTED above);
  * 0 <= k <= N (k = 0: pure low-bit attention; idx, k_sel, v_sel may be NULL);
  * idx must be strictly ascending within [0, N) per slice (not checked on the
  * device); 0 <= tail_len <= 64 (k_tail / v_tail may be NULL when 0).
