@@ -1,17 +1,23 @@
 """Decode-step benchmark of libspecache on one MI355X.
 
-One step = one pass of the decode hot path over one batch of one layer:
-  score_topk  (speculative row vs the low-bit copy C' -> top-k set for the next step)
-  gather_fp16 (that set's 16-bit K/V rows from pinned host memory, on a side stream,
-               double-buffered so it overlaps the following compute)
-  decode_attn (both query rows over C' with the previous step's fetched rows substituted)
-The prefill quantizer (quantize_pack) is timed separately, once per run.
+One step = one layer's pass of the decode hot path over one batch:
+  decode_step (both query rows over C' with this layer's fetched 16-bit rows
+               substituted, and, from the same pass, the speculative row's
+               ranking and top-k selection for the layer's next step)
+  gather_fp16 (that selection's 16-bit K/V rows from pinned host memory, on a
+               side stream limited to a few compute units)
+as in the multi-layer decode loop: several layers, each with its own low-bit
+cache C', selection and fetched rows, run in turn, and a layer's gather
+overlaps the other layers' compute until the layer comes round again.  The
+layers' C' copies together exceed the 256 MB last-level cache, so every step
+reads its C' from HBM.  The layers share one pinned host copy of the 16-bit
+cache (every gather still crosses the host link).  The prefill quantizer
+(quantize_pack) is timed separately, once per run.
 
 Inputs are resident in HBM (C', queries) and pinned host memory (the 16-bit
-cache) before the timed region starts.  Several copies of C' are rotated
-between steps so that the 256 MB last-level cache does not hold them.
+cache) before the timed region starts.
 
-Prints one JSON line (see the README/DESIGN notes for the fields).
+Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload mistral32k] [--no-cpu-baseline]
 """
@@ -30,28 +36,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_attn_mistral32k_traffic.json")
-ATTN_SOURCES = ("attention.hip", "mfma_frag.h", "common.h")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_step_mistral32k_traffic.json")
+STEP_SOURCES = ("attention.hip", "rank.hip", "mfma_frag.h", "common.h")
 
 
-def attn_sources_hash() -> str:
+def step_sources_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in ATTN_SOURCES:
+    for name in STEP_SOURCES:
         with open(os.path.join(ROOT, "decode_attention_bit_kivi_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per decode_attn launch from the committed counter record, or None when
+    """HBM bytes per decode_step call from the committed counter record, or None when
     the record is missing, is for another workload, or predates the current kernel sources."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("sources_sha256") != attn_sources_hash():
+    if rec.get("workload") != workload or rec.get("sources_sha256") != step_sources_hash():
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -62,9 +68,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mistral32k")
-    ap.add_argument("--copies", type=int, default=0, help="C' copies rotated (0: enough for >= 512 MB)")
+    ap.add_argument("--copies", type=int, default=0, help="layers (C' copies) in turn (0: enough for >= 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle sample")
+    ap.add_argument("--gather-cus", type=int, default=8, help="compute units of the gather stream")
+    ap.add_argument("--compute-stream", choices=("exclusive", "shared"), default="exclusive",
+                    help="exclusive: the compute runs on the compute units the gather stream does not use")
+    ap.add_argument("--compute-reserve", type=int, default=32,
+                    help="with an exclusive compute stream: the low compute units kept from it (the "
+                         "gather's among them); 32 leaves every shader engine the same number of units")
     ap.add_argument("--mode", choices=("step", "copy"), default="step",
                     help="copy: a plain 1 GiB device-to-device copy, the reference for scaling the "
                          "profiler's HBM byte counters")
@@ -90,20 +102,16 @@ def copy_reference(reps: int = 5):
                       "GBs": 2 * n / (us * 1e-6) / 1e9}), flush=True)
 
 
-def algorithmic_bytes_attn(cfg) -> int:
-    """Bytes decode_attn must move per launch: C' (64 B per position per KV head
-    at 1 bit, 96 B at 2 bits, D = 128), the k fetched 16-bit K and V rows, Q and O."""
+def algorithmic_bytes_step(cfg) -> int:
+    """Bytes one decode_step call must move: C' (keys and values: codes plus float16
+    zero-points and scales, 64 B per position per KV head at 1 bit and D = 128, 96 B at
+    2 bits), the k fetched 16-bit K and V rows and their indices, the next selection,
+    the queries and the output."""
     per_pos = 2 * (cfg.bits * cfg.head_dim // 8 + 4 * cfg.head_dim // 32)
     slices = cfg.batch * cfg.n_kv_heads
     rows = cfg.batch * cfg.n_q_heads * cfg.n_tokens
-    return slices * (per_pos * cfg.seq_len + 2 * 2 * cfg.head_dim * cfg.top_k) + 2 * rows * cfg.head_dim * 2
-
-
-def algorithmic_bytes_score(cfg) -> int:
-    """Bytes score_topk must move per launch: the keys of C', the rank row, the top-k indices."""
-    per_pos = cfg.bits * cfg.head_dim // 8 + 4 * cfg.head_dim // 32
-    slices = cfg.batch * cfg.n_kv_heads
-    return slices * (per_pos * cfg.seq_len + 4 * cfg.top_k) + cfg.batch * cfg.n_q_heads * cfg.head_dim * 2
+    per_slice = per_pos * cfg.seq_len + (2 * 2 * cfg.head_dim + 4) * cfg.top_k + 4 * cfg.top_k
+    return slices * per_slice + 2 * rows * cfg.head_dim * 2
 
 
 def cpu_baseline(cfg, K, V, Q, budget_s: float):
@@ -119,26 +127,29 @@ def cpu_baseline(cfg, K, V, Q, budget_s: float):
     slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads)]
     rng = np.random.default_rng(0)
     order = [slices[i] for i in rng.permutation(len(slices))]
-    spent, done = 0.0, 0
-    for (b, h) in order:
-        k1, v1 = K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1]
-        q = Q[b:b + 1, h * G:(h + 1) * G]
-        kc, kz, ks = oracle.quantize_keys(k1, cfg.bits)         # prefill: not timed
-        vc, vz, vs = oracle.quantize_values(v1, cfg.bits)
-        kh, vh = oracle.dequantize_keys(kc, kz, ks), oracle.dequantize_values(vc, vz, vs)
-        t0 = time.perf_counter()
-        idx, _ = oracle.score_topk(q, kh, 1, cfg.sm_scale, cfg.top_k)
-        sk, sv = oracle.gather_rows(k1, v1, idx)
-        oracle.mixed_attention(q, kh, vh, idx, sk, sv, sm_scale=cfg.sm_scale)
-        spent += time.perf_counter() - t0
-        done += 1
-        if spent >= budget_s:
-            break
+    spent, done, passes = 0.0, 0, 0
+    while spent < budget_s and passes < 50:   # cycle over the slices until the budget is spent
+        for (b, h) in order:
+            k1, v1 = K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1]
+            q = Q[b:b + 1, h * G:(h + 1) * G]
+            kc, kz, ks = oracle.quantize_keys(k1, cfg.bits)         # prefill: not timed
+            vc, vz, vs = oracle.quantize_values(v1, cfg.bits)
+            kh, vh = oracle.dequantize_keys(kc, kz, ks), oracle.dequantize_values(vc, vz, vs)
+            t0 = time.perf_counter()
+            idx, _ = oracle.score_topk(q, kh, 1, cfg.sm_scale, cfg.top_k)
+            sk, sv = oracle.gather_rows(k1, v1, idx)
+            oracle.mixed_attention(q, kh, vh, idx, sk, sv, sm_scale=cfg.sm_scale)
+            spent += time.perf_counter() - t0
+            done += 1
+            if spent >= budget_s:
+                break
+        passes += 1
     per_slice = spent / done
     step_s = per_slice * len(slices)
     return {"value": cfg.batch / step_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(slices)} (batch, KV head) slices of one decode step "
-                      f"({spent:.1f} s), scaled to the whole step; prefill quantization excluded",
+            "sample": f"{done} (batch, KV head) slice-steps ({passes} pass(es) over the {len(slices)} slices "
+                      f"of one layer's decode step, {spent:.1f} s of oracle time), scaled to the whole step; "
+                      f"prefill quantization excluded",
             "seconds_per_step": step_s}
 
 
@@ -154,8 +165,9 @@ def main():
 
     import torch
     from decode_attention_bit_kivi_amd import (
-        quantize_pack, score_topk, gather_fp16, decode_attn, empty_cache,
-        score_topk_workspace_size, decode_attn_workspace_size,
+        quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, empty_cache,
+        score_topk_workspace_size, decode_attn_workspace_size, decode_step_workspace_size, GatherStream,
+        ComputeStream,
     )
     from workloads import get_config, generate_all
 
@@ -164,8 +176,16 @@ def main():
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     K, V, Q, _, _, _ = generate_all(cfg)
     dev = torch.device("cuda:0")
-    comp = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    # compute on a non-default stream: the CU-limited gather stream is a blocking stream and
+    # would serialize with the legacy default stream
+    gather_stream = GatherStream(args.gather_cus)   # the prefetch runs on a few CUs only
+    side = gather_stream.torch
+    if args.compute_stream == "exclusive":
+        compute_stream = ComputeStream(max(args.compute_reserve, args.gather_cus))
+        comp = compute_stream.torch
+    else:
+        comp = torch.cuda.Stream()
+    torch.cuda.set_stream(comp)
 
     k16 = torch.from_numpy(K).to(dev)
     v16 = torch.from_numpy(V).to(dev)
@@ -186,55 +206,52 @@ def main():
     torch.cuda.synchronize()
     quant_us = e0.elapsed_time(e1) * 1e3 / nq
 
-    copies = args.copies or max(3, math.ceil(512e6 / cache0.nbytes()))
-    caches = [cache0] + [quantize_pack(k16, v16, cfg.bits) for _ in range(copies - 1)]
+    layers = args.copies or max(3, math.ceil(512e6 / cache0.nbytes()))
+    caches = [cache0] + [quantize_pack(k16, v16, cfg.bits) for _ in range(layers - 1)]
     del k16, v16
     torch.cuda.synchronize()
 
+    ws = torch.empty(decode_step_workspace_size(cache0, Hq, T, k, 0, k), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(score_topk_workspace_size(cache0, Hq, T, k), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(decode_attn_workspace_size(cache0, Hq, T, k), dtype=torch.uint8, device=dev)
-    idx_buf = [torch.zeros((B, Hkv, k), dtype=torch.int32, device=dev) for _ in range(2)]
-    for i in range(2):
-        idx_buf[i].copy_(torch.arange(k, dtype=torch.int32, device=dev).expand(B, Hkv, k))
-    sel = [(torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev),
-            torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)) for _ in range(2)]
     out = torch.empty_like(q)
-    gathered = [torch.cuda.Event() for _ in range(2)]
-    scored = torch.cuda.Event()
-    # step -1: fetch the initial set so the first step has rows to use
-    gather_fp16(idx_buf[0], hk, hv, cfg.bits, *sel[0])
-    gathered[0].record(comp)
+    # per layer: the selection (rewritten in place by each decode_step) and its fetched rows;
+    # the pre-decoding step seeds them
+    idx = [score_topk(q, c, k, rank_row=1, workspace=ws_s) for c in caches]
+    sel = [gather_fp16(idx[l], hk, hv, cfg.bits) for l in range(layers)]
+    gathered = [torch.cuda.Event() for _ in range(layers)]
+    stepped = [torch.cuda.Event() for _ in range(layers)]
+    for l in range(layers):
+        gathered[l].record(comp)
     torch.cuda.synchronize()
 
     def step(i, ev=None):
-        c = caches[i % copies]
-        cur, nxt = i % 2, (i + 1) % 2
-        if ev:
-            ev["s0"].record(comp)
-        score_topk(q, c, k, rank_row=1, idx_out=idx_buf[nxt], workspace=ws_s)
-        if ev:
-            ev["s1"].record(comp)
-        scored.record(comp)
-        side.wait_event(scored)
-        if ev:
-            ev["g0"].record(side)
-        gather_fp16(idx_buf[nxt], hk, hv, cfg.bits, *sel[nxt], stream=side)
-        if ev:
-            ev["g1"].record(side)
-        gathered[nxt].record(side)
-        comp.wait_event(gathered[cur])
-        if ev:
-            ev["a0"].record(comp)
-        decode_attn(q, c, idx_buf[cur], sel[cur][0], sel[cur][1], out=out, workspace=ws_a)
-        if ev:
-            ev["a1"].record(comp)
+        def mark(name, stream):
+            if ev and name in ev:
+                ev[name].record(stream)
 
+        l = i % layers
+        comp.wait_event(gathered[l])
+        mark("d0", comp)
+        decode_step(q, caches[l], k, rank_row=1, idx=idx[l], k_sel=sel[l][0], v_sel=sel[l][1], out=out,
+                    idx_next_out=idx[l], workspace=ws)
+        mark("d1", comp)
+        stepped[l].record(comp)
+        side.wait_event(stepped[l])
+        mark("g0", side)
+        gather_fp16(idx[l], hk, hv, cfg.bits, *sel[l], stream=side)
+        mark("g1", side)
+        gathered[l].record(side)
+
+    print(f"[bench] {args.warmup} warmup + {args.steps} timed steps over {layers} layers", file=sys.stderr,
+          flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [{n: torch.cuda.Event(enable_timing=True) for n in ("s0", "s1", "g0", "g1", "a0", "a1")}
-           for _ in range(args.steps)]
+    # timed region: timing events on the compute stream only (events on the gather stream
+    # lengthen its idle time between gathers); the gather's own duration is taken after it
+    evs = [{n: torch.cuda.Event(enable_timing=True) for n in ("d0", "d1")} for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -246,24 +263,39 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    score_us = np.array([e["s0"].elapsed_time(e["s1"]) for e in evs]) * 1e3
-    gather_us = np.array([e["g0"].elapsed_time(e["g1"]) for e in evs]) * 1e3
-    attn_us = np.array([e["a0"].elapsed_time(e["a1"]) for e in evs]) * 1e3
+    step_us = np.array([e["d0"].elapsed_time(e["d1"]) for e in evs]) * 1e3
 
-    # the same steps with the gather's result already resident: compute-only step time
-    t_start.record(comp)
-    for i in range(args.steps):
-        c = caches[i % copies]
-        score_topk(q, c, k, rank_row=1, idx_out=idx_buf[1], workspace=ws_s)
-        decode_attn(q, c, idx_buf[0], sel[0][0], sel[0][1], out=out, workspace=ws_a)
-    t_end.record(comp)
+    gevs = [{n: torch.cuda.Event(enable_timing=True) for n in ("g0", "g1")} for _ in range(min(args.steps, 20))]
+    for i, ev in enumerate(gevs):
+        step(args.warmup + args.steps + i, ev)
     torch.cuda.synchronize()
-    ms_compute = t_start.elapsed_time(t_end) / args.steps
+    gather_us = np.array([e["g0"].elapsed_time(e["g1"]) for e in gevs]) * 1e3
 
-    attn_bytes = algorithmic_bytes_attn(cfg)
-    attn_avg_s = float(attn_us.mean()) * 1e-6
-    achieved = attn_bytes / attn_avg_s / 1e9
-    score_bytes = algorithmic_bytes_score(cfg)
+    # compute only (the fetched rows already resident): the fused step, then the four-call
+    # form (score_topk + decode_attn) on the same inputs
+    def compute_loop(fn):
+        for i in range(3):
+            fn(i)
+        t_start.record(comp)
+        for i in range(args.steps):
+            fn(i)
+        t_end.record(comp)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps * 1e3
+
+    nxt = torch.empty_like(idx[0])
+    fused_us = compute_loop(lambda i: decode_step(
+        q, caches[i % layers], k, rank_row=1, idx=idx[i % layers], k_sel=sel[i % layers][0],
+        v_sel=sel[i % layers][1], out=out, idx_next_out=nxt, workspace=ws))
+    unfused_us = compute_loop(lambda i: (
+        score_topk(q, caches[i % layers], k, rank_row=1, idx_out=nxt, workspace=ws_s),
+        decode_attn(q, caches[i % layers], idx[i % layers], sel[i % layers][0], sel[i % layers][1], out=out,
+                    workspace=ws_a)))
+
+    step_bytes = algorithmic_bytes_step(cfg)
+    step_avg_s = float(step_us.mean()) * 1e-6
+    achieved = step_bytes / step_avg_s / 1e9
+    fused_bw = step_bytes / (fused_us * 1e-6) / 1e9
     gather_bytes = 2 * B * Hkv * k * D * 2
 
     result = {
@@ -280,36 +312,40 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: Mistral-7B-shaped single layer, batch {B}, {Hq} query / {Hkv} KV heads, "
+            "workload": f"{cfg.name}: Mistral-7B-shaped layer, batch {B}, {Hq} query / {Hkv} KV heads, "
                         f"head_dim {D}, context {N}, {T} query tokens, {cfg.bits}-bit K/V, group {cfg.group}, "
-                        f"top-k {k} per KV head gathered from pinned host memory",
+                        f"top-k {k} per KV head gathered from pinned host memory; {layers} layers in turn",
             "batch": B, "seq_len": N, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "bits": cfg.bits,
-            "top_k": k, "n_tokens": T, "cache_copies_rotated": copies,
+            "top_k": k, "n_tokens": T, "layers_rotated": layers, "gather_stream_cus": args.gather_cus,
+            "compute_stream": args.compute_stream,
+            "compute_stream_reserved_cus": max(args.compute_reserve, args.gather_cus)
+            if args.compute_stream == "exclusive" else 0,
         },
         "roofline": {
-            "kernel": "decode_attn (split-K attention + merge launches)",
+            "kernel": "decode_step (attn_split_kernel with ranking + rank_keys + rank_select + attn_merge)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": recorded_traffic(cfg.name),
-            "algorithmic_bytes_per_launch": attn_bytes,
+            "algorithmic_bytes_per_launch": step_bytes,
         },
         "latency_us": {
             "step": ms_step * 1e3,
-            "step_compute_only": ms_compute * 1e3,
-            "exposed_gather": max(0.0, (ms_step - ms_compute) * 1e3),
-            "score_topk": float(np.median(score_us)),
-            "decode_attn": float(np.median(attn_us)),
-            "decode_attn_mean": float(attn_us.mean()),
+            "decode_step_in_pipeline": float(np.median(step_us)),
+            "decode_step_in_pipeline_mean": float(step_us.mean()),
             "gather_fp16_side_stream": float(np.median(gather_us)),
+            "step_compute_only_fused": fused_us,
+            "step_compute_only_four_call": unfused_us,
+            "exposed_gather": max(0.0, ms_step * 1e3 - fused_us),
             "quantize_pack_prefill": quant_us,
         },
         "bandwidth_GBs": {
-            "decode_attn": achieved,
-            "score_topk": score_bytes / (float(np.median(score_us)) * 1e-6) / 1e9,
+            "decode_step_in_pipeline": achieved,
+            "decode_step_compute_only": fused_bw,
             "gather_host_link": gather_bytes / (float(np.median(gather_us)) * 1e-6) / 1e9,
+            "gather_host_link_whole_step": gather_bytes / (ms_step * 1e-3) / 1e9,
             "quantize_pack": (2 * B * Hkv * N * D * 2 + caches[0].nbytes()) / (quant_us * 1e-6) / 1e9,
         },
         "wall_s_timed": wall,

@@ -7,12 +7,14 @@ package is its thin Python binding.  Build the library with
 """
 from .api import (
     LowBitCache, empty_cache, lowbit_sizes, quantize_pack, score_topk, score_topk_workspace_size,
-    gather_fp16, decode_attn, decode_attn_workspace_size,
+    gather_fp16, decode_attn, decode_attn_workspace_size, decode_step, decode_step_workspace_size,
+    GatherStream, ComputeStream,
 )
 from ._lib import SpecacheError
 
 __all__ = [
     "LowBitCache", "empty_cache", "lowbit_sizes", "quantize_pack", "score_topk",
     "score_topk_workspace_size", "gather_fp16", "decode_attn", "decode_attn_workspace_size",
+    "decode_step", "decode_step_workspace_size", "GatherStream", "ComputeStream",
     "SpecacheError",
 ]

@@ -14,7 +14,7 @@ import threading
 LIB_PATH = os.environ.get("SPECACHE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libspecache.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 SPECACHE_OK = 0
 SPECACHE_ERR_INVALID = 1
@@ -31,6 +31,11 @@ EXPORTED = (
     "specache_gather_fp16",
     "specache_decode_attn_workspace_size",
     "specache_decode_attn",
+    "specache_decode_step_workspace_size",
+    "specache_decode_step",
+    "specache_gather_stream_create",
+    "specache_compute_stream_create",
+    "specache_stream_destroy",
     "specache_status_string",
     "specache_abi_version",
 )
@@ -87,6 +92,11 @@ def load() -> ctypes.CDLL:
             "specache_gather_fp16": (I, [SP, P, I, P, P, P, P, P]),
             "specache_decode_attn_workspace_size": (SZ, [SP, I, I, I]),
             "specache_decode_attn": (I, [SP, P, I, LP, P, I, P, P, P, P, I, F, P, P, SZ, P]),
+            "specache_decode_step_workspace_size": (SZ, [SP, I, I, I, I]),
+            "specache_decode_step": (I, [SP, P, I, I, LP, P, I, P, P, P, P, I, F, P, I, P, P, P, SZ, P]),
+            "specache_gather_stream_create": (I, [I, ctypes.POINTER(P)]),
+            "specache_compute_stream_create": (I, [I, ctypes.POINTER(P)]),
+            "specache_stream_destroy": (I, [P]),
             "specache_status_string": (ctypes.c_char_p, [I]),
             "specache_abi_version": (I, []),
         }

@@ -1,4 +1,4 @@
-"""Python binding of libspecache: the four C-ABI calls on torch tensors.
+"""Python binding of libspecache: the C-ABI calls on torch tensors.
 
 Argument marshalling only -- every step of the path runs in the HIP kernels
 behind include/specache.h.  torch provides device memory (outputs and
@@ -46,6 +46,8 @@ def _stream(stream) -> int:
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
+    if hasattr(stream, "handle"):       # GatherStream
+        return stream.handle
     return int(stream)
 
 
@@ -159,21 +161,49 @@ def gather_fp16(idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor,
     return k_sel, v_sel
 
 
+class CUStream:
+    """A HIP stream limited to a set of compute units (created by the library,
+    released by close()).  `.torch` is a torch stream view of it."""
+
+    _create = None
+
+    def __init__(self, n_cus: int = 8):
+        handle = ctypes.c_void_p()
+        _lib.check(getattr(_lib.load(), self._create)(n_cus, ctypes.byref(handle)), self._create)
+        self.handle = handle.value
+        self.n_cus = n_cus
+        self.torch = torch.cuda.ExternalStream(self.handle)
+
+    def close(self):
+        if self.handle:
+            torch.cuda.synchronize()
+            _lib.check(_lib.load().specache_stream_destroy(self.handle), "specache_stream_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class GatherStream(CUStream):
+    """specache_gather_stream_create: compute units [0, n_cus), for gather_fp16."""
+    _create = "specache_gather_stream_create"
+
+
+class ComputeStream(CUStream):
+    """specache_compute_stream_create: every compute unit but the n_cus of a GatherStream(n_cus)."""
+    _create = "specache_compute_stream_create"
+
+
 def decode_attn_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int, tail_len: int = 0) -> int:
     shape = cache.shape(n_q_heads)
     return int(_lib.load().specache_decode_attn_workspace_size(ctypes.byref(shape), n_tokens, k, tail_len))
 
 
-def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None = None,
-                k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None,
-                k_tail: torch.Tensor | None = None, v_tail: torch.Tensor | None = None,
-                sm_scale: float | None = None, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """specache_decode_attn: O [B, Hq, T, D] float16 = Attn(q, C' with rows idx replaced by
-    k_sel / v_sel, then the optional tail)."""
+def _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail):
     _need(q16, "q16", torch.float16, 4)
-    B, Hq, T, D = q16.shape
-    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     k = 0
     ip = kp = vp = 0
     if idx is not None:
@@ -190,6 +220,19 @@ def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None 
         _need(v_tail, "v_tail", torch.float16, 4)
         R = k_tail.shape[2]
         ktp, vtp = k_tail.data_ptr(), v_tail.data_ptr()
+    return k, ip, kp, vp, R, ktp, vtp
+
+
+def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None = None,
+                k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None,
+                k_tail: torch.Tensor | None = None, v_tail: torch.Tensor | None = None,
+                sm_scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """specache_decode_attn: O [B, Hq, T, D] float16 = Attn(q, C' with rows idx replaced by
+    k_sel / v_sel, then the optional tail)."""
+    k, ip, kp, vp, R, ktp, vtp = _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail)
+    B, Hq, T, D = q16.shape
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     lib = _lib.load()
     shape = cache.shape(Hq)
     need = lib.specache_decode_attn_workspace_size(ctypes.byref(shape), T, k, R)
@@ -205,3 +248,47 @@ def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None 
                                         _stream(stream)),
                "specache_decode_attn")
     return out
+
+
+def decode_step_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int, tail_len: int,
+                               k_next: int) -> int:
+    shape = cache.shape(n_q_heads)
+    return int(_lib.load().specache_decode_step_workspace_size(ctypes.byref(shape), n_tokens, k, tail_len,
+                                                                k_next))
+
+
+def decode_step(q16: torch.Tensor, cache: LowBitCache, k_next: int, rank_row: int = 1,
+                idx: torch.Tensor | None = None, k_sel: torch.Tensor | None = None,
+                v_sel: torch.Tensor | None = None, k_tail: torch.Tensor | None = None,
+                v_tail: torch.Tensor | None = None, sm_scale: float | None = None,
+                out: torch.Tensor | None = None, idx_next_out: torch.Tensor | None = None,
+                rank_key_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None):
+    """specache_decode_step: (O, idx_next) -- decode_attn's output and score_topk's
+    selection for row rank_row, from one pass over C'."""
+    k, ip, kp, vp, R, ktp, vtp = _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail)
+    B, Hq, T, D = q16.shape
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    lib = _lib.load()
+    shape = cache.shape(Hq)
+    need = lib.specache_decode_step_workspace_size(ctypes.byref(shape), T, k, R, k_next)
+    if need == 0:
+        raise ValueError("invalid decode_step arguments (shape, n_tokens, k, tail length or k_next)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    if out is None:
+        out = torch.empty_like(q16)
+    if idx_next_out is None:
+        idx_next_out = torch.empty((B, cache.n_kv_heads, k_next), dtype=torch.int32, device=q16.device)
+    _need(idx_next_out, "idx_next_out", torch.int32, 3)
+    rk = 0
+    if rank_key_out is not None:
+        _need(rank_key_out, "rank_key_out", torch.float32, 3)
+        rk = rank_key_out.data_ptr()
+    _lib.check(lib.specache_decode_step(ctypes.byref(shape), q16.data_ptr(), T, rank_row,
+                                        ctypes.byref(cache.c_struct()), ip, k, kp, vp, ktp, vtp, R, sm_scale,
+                                        out.data_ptr(), k_next, idx_next_out.data_ptr(), rk,
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream(stream)),
+               "specache_decode_step")
+    return out, idx_next_out

@@ -67,14 +67,30 @@ ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
 
 struct AttnWs {
   size_t ml, acc, total;
+  // fused step only:
+  size_t logits, rank_m, rank_l, keys, hist, total_step;
 };
 
-AttnWs attn_ws(const Dims& d, const AttnPlan& p, int T) {
+// Sized for attn_max_splits, the most splits any launch plan uses.
+AttnWs attn_ws(const Dims& d, int T) {
   AttnWs w;
   const size_t rows = (size_t)d.B * d.Hq * T;
+  const size_t S = (size_t)attn_max_splits(d);
   w.ml = 0;
-  w.acc = align256(sizeof(float) * rows * p.S * 2);
-  w.total = w.acc + align256(sizeof(float) * rows * p.S * d.D);
+  w.acc = align256(sizeof(float) * rows * S * 2);
+  w.total = w.acc + align256(sizeof(float) * rows * S * d.D);
+  size_t off = w.total;
+  w.logits = off;
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * d.N);
+  w.rank_m = off;
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * S);
+  w.rank_l = off;
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * S);
+  w.keys = off;
+  off += align256(sizeof(float) * (size_t)d.slices() * d.N);
+  w.hist = off;
+  off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
+  w.total_step = off;
   return w;
 }
 
@@ -168,7 +184,7 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
                               static_cast<const uint32_t*>(cache->k_codes), static_cast<const _Float16*>(cache->k_meta),
                               sm_scale, logits, part_m, part_l, hist, s);
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
-  e = launch_rank_select(d, plan, logits, part_m, part_l, k, keys, hist, idx_out, s);
+  e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, hist, idx_out, s);
   return hip_status(e);
 }
 
@@ -194,8 +210,57 @@ size_t specache_decode_attn_workspace_size(const specache_shape* shape, int n_to
   if (!make_dims(shape, &d, &err) || n_tokens < 1 || n_tokens > 2 || k < 0 || k > d.N || tail_len < 0 ||
       tail_len > kMaxTail || d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen)
     return 0;
-  return attn_ws(d, attn_plan(d, k, tail_len), n_tokens).total;
+  return attn_ws(d, n_tokens).total;
 }
+
+namespace {
+
+// Compute units a stream's kernels may use: its CU mask (streams made by
+// specache_*_stream_create), else the whole device.
+int stream_cus(hipStream_t s) {
+  int dev = 0, cus = kPlanMaxCUs;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return kPlanMaxCUs;
+  uint32_t mask[64] = {0};
+  if (s == nullptr || hipExtStreamGetCUMask(s, 64, mask) != hipSuccess) {
+    (void)hipGetLastError();
+    return cus;
+  }
+  int n = 0;
+  for (int i = 0; i < 64; ++i) n += __builtin_popcount(mask[i]);
+  return n > 0 && n < cus ? n : cus;
+}
+
+int fill_attn_args(const Dims& d, const void* q16, int n_tokens, const specache_lowbit* cache, const int32_t* idx,
+                   int k, const void* k_sel, const void* v_sel, const void* k_tail, const void* v_tail, int tail_len,
+                   float sm_scale, void* out16, AttnArgs* a) {
+  if (n_tokens < 1 || n_tokens > 2 || k < 0 || k > d.N || tail_len < 0 || tail_len > kMaxTail || !q16 ||
+      !lowbit_ok(cache) || !out16 || !(sm_scale > 0.0f) || sm_scale == INFINITY)
+    return SPECACHE_ERR_INVALID;
+  if (d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen) return SPECACHE_ERR_UNSUPPORTED;
+  if (k > 0 && (!idx || !k_sel || !v_sel)) return SPECACHE_ERR_INVALID;
+  if (tail_len > 0 && (!k_tail || !v_tail)) return SPECACHE_ERR_INVALID;
+  std::memset(a, 0, sizeof(*a));
+  a->q16 = static_cast<const _Float16*>(q16);
+  a->T = n_tokens;
+  a->k_codes = static_cast<const uint32_t*>(cache->k_codes);
+  a->k_meta = static_cast<const _Float16*>(cache->k_meta);
+  a->v_codes = static_cast<const uint32_t*>(cache->v_codes);
+  a->v_meta = static_cast<const _Float16*>(cache->v_meta);
+  a->idx = idx;
+  a->k = k;
+  a->k_sel = static_cast<const _Float16*>(k_sel);
+  a->v_sel = static_cast<const _Float16*>(v_sel);
+  a->k_tail = static_cast<const _Float16*>(k_tail);
+  a->v_tail = static_cast<const _Float16*>(v_tail);
+  a->tail = tail_len;
+  a->sm_scale = sm_scale;
+  a->out16 = static_cast<_Float16*>(out16);
+  return SPECACHE_OK;
+}
+
+}  // namespace
 
 int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tokens, const specache_lowbit* cache,
                          const int32_t* idx, int k, const void* k_sel, const void* v_sel, const void* k_tail,
@@ -204,35 +269,101 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
   Dims d;
   int err;
   if (!make_dims(shape, &d, &err)) return err;
-  if (n_tokens < 1 || n_tokens > 2 || k < 0 || k > d.N || tail_len < 0 || tail_len > kMaxTail || !q16 ||
-      !lowbit_ok(cache) || !out16 || !(sm_scale > 0.0f) || sm_scale == INFINITY)
-    return SPECACHE_ERR_INVALID;
-  if (d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen) return SPECACHE_ERR_UNSUPPORTED;
-  if (k > 0 && (!idx || !k_sel || !v_sel)) return SPECACHE_ERR_INVALID;
-  if (tail_len > 0 && (!k_tail || !v_tail)) return SPECACHE_ERR_INVALID;
-  const AttnPlan plan = attn_plan(d, k, tail_len);
-  const AttnWs ws = attn_ws(d, plan, n_tokens);
+  AttnArgs a;
+  err = fill_attn_args(d, q16, n_tokens, cache, idx, k, k_sel, v_sel, k_tail, v_tail, tail_len, sm_scale, out16, &a);
+  if (err != SPECACHE_OK) return err;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AttnPlan plan = attn_plan(d, stream_cus(s));
+  const AttnWs ws = attn_ws(d, n_tokens);
   if (!workspace || workspace_bytes < ws.total) return SPECACHE_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);
-  AttnArgs a;
-  a.q16 = static_cast<const _Float16*>(q16);
-  a.T = n_tokens;
-  a.k_codes = static_cast<const uint32_t*>(cache->k_codes);
-  a.k_meta = static_cast<const _Float16*>(cache->k_meta);
-  a.v_codes = static_cast<const uint32_t*>(cache->v_codes);
-  a.v_meta = static_cast<const _Float16*>(cache->v_meta);
-  a.idx = idx;
-  a.k = k;
-  a.k_sel = static_cast<const _Float16*>(k_sel);
-  a.v_sel = static_cast<const _Float16*>(v_sel);
-  a.k_tail = static_cast<const _Float16*>(k_tail);
-  a.v_tail = static_cast<const _Float16*>(v_tail);
-  a.tail = tail_len;
-  a.sm_scale = sm_scale;
-  a.out16 = static_cast<_Float16*>(out16);
   a.part_ml = reinterpret_cast<float*>(base + ws.ml);
   a.part_acc = reinterpret_cast<float*>(base + ws.acc);
-  return hip_status(launch_decode_attn(d, plan, a, static_cast<hipStream_t>(stream)));
+  if (launch_attn_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
+  return hip_status(launch_attn_merge(d, plan, a, s));
+}
+
+size_t specache_decode_step_workspace_size(const specache_shape* shape, int n_tokens, int k, int tail_len,
+                                           int k_next) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err) || n_tokens < 1 || n_tokens > 2 || k < 0 || k > d.N || tail_len < 0 ||
+      tail_len > kMaxTail || d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen || k_next < 1 || k_next > d.N)
+    return 0;
+  return attn_ws(d, n_tokens).total_step;
+}
+
+int specache_decode_step(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
+                         const specache_lowbit* cache, const int32_t* idx, int k, const void* k_sel,
+                         const void* v_sel, const void* k_tail, const void* v_tail, int tail_len, float sm_scale,
+                         void* out16, int k_next, int32_t* idx_next_out, float* rank_key_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err)) return err;
+  AttnArgs a;
+  err = fill_attn_args(d, q16, n_tokens, cache, idx, k, k_sel, v_sel, k_tail, v_tail, tail_len, sm_scale, out16, &a);
+  if (err != SPECACHE_OK) return err;
+  if (rank_row < 0 || rank_row >= n_tokens || k_next < 1 || k_next > d.N || !idx_next_out)
+    return SPECACHE_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AttnPlan plan = attn_plan(d, stream_cus(s));
+  const AttnWs ws = attn_ws(d, n_tokens);
+  if (!workspace || workspace_bytes < ws.total_step) return SPECACHE_ERR_WORKSPACE;
+  char* base = static_cast<char*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(base + ws.ml);
+  a.part_acc = reinterpret_cast<float*>(base + ws.acc);
+  a.rank_row = rank_row;
+  a.rank_logits = reinterpret_cast<float*>(base + ws.logits);
+  a.rank_m = reinterpret_cast<float*>(base + ws.rank_m);
+  a.rank_l = reinterpret_cast<float*>(base + ws.rank_l);
+  a.rank_hist = reinterpret_cast<uint32_t*>(base + ws.hist);
+  float* keys = rank_key_out ? rank_key_out : reinterpret_cast<float*>(base + ws.keys);
+  // the ranking first: the prefetch of the next set waits on it, the merge does not
+  if (launch_attn_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
+  if (launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys, a.rank_hist, idx_next_out, s) !=
+      hipSuccess)
+    return SPECACHE_ERR_HIP;
+  return hip_status(launch_attn_merge(d, plan, a, s));
+}
+
+namespace {
+
+// A stream whose kernels run on compute units [first, first + count) of the current device.
+int create_cu_stream(int first, int count, bool all_from_first, void** stream_out) {
+  if (!stream_out) return SPECACHE_ERR_INVALID;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return SPECACHE_ERR_HIP;
+  if (all_from_first) count = cus - first;
+  if (first < 0 || count < kMinGatherCUs || first + count > cus) return SPECACHE_ERR_INVALID;
+  const int words = (cus + 31) / 32;
+  if (words > 64) return SPECACHE_ERR_UNSUPPORTED;
+  // The mask is passed with a length of words * 32 entries, all zero past the first `words`, so
+  // that it is read in bounds and means the same whether that length counts bits or words.
+  uint32_t mask[64 * 32] = {0};
+  for (int i = first; i < first + count; ++i) mask[i / 32] |= 1u << (i % 32);
+  hipStream_t st = nullptr;
+  if (hipExtStreamCreateWithCUMask(&st, (uint32_t)(words * 32), mask) != hipSuccess) return SPECACHE_ERR_HIP;
+  *stream_out = st;
+  return SPECACHE_OK;
+}
+
+}  // namespace
+
+int specache_gather_stream_create(int n_cus, void** stream_out) {
+  return create_cu_stream(0, n_cus, false, stream_out);
+}
+
+int specache_compute_stream_create(int reserved_cus, void** stream_out) {
+  if (reserved_cus < kMinGatherCUs) return SPECACHE_ERR_INVALID;
+  return create_cu_stream(reserved_cus, 0, true, stream_out);
+}
+
+int specache_stream_destroy(void* stream) {
+  if (!stream) return SPECACHE_ERR_INVALID;
+  return hip_status(hipStreamDestroy(static_cast<hipStream_t>(stream)));
 }
 
 const char* specache_status_string(int status) {

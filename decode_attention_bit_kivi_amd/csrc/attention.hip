@@ -43,7 +43,9 @@ struct AttnSmem {
   static constexpr int W = D / 32;
   static constexpr int RS = 36;  // row stride (halves, a multiple of 4 for 8-byte reads) of the transposed tile
   uint32_t kmask[kMaxBlocksPerSplit];
+  float rank_m[4][16], rank_l[4][16];  // per wave: ranking statistics of each query row
   float cst[4][16][16];          // per wave: [block of the 16-block group][row]
+  uint4 kscale[4][16][4][W];     // per wave: key scales [block of the group][k-group][chunk]
   int sel_range[2];
   union {
     _Float16 vt[4][D][RS];       // per wave: 16-bit value rows, transposed
@@ -58,7 +60,7 @@ struct AttnSmem {
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D, int BITS, int PACK>
+template <int D, int BITS, int PACK, bool RANK>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L,
                                                             int S) {
   constexpr int W = D / 32;
@@ -83,6 +85,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   const int64_t p1 = p0 + L < N ? p0 + L : N;
   const int nb = (int)((p1 - p0) / 32);
   const int64_t blk0 = p0 / 32;
+
+  if (RANK && split == 0)  // the rank kernels accumulate a per-slice histogram here
+    for (int i = tid; i < 2048; i += 256) a.rank_hist[slice * 2048 + i] = 0u;
 
   // ---- kappa positions of this split: a bitmask over its blocks and the range [i0, i1) of
   // fetched rows whose positions fall in it (idx is ascending), found by one parallel pass.
@@ -125,27 +130,43 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 
   float m_used = kEmpty;   // running max (log2 units) of accumulator row n16
   float l_part = 0.0f;     // this lane's share of that row's sum of exponentials
+  // ranking: the C' terms of kappa positions (masked out of the attention), kept relative to
+  // their own running max m_corr (row-uniform) so that the attention's arithmetic is untouched
+  float m_corr = kEmpty, l_corr = 0.0f;
   f32x4 Oacc[CPL];
 #pragma unroll
   for (int ct = 0; ct < CPL; ++ct) Oacc[ct] = zero4();
   f32x4 Ozs = zero4();
 
   const int wv_grp = (CPL * n16) / 32;  // value group of this lane's channels
+  const int arow = PACK == 2 ? (n16 & 7) : n16;  // query row of this lane's logits
+  const bool rank_lane = RANK && arow < R && (arow % T) == a.rank_row;
   // token (within a block) of A/B k-slot j for k-group g: j < 4 -> 4g + j, else 16 + 4g + j - 4
   // bit position of an even token t inside a value word: t / 2
   const int shv[4] = {15 - 2 * g, 14 - 2 * g, 7 - 2 * g, 6 - 2 * g};
 
-  auto online_update = [&](float (&x)[PACK == 2 ? 4 : 8]) {
-    constexpr int NX = PACK == 2 ? 4 : 8;
-    float bm = x[0];
+  constexpr int NX = PACK == 2 ? 4 : 8;
+  const float k1 = -0.5f * qscale;  // the expanded key operand is -(2b - 1) s
+
+  // Rescale the accumulators of this lane's rows when a block raises a row maximum by more
+  // than 2^kRescale.  xr holds logits relative to the current maximum; on a rescale they are
+  // recomputed from the absolute values xa.
+  auto online_update = [&](float (&xr)[NX], const float (&xa)[NX]) {
+    float bm = xr[0];
 #pragma unroll
-    for (int i = 1; i < NX; ++i) bm = fmaxf(bm, x[i]);
+    for (int i = 1; i < NX; ++i) bm = fmaxf(bm, xr[i]);
     bm = max_over_groups(bm);
-    if (__any(bm > m_used + kRescale)) {
-      const float mn = fmaxf(m_used, bm);
+    if (__any(bm > kRescale)) {
+      float ba = xa[0];
+#pragma unroll
+      for (int i = 1; i < NX; ++i) ba = fmaxf(ba, xa[i]);
+      ba = max_over_groups(ba);
+      const float mn = fmaxf(m_used, ba);
       const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
       m_used = mn;
       l_part *= alpha;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) xr[i] = xa[i] - mn;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float ai = __shfl(alpha, 4 * g + i);
@@ -156,11 +177,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
   };
 
+  auto pack2 = [](float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+  };
   // P (float32) -> float16 A fragment; slots j < 4 hold tile-0 tokens, j >= 4 tile-1 tokens.
-  auto make_p = [&](const float (&p)[PACK == 2 ? 4 : 8], float mul) {
+  auto make_p = [&](const float (&p)[NX], float mul) {
     Frag A;
     if constexpr (PACK == 2) {
-      const uint32_t lo = pack_half2(p[0] * mul, p[1] * mul), hi = pack_half2(p[2] * mul, p[3] * mul);
+      const uint32_t lo = pack2(p[0] * mul, p[1] * mul), hi = pack2(p[2] * mul, p[3] * mul);
       const bool t1 = n16 >= 8;
       A.u[0] = t1 ? 0u : lo;
       A.u[1] = t1 ? 0u : hi;
@@ -168,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       A.u[3] = t1 ? hi : 0u;
     } else {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) A.u[d] = pack_half2(p[2 * d] * mul, p[2 * d + 1] * mul);
+      for (int d = 0; d < 4; ++d) A.u[d] = pack2(p[2 * d] * mul, p[2 * d + 1] * mul);
     }
     return A;
   };
@@ -176,71 +200,61 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   // ================= low-bit blocks =================
   struct BlockData {
     Words<W> kw[2][BITS];
-    uint4 ks[W];
     Words<CPL> vw[BITS];
     uint2 vs_lo, vs_hi, zs_lo, zs_hi;
   };
-  // All loads are unconditional (clamped to valid addresses) so that they issue back to back.
+  const uint32_t* kc_slice = a.k_codes + slice * N * BITS * W;
+  const uint32_t* vc_slice = a.v_codes + slice * nblk * BITS * D;
+  const _Float16* vm_slice = a.v_meta + slice * nblk * 2 * W * 32;
+  const _Float16* km_slice = a.k_meta + slice * nblk * 2 * D;
+  const int zrow = n16 < 2 * W ? n16 : 0;  // value-metadata row of the zero-point / scale column
+  const bool zs_lane = n16 < 2 * W;
+  // All loads are unconditional (clamped to valid blocks) so that they issue back to back.
   auto load_block = [&](int jj) {
     BlockData bd;
     const int64_t blk = blk0 + jj;
-    const uint32_t* kc = a.k_codes + (slice * N + blk * 32) * BITS * W;
+    const uint32_t* kc = kc_slice + blk * 32 * BITS * W;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int pl = 0; pl < BITS; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * BITS + pl) * W);
-    const _Float16* kms = a.k_meta + ((slice * nblk + blk) * 2 + 1) * D;
-#pragma unroll
-    for (int w = 0; w < W; ++w) bd.ks[w] = load_u4(kms + 32 * w + 8 * g);
-    const uint32_t* vc = a.v_codes + (slice * nblk + blk) * BITS * D;
+    const uint32_t* vc = vc_slice + blk * BITS * D;
 #pragma unroll
     for (int pl = 0; pl < BITS; ++pl) bd.vw[pl] = load_words<CPL>(vc + pl * D + CPL * n16);
-    const _Float16* vm = a.v_meta + (slice * nblk + blk) * 2 * W * 32;
+    const _Float16* vm = vm_slice + blk * 2 * W * 32;
     bd.vs_lo = load_u2(vm + W * 32 + wv_grp * 32 + 4 * g);
     bd.vs_hi = load_u2(vm + W * 32 + wv_grp * 32 + 16 + 4 * g);
     // rows 0..W-1 of the value metadata are the zero-points of groups 0..W-1, rows W..2W-1 the scales
-    const _Float16* zr = vm + (n16 < 2 * W ? n16 : 0) * 32;
-    bd.zs_lo = load_u2(zr + 4 * g);
-    bd.zs_hi = load_u2(zr + 16 + 4 * g);
+    bd.zs_lo = load_u2(vm + zrow * 32 + 4 * g);
+    bd.zs_hi = load_u2(vm + zrow * 32 + 16 + 4 * g);
     return bd;
   };
-  const bool zs_lane = n16 < 2 * W;
-
-  BlockData cur;
-  if (wave < nb) cur = load_block(wave);
-  for (int jj = wave; jj < nb; jj += 4) {
-    const int step = (jj - wave) >> 2;  // index among this wave's blocks
-    const bool prepass = (step & 15) == 0;
-    Frag az[W], as[W];
-    if (prepass) {
-      // constant term of the next 16 blocks of this wave (rows x blocks, via MFMA below)
-      const int bi = jj + 4 * n16;
-      const _Float16* km = a.k_meta + (slice * nblk + blk0 + (bi < nb ? bi : jj)) * 2 * D;
+  // Prepass over the wave's next 16 blocks: zero-points and scales of the keys against the
+  // queries give the per-block constant; the scales also go to LDS for the expansion.
+  Frag pz[W], ps[W];
+  auto prepass_load = [&](int jj) {
+    const int bi = jj + 4 * n16;
+    const _Float16* km = km_slice + (blk0 + (bi < nb ? bi : jj)) * 2 * D;
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        az[w].v = load_u4(km + 32 * w + 8 * g);
-        as[w].v = load_u4(km + D + 32 * w + 8 * g);
-      }
+    for (int w = 0; w < W; ++w) {
+      pz[w].v = load_u4(km + 32 * w + 8 * g);
+      ps[w].v = load_u4(km + D + 32 * w + 8 * g);
     }
-    const BlockData nxt = load_block(jj + 4 < nb ? jj + 4 : jj);
-    if (prepass) {
-      f32x4 accZ = zero4(), accS = zero4();
+  };
+  auto prepass_finish = [&]() {
+    f32x4 accZ = zero4(), accS = zero4();
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        accZ = mma(az[w], B0[w], accZ);
-        accS = mma(as[w], B0[w], accS);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.cst[wave][4 * g + i][n16] = (accZ[i] + hK * accS[i]) * qscale;
-      lds_fence();
+    for (int w = 0; w < W; ++w) {
+      accZ = mma(pz[w], B0[w], accZ);
+      accS = mma(ps[w], B0[w], accS);
+      sm.kscale[wave][n16][g][w] = ps[w].v;
     }
-    const Words<W>(&kw)[2][BITS] = cur.kw;
-    const uint4* ks = cur.ks;
-    const Words<CPL>* vw = cur.vw;
-    const uint2 vs_lo = cur.vs_lo, vs_hi = cur.vs_hi;
-    const uint2 zs_lo = zs_lane ? cur.zs_lo : make_uint2(0, 0);
-    const uint2 zs_hi = zs_lane ? cur.zs_hi : make_uint2(0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.cst[wave][4 * g + i][n16] = (accZ[i] + hK * accS[i]) * qscale;
+    lds_fence();
+  };
 
+  auto compute_block = [&](const BlockData& bd, int jj, int step) {
     // scores
     f32x4 acc[2][BITS];
 #pragma unroll
@@ -249,14 +263,15 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       for (int pl = 0; pl < BITS; ++pl) acc[tau][pl] = zero4();
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const uint32_t* mag = reinterpret_cast<const uint32_t*>(&ks[w]);
+      const uint4 ksv = sm.kscale[wave][step & 15][g][w];
+      const uint32_t mag[4] = {ksv.x, ksv.y, ksv.z, ksv.w};
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
         for (int pl = 0; pl < BITS; ++pl) {
           Frag A;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
+          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(bd.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
           if constexpr (PACK == 2)
             acc[0][pl] = mma(A, tau == 0 ? B0[w] : B1[w], acc[0][pl]);
           else
@@ -264,54 +279,111 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
         }
       }
     }
-    constexpr int NX = PACK == 2 ? 4 : 8;
-    float x[NX];
     const float c0 = sm.cst[wave][step & 15][PACK == 2 ? (n16 & 7) : n16];
+    const float c0m = c0 - m_used;
+    float xr[NX], xa[NX];
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int tau = PACK == 2 ? 0 : i / 4;
-      // the expanded operand is -(2b - 1) s: a set bit becomes a negative sign
-      const float s = BITS == 1 ? -0.5f * acc[tau][0][i & 3] : -0.5f * acc[tau][0][i & 3] - acc[tau][BITS - 1][i & 3];
-      x[i] = fmaf(s, qscale, c0);
+      const float sacc = BITS == 1 ? acc[tau][0][i & 3] : acc[tau][0][i & 3] + 2.0f * acc[tau][BITS - 1][i & 3];
+      xr[i] = fmaf(sacc, k1, c0m);
+      xa[i] = fmaf(sacc, k1, c0);
     }
+    if constexpr (RANK) {
+      // the rank row's logits against C' (before any kappa masking), natural units
+      if (rank_lane) {
+        float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
+        constexpr float kLn2 = 0.69314718055994531f;
+        if constexpr (PACK == 2) {
+          *reinterpret_cast<float4*>(dst + 16 * (n16 >> 3) + 4 * g) =
+              make_float4(xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2);
+        } else {
+          *reinterpret_cast<float4*>(dst + 4 * g) = make_float4(xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2);
+          *reinterpret_cast<float4*>(dst + 16 + 4 * g) =
+              make_float4(xa[4] * kLn2, xa[5] * kLn2, xa[6] * kLn2, xa[7] * kLn2);
+        }
+      }
+    }
+    float xc[NX];  // C' logits of masked positions, for the ranking statistics
     const uint32_t kmw = sm.kmask[jj];
     if (kmw) {
 #pragma unroll
       for (int i = 0; i < NX; ++i) {
         const int tok = PACK == 2 ? (16 * (n16 >> 3) + 4 * g + i) : (16 * (i >> 2) + 4 * g + (i & 3));
-        if ((kmw >> tok) & 1u) x[i] = -INFINITY;
+        xc[i] = -INFINITY;
+        if ((kmw >> tok) & 1u) {
+          xc[i] = xa[i];
+          xr[i] = -INFINITY;
+          xa[i] = -INFINITY;
+        }
       }
     }
-    online_update(x);
+    online_update(xr, xa);
     float p[NX];
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(x[i] - m_used);
+      p[i] = __builtin_amdgcn_exp2f(xr[i]);
       l_part += p[i];
+    }
+    if constexpr (RANK) {
+      if (kmw) {
+        float cm = xc[0];
+#pragma unroll
+        for (int i = 1; i < NX; ++i) cm = fmaxf(cm, xc[i]);
+        const float mn = fmaxf(m_corr, max_over_groups(cm));
+        l_corr *= __builtin_amdgcn_exp2f(m_corr - mn);
+        m_corr = mn;
+#pragma unroll
+        for (int i = 0; i < NX; ++i) l_corr += __builtin_amdgcn_exp2f(xc[i] - mn);
+      }
     }
     const Frag Ap = make_p(p, 1.0f);
     Frag Ap2;
     if constexpr (BITS == 2) Ap2 = make_p(p, 2.0f);
 
     // values
-    const uint32_t vmag[4] = {vs_lo.x, vs_lo.y, vs_hi.x, vs_hi.y};
+    const uint32_t vmag[4] = {bd.vs_lo.x, bd.vs_lo.y, bd.vs_hi.x, bd.vs_hi.y};
 #pragma unroll
     for (int ct = 0; ct < CPL; ++ct) {
 #pragma unroll
       for (int pl = 0; pl < BITS; ++pl) {
         Frag Bv;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) Bv.u[d] = signed_pair(vw[pl].w[ct], shv[d], vmag[d]);
+        for (int d = 0; d < 4; ++d) Bv.u[d] = signed_pair(bd.vw[pl].w[ct], shv[d], vmag[d]);
         Oacc[ct] = mma(pl == 0 ? Ap : Ap2, Bv, Oacc[ct]);
       }
     }
     Frag Bzs;
-    Bzs.u[0] = zs_lo.x;
-    Bzs.u[1] = zs_lo.y;
-    Bzs.u[2] = zs_hi.x;
-    Bzs.u[3] = zs_hi.y;
+    Bzs.u[0] = zs_lane ? bd.zs_lo.x : 0u;
+    Bzs.u[1] = zs_lane ? bd.zs_lo.y : 0u;
+    Bzs.u[2] = zs_lane ? bd.zs_hi.x : 0u;
+    Bzs.u[3] = zs_lane ? bd.zs_hi.y : 0u;
     Ozs = mma(Ap, Bzs, Ozs);
-    cur = nxt;
+  };
+
+  // Two block buffers in turn: the next block's loads are in flight while one is computed.
+  {
+    BlockData b0, b1;
+    if (wave < nb) b0 = load_block(wave);
+    for (int jj = wave; jj < nb; jj += 8) {
+      const int step = (jj - wave) >> 2;  // even; a prepass step every 16 of this wave's blocks
+      const bool pre = (step & 15) == 0;
+      if (pre) prepass_load(jj);
+      b1 = load_block(jj + 4 < nb ? jj + 4 : jj);
+      if (pre) prepass_finish();
+      compute_block(b0, jj, step);
+      if (jj + 4 >= nb) break;
+      b0 = load_block(jj + 8 < nb ? jj + 8 : jj + 4);
+      compute_block(b1, jj + 4, step + 1);
+    }
+  }
+
+  // ranking statistics over C' = the low-bit positions processed so far, kappa positions included
+  float rank_m_lane = m_used, rank_l_lane = l_part;
+  if constexpr (RANK) {
+    rank_m_lane = fmaxf(m_used, m_corr);
+    rank_l_lane = l_part * __builtin_amdgcn_exp2f(m_used - rank_m_lane) +
+                  l_corr * __builtin_amdgcn_exp2f(m_corr - rank_m_lane);
   }
 
   // ================= 16-bit rows: fetched kappa rows of this split, then the tail =================
@@ -366,24 +438,24 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
           acc[tau] = mma(A, B0[w], acc[tau]);
       }
     }
-    constexpr int NX = PACK == 2 ? 4 : 8;
-    float x[NX];
+    float xr[NX], xa[NX];
     const int row = PACK == 2 ? (n16 & 7) : n16;
     const int tq = row % T;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int tok = PACK == 2 ? (16 * (n16 >> 3) + 4 * g + i) : (16 * (i >> 2) + 4 * g + (i & 3));
       const int tau = PACK == 2 ? 0 : i >> 2;
-      float v = acc[tau][i & 3] * qscale;
+      const float v = acc[tau][i & 3] * qscale;
       bool ok = base + tok < lim;
       if (tail) ok = ok && (base + tok <= a.tail - T + tq);
-      x[i] = ok ? v : -INFINITY;
+      xa[i] = ok ? v : -INFINITY;
+      xr[i] = xa[i] - m_used;
     }
-    online_update(x);
+    online_update(xr, xa);
     float p[NX];
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(x[i] - m_used);
+      p[i] = __builtin_amdgcn_exp2f(xr[i]);
       l_part += p[i];
     }
     const Frag Ap2 = make_p(p, -2.0f);  // the value accumulator is scaled by -1/2 at the end
@@ -416,7 +488,35 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     fin_m = mm;
     fin_l = f_self * l_row + f_other * l2;
   }
+  if constexpr (RANK) {
+    // per query row: sum over the k-groups (same max), then (PACK == 2) fold the two tiles' rows
+    float rl = sum_over_groups(rank_l_lane), rm = rank_m_lane;
+    if constexpr (PACK == 2) {
+      const float m2 = __shfl_xor(rm, 8), l2 = __shfl_xor(rl, 8);
+      const float mm = fmaxf(rm, m2);
+      rl = rl * __builtin_amdgcn_exp2f(rm - mm) + l2 * __builtin_amdgcn_exp2f(m2 - mm);
+      rm = mm;
+    }
+    if (g == 0 && n16 < 16) {
+      sm.rank_m[wave][n16] = rm;
+      sm.rank_l[wave][n16] = rl;
+    }
+  }
   __syncthreads();  // all waves are done with their value tiles; the LDS union becomes the combine buffer
+  if constexpr (RANK) {
+    // one thread per head: combine the four waves and write this split's statistics
+    if (tid < G) {
+      const int r = tid * T + a.rank_row;
+      float M = kEmpty;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) M = fmaxf(M, sm.rank_m[w4][r]);
+      float Ls = 0.0f;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) Ls += sm.rank_l[w4][r] * __builtin_amdgcn_exp2f(sm.rank_m[w4][r] - M);
+      a.rank_m[(slice * G + tid) * S + split] = M;
+      a.rank_l[(slice * G + tid) * S + split] = Ls;
+    }
+  }
   if (g == 0 && n16 < (PACK == 2 ? 8 : 16)) {
     sm.u.comb.m[wave][n16] = fin_m;
     sm.u.comb.l[wave][n16] = fin_l;
@@ -529,26 +629,37 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
   out[row * D + c] = (_Float16)(o / Lrow);
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool RANK>
 void launch_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
   if (d.G * a.T <= 8)
-    attn_split_kernel<D, BITS, 2><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    attn_split_kernel<D, BITS, 2, RANK><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   else
-    attn_split_kernel<D, BITS, 1><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    attn_split_kernel<D, BITS, 1, RANK><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+}
+
+template <bool RANK>
+void launch_split_r(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  if (d.D == 128) {
+    if (d.bits == 1) launch_split<128, 1, RANK>(d, plan, a, s); else launch_split<128, 2, RANK>(d, plan, a, s);
+  } else {
+    if (d.bits == 1) launch_split<64, 1, RANK>(d, plan, a, s); else launch_split<64, 2, RANK>(d, plan, a, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode_attn(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  if (a.rank_logits) launch_split_r<true>(d, plan, a, s); else launch_split_r<false>(d, plan, a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
   const unsigned rows = (unsigned)((int64_t)d.B * d.Hq * a.T);
-  if (d.D == 128) {
-    if (d.bits == 1) launch_split<128, 1>(d, plan, a, s); else launch_split<128, 2>(d, plan, a, s);
+  if (d.D == 128)
     attn_merge_kernel<128><<<rows, 128, 0, s>>>(a.part_ml, a.part_acc, plan.S, a.out16);
-  } else {
-    if (d.bits == 1) launch_split<64, 1>(d, plan, a, s); else launch_split<64, 2>(d, plan, a, s);
+  else
     attn_merge_kernel<64><<<rows, 64, 0, s>>>(a.part_ml, a.part_acc, plan.S, a.out16);
-  }
   return hipGetLastError();
 }
 

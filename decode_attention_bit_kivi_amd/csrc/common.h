@@ -3,12 +3,16 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace specache {
 
 constexpr int kGroup = 32;        // quantization group (tokens for keys, channels for values)
 constexpr int kMaxRows = 16;      // G * T query rows per KV head handled by one workgroup
 constexpr int kMaxTail = 64;
+// The runtime only accepts a compute-unit mask that leaves at least one unit on
+// every accelerator complex die (8 on MI355X); the low mask bits interleave over them.
+constexpr int kMinGatherCUs = 8;
 constexpr int64_t kMaxAttnSeqLen = int64_t(4096) * 1024;  // 1024 splits of at most 4096 positions
 
 // Problem dimensions after validation.
@@ -46,21 +50,64 @@ inline ScorePlan score_plan(const Dims& d) {
 }
 
 struct AttnPlan {
-  int64_t L;       // positions per split (multiple of 32, at most 4096)
+  int64_t L;       // positions per split (a multiple of 32, at most 4096)
   int S;           // splits per slice; a split also handles the fetched rows of its
                    // positions, and the last split handles the tail
 };
 
-inline AttnPlan attn_plan(const Dims& d, int /*k*/, int /*tail*/) {
-  const int64_t target = 1024;  // workgroups to aim for
-  int64_t L = ceil_div(d.N * d.slices(), target);
-  L = round_up(L, 128);
-  if (L < 128) L = 128;
-  if (L > 4096) L = 4096;
+constexpr int kPlanMaxCUs = 256;     // compute units the attention plans are sized for at most
+constexpr int kAttnWGsPerCU = 2;     // resident attention workgroups per compute unit
+constexpr int kAttnMaxBlocks = 128;  // 32-position blocks per split (the kernel's kappa bitmask)
+constexpr int kAttnMaxSplits = 1024; // splits per slice (the merge kernel's weight table)
+
+inline int64_t attn_min_splits(const Dims& d) { return ceil_div(d.nblk, kAttnMaxBlocks); }
+
+// Most splits per slice any compute-unit count may get: about four rounds of workgroups on
+// kPlanMaxCUs units.  The workspace is sized for it.
+inline int64_t attn_max_splits(const Dims& d) {
+  int64_t cap = ceil_div(int64_t(4) * kPlanMaxCUs * kAttnWGsPerCU, d.slices());
+  if (cap > d.nblk) cap = d.nblk;
+  if (cap < attn_min_splits(d)) cap = attn_min_splits(d);
+  if (cap > kAttnMaxSplits) cap = kAttnMaxSplits;
+  return cap;
+}
+
+inline AttnPlan attn_plan_splits(const Dims& d, int64_t S) {
   AttnPlan p;
-  p.L = L;
-  p.S = (int)ceil_div(d.N, L);
+  p.L = 32 * ceil_div(d.nblk, S);
+  p.S = (int)ceil_div(d.N, p.L);
   return p;
+}
+
+// Splits per slice for `cus` compute units: the fewest splits whose estimated time is within 3%
+// of the best.  The estimate of S splits is (rounds of the slices * S workgroups over the
+// resident slots) x (blocks of the busiest of a workgroup's four waves).
+inline AttnPlan attn_plan(const Dims& d, int cus) {
+  if (cus < 8) cus = 8;
+  if (cus > kPlanMaxCUs) cus = kPlanMaxCUs;
+  const int64_t slots = (int64_t)cus * kAttnWGsPerCU;
+  const int64_t lo = attn_min_splits(d), hi = attn_max_splits(d);
+  int64_t best = INT64_MAX;
+  int64_t cost[kAttnMaxSplits + 1];
+  for (int64_t S = lo; S <= hi; ++S) {
+    const int64_t bps = ceil_div(d.nblk, S);
+    const int64_t used = ceil_div(d.nblk, bps);
+    cost[S] = ceil_div(d.slices() * used, slots) * ceil_div(bps, 4);
+    if (cost[S] < best) best = cost[S];
+  }
+  int64_t pick = hi;
+  for (int64_t S = lo; S <= hi; ++S)
+    if (100 * cost[S] <= 103 * best) {
+      pick = S;
+      break;
+    }
+#ifdef SPECACHE_TUNING  // experiments only: force the split count
+  if (const char* e = getenv("SPECACHE_ATTN_SPLITS")) {
+    const int64_t f = atoll(e);
+    if (f >= lo && f <= hi) pick = f;
+  }
+#endif
+  return attn_plan_splits(d, pick);
 }
 
 // ---- launchers (defined in the .hip files) ----
@@ -73,9 +120,10 @@ hipError_t launch_score(const Dims& d, const ScorePlan& plan, const _Float16* q1
                         int rank_row, const uint32_t* k_codes, const _Float16* k_meta, float sm_scale,
                         float* logits, float* part_m, float* part_l, uint32_t* hist, hipStream_t s);
 
-hipError_t launch_rank_select(const Dims& d, const ScorePlan& plan, const float* logits,
-                              const float* part_m, const float* part_l, int k, float* keys, uint32_t* hist,
-                              int32_t* idx_out, hipStream_t s);
+// part_m / part_l: [slices][G][S] per-split (max, sum 2^(x - max)) of the logits, log2 units.
+hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
+                              const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
+                              hipStream_t s);
 
 hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,
                          const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, hipStream_t s);
@@ -98,8 +146,17 @@ struct AttnArgs {
   _Float16* out16;
   float* part_ml;    // [B][Hq][T][S][2]  (running max in log2 units, sum of exp2)
   float* part_acc;   // [B][Hq][T][S][D]
+  // Ranking outputs of the fused step (all null / unused for plain attention):
+  int rank_row;
+  float* rank_logits;    // [slices][G][N]: logits of the rank row against C' (natural units)
+  float* rank_m;         // [slices][G][S]: per-split max over C' (log2 units)
+  float* rank_l;         // [slices][G][S]: per-split sum of 2^(x - max)
+  uint32_t* rank_hist;   // [slices][2048]: zeroed by the split kernel for the rank kernels
 };
 
-hipError_t launch_decode_attn(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
+// Split kernel of the attention; with a.rank_logits set it also emits the ranking logits and
+// statistics of the rank row against C'.
+hipError_t launch_attn_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_merge(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 
 }  // namespace specache

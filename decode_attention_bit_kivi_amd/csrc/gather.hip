@@ -51,8 +51,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
         const int32_t p = idx[row];
         if (p >= 0 && p < N) {
           const int64_t src = (slice * N + p) * kLanesPerRow + part;
+#ifdef SPECACHE_GATHER_NT
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_src + src));
+          const u32x4_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_src + src));
+          kv[u] = make_uint4(a.x, a.y, a.z, a.w);
+          vv[u] = make_uint4(c.x, c.y, c.z, c.w);
+#else
           kv[u] = k_src[src];
           vv[u] = v_src[src];
+#endif
         }
       }
     }

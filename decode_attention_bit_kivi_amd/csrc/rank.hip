@@ -243,11 +243,11 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* _
 
 }  // namespace
 
-hipError_t launch_rank_select(const Dims& d, const ScorePlan& plan, const float* logits,
-                              const float* part_m, const float* part_l, int k, float* keys, uint32_t* hist,
-                              int32_t* idx_out, hipStream_t s) {
+hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
+                              const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
+                              hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(d.N, kKeyChunk), (unsigned)d.slices());
-  rank_keys_kernel<<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, plan.S, d.N, keys, hist);
+  rank_keys_kernel<<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, S, d.N, keys, hist);
   rank_select_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, idx_out);
   return hipGetLastError();
 }

@@ -18,6 +18,11 @@
  *   Attn(.., C' U C_kappa) (Algorithm 3)      -> specache_decode_attn
  *   Offload(C)             is the caller's own device-to-host copy.
  *
+ * specache_decode_step fuses the last two compute steps of one decode step:
+ * the attention of Algorithm 3 and the ArgTopK of its speculative row come
+ * out of one pass over C' (the speculative row's logits against C' are
+ * formed by that attention anyway).
+ *
  * ------------------------------------------------------------------------
  * Conventions (every call)
  * ------------------------------------------------------------------------
@@ -31,6 +36,11 @@
  *  - The library keeps no state and allocates nothing: scratch space comes
  *    from a caller-provided workspace whose size the *_workspace_size
  *    functions return.
+ *  - The attention calls split the positions of each slice over a number of
+ *    workgroups chosen for the compute units `stream` may use (its CU mask,
+ *    else the whole device).  Results are deterministic for a given stream
+ *    configuration; on streams with different CU counts they may differ in
+ *    the last bits (the order of float32 accumulation changes).
  *  - Return value: a specache_status.  Argument errors are detected on the
  *    host before anything is enqueued; SPECACHE_ERR_HIP means a HIP runtime
  *    call or a kernel launch failed (faults inside kernels surface at the
@@ -104,7 +114,7 @@
 extern "C" {
 #endif
 
-#define SPECACHE_ABI_VERSION 1
+#define SPECACHE_ABI_VERSION 2
 
 typedef enum specache_status {
   SPECACHE_OK = 0,
@@ -185,6 +195,37 @@ int specache_gather_fp16(const specache_shape* shape, const int32_t* idx, int k,
                          void* stream);
 
 /*
+ * A stream for specache_gather_fp16 whose kernels run on only `n_cus` compute
+ * units of the current device (hipExtStreamCreateWithCUMask, default
+ * priority).  The prefetch is meant to run in the background, in parallel
+ * with the compute that follows (SpeCache summary, quick read, second
+ * mechanism; §3); a zero-copy gather waits on the host link for most of its
+ * life, and the compute units that host its waves serve other kernels'
+ * memory requests far slower meanwhile, so confining it to a few compute
+ * units keeps the overlapped attention and scoring at full speed.  8 units
+ * sustain the host link.  8 <= n_cus <= the device's compute-unit count (the
+ * runtime needs at least one unit on each of the 8 accelerator complex dies;
+ * the low mask bits interleave over them).
+ * *stream_out receives a hipStream_t owned by the caller; release it with
+ * specache_stream_destroy.  It is a blocking stream (the runtime creates
+ * CU-masked streams without hipStreamNonBlocking): work on the legacy default
+ * (NULL) stream serializes with it, so run the overlapped compute on a
+ * non-default stream.
+ */
+int specache_gather_stream_create(int n_cus, void** stream_out);
+
+/*
+ * The complement of specache_gather_stream_create(reserved_cus): a stream
+ * whose kernels run on every compute unit except the `reserved_cus` ones a
+ * gather stream of that size uses, so that the overlapped compute never shares
+ * a compute unit with the gather's waves.  8 <= reserved_cus, and at least 8
+ * units must remain.  Blocking stream, released with
+ * specache_stream_destroy, like the gather stream.
+ */
+int specache_compute_stream_create(int reserved_cus, void** stream_out);
+int specache_stream_destroy(void* stream);
+
+/*
  * O = Attn([T_t, T'_{t+1}], C' U C_kappa) (the summary's quick read, third
  * mechanism; §3 "decoding"; Algorithm 3): softmax attention of every query
  * row over the N cached positions, where the k positions listed in idx use
@@ -206,6 +247,35 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
                          const specache_lowbit* cache, const int32_t* idx, int k,
                          const void* k_sel, const void* v_sel, const void* k_tail,
                          const void* v_tail, int tail_len, float sm_scale, void* out16,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step's compute in one pass over C' (Algorithm 3 of the
+ * SpeCache summary: Attn over C' U C_kappa, and ArgTopK(A_{1,:}) of the
+ * speculative row for the next step's prefetch).  Equivalent to
+ *     specache_decode_attn(shape, q16, n_tokens, cache, idx, k, k_sel, v_sel,
+ *                          k_tail, v_tail, tail_len, sm_scale, out16, ...)
+ *     specache_score_topk(shape, q16, n_tokens, rank_row, cache, sm_scale,
+ *                         k_next, idx_next_out, rank_key_out, ...)
+ * (same out16 bits; the ranking is the one of specache_score_topk, the
+ * logits of row rank_row against C' with the 16-bit rows and the tail
+ * taking no part) but the low-bit cache is read once.
+ *
+ * Arguments as for the two calls; 0 <= rank_row < n_tokens;
+ * 1 <= k_next <= N; idx_next_out [B][Hkv][k_next] int32, ascending.
+ * idx_next_out may be the same buffer as idx (the attention has consumed idx
+ * before the selection writes, in stream order); rank_key_out [B][Hkv][N]
+ * float32 or NULL.  Workspace: specache_decode_step_workspace_size bytes,
+ * device memory (it holds the speculative row's logits, 4*B*Hq*N bytes, plus
+ * the attention partials).
+ */
+size_t specache_decode_step_workspace_size(const specache_shape* shape, int n_tokens, int k,
+                                           int tail_len, int k_next);
+int specache_decode_step(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
+                         const specache_lowbit* cache, const int32_t* idx, int k,
+                         const void* k_sel, const void* v_sel, const void* k_tail,
+                         const void* v_tail, int tail_len, float sm_scale, void* out16,
+                         int k_next, int32_t* idx_next_out, float* rank_key_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */

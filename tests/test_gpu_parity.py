@@ -6,7 +6,9 @@ Bars (fixed before the kernels were written):
     difference with the oracle's set has an oracle rank within 1e-5 of the k-th
     largest (ties go to the lower position);
   * gather_fp16: bitwise copy;
-  * decode_attn: max |O_gpu - O_ref| / max |O_ref| <= 2e-3 (float16 output).
+  * decode_attn: max |O_gpu - O_ref| / max |O_ref| <= 2e-3 (float16 output);
+  * decode_step: O bitwise equal to decode_attn's on the same inputs, and the
+    next selection held to score_topk's bar.
 Small cases are checked in full; the large workloads run at full size in the
 launch configuration the benchmark uses, with a few seeded slices filled and
 checked against the oracle (the other slices are left zero).
@@ -21,7 +23,8 @@ import torch
 
 import oracle
 from decode_attention_bit_kivi_amd import (
-    quantize_pack, score_topk, gather_fp16, decode_attn, SpecacheError,
+    quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, GatherStream, ComputeStream,
+    SpecacheError,
 )
 from tests.layout import unpack_keys, unpack_values
 from workloads import get_config, generate_all
@@ -263,6 +266,99 @@ def test_decode_attn_matches_oracle(gpu, name, over, mode):
     assert err <= ATTN_TOL, err
 
 
+@pytest.mark.parametrize("name,over,mode", [
+    ("tiny", {}, "none"),
+    ("tiny", {}, "random"),
+    ("tiny", dict(bits=2), "all"),                           # every low-bit row replaced
+    ("tiny", dict(seq_len=96, top_k=96), "tail"),            # k_next = N
+    ("tiny", dict(n_tokens=1, top_k=1), "random"),           # pre-decoding shape, row 0
+    ("llama8k", {}, "random"),
+    ("llama8k", dict(bits=1, seed=4, tail_len=3), "tail"),
+    ("llama8k", dict(seq_len=8192 + 96, seed=5), "random"),  # ragged last split
+    ("llama8k", dict(n_q_heads=64, n_kv_heads=8), "random"),  # G = 8: 16 rows
+])
+def test_fused_step_matches_separate_calls(gpu, name, over, mode):
+    cfg = get_config(name).with_(**over)
+    if mode == "tail" and cfg.tail_len == 0:
+        cfg = cfg.with_(tail_len=2)
+    K, V, Q, _, KT, VT = generate_all(cfg)
+    B, Hkv, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    rng = np.random.default_rng(11)
+    idx = None
+    if mode in ("random", "tail"):
+        idx = _random_idx(rng, B, Hkv, N, min(cfg.top_k, N))
+    elif mode == "all":
+        idx = np.broadcast_to(np.arange(N, dtype=np.int32), (B, Hkv, N)).copy()
+    ks = vs = None
+    if idx is not None:
+        ks, vs = oracle.gather_rows(K, V, idx)
+    args = (_dev(Q), cache, None if idx is None else _dev(idx), None if ks is None else _dev(ks),
+            None if vs is None else _dev(vs), None if KT is None else _dev(KT), None if VT is None else _dev(VT))
+    row = 1 if cfg.n_tokens == 2 else 0
+    o_sep = decode_attn(*args)
+    rk = torch.empty((B, Hkv, N), dtype=torch.float32, device="cuda")
+    o_fused, idx_next = decode_step(args[0], cache, cfg.top_k, rank_row=row, idx=args[2], k_sel=args[3],
+                                    v_sel=args[4], k_tail=args[5], v_tail=args[6], rank_key_out=rk)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fused.view(torch.int16), o_sep.view(torch.int16))
+    _, kh, vh = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores(Q, kh, row, cfg.sm_scale)
+    slices = [(b, h) for b in range(B) for h in range(Hkv)]
+    _assert_topk(_np(idx_next), r_ref, cfg.top_k, slices)
+    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    ref = oracle.mixed_attention(Q, kh, vh, idx, ks, vs, KT, VT, sm_scale=cfg.sm_scale)
+    assert _attn_err(_np(o_fused), ref) <= ATTN_TOL
+
+
+def test_fused_step_next_selection_may_alias_current(gpu):
+    cfg = get_config("llama8k").with_(seq_len=4096, seed=7)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    q = _dev(Q)
+    idx = score_topk(q, cache, cfg.top_k)
+    hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
+    ks, vs = gather_fp16(idx, hk, hv)
+    o_sep = decode_attn(q, cache, idx, ks, vs)
+    want_next = score_topk(q, cache, cfg.top_k).clone()
+    o, nxt = decode_step(q, cache, cfg.top_k, idx=idx, k_sel=ks, v_sel=vs, idx_next_out=idx)
+    torch.cuda.synchronize()
+    assert nxt.data_ptr() == idx.data_ptr()
+    assert torch.equal(o.view(torch.int16), o_sep.view(torch.int16))
+    _, kh, _ = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
+    slices = [(0, h) for h in range(cfg.n_kv_heads)]
+    _assert_topk(_np(nxt), r_ref, cfg.top_k, slices)
+    _assert_topk(_np(want_next), r_ref, cfg.top_k, slices)
+
+
+@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
+def test_fused_step_full_size_sampled(gpu, name):
+    """Two chained fused steps at full size, in the benchmark's launch configuration:
+    score_topk seeds the first selection, each step gathers its rows from pinned
+    host memory and returns the next selection."""
+    cfg = get_config(name)
+    sl = _sampled(cfg, 3)
+    K, V, Q, _, _, _ = generate_all(cfg, slices=sl)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    q = _dev(Q)
+    hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
+    idx = score_topk(q, cache, cfg.top_k)
+    ks, vs = gather_fp16(idx, hk, hv)
+    out, nxt = decode_step(q, cache, cfg.top_k, idx=idx, k_sel=ks, v_sel=vs)
+    idx_np, out, nxt = _np(idx), _np(out), _np(nxt)
+    G = cfg.gqa
+    for (b, h) in sl:
+        q1 = Q[b:b + 1, h * G:(h + 1) * G]
+        _, kh, vh = _reference_cache(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], cfg.bits)
+        i = idx_np[b:b + 1, h:h + 1]
+        rks, rvs = oracle.gather_rows(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], i)
+        ref = oracle.mixed_attention(q1, kh, vh, i, rks, rvs, sm_scale=cfg.sm_scale)
+        assert _attn_err(out[b:b + 1, h * G:(h + 1) * G], ref) <= ATTN_TOL
+        r_ref = oracle.rank_scores(q1, kh, 1, cfg.sm_scale)
+        _assert_topk(nxt[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)])
+
+
 @pytest.mark.parametrize("name", ["mistral32k", "long128k"])
 def test_decode_step_full_size_sampled(gpu, name):
     """The whole step at full size: score_topk -> gather from pinned host -> decode_attn."""
@@ -285,31 +381,77 @@ def test_decode_step_full_size_sampled(gpu, name):
         assert _attn_err(out[b:b + 1, h * G:(h + 1) * G], ref) <= ATTN_TOL
 
 
-def test_overlapped_streams_match_serial(gpu):
+def test_gather_on_cu_limited_stream(gpu):
+    cfg = get_config("llama8k").with_(seq_len=4096, batch=2)
+    K, V, _, _, _, _ = generate_all(cfg)
+    rng = np.random.default_rng(6)
+    idx = _dev(_random_idx(rng, cfg.batch, cfg.n_kv_heads, cfg.seq_len, 50))
+    hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
+    gs = GatherStream(8)
+    ev = torch.cuda.Event()
+    ev.record()
+    gs.torch.wait_event(ev)
+    ks, vs = gather_fp16(idx, hk, hv, stream=gs)
+    gs.torch.synchronize()
+    wk, wv = oracle.gather_rows(K, V, _np(idx))
+    assert np.array_equal(_np(ks).view(np.uint16), wk.view(np.uint16))
+    assert np.array_equal(_np(vs).view(np.uint16), wv.view(np.uint16))
+    gs.close()
+    with pytest.raises(SpecacheError):
+        GatherStream(100000)
+    with pytest.raises(SpecacheError):
+        GatherStream(4)
+    with pytest.raises(SpecacheError):
+        ComputeStream(4)
+    with pytest.raises(SpecacheError):
+        ComputeStream(100000)
+
+
+@pytest.mark.parametrize("compute", ["torch", "exclusive"])
+def test_overlapped_streams_match_serial(gpu, compute):
     """score_topk on the compute stream, gather on a side stream after an event,
-    attention after the gather's event: bitwise equal to the serialized run."""
+    attention after the gather's event, then the fused step: bitwise equal to the
+    same calls serialized on the same compute stream (the split plan follows the
+    stream's compute units).  The compute stream is a plain torch stream or the
+    library's stream on the compute units the gather stream leaves free."""
     cfg = get_config("llama8k").with_(batch=2)
     K, V, Q, _, _, _ = generate_all(cfg)
     cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
     q = _dev(Q)
     hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
-    idx0 = score_topk(q, cache, cfg.top_k)
-    ks0, vs0 = gather_fp16(idx0, hk, hv)
-    o0 = decode_attn(q, cache, idx0, ks0, vs0)
-    torch.cuda.synchronize()
+    gs = GatherStream(8)
+    side = gs.torch
+    cs = ComputeStream(8) if compute == "exclusive" else None
+    comp = cs.torch if cs else torch.cuda.Stream()   # non-default: the gather stream is a blocking stream
+    comp.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(comp):
+        idx0 = score_topk(q, cache, cfg.top_k)
+        ks0, vs0 = gather_fp16(idx0, hk, hv)
+        o0 = decode_attn(q, cache, idx0, ks0, vs0)
+        of0, nx0 = decode_step(q, cache, cfg.top_k, idx=idx0, k_sel=ks0, v_sel=vs0)
+        comp.synchronize()
 
-    side = torch.cuda.Stream()
-    ks = torch.full_like(ks0, float("nan"))
-    vs = torch.full_like(vs0, float("nan"))
-    idx = score_topk(q, cache, cfg.top_k)
-    ev = torch.cuda.Event()
-    ev.record()
-    side.wait_event(ev)
-    gather_fp16(idx, hk, hv, k_sel=ks, v_sel=vs, stream=side)
-    ev2 = torch.cuda.Event()
-    ev2.record(side)
-    torch.cuda.current_stream().wait_event(ev2)
-    o1 = decode_attn(q, cache, idx, ks, vs)
+        ks = torch.full_like(ks0, float("nan"))
+        vs = torch.full_like(vs0, float("nan"))
+        idx = score_topk(q, cache, cfg.top_k)
+        ev = torch.cuda.Event()
+        ev.record(comp)
+        side.wait_event(ev)
+        gather_fp16(idx, hk, hv, k_sel=ks, v_sel=vs, stream=side)
+        ev2 = torch.cuda.Event()
+        ev2.record(side)
+        comp.wait_event(ev2)
+        o1 = decode_attn(q, cache, idx, ks, vs)
+        of1, nx1 = decode_step(q, cache, cfg.top_k, idx=idx, k_sel=ks, v_sel=vs)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx0)
     assert torch.equal(o1.view(torch.int16), o0.view(torch.int16))
+    assert torch.equal(of1.view(torch.int16), of0.view(torch.int16))
+    assert torch.equal(nx1, nx0)
+    # the result on the default stream (whole device) agrees to the attention tolerance
+    o_dev = decode_attn(q, cache, idx0, ks0, vs0)
+    torch.cuda.synchronize()
+    assert _attn_err(_np(o1), _np(o_dev).astype(np.float64)) <= ATTN_TOL
+    gs.close()
+    if cs:
+        cs.close()
