@@ -1,22 +1,28 @@
 // ArgTopK of the speculative row: merge the split statistics into each head's
 // log-sum-exp, form the rank r(p) = log sum_g exp(s_g(p) - LSE_g) (the
-// attention mass the G heads put on p), and select the k largest with a
-// most-significant-digit radix select, ties to the lower position, emitted in
-// ascending order.
+// attention mass the G heads put on p), and select the k largest, ties to the
+// lower position, emitted in ascending order.
 //
 // SpeCache summary, §7 Algorithms 2 and 3 (ArgTopK of the attention row), and
 // §2 "attention sparsity" (a position is worth the attention mass it holds).
 //
 // Two kernels:
 //   rank_keys    (grid: position chunks x slices) computes r(p) for every
-//                position, writes it as an order-preserving 32-bit key, and
-//                adds the histogram of the keys' top 11 bits into a per-slice
-//                global histogram (zeroed by the score kernel of the same call);
-//   rank_select  (one 1024-thread workgroup per slice) picks the digit that
-//                holds the k-th largest key, refines it with two more digit
-//                passes (11 and 10 bits), and compacts the selected positions
-//                in ascending order.  Both passes and the compaction read the
-//                keys (L2-resident) as 32 consecutive keys per thread.
+//                position, writes it, and adds a coarse histogram of r into a
+//                per-slice global histogram (zeroed by the kernel that wrote
+//                the logits).  The coarse bins are linear in r over a window of
+//                32 below log G (r <= log G always): 64 bins per unit of r.
+//   rank_select  (one 1024-thread workgroup per slice) finds the coarse bin
+//                that holds the k-th largest r, gathers that bin's keys into
+//                LDS in one sweep, finds the exact k-th largest key there by a
+//                three-digit radix select, and in a second sweep marks the
+//                selected positions in LDS bitmaps (128K positions at a time),
+//                whose set bits one prefix sum turns into the ascending output.
+//                A bin too large for LDS falls back to the radix select over
+//                all keys (three sweeps).  Every sweep reads 4096 consecutive
+//                values per step, a float4 per thread.
+//   The exact selection compares order-preserving 32-bit integer keys of the
+//   float r.
 #include "common.h"
 
 namespace specache {
@@ -25,16 +31,31 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRun = 32;                       // consecutive keys per thread in rank_select
-constexpr int kTile = kSelThreads * kRun;      // positions per rank_select sweep
 constexpr int kKeyThreads = 256;
 constexpr int kKeyChunk = kKeyThreads * 16;    // positions per rank_keys workgroup
+constexpr int kBins = 2048;
+constexpr float kBinSpan = 32.0f;              // r window of the coarse bins, below log G
+constexpr float kBinScale = kBins / kBinSpan;  // bins per unit of r (a power of two: exact)
+constexpr int kCand = 16384;                   // keys of the threshold bin held in LDS
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint32_t order_key(float r) {
   const uint32_t f = __float_as_uint(r);
   return (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Coarse bin of r: non-decreasing in r (subtraction and truncation are monotone, the scale is
+// exact), so every key of a higher bin is larger than every key of a lower one.
+__device__ __forceinline__ uint32_t coarse_bin(float r, float r_lo) {
+  const float x = (r - r_lo) * kBinScale;
+  if (!(x >= 0.0f)) return 0u;  // below the window (or NaN)
+  if (x >= (float)(kBins - 1)) return kBins - 1;
+  return (uint32_t)x;
 }
 
 // Exclusive prefix sum over the 1024-thread workgroup; returns the exclusive value, writes the total.
@@ -66,179 +87,358 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 
 // ---------------------------------------------------------------- rank_keys
 
+template <int GM>  // GM >= G: the heads' logits of a run are held in registers
 __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* __restrict__ logits,
                                                                 const float* __restrict__ part_m,
                                                                 const float* __restrict__ part_l, int G, int S,
-                                                                int64_t N, float* __restrict__ rkey,
+                                                                int64_t N, float r_lo, float* __restrict__ rkey,
                                                                 uint32_t* __restrict__ ghist) {
-  __shared__ float lse2[kMaxRows];  // log2-sum-exp2 of each head, in log2 units
-  __shared__ uint32_t hist[2048];
+  __shared__ float lse2[GM];  // log2-sum-exp2 of each head, in log2 units
+  __shared__ uint32_t hist[kBins];
   const int t = threadIdx.x;
   const int64_t slice = blockIdx.y;
   const int64_t c0 = (int64_t)blockIdx.x * kKeyChunk;
-  if (t < G) {  // split statistics are (max, sum 2^(x - max)) in log2 units
-    const float* pm = part_m + (slice * G + t) * S;
-    const float* pl = part_l + (slice * G + t) * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pm[s]);
-    float Ls = 0.0f;
-    for (int s = 0; s < S; ++s)
-      if (pm[s] != -INFINITY) Ls += pl[s] * exp2f(pm[s] - M);
-    lse2[t] = M + log2f(Ls);
+  {
+    // Each head's log-sum-exp from the split statistics (max, sum 2^(x - max)), log2 units:
+    // kKeyThreads / GM threads per head load the splits in parallel and merge by shuffles.
+    constexpr int TPH = kKeyThreads / GM;  // 64, 32 or 16: within one wave
+    const int g = t / TPH, j = t % TPH;
+    float M = -INFINITY, L = 0.0f;
+    if (g < G) {
+      const float* pm = part_m + (slice * G + g) * S;
+      const float* pl = part_l + (slice * G + g) * S;
+      for (int s = j; s < S; s += TPH) {
+        const float m = pm[s], l = pl[s];
+        const float mn = fmaxf(M, m);
+        L = (M == -INFINITY ? 0.0f : L * exp2f(M - mn)) + (m == -INFINITY ? 0.0f : l * exp2f(m - mn));
+        M = mn;
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < TPH; off <<= 1) {
+      const float m = __shfl_xor(M, off), l = __shfl_xor(L, off);
+      const float mn = fmaxf(M, m);
+      L = (M == -INFINITY ? 0.0f : L * exp2f(M - mn)) + (m == -INFINITY ? 0.0f : l * exp2f(m - mn));
+      M = mn;
+    }
+    if (g < G && j == 0) lse2[g] = M + log2f(L);
   }
-  for (int i = t; i < 2048; i += kKeyThreads) hist[i] = 0u;
-  __syncthreads();
+  for (int i = t; i < kBins; i += kKeyThreads) hist[i] = 0u;
 
-  // each thread: 4 runs of 4 consecutive positions (float4 per head)
+  // each thread: 4 runs of 4 consecutive positions (a float4 per head); NB runs' loads are in
+  // flight at a time (all four for up to 4 heads)
+  constexpr int NB = GM <= 4 ? 4 : 2;
   const float* lg = logits + slice * G * N;
+  float4 x[NB][GM];
+  auto load = [&](int rr, float4 (&dst)[GM]) {
+    const int64_t p = c0 + 4 * (t + rr * kKeyThreads);
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+      if (g < G && p < N) dst[g] = *reinterpret_cast<const float4*>(lg + (int64_t)g * N + p);
+  };
+#pragma unroll
+  for (int rr = 0; rr < NB - 1; ++rr) load(rr, x[rr]);
+  __syncthreads();
+  uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
+    if (rr + NB - 1 < 4) load(rr + NB - 1, x[(rr + NB - 1) % NB]);
     const int64_t p = c0 + 4 * (t + rr * kKeyThreads);
-    if (p >= N) break;
-    float4 x[kMaxRows];
+    if (p < N) {  // N is a multiple of 32: the whole float4 is in range
+      float r[4];
 #pragma unroll
-    for (int g = 0; g < kMaxRows; ++g)
-      if (g < G) x[g] = *reinterpret_cast<const float4*>(lg + (int64_t)g * N + p);
-    float r[4];
+      for (int e = 0; e < 4; ++e) {
+        float lp[GM];
+        float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float lp[kMaxRows];
-      float mx = -INFINITY;
+        for (int g = 0; g < GM; ++g)
+          if (g < G) {
+            const float4 v4 = x[rr % NB][g];
+            const float v = e == 0 ? v4.x : (e == 1 ? v4.y : (e == 2 ? v4.z : v4.w));
+            lp[g] = fmaf(v, kLog2e, -lse2[g]);  // log2 of the head's probability
+            mx = fmaxf(mx, lp[g]);
+          }
+        float sum = 0.0f;
 #pragma unroll
-      for (int g = 0; g < kMaxRows; ++g)
-        if (g < G) {
-          const float v = e == 0 ? x[g].x : (e == 1 ? x[g].y : (e == 2 ? x[g].z : x[g].w));
-          lp[g] = fmaf(v, kLog2e, -lse2[g]);  // log2 of the head's probability
-          mx = fmaxf(mx, lp[g]);
-        }
-      float sum = 0.0f;
+        for (int g = 0; g < GM; ++g)
+          if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
+        // v_log_f32 is log2; adding +0 turns a -0 into +0, so that comparing the floats and
+        // comparing their order-preserving keys agree
+        r[e] = (mx + __builtin_amdgcn_logf(sum)) * kLn2 + 0.0f;
+      }
+      *reinterpret_cast<float4*>(rkey + slice * N + p) = make_float4(r[0], r[1], r[2], r[3]);
 #pragma unroll
-      for (int g = 0; g < kMaxRows; ++g)
-        if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
-      r[e] = (mx + __builtin_amdgcn_logf(sum)) * kLn2;  // v_log_f32 is log2
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b = coarse_bin(r[e], r_lo);
+        if (cur_cnt != 0u && b != cur_bin) atomicAdd(&hist[cur_bin], cur_cnt), cur_cnt = 0u;
+        cur_bin = b;
+        ++cur_cnt;
+      }
     }
-    *reinterpret_cast<float4*>(rkey + slice * N + p) = make_float4(r[0], r[1], r[2], r[3]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) atomicAdd(&hist[order_key(r[e]) >> 21], 1u);
   }
+  if (cur_cnt) atomicAdd(&hist[cur_bin], cur_cnt);
   __syncthreads();
-  uint32_t* gh = ghist + slice * 2048;
-  for (int i = t; i < 2048; i += kKeyThreads)
+  uint32_t* gh = ghist + slice * kBins;
+  for (int i = t; i < kBins; i += kKeyThreads)
     if (hist[i]) atomicAdd(&gh[i], hist[i]);
 }
 
 // ---------------------------------------------------------------- rank_select
 
-// 32 keys of one thread's run, as order-preserving integers (positions >= N read as 0).
-__device__ __forceinline__ void load_run(const float* ky, int64_t N, int64_t p, uint32_t (&u)[kRun]) {
-  if (p + kRun <= N) {
+constexpr int kChunk = 131072;        // positions per compaction chunk
+constexpr int kWords = kChunk / 32;   // bitmap words of a chunk
+constexpr int kWordsPerThread = kWords / kSelThreads;
+
+struct SelectSmem {
+  uint32_t hist[kBins];
+  uint32_t scan_scratch[2 * kSelWaves];
+  uint32_t sel_digit, sel_above, n_cand;
+  union {
+    uint32_t cand[kCand];  // keys of the threshold bin
+    struct {
+      uint32_t gt[kWords];  // positions of the chunk above the threshold
+      uint32_t eq[kWords];  // positions of the chunk equal to it
+    } bm;
+  } u;
+};
+
+// Visit the values of positions [p0, p1) (multiples of 4), coalesced: each float4 load of the
+// workgroup reads 4096 consecutive values, and a thread has kSweepU of them in flight before
+// it processes any.  fn(base, v) gets this thread's values of one step: v[4u + e] is position
+// base + 4 * (threadIdx.x + u * kSelThreads) + e, -inf past p1.
+constexpr int kSweepU = 8;
+template <typename Fn>
+__device__ __forceinline__ void sweep(const float* ky, int64_t p0, int64_t p1, Fn fn) {
+  for (int64_t base = p0; base < p1; base += (int64_t)kSweepU * 4 * kSelThreads) {
+    float v[4 * kSweepU];
 #pragma unroll
-    for (int v = 0; v < kRun / 4; ++v) {
-      const float4 f = *reinterpret_cast<const float4*>(ky + p + 4 * v);
-      u[4 * v] = order_key(f.x);
-      u[4 * v + 1] = order_key(f.y);
-      u[4 * v + 2] = order_key(f.z);
-      u[4 * v + 3] = order_key(f.w);
+    for (int u = 0; u < kSweepU; ++u) {
+      const int64_t p = base + 4 * ((int64_t)threadIdx.x + u * kSelThreads);
+      const float4 f = p < p1 ? *reinterpret_cast<const float4*>(ky + p)
+                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      v[4 * u] = f.x;
+      v[4 * u + 1] = f.y;
+      v[4 * u + 2] = f.z;
+      v[4 * u + 3] = f.w;
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kRun; ++e) u[e] = p + e < N ? order_key(ky[p + e]) : 0u;
+    fn(base, v);
   }
+}
+
+__device__ __forceinline__ int64_t sweep_pos(int64_t base, int i) {
+  return base + 4 * ((int64_t)threadIdx.x + (i >> 2) * kSelThreads) + (i & 3);
+}
+
+// The digit of hist[0, nbins) holding the krem-th largest element, counted from the top, and the
+// number of elements in the digits above it.
+__device__ __forceinline__ void pick_digit(SelectSmem& sm, int nbins, uint32_t krem, uint32_t& digit,
+                                           uint32_t& above) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    sm.sel_digit = 0u;
+    sm.sel_above = 0u;
+  }
+  // thread t covers digits nbins-1-2t and nbins-2-2t
+  const int dhi = nbins - 1 - 2 * t, dlo = dhi - 1;
+  const uint32_t hhi = dhi >= 0 ? sm.hist[dhi] : 0u;
+  const uint32_t hlo = dlo >= 0 ? sm.hist[dlo] : 0u;
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(hhi + hlo, sm.scan_scratch, tot);
+  if (dhi >= 0 && excl < krem && excl + hhi >= krem) {
+    sm.sel_digit = (uint32_t)dhi;
+    sm.sel_above = excl;
+  } else if (dlo >= 0 && excl + hhi < krem && excl + hhi + hlo >= krem) {
+    sm.sel_digit = (uint32_t)dlo;
+    sm.sel_above = excl + hhi;
+  }
+  __syncthreads();
+  digit = sm.sel_digit;
+  above = sm.sel_above;
+  __syncthreads();
+}
+
+// Exact radix select: the krem-th largest key among those `count` feeds to the histogram, as
+// (key thr, number of keys equal to thr to take, number of keys equal to thr).
+// count(shift, nbins, prefix, mask) adds every key u with (u & mask) == prefix to
+// sm.hist[(u >> shift) & (nbins - 1)].
+template <typename Count>
+__device__ __forceinline__ void radix_select(SelectSmem& sm, uint32_t krem, Count count, uint32_t& thr,
+                                             uint32_t& need_eq, uint32_t& n_eq) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0u, mask = 0u;
+  for (int pass = 0; pass < 3; ++pass) {  // digits: bits 31..21, 20..10, 9..0
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nbins = pass == 2 ? 1024 : 2048;
+    for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    count(shift, nbins, prefix, mask);
+    __syncthreads();
+    uint32_t dg, ab;
+    pick_digit(sm, nbins, krem, dg, ab);
+    prefix |= dg << shift;
+    mask |= (uint32_t)(nbins - 1) << shift;
+    krem -= ab;
+    if (pass == 2) n_eq = sm.hist[dg];  // the last digit's bin holds exactly the keys equal to thr
+  }
+  thr = prefix;
+  need_eq = krem;
+}
+
+// Smallest order key of a non-NaN value whose coarse bin is >= b, for b < kBins.  Between the
+// keys of -inf and +inf the bins are non-decreasing in the key, and bin(+inf) = kBins - 1 >= b.
+__device__ uint32_t first_key_of_bin(uint32_t b, float r_lo) {
+  uint32_t lo = 0x007fffffu, hi = 0xff800000u;  // order keys of -inf and +inf
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (coarse_bin(key_value(mid), r_lo) >= b) hi = mid; else lo = mid + 1u;
+  }
+  return lo;
 }
 
 __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* __restrict__ rkey,
                                                                   const uint32_t* __restrict__ ghist, int64_t N,
-                                                                  int k, int32_t* __restrict__ idx_out) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t scan_scratch[2 * kSelWaves];
-  __shared__ uint32_t sel_digit, sel_above;
-
-  const int t = threadIdx.x;
+                                                                  int k, float r_lo, int32_t* __restrict__ idx_out) {
+  __shared__ SelectSmem sm;
+  __shared__ float bin_vals[2];
+  const int t = threadIdx.x, lane = t & 63;
   const int64_t slice = blockIdx.x;
   const float* ky = rkey + slice * N;
-  const uint32_t* gh = ghist + slice * 2048;
-  for (int i = t; i < 2048; i += kSelThreads) hist[i] = gh[i];
-  if (t == 0) {
-    sel_digit = 0u;
-    sel_above = 0u;
-  }
+  const uint32_t* gh = ghist + slice * kBins;
+  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
+  if (t == 0) sm.n_cand = 0u;
   __syncthreads();
 
-  // digits: bits 31..21 (11, histogram from rank_keys), 20..10 (11), 9..0 (10)
-  uint32_t prefix = 0u, mask = 0u, krem = (uint32_t)k;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 2 ? 1024 : 2048;
-    if (pass > 0) {
-      for (int i = t; i < 2048; i += kSelThreads) hist[i] = 0u;
-      __syncthreads();
-      for (int64_t p0 = 0; p0 < N; p0 += kTile) {
-        const int64_t p = p0 + (int64_t)t * kRun;
-        if (p < N) {
-          uint32_t u[kRun];
-          load_run(ky, N, p, u);
-#pragma unroll
-          for (int e = 0; e < kRun; ++e)
-            if (p + e < N && (u[e] & mask) == prefix) atomicAdd(&hist[(u[e] >> shift) & (uint32_t)(nbins - 1)], 1u);
-        }
-      }
-      __syncthreads();
-    }
-    // counts from the top digit down: thread t covers digits nbins-1-2t and nbins-2-2t
-    const int dhi = nbins - 1 - 2 * t, dlo = dhi - 1;
-    const uint32_t hhi = dhi >= 0 ? hist[dhi] : 0u;
-    const uint32_t hlo = dlo >= 0 ? hist[dlo] : 0u;
-    uint32_t tot;
-    const uint32_t excl = block_exclusive_scan(hhi + hlo, scan_scratch, tot);
-    if (dhi >= 0 && excl < krem && excl + hhi >= krem) {
-      sel_digit = (uint32_t)dhi;
-      sel_above = excl;
-    } else if (dlo >= 0 && excl + hhi < krem && excl + hhi + hlo >= krem) {
-      sel_digit = (uint32_t)dlo;
-      sel_above = excl + hhi;
-    }
-    __syncthreads();
-    prefix |= sel_digit << shift;
-    mask |= (uint32_t)(nbins - 1) << shift;
-    krem -= sel_above;
-    __syncthreads();
-  }
+  uint32_t bin, above;
+  pick_digit(sm, kBins, (uint32_t)k, bin, above);
+  const uint32_t in_bin = sm.hist[bin];
+  // the threshold bin as an interval of values [lo, hi) (the top bin runs to +inf), found by two
+  // binary searches over the keys.  The ranks hold no -0 and no NaN, so comparing the floats
+  // orders them as their keys do.
+  if (t == 0) bin_vals[0] = key_value(first_key_of_bin(bin, r_lo));
+  if (t == 64) bin_vals[1] = bin + 1 < (uint32_t)kBins ? key_value(first_key_of_bin(bin + 1, r_lo)) : INFINITY;
+  __syncthreads();
+  const float va = bin_vals[0], vb = bin_vals[1];
+  const bool top_open = bin + 1 >= (uint32_t)kBins;
 
-  // prefix is the k-th largest key: take every key above it and the first krem equal to it
-  uint32_t out_base = 0u, eq_seen = 0u;
-  for (int64_t p0 = 0; p0 < N; p0 += kTile) {
-    const int64_t p = p0 + (int64_t)t * kRun;
-    uint32_t u[kRun];
-    uint32_t ngt = 0u, neq = 0u;
-    if (p < N) {
-      load_run(ky, N, p, u);
+  uint32_t thr, need_eq, n_thr;
+  if (in_bin <= (uint32_t)kCand) {
+    // gather the threshold bin's keys into LDS (any order)
+    sweep(ky, 0, N, [&](int64_t base, const float (&v)[4 * kSweepU]) {
+      uint32_t mine = 0u;
 #pragma unroll
-      for (int e = 0; e < kRun; ++e) {
-        const bool in = p + e < N;
-        ngt += (in && u[e] > prefix) ? 1u : 0u;
-        neq += (in && u[e] == prefix) ? 1u : 0u;
+      for (int i = 0; i < 4 * kSweepU; ++i)
+        mine |= (sweep_pos(base, i) < N && v[i] >= va && (top_open || v[i] < vb)) ? (1u << i) : 0u;
+      if (!__any(mine != 0u)) return;
+      // slots: one prefix sum over the wave and one LDS atomic per wave
+      const uint32_t n = __popc(mine);
+      uint32_t incl = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
       }
-    }
-    uint32_t eq_tot, take_tot;
-    const uint32_t eq_before = eq_seen + block_exclusive_scan(neq, scan_scratch, eq_tot);
-    const uint32_t eq_take = eq_before >= krem ? 0u : (krem - eq_before < neq ? krem - eq_before : neq);
-    uint32_t out = out_base + block_exclusive_scan(ngt + eq_take, scan_scratch, take_tot);
-    if (p < N) {
-      uint32_t eq_left = eq_take;
+      uint32_t base_slot = 0u;
+      if (lane == 63) base_slot = atomicAdd(&sm.n_cand, incl);
+      base_slot = __shfl(base_slot, 63);
+      uint32_t slot = base_slot + incl - n;
 #pragma unroll
-      for (int e = 0; e < kRun; ++e) {
-        const bool in = p + e < N;
-        bool take = in && u[e] > prefix;
-        if (in && u[e] == prefix && eq_left > 0u) {
-          take = true;
-          --eq_left;
+      for (int i = 0; i < 4 * kSweepU; ++i)
+        if ((mine >> i) & 1u) {
+          if (slot < (uint32_t)kCand) sm.u.cand[slot] = order_key(v[i]);
+          ++slot;
         }
-        if (take && out < (uint32_t)k) idx_out[slice * k + out++] = (int32_t)(p + e);
+    });
+    __syncthreads();
+    const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
+    radix_select(sm, (uint32_t)k - above,
+                 [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+                   for (uint32_t i = t; i < nc; i += kSelThreads) {
+                     const uint32_t u = sm.u.cand[i];
+                     if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                   }
+                 },
+                 thr, need_eq, n_thr);
+  } else {
+    radix_select(sm, (uint32_t)k,
+                 [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+                   sweep(ky, 0, N, [&](int64_t base, const float (&v)[4 * kSweepU]) {
+#pragma unroll
+                     for (int i = 0; i < 4 * kSweepU; ++i) {
+                       const uint32_t u = order_key(v[i]);
+                       if (sweep_pos(base, i) < N && (u & mask) == prefix)
+                         atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                     }
+                   });
+                 },
+                 thr, need_eq, n_thr);
+  }
+  __syncthreads();  // the candidate keys are dead: their LDS becomes the bitmaps
+
+  // Every value above thr and the first need_eq equal to it, in position order: per chunk, mark
+  // them in two bitmaps, then compact the bitmaps' set bits with one prefix sum.
+  const float vthr = key_value(thr);
+  const bool all_eq = need_eq == n_thr;  // every key equal to thr is taken: one bitmap, one prefix sum
+  uint32_t out_base = 0u, eq_seen = 0u;
+  for (int64_t c0 = 0; c0 < N; c0 += kChunk) {
+    const int64_t c1 = c0 + kChunk < N ? c0 + kChunk : N;
+    for (int i = t; i < kWords; i += kSelThreads) {
+      sm.u.bm.gt[i] = 0u;
+      sm.u.bm.eq[i] = 0u;
+    }
+    __syncthreads();
+    sweep(ky, c0, c1, [&](int64_t base, const float (&v)[4 * kSweepU]) {
+#pragma unroll
+      for (int i = 0; i < 4 * kSweepU; ++i) {
+        const int64_t q = sweep_pos(base, i) - c0;
+        if (q >= c1 - c0) continue;
+        if (v[i] > vthr || (all_eq && v[i] == vthr)) atomicOr(&sm.u.bm.gt[q >> 5], 1u << (q & 31));
+        else if (v[i] == vthr) atomicOr(&sm.u.bm.eq[q >> 5], 1u << (q & 31));
+      }
+    });
+    __syncthreads();
+    uint32_t ngt = 0u, neq = 0u;
+#pragma unroll
+    for (int j = 0; j < kWordsPerThread; ++j) {
+      ngt += __popc(sm.u.bm.gt[t * kWordsPerThread + j]);
+      neq += __popc(sm.u.bm.eq[t * kWordsPerThread + j]);
+    }
+    uint32_t eq_tot = 0u, take_tot;
+    uint32_t eq_take = 0u;
+    if (!all_eq) {
+      const uint32_t eq_before = eq_seen + block_exclusive_scan(neq, sm.scan_scratch, eq_tot);
+      eq_take = eq_before >= need_eq ? 0u : (need_eq - eq_before < neq ? need_eq - eq_before : neq);
+    }
+    uint32_t out = out_base + block_exclusive_scan(ngt + eq_take, sm.scan_scratch, take_tot);
+    uint32_t eq_left = eq_take;
+#pragma unroll
+    for (int j = 0; j < kWordsPerThread; ++j) {
+      const int w = t * kWordsPerThread + j;
+      uint32_t m = sm.u.bm.gt[w];
+      uint32_t e = sm.u.bm.eq[w];
+      while (eq_left > 0u && e != 0u) {  // the lowest equal positions first
+        const uint32_t low = e & (0u - e);
+        m |= low;
+        e ^= low;
+        --eq_left;
+      }
+      while (m != 0u) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1u;
+        if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(c0 + 32 * w + b);
+        ++out;
       }
     }
     out_base += take_tot;
     eq_seen += eq_tot;
+    __syncthreads();  // the bitmaps are rewritten by the next chunk
   }
+}
+
+template <int GM>
+void launch_keys(const Dims& d, int S, const float* logits, const float* part_m, const float* part_l, float r_lo,
+                 float* keys, uint32_t* hist, hipStream_t s) {
+  const dim3 grid((unsigned)ceil_div(d.N, kKeyChunk), (unsigned)d.slices());
+  rank_keys_kernel<GM><<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, S, d.N, r_lo, keys, hist);
 }
 
 }  // namespace
@@ -246,9 +446,14 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* _
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
                               hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(d.N, kKeyChunk), (unsigned)d.slices());
-  rank_keys_kernel<<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, S, d.N, keys, hist);
-  rank_select_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, idx_out);
+  const float r_lo = logf((float)d.G) - kBinSpan;  // the same value for both kernels
+  if (d.G <= 4)
+    launch_keys<4>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
+  else if (d.G <= 8)
+    launch_keys<8>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
+  else
+    launch_keys<16>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
+  rank_select_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out);
   return hipGetLastError();
 }
 

@@ -165,6 +165,26 @@ def test_score_topk_matches_oracle(gpu, name, over):
     assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
 
 
+@pytest.mark.parametrize("qscale", [0.0, 1e-3, 1.0])
+def test_score_topk_crowded_and_tied_ranks(gpu, qscale):
+    """qscale 0: every rank equal (one coarse bin holds all 20480 positions, more than the
+    selection keeps in LDS): the k lowest positions.  1e-3: the ranks differ by less than a
+    coarse bin, the threshold bin is crowded with distinct keys.  1: the ordinary spread."""
+    cfg = get_config("llama8k").with_(seq_len=20480, top_k=300, seed=3)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    Q = (Q.astype(np.float32) * qscale).astype(np.float16)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    rk = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    idx = _np(score_topk(_dev(Q), cache, cfg.top_k, rank_key_out=rk))
+    _, kh, _ = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
+    slices = [(0, h) for h in range(cfg.n_kv_heads)]
+    if qscale == 0.0:
+        assert np.array_equal(idx, np.broadcast_to(np.arange(cfg.top_k, dtype=np.int32), idx.shape))
+    _assert_topk(idx, r_ref, cfg.top_k, slices)
+    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+
+
 @pytest.mark.parametrize("name", ["mistral32k", "long128k"])
 def test_score_topk_full_size_sampled(gpu, name):
     cfg = get_config(name)
