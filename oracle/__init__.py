@@ -25,12 +25,12 @@ invariants, brute force).  No function is "parity unpinned".
 from .quantize import (
     quantize_keys, quantize_values, dequantize_keys, dequantize_values, zero_point_scale,
 )
-from .rank import rank_scores, topk_positions, score_topk
+from .rank import rank_scores, rank_scores_mixed, topk_positions, score_topk
 from .attention import mixed_attention, attention_probs
 from .gather import gather_rows
 
 __all__ = [
     "quantize_keys", "quantize_values", "dequantize_keys", "dequantize_values",
-    "zero_point_scale", "rank_scores", "topk_positions", "score_topk",
+    "zero_point_scale", "rank_scores", "rank_scores_mixed", "topk_positions", "score_topk",
     "mixed_attention", "attention_probs", "gather_rows",
 ]

@@ -237,6 +237,69 @@ def test_rank_uses_requested_row():
     assert oracle.topk_positions(oracle.rank_scores(q, k, 1, 1.0), 1)[0, 0, 0] == 30
 
 
+def _torch_mass(q_row, keys, sm_scale, n_cached):
+    """log of the summed softmax mass of the G heads (torch softmax over all given keys) on the
+    first n_cached keys.  q_row [B, Hkv, G, D], keys [B, Hkv, M, D]."""
+    logits = sm_scale * torch.from_numpy(q_row) @ torch.from_numpy(keys).transpose(-1, -2)
+    p = torch.softmax(logits, dim=-1)[..., :n_cached]
+    return torch.log(p.sum(dim=2)).numpy()
+
+
+def test_mixed_rank_fetching_everything_is_fp16_attention_mass():
+    """Algorithm 3's reading with every row fetched: the rank is the attention mass of the
+    16-bit keys, computed here with torch's softmax."""
+    rng = np.random.default_rng(21)
+    q, k = _rand_case(rng, B=2, Hkv=2, G=3, N=64, D=16)
+    k16 = (k + 0.1 * rng.standard_normal(k.shape)).astype(np.float16)
+    idx = np.broadcast_to(np.arange(64, dtype=np.int32), (2, 2, 64)).copy()
+    for row in (0, 1):
+        r = oracle.rank_scores_mixed(q, k, row, 0.3, idx=idx, k_sel=k16)
+        qr = q[:, :, row, :].astype(np.float64).reshape(2, 2, 3, 16)
+        want = _torch_mass(qr, k16.astype(np.float64), 0.3, 64)
+        assert np.allclose(r, want, atol=1e-12)
+
+
+def test_mixed_rank_replaces_fetched_rows_and_normalizes_over_visible_tail():
+    """Fetched rows use their 16-bit keys; the visible tail entries (j <= R - T + t) share
+    each head's softmax but are no candidates."""
+    rng = np.random.default_rng(22)
+    B, Hkv, G, T, N, D, R = 1, 2, 2, 2, 48, 8, 3
+    q, k = _rand_case(rng, B=B, Hkv=Hkv, G=G, T=T, N=N, D=D)
+    idx = np.stack([np.sort(rng.choice(N, 5, replace=False)) for _ in range(Hkv)])[None].astype(np.int32)
+    k_sel = rng.standard_normal((B, Hkv, 5, D)).astype(np.float16)
+    k_tail = rng.standard_normal((B, Hkv, R, D)).astype(np.float16)
+    mixed = k.copy()
+    for h in range(Hkv):
+        mixed[0, h, idx[0, h]] = k_sel[0, h].astype(np.float64)
+    for row in (0, 1):
+        visible = R - T + row + 1
+        keys = np.concatenate([mixed, k_tail[:, :, :visible].astype(np.float64)], axis=2)
+        qr = q[:, :, row, :].astype(np.float64).reshape(B, Hkv, G, D)
+        want = _torch_mass(qr, keys, 0.5, N)
+        got = oracle.rank_scores_mixed(q, k, row, 0.5, idx=idx, k_sel=k_sel, k_tail=k_tail)
+        assert np.allclose(got, want, atol=1e-12)
+        assert np.all(np.exp(got).sum(axis=-1) < G)       # the tail holds some of the mass
+
+
+def test_mixed_rank_hides_the_speculative_entry_from_the_real_row():
+    B, Hkv, G, T, N, D, R = 1, 1, 1, 2, 32, 4, 2
+    k = np.zeros((B, Hkv, N, D))
+    q = np.zeros((B, 1, T, D), dtype=np.float16)
+    q[..., 0] = 1.0
+    k_tail = np.zeros((B, Hkv, R, D), dtype=np.float16)
+    k_tail[0, 0, R - 1, 0] = 30.0                    # the speculative token's own key
+    r0 = oracle.rank_scores_mixed(q, k, 0, 1.0, k_tail=k_tail)
+    r1 = oracle.rank_scores_mixed(q, k, 1, 1.0, k_tail=k_tail)
+    assert np.allclose(np.exp(r0).sum(), N / (N + 1))   # row 0 sees one tail entry, logit 0
+    assert np.exp(r1).sum() < 1e-9                       # row 1 also sees the logit-30 entry
+
+
+def test_mixed_rank_without_fetch_or_tail_is_the_c_prime_rank():
+    rng = np.random.default_rng(23)
+    q, k = _rand_case(rng, G=4)
+    assert np.allclose(oracle.rank_scores_mixed(q, k, 1, 0.25), oracle.rank_scores(q, k, 1, 0.25), atol=1e-12)
+
+
 def test_topk_ties_and_full_set():
     r = np.zeros((1, 2, 50))
     r[0, 1, 7] = 1.0
