@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--gather-cus", type=int, default=8, help="compute units of the gather stream")
     ap.add_argument("--compute-stream", choices=("exclusive", "shared"), default="exclusive",
                     help="exclusive: the compute runs on the compute units the gather stream does not use")
+    ap.add_argument("--rank", choices=("lowbit", "mixed"), default="lowbit",
+                    help="lowbit: rank against C'; mixed: by the attention row itself (fetched rows and tail in)")
     ap.add_argument("--compute-reserve", type=int, default=32,
                     help="with an exclusive compute stream: the low compute units kept from it (the "
                          "gather's among them); 32 leaves every shader engine the same number of units")
@@ -233,8 +235,8 @@ def main():
         l = i % layers
         comp.wait_event(gathered[l])
         mark("d0", comp)
-        decode_step(q, caches[l], k, rank_row=1, idx=idx[l], k_sel=sel[l][0], v_sel=sel[l][1], out=out,
-                    idx_next_out=idx[l], workspace=ws)
+        decode_step(q, caches[l], k, rank_row=1, rank_mixed=args.rank == "mixed", idx=idx[l], k_sel=sel[l][0],
+                    v_sel=sel[l][1], out=out, idx_next_out=idx[l], workspace=ws)
         mark("d1", comp)
         stepped[l].record(comp)
         side.wait_event(stepped[l])
@@ -285,7 +287,7 @@ def main():
 
     nxt = torch.empty_like(idx[0])
     fused_us = compute_loop(lambda i: decode_step(
-        q, caches[i % layers], k, rank_row=1, idx=idx[i % layers], k_sel=sel[i % layers][0],
+        q, caches[i % layers], k, rank_row=1, rank_mixed=args.rank == "mixed", idx=idx[i % layers], k_sel=sel[i % layers][0],
         v_sel=sel[i % layers][1], out=out, idx_next_out=nxt, workspace=ws))
     unfused_us = compute_loop(lambda i: (
         score_topk(q, caches[i % layers], k, rank_row=1, idx_out=nxt, workspace=ws_s),
@@ -317,7 +319,7 @@ def main():
                         f"top-k {k} per KV head gathered from pinned host memory; {layers} layers in turn",
             "batch": B, "seq_len": N, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "bits": cfg.bits,
             "top_k": k, "n_tokens": T, "layers_rotated": layers, "gather_stream_cus": args.gather_cus,
-            "compute_stream": args.compute_stream,
+            "compute_stream": args.compute_stream, "rank": args.rank,
             "compute_stream_reserved_cus": max(args.compute_reserve, args.gather_cus)
             if args.compute_stream == "exclusive" else 0,
         },

@@ -93,7 +93,7 @@ def load() -> ctypes.CDLL:
             "specache_decode_attn_workspace_size": (SZ, [SP, I, I, I]),
             "specache_decode_attn": (I, [SP, P, I, LP, P, I, P, P, P, P, I, F, P, P, SZ, P]),
             "specache_decode_step_workspace_size": (SZ, [SP, I, I, I, I]),
-            "specache_decode_step": (I, [SP, P, I, I, LP, P, I, P, P, P, P, I, F, P, I, P, P, P, SZ, P]),
+            "specache_decode_step": (I, [SP, P, I, I, I, LP, P, I, P, P, P, P, I, F, P, I, P, P, P, SZ, P]),
             "specache_gather_stream_create": (I, [I, ctypes.POINTER(P)]),
             "specache_compute_stream_create": (I, [I, ctypes.POINTER(P)]),
             "specache_stream_destroy": (I, [P]),

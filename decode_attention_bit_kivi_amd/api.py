@@ -258,14 +258,15 @@ def decode_step_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int
 
 
 def decode_step(q16: torch.Tensor, cache: LowBitCache, k_next: int, rank_row: int = 1,
-                idx: torch.Tensor | None = None, k_sel: torch.Tensor | None = None,
+                rank_mixed: bool = False, idx: torch.Tensor | None = None, k_sel: torch.Tensor | None = None,
                 v_sel: torch.Tensor | None = None, k_tail: torch.Tensor | None = None,
                 v_tail: torch.Tensor | None = None, sm_scale: float | None = None,
                 out: torch.Tensor | None = None, idx_next_out: torch.Tensor | None = None,
                 rank_key_out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                 stream=None):
-    """specache_decode_step: (O, idx_next) -- decode_attn's output and score_topk's
-    selection for row rank_row, from one pass over C'."""
+    """specache_decode_step: (O, idx_next) -- decode_attn's output and the next selection
+    for row rank_row from one pass over C': ranked against C' (score_topk's ranking), or
+    with rank_mixed by that row of the attention itself (fetched rows and tail included)."""
     k, ip, kp, vp, R, ktp, vtp = _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail)
     B, Hq, T, D = q16.shape
     sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
@@ -285,7 +286,7 @@ def decode_step(q16: torch.Tensor, cache: LowBitCache, k_next: int, rank_row: in
     if rank_key_out is not None:
         _need(rank_key_out, "rank_key_out", torch.float32, 3)
         rk = rank_key_out.data_ptr()
-    _lib.check(lib.specache_decode_step(ctypes.byref(shape), q16.data_ptr(), T, rank_row,
+    _lib.check(lib.specache_decode_step(ctypes.byref(shape), q16.data_ptr(), T, rank_row, int(bool(rank_mixed)),
                                         ctypes.byref(cache.c_struct()), ip, k, kp, vp, ktp, vtp, R, sm_scale,
                                         out.data_ptr(), k_next, idx_next_out.data_ptr(), rk,
                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),

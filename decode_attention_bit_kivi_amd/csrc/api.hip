@@ -294,7 +294,7 @@ size_t specache_decode_step_workspace_size(const specache_shape* shape, int n_to
 }
 
 int specache_decode_step(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
-                         const specache_lowbit* cache, const int32_t* idx, int k, const void* k_sel,
+                         int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k, const void* k_sel,
                          const void* v_sel, const void* k_tail, const void* v_tail, int tail_len, float sm_scale,
                          void* out16, int k_next, int32_t* idx_next_out, float* rank_key_out, void* workspace,
                          size_t workspace_bytes, void* stream) {
@@ -304,7 +304,8 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
   AttnArgs a;
   err = fill_attn_args(d, q16, n_tokens, cache, idx, k, k_sel, v_sel, k_tail, v_tail, tail_len, sm_scale, out16, &a);
   if (err != SPECACHE_OK) return err;
-  if (rank_row < 0 || rank_row >= n_tokens || k_next < 1 || k_next > d.N || !idx_next_out)
+  if (rank_row < 0 || rank_row >= n_tokens || k_next < 1 || k_next > d.N || !idx_next_out ||
+      (rank_mixed != 0 && rank_mixed != 1))
     return SPECACHE_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const AttnPlan plan = attn_plan(d, stream_cus(s));
@@ -314,6 +315,7 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
   a.part_ml = reinterpret_cast<float*>(base + ws.ml);
   a.part_acc = reinterpret_cast<float*>(base + ws.acc);
   a.rank_row = rank_row;
+  a.rank_mixed = rank_mixed;
   a.rank_logits = reinterpret_cast<float*>(base + ws.logits);
   a.rank_m = reinterpret_cast<float*>(base + ws.rank_m);
   a.rank_l = reinterpret_cast<float*>(base + ws.rank_l);

@@ -289,9 +289,19 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       xr[i] = fmaf(sacc, k1, c0m);
       xa[i] = fmaf(sacc, k1, c0);
     }
+    const uint32_t kmw = sm.kmask[jj];
     if constexpr (RANK) {
-      // the rank row's logits against C' (before any kappa masking), natural units
-      if (rank_lane) {
+      // the rank row's logits against C' (before any kappa masking), natural units; when ranking
+      // by the mixed cache the kappa positions are written by the 16-bit pass instead
+      if (rank_lane && a.rank_mixed && kmw) {
+        float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
+        constexpr float kLn2 = 0.69314718055994531f;
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+          const int tok = PACK == 2 ? (16 * (n16 >> 3) + 4 * g + i) : (16 * (i >> 2) + 4 * g + (i & 3));
+          if (!((kmw >> tok) & 1u)) dst[tok] = xa[i] * kLn2;
+        }
+      } else if (rank_lane) {
         float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
         constexpr float kLn2 = 0.69314718055994531f;
         if constexpr (PACK == 2) {
@@ -305,7 +315,6 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       }
     }
     float xc[NX];  // C' logits of masked positions, for the ranking statistics
-    const uint32_t kmw = sm.kmask[jj];
     if (kmw) {
 #pragma unroll
       for (int i = 0; i < NX; ++i) {
@@ -447,6 +456,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       const int tau = PACK == 2 ? 0 : i >> 2;
       const float v = acc[tau][i & 3] * qscale;
       bool ok = base + tok < lim;
+      if constexpr (RANK) {
+        // ranking by the mixed cache: a fetched row's logit replaces its low-bit one
+        if (a.rank_mixed && rank_lane && !tail && ok) {
+          const int64_t pos = a.idx[slice * a.k + base + tok];
+          a.rank_logits[(slice * G + arow / T) * N + pos] = v * 0.69314718055994531f;
+        }
+      }
       if (tail) ok = ok && (base + tok <= a.tail - T + tq);
       xa[i] = ok ? v : -INFINITY;
       xr[i] = xa[i] - m_used;
@@ -504,8 +520,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   }
   __syncthreads();  // all waves are done with their value tiles; the LDS union becomes the combine buffer
   if constexpr (RANK) {
-    // one thread per head: combine the four waves and write this split's statistics
-    if (tid < G) {
+    // one thread per head: combine the four waves and write this split's statistics over C'
+    if (!a.rank_mixed && tid < G) {
       const int r = tid * T + a.rank_row;
       float M = kEmpty;
 #pragma unroll
@@ -566,6 +582,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     if (c == 0) {
       a.part_ml[(row * S + split) * 2] = M;
       a.part_ml[(row * S + split) * 2 + 1] = lsum;
+      if constexpr (RANK) {
+        // ranking by the mixed cache: the rank row's own softmax statistics of this split
+        if (a.rank_mixed && r % T == a.rank_row) {
+          a.rank_m[(slice * G + r / T) * S + split] = M;
+          a.rank_l[(slice * G + r / T) * S + split] = lsum;
+        }
+      }
     }
   }
 }

@@ -148,14 +148,16 @@ struct AttnArgs {
   float* part_acc;   // [B][Hq][T][S][D]
   // Ranking outputs of the fused step (all null / unused for plain attention):
   int rank_row;
-  float* rank_logits;    // [slices][G][N]: logits of the rank row against C' (natural units)
-  float* rank_m;         // [slices][G][S]: per-split max over C' (log2 units)
+  int rank_mixed;        // 0: rank against C'; 1: rank by the row of the mixed-cache attention
+  float* rank_logits;    // [slices][G][N]: the rank row's logits (natural units)
+  float* rank_m;         // [slices][G][S]: per-split max of its softmax (log2 units)
   float* rank_l;         // [slices][G][S]: per-split sum of 2^(x - max)
   uint32_t* rank_hist;   // [slices][2048]: zeroed by the split kernel for the rank kernels
 };
 
 // Split kernel of the attention; with a.rank_logits set it also emits the ranking logits and
-// statistics of the rank row against C'.
+// statistics of the rank row: against C' (rank_mixed = 0), or those of the attention itself
+// over C' with the fetched rows substituted and the visible tail (rank_mixed = 1).
 hipError_t launch_attn_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 

@@ -252,7 +252,9 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
 /*
  * One decode step's compute in one pass over C' (Algorithm 3 of the
  * SpeCache summary: Attn over C' U C_kappa, and ArgTopK(A_{1,:}) of the
- * speculative row for the next step's prefetch).  Equivalent to
+ * speculative row for the next step's prefetch; §3 "prefetch and offload
+ * during decoding": the indices are recorded during the attention).  With
+ * rank_mixed = 0 it is equivalent to
  *     specache_decode_attn(shape, q16, n_tokens, cache, idx, k, k_sel, v_sel,
  *                          k_tail, v_tail, tail_len, sm_scale, out16, ...)
  *     specache_score_topk(shape, q16, n_tokens, rank_row, cache, sm_scale,
@@ -261,8 +263,16 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
  * logits of row rank_row against C' with the 16-bit rows and the tail
  * taking no part) but the low-bit cache is read once.
  *
+ * rank_mixed = 1 takes Algorithm 3's A_{1,:} literally: row rank_row's
+ * masked softmax over the keys the attention uses -- C' with the fetched
+ * 16-bit rows in place of theirs, and the tail entries visible to that row
+ * -- so r(p) = log sum_gi A_gi(p) over the N cached positions (the tail
+ * shares each head's normalization but is no candidate).  out16 is the same
+ * in both modes.
+ *
  * Arguments as for the two calls; 0 <= rank_row < n_tokens;
- * 1 <= k_next <= N; idx_next_out [B][Hkv][k_next] int32, ascending.
+ * rank_mixed in {0, 1}; 1 <= k_next <= N; idx_next_out [B][Hkv][k_next]
+ * int32, ascending.
  * idx_next_out may be the same buffer as idx (the attention has consumed idx
  * before the selection writes, in stream order); rank_key_out [B][Hkv][N]
  * float32 or NULL.  Workspace: specache_decode_step_workspace_size bytes,
@@ -272,7 +282,7 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
 size_t specache_decode_step_workspace_size(const specache_shape* shape, int n_tokens, int k,
                                            int tail_len, int k_next);
 int specache_decode_step(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
-                         const specache_lowbit* cache, const int32_t* idx, int k,
+                         int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k,
                          const void* k_sel, const void* v_sel, const void* k_tail,
                          const void* v_tail, int tail_len, float sm_scale, void* out16,
                          int k_next, int32_t* idx_next_out, float* rank_key_out,

@@ -331,6 +331,50 @@ def test_fused_step_matches_separate_calls(gpu, name, over, mode):
     assert _attn_err(_np(o_fused), ref) <= ATTN_TOL
 
 
+@pytest.mark.parametrize("name,over,mode", [
+    ("tiny", {}, "none"),
+    ("tiny", {}, "random"),
+    ("tiny", dict(bits=2), "all"),                           # every row fetched: 16-bit attention mass
+    ("tiny", dict(seq_len=96, top_k=96), "tail"),            # k_next = N, tail in the normalization
+    ("tiny", dict(n_tokens=1, top_k=1), "random"),
+    ("llama8k", {}, "random"),
+    ("llama8k", dict(bits=1, seed=4, tail_len=3), "tail"),
+    ("llama8k", dict(seq_len=8192 + 96, seed=5), "random"),
+    ("llama8k", dict(n_q_heads=64, n_kv_heads=8), "tail"),    # G = 8: 16 rows
+])
+def test_fused_step_mixed_cache_rank(gpu, name, over, mode):
+    """Algorithm 3's reading: the next set ranked by the speculative row of the attention
+    over C' with the fetched rows substituted and the visible tail."""
+    cfg = get_config(name).with_(**over)
+    if mode == "tail" and cfg.tail_len == 0:
+        cfg = cfg.with_(tail_len=2)
+    K, V, Q, _, KT, VT = generate_all(cfg)
+    B, Hkv, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    rng = np.random.default_rng(12)
+    idx = None
+    if mode in ("random", "tail"):
+        idx = _random_idx(rng, B, Hkv, N, min(cfg.top_k, N))
+    elif mode == "all":
+        idx = np.broadcast_to(np.arange(N, dtype=np.int32), (B, Hkv, N)).copy()
+    ks = vs = None
+    if idx is not None:
+        ks, vs = oracle.gather_rows(K, V, idx)
+    args = (_dev(Q), cache, None if idx is None else _dev(idx), None if ks is None else _dev(ks),
+            None if vs is None else _dev(vs), None if KT is None else _dev(KT), None if VT is None else _dev(VT))
+    row = 1 if cfg.n_tokens == 2 else 0
+    o_sep = decode_attn(*args)
+    rk = torch.empty((B, Hkv, N), dtype=torch.float32, device="cuda")
+    o_fused, idx_next = decode_step(args[0], cache, cfg.top_k, rank_row=row, rank_mixed=True, idx=args[2],
+                                    k_sel=args[3], v_sel=args[4], k_tail=args[5], v_tail=args[6], rank_key_out=rk)
+    torch.cuda.synchronize()
+    assert torch.equal(o_fused.view(torch.int16), o_sep.view(torch.int16))
+    _, kh, _ = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores_mixed(Q, kh, row, cfg.sm_scale, idx=idx, k_sel=ks, k_tail=KT)
+    _assert_topk(_np(idx_next), r_ref, cfg.top_k, [(b, h) for b in range(B) for h in range(Hkv)])
+    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+
+
 def test_fused_step_next_selection_may_alias_current(gpu):
     cfg = get_config("llama8k").with_(seq_len=4096, seed=7)
     K, V, Q, _, _, _ = generate_all(cfg)
@@ -352,11 +396,11 @@ def test_fused_step_next_selection_may_alias_current(gpu):
     _assert_topk(_np(want_next), r_ref, cfg.top_k, slices)
 
 
-@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
-def test_fused_step_full_size_sampled(gpu, name):
-    """Two chained fused steps at full size, in the benchmark's launch configuration:
-    score_topk seeds the first selection, each step gathers its rows from pinned
-    host memory and returns the next selection."""
+@pytest.mark.parametrize("name,mixed", [("mistral32k", False), ("long128k", False), ("mistral32k", True)])
+def test_fused_step_full_size_sampled(gpu, name, mixed):
+    """The fused step at full size, in the benchmark's launch configuration: score_topk
+    seeds the selection, the step gathers its rows from pinned host memory and returns the
+    next selection (ranked against C', or by the mixed-cache attention row)."""
     cfg = get_config(name)
     sl = _sampled(cfg, 3)
     K, V, Q, _, _, _ = generate_all(cfg, slices=sl)
@@ -365,7 +409,7 @@ def test_fused_step_full_size_sampled(gpu, name):
     hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
     idx = score_topk(q, cache, cfg.top_k)
     ks, vs = gather_fp16(idx, hk, hv)
-    out, nxt = decode_step(q, cache, cfg.top_k, idx=idx, k_sel=ks, v_sel=vs)
+    out, nxt = decode_step(q, cache, cfg.top_k, rank_mixed=mixed, idx=idx, k_sel=ks, v_sel=vs)
     idx_np, out, nxt = _np(idx), _np(out), _np(nxt)
     G = cfg.gqa
     for (b, h) in sl:
@@ -375,7 +419,10 @@ def test_fused_step_full_size_sampled(gpu, name):
         rks, rvs = oracle.gather_rows(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], i)
         ref = oracle.mixed_attention(q1, kh, vh, i, rks, rvs, sm_scale=cfg.sm_scale)
         assert _attn_err(out[b:b + 1, h * G:(h + 1) * G], ref) <= ATTN_TOL
-        r_ref = oracle.rank_scores(q1, kh, 1, cfg.sm_scale)
+        if mixed:
+            r_ref = oracle.rank_scores_mixed(q1, kh, 1, cfg.sm_scale, idx=i, k_sel=rks)
+        else:
+            r_ref = oracle.rank_scores(q1, kh, 1, cfg.sm_scale)
         _assert_topk(nxt[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)])
 
 

@@ -108,7 +108,7 @@ def test_argument_validation(lib):
     assert lib.specache_decode_step_workspace_size(ctypes.byref(s), 2, 16, 2, s.seq_len + 1) == 0
     assert lib.specache_decode_step_workspace_size(ctypes.byref(s16), 2, 0, 0, 8) == 0
     step = lambda **kw: lib.specache_decode_step(  # noqa: E731
-        ctypes.byref(s), 1, kw.get("T", 2), kw.get("row", 1), ctypes.byref(lb), kw.get("idx", 1),
+        ctypes.byref(s), 1, kw.get("T", 2), kw.get("row", 1), kw.get("mixed", 0), ctypes.byref(lb), kw.get("idx", 1),
         kw.get("k", 16), 1, 1, 1, 1, 2, 0.1, 1, kw.get("kn", 16), kw.get("idx_next", 1), None,
         kw.get("ws", 1), kw.get("wsb", wf), None)
     assert step(kn=0) == _lib.SPECACHE_ERR_INVALID
@@ -117,6 +117,7 @@ def test_argument_validation(lib):
     assert step(row=-1) == _lib.SPECACHE_ERR_INVALID
     assert step(T=1, row=1) == _lib.SPECACHE_ERR_INVALID
     assert step(idx_next=0) == _lib.SPECACHE_ERR_INVALID
+    assert step(mixed=2) == _lib.SPECACHE_ERR_INVALID
     assert step(idx=0) == _lib.SPECACHE_ERR_INVALID
     assert step(ws=0) == _lib.SPECACHE_ERR_WORKSPACE
     assert step(wsb=wf - 1) == _lib.SPECACHE_ERR_WORKSPACE
