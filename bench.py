@@ -4,8 +4,11 @@ One step = one layer's pass of the decode hot path over one batch:
   decode_step (both query rows over C' with this layer's fetched 16-bit rows
                substituted, and, from the same pass, the speculative row's
                ranking and top-k selection for the layer's next step)
-  gather_fp16 (that selection's 16-bit K/V rows from pinned host memory, on a
-               side stream limited to a few compute units)
+  gather      (that selection's 16-bit K/V rows into the layer's other row
+               buffer: rows the previous selection also held are copied on the
+               device (gather_reuse), the others fetched from pinned host
+               memory on a side stream limited to a few compute units
+               (gather_fp16_missing); with --no-reuse every row is fetched)
 as in the multi-layer decode loop: several layers, each with its own low-bit
 cache C', selection and fetched rows, run in turn, and a layer's gather
 overlaps the other layers' compute until the layer comes round again.  The
@@ -15,7 +18,9 @@ cache (every gather still crosses the host link).  The prefill quantizer
 (quantize_pack) is timed separately, once per run.
 
 Inputs are resident in HBM (C', queries) and pinned host memory (the 16-bit
-cache) before the timed region starts.
+cache) before the timed region starts.  Each step of a layer takes the next of
+8 fresh query draws from the workload's distribution; the planted positions
+stay relevant to all of them, the rest of each top-k set is the step's own.
 
 Prints one JSON line.
 
@@ -74,6 +79,9 @@ def parse():
     ap.add_argument("--gather-cus", type=int, default=8, help="compute units of the gather stream")
     ap.add_argument("--compute-stream", choices=("exclusive", "shared"), default="exclusive",
                     help="exclusive: the compute runs on the compute units the gather stream does not use")
+    ap.add_argument("--reuse", action=argparse.BooleanOptionalAction, default=True,
+                    help="fetch only the rows of the new top-k not already resident (the step time of "
+                         "fetching every row is reported beside it)")
     ap.add_argument("--rank", choices=("lowbit", "mixed"), default="lowbit",
                     help="lowbit: rank against C'; mixed: by the attention row itself (fetched rows and tail in)")
     ap.add_argument("--compute-reserve", type=int, default=32,
@@ -169,9 +177,9 @@ def main():
     from decode_attention_bit_kivi_amd import (
         quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, empty_cache,
         score_topk_workspace_size, decode_attn_workspace_size, decode_step_workspace_size, GatherStream,
-        ComputeStream,
+        ComputeStream, gather_reuse, gather_fp16_missing,
     )
-    from workloads import get_config, generate_all
+    from workloads import get_config, generate_all, generate_step_queries
 
     cfg = get_config(args.workload)
     B, Hq, Hkv, N, D, T, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.seq_len, cfg.head_dim, cfg.n_tokens, cfg.top_k
@@ -217,61 +225,96 @@ def main():
     ws_s = torch.empty(score_topk_workspace_size(cache0, Hq, T, k), dtype=torch.uint8, device=dev)
     ws_a = torch.empty(decode_attn_workspace_size(cache0, Hq, T, k), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
-    # per layer: the selection (rewritten in place by each decode_step) and its fetched rows;
-    # the pre-decoding step seeds them
-    idx = [score_topk(q, c, k, rank_row=1, workspace=ws_s) for c in caches]
-    sel = [gather_fp16(idx[l], hk, hv, cfg.bits) for l in range(layers)]
+    # every step of a layer takes the next of n_q fresh query draws (same distribution)
+    print("[bench] drawing the step queries", file=sys.stderr, flush=True)
+    n_q = 8
+    qs_np = generate_step_queries(cfg, n_q)
+    qs = [torch.from_numpy(qs_np[i]).to(dev) for i in range(n_q)]
+    mixed = args.rank == "mixed"
     gathered = [torch.cuda.Event() for _ in range(layers)]
     stepped = [torch.cuda.Event() for _ in range(layers)]
-    for l in range(layers):
-        gathered[l].record(comp)
-    torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def new_state():
+        """Per layer: two selections and two row buffers in turn (the step reads one pair and
+        its ranking fills the other), seeded by a pre-decoding score_topk + gather."""
+        st = {"occ": [0] * layers, "idx": [], "sel": [], "fetch": []}
+        for l in range(layers):
+            i0 = score_topk(qs[n_q - 1], caches[l], k, rank_row=1, workspace=ws_s)
+            st["idx"].append([i0, torch.empty_like(i0)])
+            st["sel"].append([gather_fp16(i0, hk, hv, cfg.bits),
+                              (torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev),
+                               torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev))])
+            st["fetch"].append(torch.empty_like(i0))
+            gathered[l].record(comp)
+        torch.cuda.synchronize()
+        return st
+
+    def step(st, i, reuse, ev=None):
         def mark(name, stream):
             if ev and name in ev:
                 ev[name].record(stream)
 
         l = i % layers
+        r = st["occ"][l]
+        st["occ"][l] += 1
+        cur, nxt = r % 2, 1 - r % 2
+        idx_c, idx_n = st["idx"][l][cur], st["idx"][l][nxt]
+        sel_c, sel_n = st["sel"][l][cur], st["sel"][l][nxt]
         comp.wait_event(gathered[l])
         mark("d0", comp)
-        decode_step(q, caches[l], k, rank_row=1, rank_mixed=args.rank == "mixed", idx=idx[l], k_sel=sel[l][0],
-                    v_sel=sel[l][1], out=out, idx_next_out=idx[l], workspace=ws)
+        decode_step(qs[r % n_q], caches[l], k, rank_row=1, rank_mixed=mixed, idx=idx_c, k_sel=sel_c[0],
+                    v_sel=sel_c[1], out=out, idx_next_out=idx_n, workspace=ws)
         mark("d1", comp)
+        if reuse:  # rows of the new set already resident: device copy on the compute stream
+            gather_reuse(idx_n, idx_c, sel_c[0], sel_c[1], N, k_sel=sel_n[0], v_sel=sel_n[1],
+                         fetch_idx=st["fetch"][l])
         stepped[l].record(comp)
         side.wait_event(stepped[l])
         mark("g0", side)
-        gather_fp16(idx[l], hk, hv, cfg.bits, *sel[l], stream=side)
+        if reuse:
+            gather_fp16_missing(st["fetch"][l], hk, hv, sel_n[0], sel_n[1], cfg.bits, stream=side)
+        else:
+            gather_fp16(idx_n, hk, hv, cfg.bits, sel_n[0], sel_n[1], stream=side)
         mark("g1", side)
         gathered[l].record(side)
 
-    print(f"[bench] {args.warmup} warmup + {args.steps} timed steps over {layers} layers", file=sys.stderr,
-          flush=True)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: timing events on the compute stream only (events on the gather stream
-    # lengthen its idle time between gathers); the gather's own duration is taken after it
-    evs = [{n: torch.cuda.Event(enable_timing=True) for n in ("d0", "d1")} for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(comp)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    comp.wait_stream(side)
-    t_end.record(comp)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    step_us = np.array([e["d0"].elapsed_time(e["d1"]) for e in evs]) * 1e3
 
-    gevs = [{n: torch.cuda.Event(enable_timing=True) for n in ("g0", "g1")} for _ in range(min(args.steps, 20))]
-    for i, ev in enumerate(gevs):
-        step(args.warmup + args.steps + i, ev)
-    torch.cuda.synchronize()
-    gather_us = np.array([e["g0"].elapsed_time(e["g1"]) for e in gevs]) * 1e3
+    def run_pipeline(reuse):
+        """(ms per step, decode_step µs per call in the pipeline, gather µs, fetched fraction)."""
+        st = new_state()
+        for i in range(args.warmup):
+            step(st, i, reuse)
+        torch.cuda.synchronize()
+        # timed region: timing events on the compute stream only (events on the gather stream
+        # lengthen its idle time between gathers); the gather's own duration is taken after it
+        evs = [{n: torch.cuda.Event(enable_timing=True) for n in ("d0", "d1")} for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_start.record(comp)
+        for i in range(args.steps):
+            step(st, args.warmup + i, reuse, evs[i])
+        comp.wait_stream(side)
+        t_end.record(comp)
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
+        d_us = np.array([e["d0"].elapsed_time(e["d1"]) for e in evs]) * 1e3
+        fetched = None
+        if reuse:
+            fetched = float(np.mean([(f >= 0).float().mean().item() for f in st["fetch"]]))
+        gevs = [{n: torch.cuda.Event(enable_timing=True) for n in ("g0", "g1")} for _ in range(min(args.steps, 20))]
+        for i, ev in enumerate(gevs):
+            step(st, args.warmup + args.steps + i, reuse, ev)
+        torch.cuda.synchronize()
+        g_us = np.array([e["g0"].elapsed_time(e["g1"]) for e in gevs]) * 1e3
+        return ms, d_us, g_us, fetched
+
+    modes = ["reuse", "full"] if args.reuse else ["full"]
+    runs = {}
+    for m in modes:
+        print(f"[bench] {m} fetch: {args.warmup} warmup + {args.steps} timed steps over {layers} layers",
+              file=sys.stderr, flush=True)
+        runs[m] = run_pipeline(m == "reuse")
+    ms_step, step_us, gather_us, fetched = runs[modes[0]]
 
     # compute only (the fetched rows already resident): the fused step, then the four-call
     # form (score_topk + decode_attn) on the same inputs
@@ -285,21 +328,22 @@ def main():
         torch.cuda.synchronize()
         return t_start.elapsed_time(t_end) / args.steps * 1e3
 
-    nxt = torch.empty_like(idx[0])
+    st = new_state()
+    nxt = torch.empty_like(st["idx"][0][0])
     fused_us = compute_loop(lambda i: decode_step(
-        q, caches[i % layers], k, rank_row=1, rank_mixed=args.rank == "mixed", idx=idx[i % layers], k_sel=sel[i % layers][0],
-        v_sel=sel[i % layers][1], out=out, idx_next_out=nxt, workspace=ws))
+        qs[i % n_q], caches[i % layers], k, rank_row=1, rank_mixed=mixed, idx=st["idx"][i % layers][0],
+        k_sel=st["sel"][i % layers][0][0], v_sel=st["sel"][i % layers][0][1], out=out, idx_next_out=nxt,
+        workspace=ws))
     unfused_us = compute_loop(lambda i: (
-        score_topk(q, caches[i % layers], k, rank_row=1, idx_out=nxt, workspace=ws_s),
-        decode_attn(q, caches[i % layers], idx[i % layers], sel[i % layers][0], sel[i % layers][1], out=out,
-                    workspace=ws_a)))
+        score_topk(qs[i % n_q], caches[i % layers], k, rank_row=1, idx_out=nxt, workspace=ws_s),
+        decode_attn(qs[i % n_q], caches[i % layers], st["idx"][i % layers][0], st["sel"][i % layers][0][0],
+                    st["sel"][i % layers][0][1], out=out, workspace=ws_a)))
 
     step_bytes = algorithmic_bytes_step(cfg)
     step_avg_s = float(step_us.mean()) * 1e-6
     achieved = step_bytes / step_avg_s / 1e9
     fused_bw = step_bytes / (fused_us * 1e-6) / 1e9
     gather_bytes = 2 * B * Hkv * k * D * 2
-
     result = {
         "metric": "decode-step attention latency + tokens/s; achieved HBM GB/s vs peak at 32K ctx",
         "value": B / (ms_step * 1e-3),
@@ -320,6 +364,8 @@ def main():
             "batch": B, "seq_len": N, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "bits": cfg.bits,
             "top_k": k, "n_tokens": T, "layers_rotated": layers, "gather_stream_cus": args.gather_cus,
             "compute_stream": args.compute_stream, "rank": args.rank,
+            "fetch": "resident rows reused, only new top-k rows fetched" if args.reuse else "every top-k row fetched",
+            "queries": f"fresh draws every step ({n_q} in turn), planted peak shared",
             "compute_stream_reserved_cus": max(args.compute_reserve, args.gather_cus)
             if args.compute_stream == "exclusive" else 0,
         },
@@ -335,9 +381,11 @@ def main():
         },
         "latency_us": {
             "step": ms_step * 1e3,
+            "step_full_fetch": runs["full"][0] * 1e3,
             "decode_step_in_pipeline": float(np.median(step_us)),
             "decode_step_in_pipeline_mean": float(step_us.mean()),
             "gather_fp16_side_stream": float(np.median(gather_us)),
+            "gather_full_fetch": float(np.median(runs["full"][2])),
             "step_compute_only_fused": fused_us,
             "step_compute_only_four_call": unfused_us,
             "exposed_gather": max(0.0, ms_step * 1e3 - fused_us),
@@ -346,11 +394,12 @@ def main():
         "bandwidth_GBs": {
             "decode_step_in_pipeline": achieved,
             "decode_step_compute_only": fused_bw,
-            "gather_host_link": gather_bytes / (float(np.median(gather_us)) * 1e-6) / 1e9,
-            "gather_host_link_whole_step": gather_bytes / (ms_step * 1e-3) / 1e9,
+            "gather_host_link": gather_bytes / (float(np.median(runs["full"][2])) * 1e-6) / 1e9,
+            "gather_host_link_whole_step": gather_bytes * (fetched if fetched is not None else 1.0)
+            / (ms_step * 1e-3) / 1e9,
             "quantize_pack": (2 * B * Hkv * N * D * 2 + caches[0].nbytes()) / (quant_us * 1e-6) / 1e9,
         },
-        "wall_s_timed": wall,
+        "fetched_fraction": fetched,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)

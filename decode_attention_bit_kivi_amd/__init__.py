@@ -8,13 +8,13 @@ package is its thin Python binding.  Build the library with
 from .api import (
     LowBitCache, empty_cache, lowbit_sizes, quantize_pack, score_topk, score_topk_workspace_size,
     gather_fp16, decode_attn, decode_attn_workspace_size, decode_step, decode_step_workspace_size,
-    GatherStream, ComputeStream,
+    GatherStream, ComputeStream, gather_reuse, gather_fp16_missing,
 )
 from ._lib import SpecacheError
 
 __all__ = [
     "LowBitCache", "empty_cache", "lowbit_sizes", "quantize_pack", "score_topk",
     "score_topk_workspace_size", "gather_fp16", "decode_attn", "decode_attn_workspace_size",
-    "decode_step", "decode_step_workspace_size", "GatherStream", "ComputeStream",
+    "decode_step", "decode_step_workspace_size", "GatherStream", "ComputeStream", "gather_reuse", "gather_fp16_missing",
     "SpecacheError",
 ]

@@ -29,6 +29,8 @@ EXPORTED = (
     "specache_score_topk_workspace_size",
     "specache_score_topk",
     "specache_gather_fp16",
+    "specache_gather_reuse",
+    "specache_gather_fp16_missing",
     "specache_decode_attn_workspace_size",
     "specache_decode_attn",
     "specache_decode_step_workspace_size",
@@ -90,6 +92,8 @@ def load() -> ctypes.CDLL:
             "specache_score_topk_workspace_size": (SZ, [SP, I, I]),
             "specache_score_topk": (I, [SP, P, I, I, LP, F, I, P, P, P, SZ, P]),
             "specache_gather_fp16": (I, [SP, P, I, P, P, P, P, P]),
+            "specache_gather_reuse": (I, [SP, P, I, P, I, P, P, P, P, P, P]),
+            "specache_gather_fp16_missing": (I, [SP, P, I, P, P, P, P, P]),
             "specache_decode_attn_workspace_size": (SZ, [SP, I, I, I]),
             "specache_decode_attn": (I, [SP, P, I, LP, P, I, P, P, P, P, I, F, P, P, SZ, P]),
             "specache_decode_step_workspace_size": (SZ, [SP, I, I, I, I]),

@@ -161,6 +161,54 @@ def gather_fp16(idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor,
     return k_sel, v_sel
 
 
+def gather_reuse(idx: torch.Tensor, idx_prev: torch.Tensor, k_sel_prev: torch.Tensor, v_sel_prev: torch.Tensor,
+                 seq_len: int, k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None,
+                 fetch_idx: torch.Tensor | None = None, stream=None):
+    """specache_gather_reuse: rows of idx also in idx_prev are copied from the previous
+    rows; returns (k_sel, v_sel, fetch_idx) with fetch_idx = -1 for the copied rows."""
+    _need(idx, "idx", torch.int32, 3)
+    _need(idx_prev, "idx_prev", torch.int32, 3)
+    _need(k_sel_prev, "k_sel_prev", torch.float16, 4)
+    _need(v_sel_prev, "v_sel_prev", torch.float16, 4)
+    B, Hkv, k = idx.shape
+    k_prev = idx_prev.shape[2]
+    D = k_sel_prev.shape[3]
+    dev = idx.device
+    if k_sel is None:
+        k_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
+    if v_sel is None:
+        v_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
+    if fetch_idx is None:
+        fetch_idx = torch.empty_like(idx)
+    shape = _lib.Shape(B, Hkv, Hkv, D, seq_len, 1, 32)
+    _lib.check(_lib.load().specache_gather_reuse(ctypes.byref(shape), idx.data_ptr(), k, idx_prev.data_ptr(), k_prev,
+                                                 k_sel_prev.data_ptr(), v_sel_prev.data_ptr(), k_sel.data_ptr(),
+                                                 v_sel.data_ptr(), fetch_idx.data_ptr(), _stream(stream)),
+               "specache_gather_reuse")
+    return k_sel, v_sel, fetch_idx
+
+
+def gather_fp16_missing(fetch_idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor,
+                        k_sel: torch.Tensor, v_sel: torch.Tensor, bits: int = 1, stream=None):
+    """specache_gather_fp16_missing: fetch the rows fetch_idx marks (>= 0) into k_sel / v_sel."""
+    _need(fetch_idx, "fetch_idx", torch.int32, 3)
+    _need(k16_src, "k16_src", torch.float16, 4, cuda=False)
+    _need(v16_src, "v16_src", torch.float16, 4, cuda=False)
+    _need(k_sel, "k_sel", torch.float16, 4)
+    _need(v_sel, "v_sel", torch.float16, 4)
+    for name, t in (("k16_src", k16_src), ("v16_src", v16_src)):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    B, Hkv, N, D = k16_src.shape
+    k = fetch_idx.shape[2]
+    shape = _lib.Shape(B, Hkv, Hkv, D, N, bits, 32)
+    _lib.check(_lib.load().specache_gather_fp16_missing(ctypes.byref(shape), fetch_idx.data_ptr(), k,
+                                                        k16_src.data_ptr(), v16_src.data_ptr(), k_sel.data_ptr(),
+                                                        v_sel.data_ptr(), _stream(stream)),
+               "specache_gather_fp16_missing")
+    return k_sel, v_sel
+
+
 class CUStream:
     """A HIP stream limited to a set of compute units (created by the library,
     released by close()).  `.torch` is a torch stream view of it."""

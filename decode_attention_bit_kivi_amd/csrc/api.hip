@@ -200,8 +200,40 @@ int specache_gather_fp16(const specache_shape* shape, const int32_t* idx, int k,
   const void* vs = device_view(v16_src);
   if (!ks || !vs) return SPECACHE_ERR_NOT_PINNED;
   return hip_status(launch_gather(d, idx, k, static_cast<const _Float16*>(ks), static_cast<const _Float16*>(vs),
-                                  static_cast<_Float16*>(k_sel), static_cast<_Float16*>(v_sel),
+                                  static_cast<_Float16*>(k_sel), static_cast<_Float16*>(v_sel), false,
                                   static_cast<hipStream_t>(stream)));
+}
+
+int specache_gather_reuse(const specache_shape* shape, const int32_t* idx, int k, const int32_t* idx_prev,
+                          int k_prev, const void* k_sel_prev, const void* v_sel_prev, void* k_sel, void* v_sel,
+                          int32_t* fetch_idx, void* stream) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err)) return err;
+  if (k < 0 || k > d.N || k_prev < 0 || k_prev > d.N) return SPECACHE_ERR_INVALID;
+  if (k == 0) return SPECACHE_OK;
+  if (!idx || !k_sel || !v_sel || !fetch_idx) return SPECACHE_ERR_INVALID;
+  if (k_prev > 0 && (!idx_prev || !k_sel_prev || !v_sel_prev)) return SPECACHE_ERR_INVALID;
+  if (k_sel == k_sel_prev || v_sel == v_sel_prev) return SPECACHE_ERR_INVALID;
+  return hip_status(launch_reuse(d, idx, k, idx_prev, k_prev, static_cast<const _Float16*>(k_sel_prev),
+                                 static_cast<const _Float16*>(v_sel_prev), static_cast<_Float16*>(k_sel),
+                                 static_cast<_Float16*>(v_sel), fetch_idx, static_cast<hipStream_t>(stream)));
+}
+
+int specache_gather_fp16_missing(const specache_shape* shape, const int32_t* fetch_idx, int k, const void* k16_src,
+                                 const void* v16_src, void* k_sel, void* v_sel, void* stream) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err)) return err;
+  if (k < 0 || k > d.N) return SPECACHE_ERR_INVALID;
+  if (k == 0) return SPECACHE_OK;
+  if (!fetch_idx || !k16_src || !v16_src || !k_sel || !v_sel) return SPECACHE_ERR_INVALID;
+  const void* ks = device_view(k16_src);
+  const void* vs = device_view(v16_src);
+  if (!ks || !vs) return SPECACHE_ERR_NOT_PINNED;
+  return hip_status(launch_gather(d, fetch_idx, k, static_cast<const _Float16*>(ks),
+                                  static_cast<const _Float16*>(vs), static_cast<_Float16*>(k_sel),
+                                  static_cast<_Float16*>(v_sel), true, static_cast<hipStream_t>(stream)));
 }
 
 size_t specache_decode_attn_workspace_size(const specache_shape* shape, int n_tokens, int k, int tail_len) {

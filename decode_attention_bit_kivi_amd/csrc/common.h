@@ -125,8 +125,14 @@ hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const f
                               const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
                               hipStream_t s);
 
+// skip_negative: rows with a negative index are left untouched (resident-set reuse).
 hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,
-                         const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, hipStream_t s);
+                         const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, bool skip_negative,
+                         hipStream_t s);
+
+hipError_t launch_reuse(const Dims& d, const int32_t* idx, int k, const int32_t* idx_prev, int k_prev,
+                        const _Float16* k_prev_rows, const _Float16* v_prev_rows, _Float16* k_sel, _Float16* v_sel,
+                        int32_t* fetch_idx, hipStream_t s);
 
 struct AttnArgs {
   const _Float16* q16;

@@ -27,7 +27,9 @@ namespace {
 constexpr int kGatherBlocks = SPECACHE_GATHER_BLOCKS;
 constexpr int kUnroll = SPECACHE_GATHER_UNROLL;
 
-template <int D>
+// SKIP_NEG: rows whose index is negative are left untouched (they were filled from the
+// resident rows); otherwise an index outside [0, N) gives a NaN row.
+template <int D, bool SKIP_NEG>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx, int k, int64_t N,
                                                      const uint4* __restrict__ k_src,
                                                      const uint4* __restrict__ v_src,
@@ -41,14 +43,17 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   for (int64_t base = (int64_t)blockIdx.x * kRowsPerPass + threadIdx.x / kLanesPerRow; base < total_rows;
        base += stride * kUnroll) {
     uint4 kv[kUnroll], vv[kUnroll];
+    bool skip[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t row = base + u * stride;
       kv[u] = make_uint4(nan2, nan2, nan2, nan2);
       vv[u] = kv[u];
+      skip[u] = false;
       if (row < total_rows) {
         const int64_t slice = row / k;
         const int32_t p = idx[row];
+        skip[u] = SKIP_NEG && p < 0;
         if (p >= 0 && p < N) {
           const int64_t src = (slice * N + p) * kLanesPerRow + part;
 #ifdef SPECACHE_GATHER_NT
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t row = base + u * stride;
-      if (row < total_rows) {
+      if (row < total_rows && !skip[u]) {
         k_sel[row * kLanesPerRow + part] = kv[u];
         v_sel[row * kLanesPerRow + part] = vv[u];
       }
@@ -75,23 +80,95 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   }
 }
 
+// Resident-set reuse: row i of the new selection whose position is also in the previous
+// selection (at row j) is copied from the previous rows (device to device); the others are
+// marked for fetching: fetch_idx[i] = position, or -1 for a copied row.  A position outside
+// [0, N) is marked with N, so that the fetch writes a NaN row for it.  Grid: (row chunks of
+// kReuseRows, slices); the previous selection of the slice is searched in LDS.
+constexpr int kReuseRows = 64;
+constexpr int kPrevLds = 8192;
+
+template <int D>
+__global__ __launch_bounds__(256) void reuse_kernel(const int32_t* __restrict__ idx, int k,
+                                                    const int32_t* __restrict__ idx_prev, int k_prev, int64_t N,
+                                                    const uint4* __restrict__ k_prev_rows,
+                                                    const uint4* __restrict__ v_prev_rows, uint4* __restrict__ k_sel,
+                                                    uint4* __restrict__ v_sel, int32_t* __restrict__ fetch_idx) {
+  constexpr int kLanesPerRow = D * 2 / 16;
+  __shared__ int32_t prev[kPrevLds];
+  const int tid = threadIdx.x;
+  const int64_t slice = blockIdx.y;
+  const int32_t* ip = idx_prev + slice * k_prev;
+  const bool in_lds = k_prev <= kPrevLds;
+  if (in_lds)
+    for (int i = tid; i < k_prev; i += 256) prev[i] = ip[i];
+  __syncthreads();
+  const int part = tid % kLanesPerRow;
+  const int i0 = blockIdx.x * kReuseRows;
+  for (int r = tid / kLanesPerRow; r < kReuseRows; r += 256 / kLanesPerRow) {
+    const int i = i0 + r;
+    if (i >= k) break;
+    const int32_t p = idx[slice * k + i];
+    int lo = 0, hi = k_prev;  // first entry of the previous selection >= p
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const int32_t v = in_lds ? prev[mid] : ip[mid];
+      if (v < p) lo = mid + 1; else hi = mid;
+    }
+    const bool valid = p >= 0 && p < N;
+    const bool found = valid && lo < k_prev && (in_lds ? prev[lo] : ip[lo]) == p;
+    if (found) {
+      const int64_t src = (slice * k_prev + lo) * kLanesPerRow + part;
+      const int64_t dst = (slice * k + i) * kLanesPerRow + part;
+      k_sel[dst] = k_prev_rows[src];
+      v_sel[dst] = v_prev_rows[src];
+    }
+    if (part == 0) fetch_idx[slice * k + i] = found ? -1 : (valid ? p : (int32_t)N);
+  }
+}
+
+template <int D, bool SKIP_NEG>
+void launch_gather_t(const Dims& d, const int32_t* idx, int k, const _Float16* k_src, const _Float16* v_src,
+                     _Float16* k_sel, _Float16* v_sel, hipStream_t s) {
+  const int64_t rows = d.slices() * k;
+  const int rows_per_pass = 256 / (D * 2 / 16);
+  const int64_t need = ceil_div(rows, rows_per_pass);
+  const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
+  gather_kernel<D, SKIP_NEG><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
+                                                  reinterpret_cast<const uint4*>(v_src),
+                                                  reinterpret_cast<uint4*>(k_sel), reinterpret_cast<uint4*>(v_sel),
+                                                  rows);
+}
+
 }  // namespace
 
 hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,
-                         const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, hipStream_t s) {
-  const int64_t rows = d.slices() * k;
-  if (rows == 0) return hipSuccess;
-  const int rows_per_pass = 256 / (d.D * 2 / 16);
-  const int64_t need = ceil_div(rows, rows_per_pass);
-  const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
+                         const _Float16* v_src, _Float16* k_sel, _Float16* v_sel, bool skip_negative,
+                         hipStream_t s) {
+  if (d.slices() * k == 0) return hipSuccess;
+  if (d.D == 128) {
+    if (skip_negative) launch_gather_t<128, true>(d, idx, k, k_src, v_src, k_sel, v_sel, s);
+    else launch_gather_t<128, false>(d, idx, k, k_src, v_src, k_sel, v_sel, s);
+  } else {
+    if (skip_negative) launch_gather_t<64, true>(d, idx, k, k_src, v_src, k_sel, v_sel, s);
+    else launch_gather_t<64, false>(d, idx, k, k_src, v_src, k_sel, v_sel, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reuse(const Dims& d, const int32_t* idx, int k, const int32_t* idx_prev, int k_prev,
+                        const _Float16* k_prev_rows, const _Float16* v_prev_rows, _Float16* k_sel, _Float16* v_sel,
+                        int32_t* fetch_idx, hipStream_t s) {
+  if (d.slices() * k == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(k, kReuseRows), (unsigned)d.slices());
+  auto u4 = [](const _Float16* p) { return reinterpret_cast<const uint4*>(p); };
+  auto w4 = [](_Float16* p) { return reinterpret_cast<uint4*>(p); };
   if (d.D == 128)
-    gather_kernel<128><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
-                                            reinterpret_cast<const uint4*>(v_src), reinterpret_cast<uint4*>(k_sel),
-                                            reinterpret_cast<uint4*>(v_sel), rows);
+    reuse_kernel<128><<<grid, 256, 0, s>>>(idx, k, idx_prev, k_prev, d.N, u4(k_prev_rows), u4(v_prev_rows), w4(k_sel),
+                                           w4(v_sel), fetch_idx);
   else
-    gather_kernel<64><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
-                                           reinterpret_cast<const uint4*>(v_src), reinterpret_cast<uint4*>(k_sel),
-                                           reinterpret_cast<uint4*>(v_sel), rows);
+    reuse_kernel<64><<<grid, 256, 0, s>>>(idx, k, idx_prev, k_prev, d.N, u4(k_prev_rows), u4(v_prev_rows), w4(k_sel),
+                                          w4(v_sel), fetch_idx);
   return hipGetLastError();
 }
 

@@ -195,6 +195,35 @@ int specache_gather_fp16(const specache_shape* shape, const int32_t* idx, int k,
                          void* stream);
 
 /*
+ * Resident-set reuse (SpeCache summary, §3 "prefetch and offload during
+ * decoding": once the attention ends the next top-k rows are prefetched while
+ * the used rows outside the new top-k are evicted -- so rows in both sets stay
+ * on the device).  Two calls together produce what specache_gather_fp16(idx)
+ * would, fetching only the rows that are not resident:
+ *
+ * specache_gather_reuse: for every slice and row i of the new selection idx
+ * [B][Hkv][k] (ascending), if idx[i] is also in the previous selection
+ * idx_prev [B][Hkv][k_prev] (ascending) at row j, copy row j of k_sel_prev /
+ * v_sel_prev ([B][Hkv][k_prev][D] float16, device) into row i of k_sel / v_sel
+ * ([B][Hkv][k][D], device; must not be the previous buffers) and set
+ * fetch_idx[i] = -1; otherwise set fetch_idx[i] = idx[i] (N for an entry
+ * outside [0, N)) and leave the row.  fetch_idx [B][Hkv][k] int32, device.
+ * Device-to-device work: run it on the compute stream.
+ *
+ * specache_gather_fp16_missing: specache_gather_fp16 over fetch_idx, except
+ * that rows with a negative entry are left untouched.  Host-link work: run it
+ * on the gather stream after an event behind specache_gather_reuse.
+ *
+ * 0 <= k, k_prev <= N; k_prev = 0 marks every row for fetching.
+ */
+int specache_gather_reuse(const specache_shape* shape, const int32_t* idx, int k, const int32_t* idx_prev,
+                          int k_prev, const void* k_sel_prev, const void* v_sel_prev, void* k_sel, void* v_sel,
+                          int32_t* fetch_idx, void* stream);
+int specache_gather_fp16_missing(const specache_shape* shape, const int32_t* fetch_idx, int k,
+                                 const void* k16_src, const void* v16_src, void* k_sel, void* v_sel,
+                                 void* stream);
+
+/*
  * A stream for specache_gather_fp16 whose kernels run on only `n_cus` compute
  * units of the current device (hipExtStreamCreateWithCUMask, default
  * priority).  The prefetch is meant to run in the background, in parallel

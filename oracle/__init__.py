@@ -27,10 +27,10 @@ from .quantize import (
 )
 from .rank import rank_scores, rank_scores_mixed, topk_positions, score_topk
 from .attention import mixed_attention, attention_probs
-from .gather import gather_rows
+from .gather import gather_rows, resident_rows
 
 __all__ = [
     "quantize_keys", "quantize_values", "dequantize_keys", "dequantize_values",
     "zero_point_scale", "rank_scores", "rank_scores_mixed", "topk_positions", "score_topk",
-    "mixed_attention", "attention_probs", "gather_rows",
+    "mixed_attention", "attention_probs", "gather_rows", "resident_rows",
 ]

@@ -24,7 +24,7 @@ import torch
 import oracle
 from decode_attention_bit_kivi_amd import (
     quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, GatherStream, ComputeStream,
-    SpecacheError,
+    SpecacheError, gather_reuse, gather_fp16_missing,
 )
 from tests.layout import unpack_keys, unpack_values
 from workloads import get_config, generate_all
@@ -219,6 +219,65 @@ def test_gather_bitwise(gpu, pinned):
     wk, wv = oracle.gather_rows(K, V, idx)
     assert np.array_equal(_np(ks).view(np.uint16), wk.view(np.uint16))
     assert np.array_equal(_np(vs).view(np.uint16), wv.view(np.uint16))
+
+
+def _overlapping_sets(rng, B, H, N, k, k_prev, overlap):
+    """(idx, idx_prev) ascending per slice, with round(overlap * min(k, k_prev)) shared positions."""
+    idx = np.zeros((B, H, k), dtype=np.int32)
+    prev = np.zeros((B, H, k_prev), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            perm = rng.permutation(N)
+            shared = int(round(overlap * min(k, k_prev)))
+            prev[b, h] = np.sort(perm[:k_prev])
+            idx[b, h] = np.sort(np.concatenate([perm[:shared], perm[k_prev:k_prev + k - shared]]))
+    return idx, prev
+
+
+@pytest.mark.parametrize("k,k_prev,overlap", [
+    (37, 37, 0.5), (64, 20, 0.9), (20, 64, 0.3), (33, 0, 0.0), (50, 50, 1.0), (50, 50, 0.0), (300, 280, 0.7),
+])
+def test_reuse_then_fetch_missing_equals_full_gather(gpu, k, k_prev, overlap):
+    """Rows of the new set held by the previous set come from the previous buffers (marked
+    here, to prove they were copied, not fetched); the rest from pinned host memory."""
+    cfg = get_config("llama8k").with_(seq_len=2048, batch=2)
+    K, V, _, _, _, _ = generate_all(cfg)
+    B, H, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
+    rng = np.random.default_rng(k * 1000 + k_prev)
+    idx, prev = _overlapping_sets(rng, B, H, N, k, k_prev, overlap)
+    pk, pv = oracle.gather_rows(K, V, prev) if k_prev else (np.zeros((B, H, 0, cfg.head_dim), np.float16),) * 2
+    mark_k = (pk.astype(np.float32) + 1).astype(np.float16)
+    mark_v = (pv.astype(np.float32) - 1).astype(np.float16)
+    hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
+    ks = torch.full((B, H, k, cfg.head_dim), float("nan"), dtype=torch.float16, device="cuda")
+    vs = torch.full_like(ks, float("nan"))
+    ks, vs, fetch = gather_reuse(_dev(idx), _dev(prev), _dev(mark_k), _dev(mark_v), N, k_sel=ks, v_sel=vs)
+    gather_fp16_missing(fetch, hk, hv, ks, vs)
+    torch.cuda.synchronize()
+    resident = oracle.resident_rows(idx, prev)
+    assert np.array_equal(_np(fetch), np.where(resident, -1, idx))
+    wk, wv = oracle.gather_rows(K, V, idx)
+    for b in range(B):
+        for h in range(H):
+            j = np.searchsorted(prev[b, h], idx[b, h])
+            r = resident[b, h]
+            wk[b, h, r] = mark_k[b, h, j[r]]
+            wv[b, h, r] = mark_v[b, h, j[r]]
+    assert np.array_equal(_np(ks).view(np.uint16), wk.view(np.uint16))
+    assert np.array_equal(_np(vs).view(np.uint16), wv.view(np.uint16))
+
+
+def test_reuse_marks_out_of_range_rows_for_a_nan_fetch(gpu):
+    K = np.ones((1, 1, 64, 64), dtype=np.float16)
+    idx = _dev(np.array([[[3, 10, 64]]], dtype=np.int32))      # 64 is out of range
+    prev = _dev(np.array([[[10, 64]]], dtype=np.int32))
+    prow = torch.full((1, 1, 2, 64), 2.0, dtype=torch.float16, device="cuda")
+    ks, vs, fetch = gather_reuse(idx, prev, prow, prow, 64)
+    gather_fp16_missing(fetch, _dev(K), _dev(K), ks, vs)
+    torch.cuda.synchronize()
+    assert _np(fetch)[0, 0].tolist() == [3, -1, 64]
+    out = _np(ks)[0, 0]
+    assert np.all(out[0] == 1) and np.all(out[1] == 2) and np.all(np.isnan(out[2]))
 
 
 def test_gather_rejects_pageable_source_and_flags_bad_rows(gpu):

@@ -24,7 +24,8 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(specache_[a-z0-9_]+)\s*\(", text)))
 
@@ -121,6 +122,22 @@ def test_argument_validation(lib):
     assert step(idx=0) == _lib.SPECACHE_ERR_INVALID
     assert step(ws=0) == _lib.SPECACHE_ERR_WORKSPACE
     assert step(wsb=wf - 1) == _lib.SPECACHE_ERR_WORKSPACE
+
+    reuse = lambda **kw: lib.specache_gather_reuse(  # noqa: E731
+        ctypes.byref(s), kw.get("idx", 1), kw.get("k", 8), kw.get("prev", 1), kw.get("kp", 8), kw.get("kprev", 2),
+        kw.get("vprev", 3), kw.get("ks", 4), kw.get("vs", 5), kw.get("fetch", 6), None)
+    assert reuse(k=-1) == _lib.SPECACHE_ERR_INVALID
+    assert reuse(kp=s.seq_len + 1) == _lib.SPECACHE_ERR_INVALID
+    assert reuse(idx=0) == _lib.SPECACHE_ERR_INVALID
+    assert reuse(fetch=0) == _lib.SPECACHE_ERR_INVALID
+    assert reuse(prev=0) == _lib.SPECACHE_ERR_INVALID
+    assert reuse(ks=2) == _lib.SPECACHE_ERR_INVALID          # output aliases the previous rows
+    assert reuse(k=0) == _lib.SPECACHE_OK                     # nothing to do
+    missing = lambda **kw: lib.specache_gather_fp16_missing(  # noqa: E731
+        ctypes.byref(s), kw.get("fetch", 1), kw.get("k", 8), kw.get("src", 1), 1, 1, 1, None)
+    assert missing(k=-1) == _lib.SPECACHE_ERR_INVALID
+    assert missing(fetch=0) == _lib.SPECACHE_ERR_INVALID
+    assert missing(k=0) == _lib.SPECACHE_OK
 
     assert lib.specache_gather_fp16(ctypes.byref(s), 1, -1, 1, 1, 1, 1, None) == _lib.SPECACHE_ERR_INVALID
     assert lib.specache_gather_fp16(ctypes.byref(s), 0, 4, 1, 1, 1, 1, None) == _lib.SPECACHE_ERR_INVALID

@@ -419,6 +419,19 @@ def test_attention_tail_mask():
     assert np.array_equal(o2[:, :, 0], o[:, :, 0]) and not np.allclose(o2[:, :, 1], o[:, :, 1])
 
 
+def test_resident_rows_brute_force():
+    """Rows of the new set whose position the previous set also holds (numpy isin as the check)."""
+    rng = np.random.default_rng(31)
+    for k, kp in ((5, 7), (16, 16), (9, 1), (4, 0)):
+        idx = np.stack([np.sort(rng.choice(40, k, replace=False)) for _ in range(3)])[None].astype(np.int32)
+        prev = np.stack([np.sort(rng.choice(40, kp, replace=False)) for _ in range(3)])[None].astype(np.int32)
+        got = oracle.resident_rows(idx, prev)
+        for h in range(3):
+            assert got[0, h].tolist() == np.isin(idx[0, h], prev[0, h]).tolist()
+    same = np.arange(8, dtype=np.int32)[None, None]
+    assert oracle.resident_rows(same, same).all()
+
+
 def test_gather_is_index_select():
     rng = np.random.default_rng(1)
     k = rng.standard_normal((2, 3, 40, 8)).astype(np.float16)

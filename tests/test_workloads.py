@@ -44,3 +44,15 @@ def test_config_table():
     assert (m.batch, m.n_q_heads, m.n_kv_heads, m.seq_len, m.head_dim, m.bits, m.top_k) == \
         (8, 32, 8, 32768, 128, 1, 328)
     assert m.top_k == int(np.ceil(0.01 * m.seq_len))
+
+
+def test_step_queries_are_fresh_draws_sharing_the_planted_direction():
+    from workloads import generate_step_queries, generate_slice
+    cfg = get_config("llama8k").with_(batch=1)
+    qs = generate_step_queries(cfg, 3)
+    assert qs.shape == (3, 1, cfg.n_q_heads, cfg.n_tokens, cfg.head_dim) and qs.dtype == np.float16
+    assert not np.array_equal(qs[0], qs[1])
+    assert np.array_equal(qs, generate_step_queries(cfg, 3))            # seeded
+    u = generate_slice(cfg, 0, 0).direction
+    proj = qs[:, 0, : cfg.gqa].astype(np.float64) @ u                    # heads of KV head 0
+    assert np.all(np.abs(proj.mean() - cfg.peak) < 1.0)

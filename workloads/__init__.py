@@ -6,9 +6,11 @@ take their inputs from here, so that a parity test compares the two on exactly
 the same tensors.
 """
 from .configs import CONFIGS, WorkloadConfig, get_config
-from .gen import SliceInputs, generate_slice, generate_query, generate_all, planted_positions
+from .gen import (SliceInputs, generate_slice, generate_query, generate_all, planted_positions,
+                  generate_step_queries)
 
 __all__ = [
     "CONFIGS", "WorkloadConfig", "get_config",
     "SliceInputs", "generate_slice", "generate_query", "generate_all", "planted_positions",
+    "generate_step_queries",
 ]

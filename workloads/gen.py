@@ -11,6 +11,8 @@ Per slice (b, h)   (tag 2): K [N, D], V [N, D], planted positions, planted unit 
                             does not also inflate the logits of every other key).
 Per query (b, hq)  (tag 3): Q [T, D]; the slice's planted direction times `peak` is added.
 Per slice (b, h)   (tag 4): tail K/V [R, D] when a tail is requested.
+Per step and query (tag 5): the queries of later decode steps (generate_step_queries): fresh
+                     draws from the same distribution, the slice's planted direction added.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ import numpy as np
 
 from .configs import WorkloadConfig
 
-_TAG_HEAD, _TAG_SLICE, _TAG_QUERY, _TAG_TAIL = 1, 2, 3, 4
+_TAG_HEAD, _TAG_SLICE, _TAG_QUERY, _TAG_TAIL, _TAG_STEP_QUERY = 1, 2, 3, 4, 5
 
 
 def _rng(seed: int, tag: int, *keys: int) -> np.random.Generator:
@@ -80,6 +82,29 @@ def generate_query(cfg: WorkloadConfig, b: int, hq: int, direction: np.ndarray |
             direction = generate_slice(cfg, b, hq // cfg.gqa, seed).direction
         q += np.float32(cfg.peak) * direction[None, :]
     return q.astype(np.float16)
+
+
+def generate_step_queries(cfg: WorkloadConfig, n_steps: int, seed: int | None = None) -> np.ndarray:
+    """Queries of n_steps decode steps, [n_steps, B, Hq, T, D] float16: every step draws new
+    N(0,1) queries, plus `peak` times the slice's planted direction as in generate_query --
+    the planted positions stay relevant to every step, the rest of each step's top-k set is
+    its own."""
+    seed = cfg.seed if seed is None else seed
+    B, Hq, T, D, G = cfg.batch, cfg.n_q_heads, cfg.n_tokens, cfg.head_dim, cfg.gqa
+    out = np.zeros((n_steps, B, Hq, T, D), dtype=np.float16)
+    dirs = {}
+    for b in range(B):
+        for h in range(cfg.n_kv_heads):
+            dirs[b, h] = generate_slice(cfg, b, h, seed).direction if cfg.peak is not None else None
+    for s in range(n_steps):
+        for b in range(B):
+            for hq in range(Hq):
+                rng = _rng(seed, _TAG_STEP_QUERY, s, b, hq)
+                q = rng.standard_normal((T, D), dtype=np.float32)
+                if cfg.peak is not None:
+                    q += np.float32(cfg.peak) * dirs[b, hq // G][None, :]
+                out[s, b, hq] = q.astype(np.float16)
+    return out
 
 
 def generate_tail(cfg: WorkloadConfig, b: int, h: int, seed: int | None = None):
