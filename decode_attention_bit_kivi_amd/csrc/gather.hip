@@ -5,6 +5,11 @@
 // affordable; the copy runs in the background, overlapped with the following
 // layers' compute (quick read, second mechanism).
 //
+// Resident-set reuse (§3 "prefetch and offload during decoding": the used rows
+// outside the new top-k are evicted, so rows in both sets stay): reuse_kernel
+// copies the rows the previous selection already holds on the device and marks
+// the others, and gather_missing_kernel fetches only the marked rows.
+//
 // The source is pinned host memory read directly by the kernel (zero copy
 // over the host link) or device memory.  The copy is bound by the host link,
 // not by the GPU, so the kernel runs on a small fixed grid (kGatherBlocks
@@ -27,9 +32,8 @@ namespace {
 constexpr int kGatherBlocks = SPECACHE_GATHER_BLOCKS;
 constexpr int kUnroll = SPECACHE_GATHER_UNROLL;
 
-// SKIP_NEG: rows whose index is negative are left untouched (they were filled from the
-// resident rows); otherwise an index outside [0, N) gives a NaN row.
-template <int D, bool SKIP_NEG>
+// An index outside [0, N) gives a NaN row.
+template <int D>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx, int k, int64_t N,
                                                      const uint4* __restrict__ k_src,
                                                      const uint4* __restrict__ v_src,
@@ -43,17 +47,14 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
   for (int64_t base = (int64_t)blockIdx.x * kRowsPerPass + threadIdx.x / kLanesPerRow; base < total_rows;
        base += stride * kUnroll) {
     uint4 kv[kUnroll], vv[kUnroll];
-    bool skip[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t row = base + u * stride;
       kv[u] = make_uint4(nan2, nan2, nan2, nan2);
       vv[u] = kv[u];
-      skip[u] = false;
       if (row < total_rows) {
         const int64_t slice = row / k;
         const int32_t p = idx[row];
-        skip[u] = SKIP_NEG && p < 0;
         if (p >= 0 && p < N) {
           const int64_t src = (slice * N + p) * kLanesPerRow + part;
 #ifdef SPECACHE_GATHER_NT
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t row = base + u * stride;
-      if (row < total_rows && !skip[u]) {
+      if (row < total_rows) {
         k_sel[row * kLanesPerRow + part] = kv[u];
         v_sel[row * kLanesPerRow + part] = vv[u];
       }
@@ -127,17 +128,73 @@ __global__ __launch_bounds__(256) void reuse_kernel(const int32_t* __restrict__ 
   }
 }
 
+// The fetch of the rows a reuse pass left (index >= 0; negative = resident, untouched): each
+// wave takes 64 consecutive rows, ballots the ones to fetch, and copies them kRowsPerWave at
+// a time (one per 16-lane group for D = 128), so its lanes stay busy however sparse they are.
+template <int D>
+__global__ __launch_bounds__(256) void gather_missing_kernel(const int32_t* __restrict__ idx, int k, int64_t N,
+                                                             const uint4* __restrict__ k_src,
+                                                             const uint4* __restrict__ v_src,
+                                                             uint4* __restrict__ k_sel, uint4* __restrict__ v_sel,
+                                                             int64_t total_rows) {
+  constexpr int kLanesPerRow = D * 2 / 16;
+  constexpr int kRowsPerWave = 64 / kLanesPerRow;
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / kLanesPerRow, part = lane % kLanesPerRow;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const uint32_t nan2 = 0x7e007e00u;
+  for (int64_t c0 = wave * 64; c0 < total_rows; c0 += nwaves * 64) {
+    const int64_t mine = c0 + lane;
+    const int32_t pm = mine < total_rows ? idx[mine] : -1;
+    uint64_t todo = __ballot(pm >= 0);
+    while (todo) {
+      // the kRowsPerWave lowest rows still to fetch; group grp takes the grp-th of them
+      int pick = -1;
+      uint64_t t = todo;
+#pragma unroll
+      for (int g = 0; g < kRowsPerWave; ++g) {
+        const int b = t ? __builtin_ctzll(t) : -1;
+        if (g == grp) pick = b;
+        if (t) t &= t - 1;
+      }
+      todo = t;
+      const int32_t p = __shfl(pm, pick < 0 ? 0 : pick);
+      if (pick >= 0) {
+        const int64_t row = c0 + pick;
+        const int64_t slice = row / k;
+        uint4 kv = make_uint4(nan2, nan2, nan2, nan2), vv = kv;
+        if (p < N) {
+          const int64_t src = (slice * N + p) * kLanesPerRow + part;
+          kv = k_src[src];
+          vv = v_src[src];
+        }
+        k_sel[row * kLanesPerRow + part] = kv;
+        v_sel[row * kLanesPerRow + part] = vv;
+      }
+    }
+  }
+}
+
 template <int D, bool SKIP_NEG>
 void launch_gather_t(const Dims& d, const int32_t* idx, int k, const _Float16* k_src, const _Float16* v_src,
                      _Float16* k_sel, _Float16* v_sel, hipStream_t s) {
   const int64_t rows = d.slices() * k;
-  const int rows_per_pass = 256 / (D * 2 / 16);
-  const int64_t need = ceil_div(rows, rows_per_pass);
-  const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
-  gather_kernel<D, SKIP_NEG><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
+  if (SKIP_NEG) {
+    const int64_t need = ceil_div(rows, 256);  // 64 rows per wave, 4 waves per workgroup
+    const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
+    gather_missing_kernel<D><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
                                                   reinterpret_cast<const uint4*>(v_src),
                                                   reinterpret_cast<uint4*>(k_sel), reinterpret_cast<uint4*>(v_sel),
                                                   rows);
+    return;
+  }
+  const int rows_per_pass = 256 / (D * 2 / 16);
+  const int64_t need = ceil_div(rows, rows_per_pass);
+  const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
+  gather_kernel<D><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
+                                         reinterpret_cast<const uint4*>(v_src), reinterpret_cast<uint4*>(k_sel),
+                                         reinterpret_cast<uint4*>(v_sel), rows);
 }
 
 }  // namespace
