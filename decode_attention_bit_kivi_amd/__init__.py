@@ -8,7 +8,7 @@ package is its thin Python binding.  Build the library with
 from .api import (
     LowBitCache, empty_cache, lowbit_sizes, quantize_pack, score_topk, score_topk_workspace_size,
     gather_fp16, decode_attn, decode_attn_workspace_size, decode_step, decode_step_workspace_size,
-    GatherStream, ComputeStream, gather_reuse, gather_fp16_missing,
+    GatherStream, ComputeStream, gather_reuse, gather_fp16_missing, quantize_append, offload_fp16,
 )
 from ._lib import SpecacheError
 
@@ -16,5 +16,6 @@ __all__ = [
     "LowBitCache", "empty_cache", "lowbit_sizes", "quantize_pack", "score_topk",
     "score_topk_workspace_size", "gather_fp16", "decode_attn", "decode_attn_workspace_size",
     "decode_step", "decode_step_workspace_size", "GatherStream", "ComputeStream", "gather_reuse", "gather_fp16_missing",
+    "quantize_append", "offload_fp16",
     "SpecacheError",
 ]

@@ -14,7 +14,7 @@ import threading
 LIB_PATH = os.environ.get("SPECACHE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libspecache.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SPECACHE_OK = 0
 SPECACHE_ERR_INVALID = 1
@@ -26,6 +26,8 @@ SPECACHE_ERR_HIP = 5
 EXPORTED = (
     "specache_lowbit_bytes",
     "specache_quantize_pack",
+    "specache_quantize_append",
+    "specache_offload_fp16",
     "specache_score_topk_workspace_size",
     "specache_score_topk",
     "specache_gather_fp16",
@@ -52,6 +54,7 @@ class Shape(ctypes.Structure):
         ("seq_len", ctypes.c_int64),
         ("bits", ctypes.c_int32),
         ("group", ctypes.c_int32),
+        ("seq_capacity", ctypes.c_int64),
     ]
 
 
@@ -89,6 +92,8 @@ def load() -> ctypes.CDLL:
         sig = {
             "specache_lowbit_bytes": (SZ, [SP, PSZ, PSZ, PSZ, PSZ]),
             "specache_quantize_pack": (I, [SP, P, P, LP, P]),
+            "specache_quantize_append": (I, [SP, P, P, I64, LP, P]),
+            "specache_offload_fp16": (I, [SP, P, P, I64, I64, P, P, P]),
             "specache_score_topk_workspace_size": (SZ, [SP, I, I]),
             "specache_score_topk": (I, [SP, P, I, I, LP, F, I, P, P, P, SZ, P]),
             "specache_gather_fp16": (I, [SP, P, I, P, P, P, P, P]),

@@ -17,17 +17,19 @@ from . import _lib
 
 @dataclass
 class LowBitCache:
-    """C' of one layer: the four device buffers written by quantize_pack."""
-    k_codes: torch.Tensor   # uint32 [B, Hkv, N, bits, D/32]   (stored as int32)
-    k_meta: torch.Tensor    # float16 [B, Hkv, N/32, 2, D]
-    v_codes: torch.Tensor   # uint32 [B, Hkv, N/32, bits, D]
-    v_meta: torch.Tensor    # float16 [B, Hkv, N/32, 2, D/32, 32]
+    """C' of one layer: the four device buffers written by quantize_pack, laid out for
+    `capacity` positions of which the first `seq_len` are in use."""
+    k_codes: torch.Tensor   # uint32 [B, Hkv, Nc, bits, D/32]   (stored as int32)
+    k_meta: torch.Tensor    # float16 [B, Hkv, Nc/32, 2, D]
+    v_codes: torch.Tensor   # uint32 [B, Hkv, Nc/32, bits, D]
+    v_meta: torch.Tensor    # float16 [B, Hkv, Nc/32, 2, D/32, 32]
     batch: int
     n_kv_heads: int
     seq_len: int
     head_dim: int
     bits: int
     group: int = 32
+    capacity: int = 0       # 0: seq_len
 
     def c_struct(self) -> _lib.LowBit:
         return _lib.LowBit(self.k_codes.data_ptr(), self.k_meta.data_ptr(),
@@ -35,7 +37,7 @@ class LowBitCache:
 
     def shape(self, n_q_heads: int | None = None) -> _lib.Shape:
         return _lib.Shape(self.batch, n_q_heads or self.n_kv_heads, self.n_kv_heads, self.head_dim,
-                          self.seq_len, self.bits, self.group)
+                          self.seq_len, self.bits, self.group, self.capacity or self.seq_len)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_meta, self.v_codes, self.v_meta))
@@ -72,32 +74,70 @@ def lowbit_sizes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, bits:
             (batch, n_kv_heads, nblk, bits, head_dim), (batch, n_kv_heads, nblk, 2, W, 32))
 
 
-def empty_cache(batch, n_kv_heads, seq_len, head_dim, bits, device="cuda") -> LowBitCache:
-    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, seq_len, head_dim, bits)
+def empty_cache(batch, n_kv_heads, seq_len, head_dim, bits, device="cuda", capacity: int | None = None) -> LowBitCache:
+    cap = capacity or seq_len
+    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, cap, head_dim, bits)
     return LowBitCache(torch.empty(kc, dtype=torch.int32, device=device),
                        torch.empty(km, dtype=torch.float16, device=device),
                        torch.empty(vc, dtype=torch.int32, device=device),
                        torch.empty(vm, dtype=torch.float16, device=device),
-                       batch, n_kv_heads, seq_len, head_dim, bits)
+                       batch, n_kv_heads, seq_len, head_dim, bits, capacity=cap)
 
 
 def quantize_pack(k16: torch.Tensor, v16: torch.Tensor, bits: int, out: LowBitCache | None = None,
-                  stream=None) -> LowBitCache:
-    """specache_quantize_pack: K, V [B, Hkv, N, D] float16 (device) -> C'."""
+                  seq_len: int | None = None, stream=None) -> LowBitCache:
+    """specache_quantize_pack: K, V [B, Hkv, Nc, D] float16 (device) -> C' laid out for Nc
+    positions, of which the first seq_len (default Nc) are quantized."""
     _need(k16, "k16", torch.float16, 4)
     _need(v16, "v16", torch.float16, 4)
     if k16.shape != v16.shape:
         raise ValueError("k16 and v16 must have the same shape")
-    B, Hkv, N, D = k16.shape
-    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device)
+    B, Hkv, Nc, D = k16.shape
+    N = Nc if seq_len is None else int(seq_len)
+    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device, capacity=Nc)
     lib = _lib.load()
+    if out is not None:
+        cache.seq_len = N
     shape = cache.shape()
-    if (cache.batch, cache.n_kv_heads, cache.seq_len, cache.head_dim, cache.bits) != (B, Hkv, N, D, bits):
+    if (cache.batch, cache.n_kv_heads, cache.capacity or cache.seq_len, cache.head_dim, cache.bits) != \
+            (B, Hkv, Nc, D, bits):
         raise ValueError("out cache shape does not match the inputs")
     _lib.check(lib.specache_quantize_pack(ctypes.byref(shape), k16.data_ptr(), v16.data_ptr(),
                                           ctypes.byref(cache.c_struct()), _stream(stream)),
                "specache_quantize_pack")
     return cache
+
+
+def quantize_append(cache: LowBitCache, k16_new: torch.Tensor, v16_new: torch.Tensor, stream=None) -> LowBitCache:
+    """specache_quantize_append: quantize K, V [B, Hkv, n_new, D] (n_new a multiple of 32) into
+    positions [seq_len, seq_len + n_new) of the cache; cache.seq_len grows by n_new."""
+    _need(k16_new, "k16_new", torch.float16, 4)
+    _need(v16_new, "v16_new", torch.float16, 4)
+    if k16_new.shape != v16_new.shape:
+        raise ValueError("k16_new and v16_new must have the same shape")
+    n_new = k16_new.shape[2]
+    _lib.check(_lib.load().specache_quantize_append(ctypes.byref(cache.shape()), k16_new.data_ptr(),
+                                                    v16_new.data_ptr(), n_new, ctypes.byref(cache.c_struct()),
+                                                    _stream(stream)),
+               "specache_quantize_append")
+    cache.seq_len += n_new
+    return cache
+
+
+def offload_fp16(k16_new: torch.Tensor, v16_new: torch.Tensor, k16_cache: torch.Tensor, v16_cache: torch.Tensor,
+                 pos0: int, stream=None):
+    """specache_offload_fp16: rows [B, Hkv, n_new, D] (device) -> positions pos0.. of the 16-bit
+    cache [B, Hkv, Nc, D] (pinned host or device)."""
+    _need(k16_new, "k16_new", torch.float16, 4)
+    _need(v16_new, "v16_new", torch.float16, 4)
+    _need(k16_cache, "k16_cache", torch.float16, 4, cuda=False)
+    _need(v16_cache, "v16_cache", torch.float16, 4, cuda=False)
+    B, Hkv, Nc, D = k16_cache.shape
+    n_new = k16_new.shape[2]
+    shape = _lib.Shape(B, Hkv, Hkv, D, Nc, 1, 32, Nc)   # only the layout (Nc) matters here
+    _lib.check(_lib.load().specache_offload_fp16(ctypes.byref(shape), k16_new.data_ptr(), v16_new.data_ptr(), n_new,
+                                                 pos0, k16_cache.data_ptr(), v16_cache.data_ptr(), _stream(stream)),
+               "specache_offload_fp16")
 
 
 def score_topk_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int) -> int:
@@ -137,23 +177,24 @@ def score_topk(q16: torch.Tensor, cache: LowBitCache, k: int, rank_row: int = 1,
 
 
 def gather_fp16(idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor, bits: int = 1,
-                k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None, stream=None):
+                k_sel: torch.Tensor | None = None, v_sel: torch.Tensor | None = None, stream=None,
+                seq_len: int | None = None):
     """specache_gather_fp16: rows idx of the 16-bit cache (pinned host or device,
-    [B, Hkv, N, D]) -> (k_sel, v_sel) [B, Hkv, k, D] on the device."""
+    [B, Hkv, Nc, D], positions [0, seq_len) in use) -> (k_sel, v_sel) [B, Hkv, k, D]."""
     _need(idx, "idx", torch.int32, 3)
     _need(k16_src, "k16_src", torch.float16, 4, cuda=False)
     _need(v16_src, "v16_src", torch.float16, 4, cuda=False)
     for name, t in (("k16_src", k16_src), ("v16_src", v16_src)):
         if not (t.is_cuda or t.is_pinned()):
             raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
-    B, Hkv, N, D = k16_src.shape
+    B, Hkv, Nc, D = k16_src.shape
     k = idx.shape[2]
     dev = idx.device
     if k_sel is None:
         k_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
     if v_sel is None:
         v_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
-    shape = _lib.Shape(B, Hkv, Hkv, D, N, bits, 32)
+    shape = _lib.Shape(B, Hkv, Hkv, D, Nc if seq_len is None else seq_len, bits, 32, Nc)
     _lib.check(_lib.load().specache_gather_fp16(ctypes.byref(shape), idx.data_ptr(), k, k16_src.data_ptr(),
                                                 v16_src.data_ptr(), k_sel.data_ptr(), v_sel.data_ptr(),
                                                 _stream(stream)),
@@ -189,7 +230,8 @@ def gather_reuse(idx: torch.Tensor, idx_prev: torch.Tensor, k_sel_prev: torch.Te
 
 
 def gather_fp16_missing(fetch_idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor,
-                        k_sel: torch.Tensor, v_sel: torch.Tensor, bits: int = 1, stream=None):
+                        k_sel: torch.Tensor, v_sel: torch.Tensor, bits: int = 1, stream=None,
+                        seq_len: int | None = None):
     """specache_gather_fp16_missing: fetch the rows fetch_idx marks (>= 0) into k_sel / v_sel."""
     _need(fetch_idx, "fetch_idx", torch.int32, 3)
     _need(k16_src, "k16_src", torch.float16, 4, cuda=False)
@@ -199,9 +241,9 @@ def gather_fp16_missing(fetch_idx: torch.Tensor, k16_src: torch.Tensor, v16_src:
     for name, t in (("k16_src", k16_src), ("v16_src", v16_src)):
         if not (t.is_cuda or t.is_pinned()):
             raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
-    B, Hkv, N, D = k16_src.shape
+    B, Hkv, Nc, D = k16_src.shape
     k = fetch_idx.shape[2]
-    shape = _lib.Shape(B, Hkv, Hkv, D, N, bits, 32)
+    shape = _lib.Shape(B, Hkv, Hkv, D, Nc if seq_len is None else seq_len, bits, 32, Nc)
     _lib.check(_lib.load().specache_gather_fp16_missing(ctypes.byref(shape), fetch_idx.data_ptr(), k,
                                                         k16_src.data_ptr(), v16_src.data_ptr(), k_sel.data_ptr(),
                                                         v_sel.data_ptr(), _stream(stream)),

@@ -16,9 +16,11 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
     *err = SPECACHE_ERR_INVALID;
     return false;
   }
+  const int64_t cap = s->seq_capacity ? s->seq_capacity : s->seq_len;
   if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 || s->seq_len <= 0 ||
       s->n_q_heads % s->n_kv_heads != 0 || s->seq_len % kGroup != 0 || s->batch > 65535 ||
-      (int64_t)s->batch * s->n_kv_heads > 65535 || s->seq_len > (int64_t(1) << 31) - 1) {
+      (int64_t)s->batch * s->n_kv_heads > 65535 || cap < s->seq_len || cap % kGroup != 0 ||
+      cap > (int64_t(1) << 31) - 1) {
     *err = SPECACHE_ERR_INVALID;
     return false;
   }
@@ -40,6 +42,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
   d->W = s->head_dim / 32;
   d->N = s->seq_len;
   d->nblk = s->seq_len / kGroup;
+  d->Ns = cap;
   return true;
 }
 
@@ -130,11 +133,12 @@ size_t specache_lowbit_bytes(const specache_shape* shape, size_t* k_codes, size_
   Dims d;
   int err;
   if (!make_dims(shape, &d, &err)) return 0;
-  const size_t pos = (size_t)d.slices() * d.N;
+  const size_t pos = (size_t)d.slices() * d.Ns;  // laid out for the capacity
+  const size_t nb = (size_t)d.Ns / kGroup;
   const size_t kc = pos * d.bits * d.W * 4;
-  const size_t km = (size_t)d.slices() * d.nblk * 2 * d.D * 2;
-  const size_t vc = (size_t)d.slices() * d.nblk * d.bits * d.D * 4;
-  const size_t vm = (size_t)d.slices() * d.nblk * 2 * d.W * 32 * 2;
+  const size_t km = (size_t)d.slices() * nb * 2 * d.D * 2;
+  const size_t vc = (size_t)d.slices() * nb * d.bits * d.D * 4;
+  const size_t vm = (size_t)d.slices() * nb * 2 * d.W * 32 * 2;
   if (k_codes) *k_codes = kc;
   if (k_meta) *k_meta = km;
   if (v_codes) *v_codes = vc;
@@ -148,10 +152,47 @@ int specache_quantize_pack(const specache_shape* shape, const void* k16, const v
   int err;
   if (!make_dims(shape, &d, &err)) return err;
   if (!k16 || !v16 || !lowbit_ok(out)) return SPECACHE_ERR_INVALID;
-  return hip_status(launch_quantize(d, static_cast<const _Float16*>(k16), static_cast<const _Float16*>(v16),
-                                    static_cast<uint32_t*>(out->k_codes), static_cast<_Float16*>(out->k_meta),
+  return hip_status(launch_quantize(d, static_cast<const _Float16*>(k16), static_cast<const _Float16*>(v16), d.Ns, 0,
+                                    d.nblk, static_cast<uint32_t*>(out->k_codes), static_cast<_Float16*>(out->k_meta),
                                     static_cast<uint32_t*>(out->v_codes), static_cast<_Float16*>(out->v_meta),
                                     static_cast<hipStream_t>(stream)));
+}
+
+int specache_quantize_append(const specache_shape* shape, const void* k16_new, const void* v16_new, int64_t n_new,
+                             const specache_lowbit* cache, void* stream) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err)) return err;
+  if (n_new < 0 || n_new % kGroup != 0 || d.N + n_new > d.Ns) return SPECACHE_ERR_INVALID;
+  if (n_new == 0) return SPECACHE_OK;
+  if (!k16_new || !v16_new || !lowbit_ok(cache)) return SPECACHE_ERR_INVALID;
+  return hip_status(launch_quantize(d, static_cast<const _Float16*>(k16_new), static_cast<const _Float16*>(v16_new),
+                                    n_new, d.nblk, n_new / kGroup, static_cast<uint32_t*>(cache->k_codes),
+                                    static_cast<_Float16*>(cache->k_meta), static_cast<uint32_t*>(cache->v_codes),
+                                    static_cast<_Float16*>(cache->v_meta), static_cast<hipStream_t>(stream)));
+}
+
+int specache_offload_fp16(const specache_shape* shape, const void* k16_new, const void* v16_new, int64_t n_new,
+                          int64_t pos0, void* k16_dst, void* v16_dst, void* stream) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err)) return err;
+  if (n_new < 0 || pos0 < 0 || pos0 + n_new > d.Ns) return SPECACHE_ERR_INVALID;
+  if (n_new == 0) return SPECACHE_OK;
+  if (!k16_new || !v16_new || !k16_dst || !v16_dst) return SPECACHE_ERR_INVALID;
+  if (!device_view(k16_dst) || !device_view(v16_dst)) return SPECACHE_ERR_NOT_PINNED;
+  const size_t row = (size_t)d.D * sizeof(_Float16);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // one strided copy per tensor: slice b*Hkv+h of the new rows -> positions pos0.. of that slice
+  const void* srcs[2] = {k16_new, v16_new};
+  void* dsts[2] = {k16_dst, v16_dst};
+  for (int t = 0; t < 2; ++t) {
+    char* dst = static_cast<char*>(dsts[t]) + (size_t)pos0 * row;
+    if (hipMemcpy2DAsync(dst, (size_t)d.Ns * row, srcs[t], (size_t)n_new * row, (size_t)n_new * row,
+                         (size_t)d.slices(), hipMemcpyDefault, s) != hipSuccess)
+      return SPECACHE_ERR_HIP;
+  }
+  return SPECACHE_OK;
 }
 
 size_t specache_score_topk_workspace_size(const specache_shape* shape, int n_tokens, int k) {
@@ -280,6 +321,7 @@ int fill_attn_args(const Dims& d, const void* q16, int n_tokens, const specache_
   a->k_meta = static_cast<const _Float16*>(cache->k_meta);
   a->v_codes = static_cast<const uint32_t*>(cache->v_codes);
   a->v_meta = static_cast<const _Float16*>(cache->v_meta);
+  a->seq_stride = d.Ns;
   a->idx = idx;
   a->k = k;
   a->k_sel = static_cast<const _Float16*>(k_sel);

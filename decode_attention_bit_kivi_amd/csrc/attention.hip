@@ -78,7 +78,6 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   const int T = a.T;
   const int R = G * T;
   const int Hq = Hkv * G;
-  const int64_t nblk = N / 32;
   const int64_t row0 = b * Hq * T + h * G * T;
   const float qscale = a.sm_scale * kLog2e;
   const int64_t p0 = (int64_t)split * L;
@@ -203,10 +202,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     Words<CPL> vw[BITS];
     uint2 vs_lo, vs_hi, zs_lo, zs_hi;
   };
-  const uint32_t* kc_slice = a.k_codes + slice * N * BITS * W;
-  const uint32_t* vc_slice = a.v_codes + slice * nblk * BITS * D;
-  const _Float16* vm_slice = a.v_meta + slice * nblk * 2 * W * 32;
-  const _Float16* km_slice = a.k_meta + slice * nblk * 2 * D;
+  const int64_t Ns = a.seq_stride, nblk_s = a.seq_stride / 32;  // the cache's layout stride
+  const uint32_t* kc_slice = a.k_codes + slice * Ns * BITS * W;
+  const uint32_t* vc_slice = a.v_codes + slice * nblk_s * BITS * D;
+  const _Float16* vm_slice = a.v_meta + slice * nblk_s * 2 * W * 32;
+  const _Float16* km_slice = a.k_meta + slice * nblk_s * 2 * D;
   const int zrow = n16 < 2 * W ? n16 : 0;  // value-metadata row of the zero-point / scale column
   const bool zs_lane = n16 < 2 * W;
   // All loads are unconditional (clamped to valid blocks) so that they issue back to back.

@@ -18,7 +18,8 @@ constexpr int64_t kMaxAttnSeqLen = int64_t(4096) * 1024;  // 1024 splits of at m
 // Problem dimensions after validation.
 struct Dims {
   int B, Hq, Hkv, D, bits, G, W;
-  int64_t N, nblk;   // positions and 32-position blocks per slice
+  int64_t N, nblk;   // positions and 32-position blocks per slice (the cache's current length)
+  int64_t Ns;        // positions per slice the cache buffers are laid out for (>= N)
   int64_t slices() const { return (int64_t)B * Hkv; }
 };
 
@@ -112,8 +113,11 @@ inline AttnPlan attn_plan(const Dims& d, int cus) {
 
 // ---- launchers (defined in the .hip files) ----
 
-hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v16, uint32_t* k_codes,
-                           _Float16* k_meta, uint32_t* v_codes, _Float16* v_meta, hipStream_t s);
+// Quantizes nblocks 32-position blocks per slice of k16 / v16 ([slices][src_len][D]) into cache
+// blocks blk0 .. blk0 + nblocks - 1.
+hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v16, int64_t src_len, int64_t blk0,
+                           int64_t nblocks, uint32_t* k_codes, _Float16* k_meta, uint32_t* v_codes,
+                           _Float16* v_meta, hipStream_t s);
 
 // Also zeroes `hist` ([slices][2048]) for the rank kernels that follow on the same stream.
 hipError_t launch_score(const Dims& d, const ScorePlan& plan, const _Float16* q16, int n_tokens,
@@ -141,6 +145,7 @@ struct AttnArgs {
   const _Float16* k_meta;
   const uint32_t* v_codes;
   const _Float16* v_meta;
+  int64_t seq_stride;  // positions per slice the low-bit cache is laid out for
   const int32_t* idx;
   int k;
   const _Float16* k_sel;

@@ -34,7 +34,7 @@ constexpr int kUnroll = SPECACHE_GATHER_UNROLL;
 
 // An index outside [0, N) gives a NaN row.
 template <int D>
-__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx, int k, int64_t N,
+__global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__ idx, int k, int64_t N, int64_t Ns,
                                                      const uint4* __restrict__ k_src,
                                                      const uint4* __restrict__ v_src,
                                                      uint4* __restrict__ k_sel, uint4* __restrict__ v_sel,
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
         const int64_t slice = row / k;
         const int32_t p = idx[row];
         if (p >= 0 && p < N) {
-          const int64_t src = (slice * N + p) * kLanesPerRow + part;
+          const int64_t src = (slice * Ns + p) * kLanesPerRow + part;
 #ifdef SPECACHE_GATHER_NT
           typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
           const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_src + src));
@@ -133,6 +133,7 @@ __global__ __launch_bounds__(256) void reuse_kernel(const int32_t* __restrict__ 
 // a time (one per 16-lane group for D = 128), so its lanes stay busy however sparse they are.
 template <int D>
 __global__ __launch_bounds__(256) void gather_missing_kernel(const int32_t* __restrict__ idx, int k, int64_t N,
+                                                             int64_t Ns,
                                                              const uint4* __restrict__ k_src,
                                                              const uint4* __restrict__ v_src,
                                                              uint4* __restrict__ k_sel, uint4* __restrict__ v_sel,
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void gather_missing_kernel(const int32_t* __re
         const int64_t slice = row / k;
         uint4 kv = make_uint4(nan2, nan2, nan2, nan2), vv = kv;
         if (p < N) {
-          const int64_t src = (slice * N + p) * kLanesPerRow + part;
+          const int64_t src = (slice * Ns + p) * kLanesPerRow + part;
           kv = k_src[src];
           vv = v_src[src];
         }
@@ -183,7 +184,7 @@ void launch_gather_t(const Dims& d, const int32_t* idx, int k, const _Float16* k
   if (SKIP_NEG) {
     const int64_t need = ceil_div(rows, 256);  // 64 rows per wave, 4 waves per workgroup
     const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
-    gather_missing_kernel<D><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
+    gather_missing_kernel<D><<<grid, 256, 0, s>>>(idx, k, d.N, d.Ns, reinterpret_cast<const uint4*>(k_src),
                                                   reinterpret_cast<const uint4*>(v_src),
                                                   reinterpret_cast<uint4*>(k_sel), reinterpret_cast<uint4*>(v_sel),
                                                   rows);
@@ -192,7 +193,7 @@ void launch_gather_t(const Dims& d, const int32_t* idx, int k, const _Float16* k
   const int rows_per_pass = 256 / (D * 2 / 16);
   const int64_t need = ceil_div(rows, rows_per_pass);
   const unsigned grid = (unsigned)(need < kGatherBlocks ? need : kGatherBlocks);
-  gather_kernel<D><<<grid, 256, 0, s>>>(idx, k, d.N, reinterpret_cast<const uint4*>(k_src),
+  gather_kernel<D><<<grid, 256, 0, s>>>(idx, k, d.N, d.Ns, reinterpret_cast<const uint4*>(k_src),
                                          reinterpret_cast<const uint4*>(v_src), reinterpret_cast<uint4*>(k_sel),
                                          reinterpret_cast<uint4*>(v_sel), rows);
 }

@@ -70,18 +70,20 @@ __device__ __forceinline__ void load_tile(const _Float16* __restrict__ src, _Flo
 
 // Keys: thread t owns channel c = 32*(t/32) + e(t%32); a wave ballot over the
 // channels of one token is then directly the packed word of that token.
+// Grid: (blocks to write, slices).  Source block b is positions 32b.. of a slice of src_len
+// positions; it becomes cache block blk0 + b of a slice of Ns positions.
 template <int D>
-__global__ __launch_bounds__(D) void quant_keys_kernel(const _Float16* __restrict__ k16,
+__global__ __launch_bounds__(D) void quant_keys_kernel(const _Float16* __restrict__ k16, int64_t src_len,
                                                        uint32_t* __restrict__ codes,
-                                                       _Float16* __restrict__ meta, int64_t N,
+                                                       _Float16* __restrict__ meta, int64_t Ns, int64_t blk0,
                                                        int bits) {
   constexpr int W = D / 32;
   __shared__ _Float16 tile[32][D + 2];
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = blk0 + blockIdx.x;
   const int64_t slice = blockIdx.y;
-  const int64_t nblk = N / 32;
+  const int64_t nblk = Ns / 32;
   const int t = threadIdx.x;
-  load_tile<D, D>(k16 + (slice * N + blk * 32) * D, tile);
+  load_tile<D, D>(k16 + (slice * src_len + (int64_t)blockIdx.x * 32) * D, tile);
   __syncthreads();
 
   const int c = 32 * (t >> 5) + bit_to_elem(t & 31);
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(D) void quant_keys_kernel(const _Float16* __restric
   }
   if (lane < 32) {
     const int w0 = 2 * (t >> 6);  // the two words this wave's 64 channels form
-    uint32_t* dst = codes + ((slice * N + blk * 32 + lane) * bits) * W;
+    uint32_t* dst = codes + ((slice * Ns + blk * 32 + lane) * bits) * W;
     for (int j = 0; j < bits; ++j) {
       dst[j * W + w0] = keep[j][0];
       dst[j * W + w0 + 1] = keep[j][1];
@@ -124,17 +126,17 @@ __global__ __launch_bounds__(D) void quant_keys_kernel(const _Float16* __restric
 // Values: thread t owns (group w = t/32, token e(t%32)); a wave ballot over
 // the tokens of one channel is then directly that channel's packed word.
 template <int D>
-__global__ __launch_bounds__(D) void quant_values_kernel(const _Float16* __restrict__ v16,
+__global__ __launch_bounds__(D) void quant_values_kernel(const _Float16* __restrict__ v16, int64_t src_len,
                                                          uint32_t* __restrict__ codes,
-                                                         _Float16* __restrict__ meta, int64_t N,
+                                                         _Float16* __restrict__ meta, int64_t Ns, int64_t blk0,
                                                          int bits) {
   constexpr int W = D / 32;
   __shared__ _Float16 tile[32][D + 2];
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = blk0 + blockIdx.x;
   const int64_t slice = blockIdx.y;
-  const int64_t nblk = N / 32;
+  const int64_t nblk = Ns / 32;
   const int t = threadIdx.x;
-  load_tile<D, D>(v16 + (slice * N + blk * 32) * D, tile);
+  load_tile<D, D>(v16 + (slice * src_len + (int64_t)blockIdx.x * 32) * D, tile);
   __syncthreads();
 
   const int w = t >> 5;
@@ -177,15 +179,17 @@ __global__ __launch_bounds__(D) void quant_values_kernel(const _Float16* __restr
 
 }  // namespace
 
-hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v16, uint32_t* k_codes,
-                           _Float16* k_meta, uint32_t* v_codes, _Float16* v_meta, hipStream_t s) {
-  const dim3 grid((unsigned)d.nblk, (unsigned)d.slices());
+hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v16, int64_t src_len, int64_t blk0,
+                           int64_t nblocks, uint32_t* k_codes, _Float16* k_meta, uint32_t* v_codes,
+                           _Float16* v_meta, hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)nblocks, (unsigned)d.slices());
   if (d.D == 128) {
-    quant_keys_kernel<128><<<grid, 128, 0, s>>>(k16, k_codes, k_meta, d.N, d.bits);
-    quant_values_kernel<128><<<grid, 128, 0, s>>>(v16, v_codes, v_meta, d.N, d.bits);
+    quant_keys_kernel<128><<<grid, 128, 0, s>>>(k16, src_len, k_codes, k_meta, d.Ns, blk0, d.bits);
+    quant_values_kernel<128><<<grid, 128, 0, s>>>(v16, src_len, v_codes, v_meta, d.Ns, blk0, d.bits);
   } else {
-    quant_keys_kernel<64><<<grid, 64, 0, s>>>(k16, k_codes, k_meta, d.N, d.bits);
-    quant_values_kernel<64><<<grid, 64, 0, s>>>(v16, v_codes, v_meta, d.N, d.bits);
+    quant_keys_kernel<64><<<grid, 64, 0, s>>>(k16, src_len, k_codes, k_meta, d.Ns, blk0, d.bits);
+    quant_values_kernel<64><<<grid, 64, 0, s>>>(v16, src_len, v_codes, v_meta, d.Ns, blk0, d.bits);
   }
   return hipGetLastError();
 }

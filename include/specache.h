@@ -54,9 +54,14 @@
  * ------------------------------------------------------------------------
  *  B = batch, Hq = query heads, Hkv = KV heads, G = Hq / Hkv (query head hq
  *  reads KV head hq / G), D = head_dim (64 or 128), N = cached positions
- *  (a positive multiple of 32), T = query tokens per step (1 or 2; row 0 is
- *  the real token T_t, row 1 the speculative token T'_{t+1}), b = bits per
- *  code (1 or 2), g = quantization group = 32, W = D / 32.  G * T <= 16.
+ *  (a positive multiple of 32; specache_shape.seq_len), Nc = positions the
+ *  cache buffers are laid out for (specache_shape.seq_capacity, 0 meaning
+ *  Nc = N; a multiple of 32, Nc >= N), T = query tokens per step (1 or 2;
+ *  row 0 is the real token T_t, row 1 the speculative token T'_{t+1}),
+ *  b = bits per code (1 or 2), g = quantization group = 32, W = D / 32.
+ *  G * T <= 16.  Every call reads and writes positions [0, N) of the caches;
+ *  positions [N, Nc) are room for specache_quantize_append and
+ *  specache_offload_fp16 (the decode-time cache update).
  *
  * ------------------------------------------------------------------------
  * Low-bit cache C' (written by specache_quantize_pack)
@@ -81,13 +86,13 @@
  *  elements in the high half-word (element e is a channel for keys, a token
  *  for values).
  *
- *  k_codes  uint32 [B][Hkv][N][b][W]       word (p, j, w) holds plane j of the
+ *  k_codes  uint32 [B][Hkv][Nc][b][W]      word (p, j, w) holds plane j of the
  *                                          codes of token p, channels 32w+e(i).
- *  k_meta   float16[B][Hkv][N/32][2][D]    [blk][0][c] = z, [blk][1][c] = s of the
+ *  k_meta   float16[B][Hkv][Nc/32][2][D]   [blk][0][c] = z, [blk][1][c] = s of the
  *                                          key group (tokens 32blk..32blk+31, channel c).
- *  v_codes  uint32 [B][Hkv][N/32][b][D]    word (blk, j, c) holds plane j of the
+ *  v_codes  uint32 [B][Hkv][Nc/32][b][D]   word (blk, j, c) holds plane j of the
  *                                          codes of channel c, tokens 32blk+e(i).
- *  v_meta   float16[B][Hkv][N/32][2][W][32] [blk][0][w][t] = z, [blk][1][w][t] = s of
+ *  v_meta   float16[B][Hkv][Nc/32][2][W][32] [blk][0][w][t] = z, [blk][1][w][t] = s of
  *                                          the value group (token 32blk+t, channels
  *                                          32w..32w+31).
  *  Bytes per position per KV head: (b*D/8 + 4*D/32) for keys and the same for
@@ -97,7 +102,7 @@
  * Other tensors
  * ------------------------------------------------------------------------
  *  q16, out16      float16 [B][Hq][T][D]
- *  k16, v16        float16 [B][Hkv][N][D]      the full 16-bit cache C
+ *  k16, v16        float16 [B][Hkv][Nc][D]     the full 16-bit cache C (positions [0, N) used)
  *  idx             int32   [B][Hkv][k]         strictly ascending, each in [0, N)
  *  k_sel, v_sel    float16 [B][Hkv][k][D]      row i = 16-bit row idx[i]
  *  k_tail, v_tail  float16 [B][Hkv][R][D]      optional 16-bit positions after the
@@ -114,7 +119,7 @@
 extern "C" {
 #endif
 
-#define SPECACHE_ABI_VERSION 2
+#define SPECACHE_ABI_VERSION 3
 
 typedef enum specache_status {
   SPECACHE_OK = 0,
@@ -131,9 +136,10 @@ typedef struct specache_shape {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   int32_t head_dim;
-  int64_t seq_len;
+  int64_t seq_len;       /* N: cached positions in use */
   int32_t bits;
   int32_t group;
+  int64_t seq_capacity;  /* Nc: positions the cache buffers hold; 0 = seq_len */
 } specache_shape;
 
 /* The four device buffers of C' (layouts above). */
@@ -144,18 +150,45 @@ typedef struct specache_lowbit {
   void* v_meta;
 } specache_lowbit;
 
-/* Byte sizes of the four C' buffers for `shape` (0 for an invalid shape). */
+/* Byte sizes of the four C' buffers for `shape`, laid out for its capacity Nc (0 for an
+ * invalid shape). */
 size_t specache_lowbit_bytes(const specache_shape* shape, size_t* k_codes, size_t* k_meta,
                              size_t* v_codes, size_t* v_meta);
 
 /*
  * Quant(K), Quant(V) of the summary's Algorithm 1 (prefill), with the §3
- * quantizer described above: reads k16, v16 [B][Hkv][N][D] (device float16)
- * and writes the four buffers of `out`.  Bit-exact by definition (no
- * floating-point freedom).  Inputs must be finite.
+ * quantizer described above: reads positions [0, N) of k16, v16
+ * [B][Hkv][Nc][D] (device float16) and writes them into the four buffers of
+ * `out`.  Bit-exact by definition (no floating-point freedom).  Inputs must
+ * be finite.
  */
 int specache_quantize_pack(const specache_shape* shape, const void* k16, const void* v16,
                            const specache_lowbit* out, void* stream);
+
+/*
+ * C' = [C', C'_t] of Algorithm 3 (the decode-time cache update): quantizes
+ * n_new new positions, k16_new / v16_new [B][Hkv][n_new][D] (device float16),
+ * into positions [N, N + n_new) of `cache`, exactly as specache_quantize_pack
+ * would have quantized them as part of the whole cache.  A key group spans 32
+ * tokens, so positions are appended in whole groups: n_new is a multiple of
+ * 32 and the newest tokens wait in the 16-bit tail (the residual window;
+ * specache_decode_attn's k_tail / v_tail) until a group is complete.
+ * N + n_new <= Nc.  After the call the cache holds N + n_new positions (pass
+ * seq_len = N + n_new from then on).
+ */
+int specache_quantize_append(const specache_shape* shape, const void* k16_new, const void* v16_new,
+                             int64_t n_new, const specache_lowbit* cache, void* stream);
+
+/*
+ * C = [C, Offload(C_t)] of Algorithm 3: copies k16_new / v16_new
+ * [B][Hkv][n_new][D] (device float16) into positions [pos0, pos0 + n_new) of
+ * the 16-bit cache k16_dst / v16_dst [B][Hkv][Nc][D] -- pinned host memory (the
+ * source of specache_gather_fp16) or device memory; anything else returns
+ * SPECACHE_ERR_NOT_PINNED.  One strided DMA copy per tensor on `stream`.
+ * 0 <= pos0, pos0 + n_new <= Nc.
+ */
+int specache_offload_fp16(const specache_shape* shape, const void* k16_new, const void* v16_new,
+                          int64_t n_new, int64_t pos0, void* k16_dst, void* v16_dst, void* stream);
 
 /*
  * ArgTopK over the speculative row (the summary's quick read, second

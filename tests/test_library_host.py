@@ -52,6 +52,8 @@ def _shape(**kw):
 
 @pytest.mark.parametrize("bad,status", [
     (dict(seq_len=1000), _lib.SPECACHE_ERR_INVALID),          # not a multiple of 32
+    (dict(seq_capacity=992), _lib.SPECACHE_ERR_INVALID),      # capacity below seq_len
+    (dict(seq_capacity=1040), _lib.SPECACHE_ERR_INVALID),     # capacity not a multiple of 32
     (dict(bits=3), _lib.SPECACHE_ERR_INVALID),
     (dict(n_q_heads=7), _lib.SPECACHE_ERR_INVALID),           # not a multiple of Hkv
     (dict(head_dim=96), _lib.SPECACHE_ERR_UNSUPPORTED),
@@ -155,6 +157,25 @@ def test_lowbit_bytes_match_layout(lib, bits, D):
     assert [o.value for o in out] == want and total == sum(want)
     per_pos = total / (3 * 2 * 4096)
     assert per_pos == 2 * (bits * D / 8 + 4 * D / 32)
+
+
+def test_capacity_sizes_the_buffers_and_bounds_append_and_offload(lib):
+    s = _shape(seq_len=1024, seq_capacity=4096, batch=2)
+    tight = _shape(seq_len=4096, batch=2)
+    assert lib.specache_lowbit_bytes(ctypes.byref(s), None, None, None, None) == \
+        lib.specache_lowbit_bytes(ctypes.byref(tight), None, None, None, None)
+    lb = _lib.LowBit(1, 1, 1, 1)
+    app = lambda n, shape=s: lib.specache_quantize_append(ctypes.byref(shape), 1, 1, n, ctypes.byref(lb), None)  # noqa: E731
+    assert app(48) == _lib.SPECACHE_ERR_INVALID                 # not whole groups
+    assert app(3072 + 32) == _lib.SPECACHE_ERR_INVALID          # past the capacity
+    assert app(-32) == _lib.SPECACHE_ERR_INVALID
+    assert app(0) == _lib.SPECACHE_OK
+    assert app(32, _shape(seq_len=1024)) == _lib.SPECACHE_ERR_INVALID   # no room without a capacity
+    off = lambda n, pos: lib.specache_offload_fp16(ctypes.byref(s), 1, 1, n, pos, 1, 1, None)  # noqa: E731
+    assert off(1, 4096) == _lib.SPECACHE_ERR_INVALID
+    assert off(2, 4095) == _lib.SPECACHE_ERR_INVALID
+    assert off(1, -1) == _lib.SPECACHE_ERR_INVALID
+    assert off(0, 0) == _lib.SPECACHE_OK
 
 
 def test_compression_ratio_matches_pages():
