@@ -82,6 +82,7 @@ def parse():
     ap.add_argument("--reuse", action=argparse.BooleanOptionalAction, default=True,
                     help="fetch only the rows of the new top-k not already resident (the step time of "
                          "fetching every row is reported beside it)")
+    ap.add_argument("--top-k", type=int, default=0, help="override the workload's top-k (latency-vs-k sweeps)")
     ap.add_argument("--rank", choices=("lowbit", "mixed"), default="lowbit",
                     help="lowbit: rank against C'; mixed: by the attention row itself (fetched rows and tail in)")
     ap.add_argument("--compute-reserve", type=int, default=32,
@@ -122,6 +123,13 @@ def algorithmic_bytes_step(cfg) -> int:
     rows = cfg.batch * cfg.n_q_heads * cfg.n_tokens
     per_slice = per_pos * cfg.seq_len + (2 * 2 * cfg.head_dim + 4) * cfg.top_k + 4 * cfg.top_k
     return slices * per_slice + 2 * rows * cfg.head_dim * 2
+
+
+def decode_attn_fp16_workspace_size_bytes(cfg) -> int:
+    import ctypes
+    from decode_attention_bit_kivi_amd import _lib
+    shape = _lib.Shape(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len, cfg.bits, 32, 0)
+    return int(_lib.load().specache_decode_attn_fp16_workspace_size(ctypes.byref(shape), cfg.n_tokens, 0))
 
 
 def cpu_baseline(cfg, K, V, Q, budget_s: float):
@@ -177,11 +185,13 @@ def main():
     from decode_attention_bit_kivi_amd import (
         quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, empty_cache,
         score_topk_workspace_size, decode_attn_workspace_size, decode_step_workspace_size, GatherStream,
-        ComputeStream, gather_reuse, gather_fp16_missing,
+        ComputeStream, gather_reuse, gather_fp16_missing, decode_attn_fp16,
     )
     from workloads import get_config, generate_all, generate_step_queries
 
     cfg = get_config(args.workload)
+    if args.top_k:
+        cfg = cfg.with_(top_k=args.top_k)
     B, Hq, Hkv, N, D, T, k = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.seq_len, cfg.head_dim, cfg.n_tokens, cfg.top_k
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     K, V, Q, _, _, _ = generate_all(cfg)
@@ -218,7 +228,6 @@ def main():
 
     layers = args.copies or max(3, math.ceil(512e6 / cache0.nbytes()))
     caches = [cache0] + [quantize_pack(k16, v16, cfg.bits) for _ in range(layers - 1)]
-    del k16, v16
     torch.cuda.synchronize()
 
     ws = torch.empty(decode_step_workspace_size(cache0, Hq, T, k, 0, k), dtype=torch.uint8, device=dev)
@@ -340,6 +349,29 @@ def main():
         decode_attn(qs[i % n_q], caches[i % layers], st["idx"][i % layers][0], st["sel"][i % layers][0][0],
                     st["sel"][i % layers][0][1], out=out, workspace=ws_a)))
 
+    # comparators (SpeCache summary: the 16-bit decoding its throughput ratios are taken against,
+    # §5 Table 3; the non-speculative serial fetch of Table 4)
+    ws16 = torch.empty(decode_attn_fp16_workspace_size_bytes(cfg), dtype=torch.uint8, device=dev)
+    fp16_us = compute_loop(lambda i: decode_attn_fp16(qs[i % n_q], k16, v16, out=out, workspace=ws16))
+    fp16_bytes = 2 * B * Hkv * N * D * 2 + 2 * B * Hq * T * D * 2
+    serial_rows = [(torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev),
+                    torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)) for _ in range(2)]
+    serial_idx = torch.empty_like(st["idx"][0][0])
+
+    def serial_step(i):
+        """Rank with the real token against C', fetch its top-k (no overlap), then attend."""
+        c = caches[i % layers]
+        score_topk(qs[i % n_q], c, k, rank_row=0, idx_out=serial_idx, workspace=ws_s)
+        stepped[0].record(comp)
+        side.wait_event(stepped[0])
+        gather_fp16(serial_idx, hk, hv, cfg.bits, *serial_rows[i % 2], stream=side)
+        gathered[0].record(side)
+        comp.wait_event(gathered[0])
+        decode_attn(qs[i % n_q], c, serial_idx, serial_rows[i % 2][0], serial_rows[i % 2][1], out=out,
+                    workspace=ws_a)
+
+    serial_us = compute_loop(serial_step)
+
     step_bytes = algorithmic_bytes_step(cfg)
     step_avg_s = float(step_us.mean()) * 1e-6
     achieved = step_bytes / step_avg_s / 1e9
@@ -401,6 +433,16 @@ def main():
             "quantize_pack": (2 * B * Hkv * N * D * 2 + caches[0].nbytes()) / (quant_us * 1e-6) / 1e9,
         },
         "fetched_fraction": fetched,
+        "comparators": {
+            "fp16_attention_us": fp16_us,
+            "fp16_attention_GBs": fp16_bytes / (fp16_us * 1e-6) / 1e9,
+            "fp16_attention_tokens_per_s": B / (fp16_us * 1e-6),
+            "step_speedup_vs_fp16_attention": fp16_us / (ms_step * 1e3),
+            "serial_fetch_step_us": serial_us,
+            "step_speedup_vs_serial_fetch": serial_us / (ms_step * 1e3),
+            "what": "fp16: attention over the whole 16-bit cache in HBM (decode_attn_fp16); serial: rank "
+                    "with the real token against C', fetch its top-k without overlap, attend",
+        },
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host cores", file=sys.stderr, flush=True)

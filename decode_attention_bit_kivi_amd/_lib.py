@@ -35,6 +35,8 @@ EXPORTED = (
     "specache_gather_fp16_missing",
     "specache_decode_attn_workspace_size",
     "specache_decode_attn",
+    "specache_decode_attn_fp16_workspace_size",
+    "specache_decode_attn_fp16",
     "specache_decode_step_workspace_size",
     "specache_decode_step",
     "specache_gather_stream_create",
@@ -101,6 +103,8 @@ def load() -> ctypes.CDLL:
             "specache_gather_fp16_missing": (I, [SP, P, I, P, P, P, P, P]),
             "specache_decode_attn_workspace_size": (SZ, [SP, I, I, I]),
             "specache_decode_attn": (I, [SP, P, I, LP, P, I, P, P, P, P, I, F, P, P, SZ, P]),
+            "specache_decode_attn_fp16_workspace_size": (SZ, [SP, I, I]),
+            "specache_decode_attn_fp16": (I, [SP, P, I, P, P, P, P, I, F, P, P, SZ, P]),
             "specache_decode_step_workspace_size": (SZ, [SP, I, I, I, I]),
             "specache_decode_step": (I, [SP, P, I, I, I, LP, P, I, P, P, P, P, I, F, P, I, P, P, P, SZ, P]),
             "specache_gather_stream_create": (I, [I, ctypes.POINTER(P)]),

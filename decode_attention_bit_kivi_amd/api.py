@@ -340,6 +340,42 @@ def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None 
     return out
 
 
+def decode_attn_fp16(q16: torch.Tensor, k16: torch.Tensor, v16: torch.Tensor, seq_len: int | None = None,
+                     k_tail: torch.Tensor | None = None, v_tail: torch.Tensor | None = None,
+                     sm_scale: float | None = None, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """specache_decode_attn_fp16: the 16-bit comparator, attention over the full float16 cache
+    k16 / v16 [B, Hkv, Nc, D] (positions [0, seq_len) used) and the optional tail."""
+    _need(q16, "q16", torch.float16, 4)
+    _need(k16, "k16", torch.float16, 4, cuda=False)
+    _need(v16, "v16", torch.float16, 4, cuda=False)
+    B, Hq, T, D = q16.shape
+    _, Hkv, Nc, _ = k16.shape
+    N = Nc if seq_len is None else int(seq_len)
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    R = 0
+    ktp = vtp = 0
+    if k_tail is not None:
+        _need(k_tail, "k_tail", torch.float16, 4)
+        _need(v_tail, "v_tail", torch.float16, 4)
+        R = k_tail.shape[2]
+        ktp, vtp = k_tail.data_ptr(), v_tail.data_ptr()
+    lib = _lib.load()
+    shape = _lib.Shape(B, Hq, Hkv, D, N, 1, 32, Nc)
+    need = lib.specache_decode_attn_fp16_workspace_size(ctypes.byref(shape), T, R)
+    if need == 0:
+        raise ValueError("invalid decode_attn_fp16 arguments (shape, n_tokens or tail length)")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    if out is None:
+        out = torch.empty_like(q16)
+    _lib.check(lib.specache_decode_attn_fp16(ctypes.byref(shape), q16.data_ptr(), T, k16.data_ptr(), v16.data_ptr(),
+                                             ktp, vtp, R, sm_scale, out.data_ptr(), workspace.data_ptr(),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)),
+               "specache_decode_attn_fp16")
+    return out
+
+
 def decode_step_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int, tail_len: int,
                                k_next: int) -> int:
     shape = cache.shape(n_q_heads)

@@ -357,6 +357,52 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
   return hip_status(launch_attn_merge(d, plan, a, s));
 }
 
+size_t specache_decode_attn_fp16_workspace_size(const specache_shape* shape, int n_tokens, int tail_len) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err) || n_tokens < 1 || n_tokens > 2 || tail_len < 0 || tail_len > kMaxTail ||
+      d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen)
+    return 0;
+  return attn_ws(d, n_tokens).total;
+}
+
+int specache_decode_attn_fp16(const specache_shape* shape, const void* q16, int n_tokens, const void* k16,
+                              const void* v16, const void* k_tail, const void* v_tail, int tail_len, float sm_scale,
+                              void* out16, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  int err;
+  if (!make_dims(shape, &d, &err)) return err;
+  if (n_tokens < 1 || n_tokens > 2 || tail_len < 0 || tail_len > kMaxTail || !q16 || !k16 || !v16 || !out16 ||
+      !(sm_scale > 0.0f) || sm_scale == INFINITY)
+    return SPECACHE_ERR_INVALID;
+  if (d.G * n_tokens > kMaxRows || d.N > kMaxAttnSeqLen) return SPECACHE_ERR_UNSUPPORTED;
+  if (tail_len > 0 && (!k_tail || !v_tail)) return SPECACHE_ERR_INVALID;
+  const void* kd = device_view(k16);
+  const void* vd = device_view(v16);
+  if (!kd || !vd) return SPECACHE_ERR_NOT_PINNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const AttnPlan plan = attn_plan(d, stream_cus(s));
+  const AttnWs ws = attn_ws(d, n_tokens);
+  if (!workspace || workspace_bytes < ws.total) return SPECACHE_ERR_WORKSPACE;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q16 = static_cast<const _Float16*>(q16);
+  a.T = n_tokens;
+  a.k = (int)d.Ns;  // the whole 16-bit cache is the row array: row p = position p
+  a.k_sel = static_cast<const _Float16*>(kd);
+  a.v_sel = static_cast<const _Float16*>(vd);
+  a.k_tail = static_cast<const _Float16*>(k_tail);
+  a.v_tail = static_cast<const _Float16*>(v_tail);
+  a.tail = tail_len;
+  a.sm_scale = sm_scale;
+  a.out16 = static_cast<_Float16*>(out16);
+  char* base = static_cast<char*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(base + ws.ml);
+  a.part_acc = reinterpret_cast<float*>(base + ws.acc);
+  if (launch_attn16_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
+  return hip_status(launch_attn_merge(d, plan, a, s));
+}
+
 size_t specache_decode_step_workspace_size(const specache_shape* shape, int n_tokens, int k, int tail_len,
                                            int k_next) {
   Dims d;

@@ -60,7 +60,9 @@ struct AttnSmem {
 
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D, int BITS, int PACK, bool RANK>
+// F16: the 16-bit comparator -- no low-bit cache; every position of the split is a 16-bit row
+// of a.k_sel / a.v_sel (the whole 16-bit cache, a.k = its positions per slice).
+template <int D, int BITS, int PACK, bool RANK, bool F16 = false>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L,
                                                             int S) {
   constexpr int W = D / 32;
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 
   // ---- kappa positions of this split: a bitmask over its blocks and the range [i0, i1) of
   // fetched rows whose positions fall in it (idx is ascending), found by one parallel pass.
+  int i0 = (int)p0, i1 = (int)p1;
+  if constexpr (!F16) {
   for (int i = tid; i < kMaxBlocksPerSplit; i += 256) sm.kmask[i] = 0u;
   if (tid < 2) sm.sel_range[tid] = 0;
   __syncthreads();
@@ -113,7 +117,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
   }
   __syncthreads();
-  const int i0 = sm.sel_range[0], i1 = sm.sel_range[1];
+  i0 = sm.sel_range[0];
+  i1 = sm.sel_range[1];
+  }
 
   // ---- query fragments: B[k-slot (g, j)][column] = q[row][32w + 8g + j]
   Frag B0[W], B1[W];
@@ -371,7 +377,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   };
 
   // Two block buffers in turn: the next block's loads are in flight while one is computed.
-  {
+  if constexpr (!F16) {
     BlockData b0, b1;
     if (wave < nb) b0 = load_block(wave);
     for (int jj = wave; jj < nb; jj += 8) {
@@ -406,19 +412,26 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     const int lim = tail ? a.tail : i1;
     const _Float16* ksrc = tail ? a.k_tail + slice * a.tail * D : a.k_sel + slice * a.k * D;
     const _Float16* vsrc = tail ? a.v_tail + slice * a.tail * D : a.v_sel + slice * a.k * D;
-    // transpose the 32 value rows into this wave's LDS tile
+    // all 32 value and key rows in flight together, then the values transposed into this
+    // wave's LDS tile
+    Frag vv[2][W], kk[2][W];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int tok = 16 * tau + n16;
+      const int64_t src_row = base + tok < lim ? base + tok : lim - 1;
+#pragma unroll
+      for (int w = 0; w < W; ++w) vv[tau][w].v = load_u4(vsrc + src_row * D + 32 * w + 8 * g);
+#pragma unroll
+      for (int w = 0; w < W; ++w) kk[tau][w].v = load_u4(ksrc + src_row * D + 32 * w + 8 * g);
+    }
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int tok = 16 * tau + n16;
       const bool ok = base + tok < lim;
-      const int64_t src_row = ok ? base + tok : lim - 1;
-      Frag vv[W];
-#pragma unroll
-      for (int w = 0; w < W; ++w) vv[w].v = load_u4(vsrc + src_row * D + 32 * w + 8 * g);
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         Frag v;
-        v.v = ok ? vv[w].v : make_uint4(0, 0, 0, 0);
+        v.v = ok ? vv[tau][w].v : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) sm.u.vt[wave][32 * w + 8 * g + j][tok] = v.h[j];
       }
@@ -426,14 +439,6 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     f32x4 acc[2];
     acc[0] = zero4();
     acc[1] = zero4();
-    Frag kk[2][W];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int tok = 16 * tau + n16;
-      const int64_t src_row = base + tok < lim ? base + tok : lim - 1;
-#pragma unroll
-      for (int w = 0; w < W; ++w) kk[tau][w].v = load_u4(ksrc + src_row * D + 32 * w + 8 * g);
-    }
 #pragma unroll
     for (int w = 0; w < W; ++w) {
 #pragma unroll
@@ -674,6 +679,19 @@ void launch_split_r(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipS
 
 hipError_t launch_attn_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
   if (a.rank_logits) launch_split_r<true>(d, plan, a, s); else launch_split_r<false>(d, plan, a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn16_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
+  const bool pack2 = d.G * a.T <= 8;
+  if (d.D == 128) {
+    if (pack2) attn_split_kernel<128, 1, 2, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    else attn_split_kernel<128, 1, 1, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  } else {
+    if (pack2) attn_split_kernel<64, 1, 2, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    else attn_split_kernel<64, 1, 1, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  }
   return hipGetLastError();
 }
 

@@ -350,6 +350,22 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
                          int k_next, int32_t* idx_next_out, float* rank_key_out,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The 16-bit comparator: O = Attn(q, C) over the full 16-bit cache held in
+ * device memory -- the "16-bit" decoding the SpeCache summary's throughput
+ * ratios are taken against (quick read, results; §5 Table 3).  Same kernel
+ * organisation and partial merge as specache_decode_attn, with every cached
+ * position a 16-bit row: k16 / v16 [B][Hkv][Nc][D] float16 (positions [0, N)
+ * used; device memory, or pinned host memory read over the host link), the
+ * optional tail and its mask as in specache_decode_attn, out16
+ * [B][Hq][T][D].  Workspace: specache_decode_attn_fp16_workspace_size bytes.
+ */
+size_t specache_decode_attn_fp16_workspace_size(const specache_shape* shape, int n_tokens, int tail_len);
+int specache_decode_attn_fp16(const specache_shape* shape, const void* q16, int n_tokens, const void* k16,
+                              const void* v16, const void* k_tail, const void* v_tail, int tail_len,
+                              float sm_scale, void* out16, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Static description of a status code. */
 const char* specache_status_string(int status);
 

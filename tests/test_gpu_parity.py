@@ -24,7 +24,7 @@ import torch
 import oracle
 from decode_attention_bit_kivi_amd import (
     quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, GatherStream, ComputeStream,
-    SpecacheError, gather_reuse, gather_fp16_missing,
+    SpecacheError, gather_reuse, gather_fp16_missing, decode_attn_fp16,
 )
 from tests.layout import unpack_keys, unpack_values
 from workloads import get_config, generate_all
@@ -483,6 +483,34 @@ def test_fused_step_full_size_sampled(gpu, name, mixed):
         else:
             r_ref = oracle.rank_scores(q1, kh, 1, cfg.sm_scale)
         _assert_topk(nxt[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)])
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}),
+    ("tiny", dict(tail_len=3)),
+    ("tiny", dict(n_tokens=1, head_dim=128, seq_len=96)),
+    ("llama8k", {}),
+    ("llama8k", dict(seq_len=8192 + 96, tail_len=2)),
+    ("llama8k", dict(n_q_heads=64, n_kv_heads=8)),
+])
+def test_fp16_comparator_matches_oracle(gpu, name, over):
+    """The 16-bit comparator: attention over the float16 cache (the oracle's mixed attention
+    with every row fetched) -- and the same as decode_attn fetching every row."""
+    cfg = get_config(name).with_(**over)
+    K, V, Q, _, KT, VT = generate_all(cfg)
+    B, H, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
+    kt = None if KT is None else _dev(KT)
+    vt = None if VT is None else _dev(VT)
+    out = decode_attn_fp16(_dev(Q), _dev(K), _dev(V), k_tail=kt, v_tail=vt)
+    torch.cuda.synchronize()
+    ref = oracle.mixed_attention(Q, K.astype(np.float64), V.astype(np.float64), sm_scale=cfg.sm_scale, k_tail=KT,
+                                 v_tail=VT)
+    assert _attn_err(_np(out), ref) <= ATTN_TOL
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    idx = np.broadcast_to(np.arange(N, dtype=np.int32), (B, H, N)).copy()
+    o_all = decode_attn(_dev(Q), cache, _dev(idx), _dev(K), _dev(V), kt, vt)
+    torch.cuda.synchronize()
+    assert _attn_err(_np(out), _np(o_all).astype(np.float64)) <= 1e-3
 
 
 @pytest.mark.parametrize("name", ["mistral32k", "long128k"])
