@@ -14,7 +14,7 @@ import threading
 LIB_PATH = os.environ.get("SPECACHE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libspecache.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 SPECACHE_OK = 0
 SPECACHE_ERR_INVALID = 1
@@ -57,6 +57,8 @@ class Shape(ctypes.Structure):
         ("bits", ctypes.c_int32),
         ("group", ctypes.c_int32),
         ("seq_capacity", ctypes.c_int64),
+        ("v_bits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

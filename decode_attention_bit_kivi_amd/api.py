@@ -30,6 +30,7 @@ class LowBitCache:
     bits: int
     group: int = 32
     capacity: int = 0       # 0: seq_len
+    v_bits: int = 0         # bits of the value codes; 0: `bits` (then bits is both)
 
     def c_struct(self) -> _lib.LowBit:
         return _lib.LowBit(self.k_codes.data_ptr(), self.k_meta.data_ptr(),
@@ -37,7 +38,7 @@ class LowBitCache:
 
     def shape(self, n_q_heads: int | None = None) -> _lib.Shape:
         return _lib.Shape(self.batch, n_q_heads or self.n_kv_heads, self.n_kv_heads, self.head_dim,
-                          self.seq_len, self.bits, self.group, self.capacity or self.seq_len)
+                          self.seq_len, self.bits, self.group, self.capacity or self.seq_len, self.v_bits or self.bits)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_meta, self.v_codes, self.v_meta))
@@ -66,35 +67,40 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, cuda: bool = True):
         raise ValueError(f"{name} must be a GPU tensor")
 
 
-def lowbit_sizes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, bits: int, group: int = 32):
-    """(k_codes, k_meta, v_codes, v_meta) element shapes of C' (see include/specache.h)."""
+def lowbit_sizes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, bits: int, group: int = 32,
+                 v_bits: int | None = None):
+    """(k_codes, k_meta, v_codes, v_meta) element shapes of C' (see include/specache.h); bits
+    of the keys, v_bits (default bits) of the values."""
     W = head_dim // 32
     nblk = seq_len // group
+    vb = v_bits or bits
     return ((batch, n_kv_heads, seq_len, bits, W), (batch, n_kv_heads, nblk, 2, head_dim),
-            (batch, n_kv_heads, nblk, bits, head_dim), (batch, n_kv_heads, nblk, 2, W, 32))
+            (batch, n_kv_heads, nblk, vb, head_dim), (batch, n_kv_heads, nblk, 2, W, 32))
 
 
-def empty_cache(batch, n_kv_heads, seq_len, head_dim, bits, device="cuda", capacity: int | None = None) -> LowBitCache:
+def empty_cache(batch, n_kv_heads, seq_len, head_dim, bits, device="cuda", capacity: int | None = None,
+                v_bits: int | None = None) -> LowBitCache:
     cap = capacity or seq_len
-    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, cap, head_dim, bits)
+    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, cap, head_dim, bits, v_bits=v_bits)
     return LowBitCache(torch.empty(kc, dtype=torch.int32, device=device),
                        torch.empty(km, dtype=torch.float16, device=device),
                        torch.empty(vc, dtype=torch.int32, device=device),
                        torch.empty(vm, dtype=torch.float16, device=device),
-                       batch, n_kv_heads, seq_len, head_dim, bits, capacity=cap)
+                       batch, n_kv_heads, seq_len, head_dim, bits, capacity=cap, v_bits=v_bits or bits)
 
 
 def quantize_pack(k16: torch.Tensor, v16: torch.Tensor, bits: int, out: LowBitCache | None = None,
-                  seq_len: int | None = None, stream=None) -> LowBitCache:
+                  seq_len: int | None = None, stream=None, v_bits: int | None = None) -> LowBitCache:
     """specache_quantize_pack: K, V [B, Hkv, Nc, D] float16 (device) -> C' laid out for Nc
-    positions, of which the first seq_len (default Nc) are quantized."""
+    positions, of which the first seq_len (default Nc) are quantized; keys with `bits`, values
+    with `v_bits` (default `bits`)."""
     _need(k16, "k16", torch.float16, 4)
     _need(v16, "v16", torch.float16, 4)
     if k16.shape != v16.shape:
         raise ValueError("k16 and v16 must have the same shape")
     B, Hkv, Nc, D = k16.shape
     N = Nc if seq_len is None else int(seq_len)
-    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device, capacity=Nc)
+    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device, capacity=Nc, v_bits=v_bits)
     lib = _lib.load()
     if out is not None:
         cache.seq_len = N

@@ -24,7 +24,8 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
     *err = SPECACHE_ERR_INVALID;
     return false;
   }
-  if (s->bits != 1 && s->bits != 2) {
+  const int vbits = s->v_bits ? s->v_bits : s->bits;
+  if ((s->bits != 1 && s->bits != 2) || (vbits != 1 && vbits != 2)) {
     *err = SPECACHE_ERR_INVALID;
     return false;
   }
@@ -38,6 +39,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
   d->Hkv = s->n_kv_heads;
   d->D = s->head_dim;
   d->bits = s->bits;
+  d->vbits = vbits;
   d->G = s->n_q_heads / s->n_kv_heads;
   d->W = s->head_dim / 32;
   d->N = s->seq_len;
@@ -137,7 +139,7 @@ size_t specache_lowbit_bytes(const specache_shape* shape, size_t* k_codes, size_
   const size_t nb = (size_t)d.Ns / kGroup;
   const size_t kc = pos * d.bits * d.W * 4;
   const size_t km = (size_t)d.slices() * nb * 2 * d.D * 2;
-  const size_t vc = (size_t)d.slices() * nb * d.bits * d.D * 4;
+  const size_t vc = (size_t)d.slices() * nb * d.vbits * d.D * 4;
   const size_t vm = (size_t)d.slices() * nb * 2 * d.W * 32 * 2;
   if (k_codes) *k_codes = kc;
   if (k_meta) *k_meta = km;

@@ -62,13 +62,13 @@ __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)
 
 // F16: the 16-bit comparator -- no low-bit cache; every position of the split is a 16-bit row
 // of a.k_sel / a.v_sel (the whole 16-bit cache, a.k = its positions per slice).
-template <int D, int BITS, int PACK, bool RANK, bool F16 = false>
+template <int D, int KB, int VB, int PACK, bool RANK, bool F16 = false>
 __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L,
                                                             int S) {
   constexpr int W = D / 32;
   constexpr int CPL = D / 16;       // channels per lane in the value product (= channel tiles)
-  constexpr float hK = BITS == 1 ? 0.5f : 1.5f;
-  constexpr float hV = BITS == 1 ? 0.5f : 1.5f;
+  constexpr float hK = KB == 1 ? 0.5f : 1.5f;  // KB, VB: bits of the key and value codes
+  constexpr float hV = VB == 1 ? 0.5f : 1.5f;
   __shared__ AttnSmem<D, PACK> sm;
 
   const int tid = threadIdx.x;
@@ -204,13 +204,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 
   // ================= low-bit blocks =================
   struct BlockData {
-    Words<W> kw[2][BITS];
-    Words<CPL> vw[BITS];
+    Words<W> kw[2][KB];
+    Words<CPL> vw[VB];
     uint2 vs_lo, vs_hi, zs_lo, zs_hi;
   };
   const int64_t Ns = a.seq_stride, nblk_s = a.seq_stride / 32;  // the cache's layout stride
-  const uint32_t* kc_slice = a.k_codes + slice * Ns * BITS * W;
-  const uint32_t* vc_slice = a.v_codes + slice * nblk_s * BITS * D;
+  const uint32_t* kc_slice = a.k_codes + slice * Ns * KB * W;
+  const uint32_t* vc_slice = a.v_codes + slice * nblk_s * VB * D;
   const _Float16* vm_slice = a.v_meta + slice * nblk_s * 2 * W * 32;
   const _Float16* km_slice = a.k_meta + slice * nblk_s * 2 * D;
   const int zrow = n16 < 2 * W ? n16 : 0;  // value-metadata row of the zero-point / scale column
@@ -219,14 +219,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   auto load_block = [&](int jj) {
     BlockData bd;
     const int64_t blk = blk0 + jj;
-    const uint32_t* kc = kc_slice + blk * 32 * BITS * W;
+    const uint32_t* kc = kc_slice + blk * 32 * KB * W;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int pl = 0; pl < BITS; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * BITS + pl) * W);
-    const uint32_t* vc = vc_slice + blk * BITS * D;
+      for (int pl = 0; pl < KB; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * KB + pl) * W);
+    const uint32_t* vc = vc_slice + blk * VB * D;
 #pragma unroll
-    for (int pl = 0; pl < BITS; ++pl) bd.vw[pl] = load_words<CPL>(vc + pl * D + CPL * n16);
+    for (int pl = 0; pl < VB; ++pl) bd.vw[pl] = load_words<CPL>(vc + pl * D + CPL * n16);
     const _Float16* vm = vm_slice + blk * 2 * W * 32;
     bd.vs_lo = load_u2(vm + W * 32 + wv_grp * 32 + 4 * g);
     bd.vs_hi = load_u2(vm + W * 32 + wv_grp * 32 + 16 + 4 * g);
@@ -262,11 +262,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 
   auto compute_block = [&](const BlockData& bd, int jj, int step) {
     // scores
-    f32x4 acc[2][BITS];
+    f32x4 acc[2][KB];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int pl = 0; pl < BITS; ++pl) acc[tau][pl] = zero4();
+      for (int pl = 0; pl < KB; ++pl) acc[tau][pl] = zero4();
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const uint4 ksv = sm.kscale[wave][step & 15][g][w];
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
-        for (int pl = 0; pl < BITS; ++pl) {
+        for (int pl = 0; pl < KB; ++pl) {
           Frag A;
 #pragma unroll
           for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(bd.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int tau = PACK == 2 ? 0 : i / 4;
-      const float sacc = BITS == 1 ? acc[tau][0][i & 3] : acc[tau][0][i & 3] + 2.0f * acc[tau][BITS - 1][i & 3];
+      const float sacc = KB == 1 ? acc[tau][0][i & 3] : acc[tau][0][i & 3] + 2.0f * acc[tau][KB - 1][i & 3];
       xr[i] = fmaf(sacc, k1, c0m);
       xa[i] = fmaf(sacc, k1, c0);
     }
@@ -354,14 +354,14 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
     const Frag Ap = make_p(p, 1.0f);
     Frag Ap2;
-    if constexpr (BITS == 2) Ap2 = make_p(p, 2.0f);
+    if constexpr (VB == 2) Ap2 = make_p(p, 2.0f);
 
     // values
     const uint32_t vmag[4] = {bd.vs_lo.x, bd.vs_lo.y, bd.vs_hi.x, bd.vs_hi.y};
 #pragma unroll
     for (int ct = 0; ct < CPL; ++ct) {
 #pragma unroll
-      for (int pl = 0; pl < BITS; ++pl) {
+      for (int pl = 0; pl < VB; ++pl) {
         Frag Bv;
 #pragma unroll
         for (int d = 0; d < 4; ++d) Bv.u[d] = signed_pair(bd.vw[pl].w[ct], shv[d], vmag[d]);
@@ -657,22 +657,27 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
   out[row * D + c] = (_Float16)(o / Lrow);
 }
 
-template <int D, int BITS, bool RANK>
+template <int D, int KB, int VB, bool RANK>
 void launch_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
   if (d.G * a.T <= 8)
-    attn_split_kernel<D, BITS, 2, RANK><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    attn_split_kernel<D, KB, VB, 2, RANK><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   else
-    attn_split_kernel<D, BITS, 1, RANK><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    attn_split_kernel<D, KB, VB, 1, RANK><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+}
+
+template <int D, bool RANK>
+void launch_split_d(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  if (d.bits == 1) {
+    if (d.vbits == 1) launch_split<D, 1, 1, RANK>(d, plan, a, s); else launch_split<D, 1, 2, RANK>(d, plan, a, s);
+  } else {
+    if (d.vbits == 1) launch_split<D, 2, 1, RANK>(d, plan, a, s); else launch_split<D, 2, 2, RANK>(d, plan, a, s);
+  }
 }
 
 template <bool RANK>
 void launch_split_r(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
-  if (d.D == 128) {
-    if (d.bits == 1) launch_split<128, 1, RANK>(d, plan, a, s); else launch_split<128, 2, RANK>(d, plan, a, s);
-  } else {
-    if (d.bits == 1) launch_split<64, 1, RANK>(d, plan, a, s); else launch_split<64, 2, RANK>(d, plan, a, s);
-  }
+  if (d.D == 128) launch_split_d<128, RANK>(d, plan, a, s); else launch_split_d<64, RANK>(d, plan, a, s);
 }
 
 }  // namespace
@@ -686,11 +691,11 @@ hipError_t launch_attn16_split(const Dims& d, const AttnPlan& plan, const AttnAr
   const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
   const bool pack2 = d.G * a.T <= 8;
   if (d.D == 128) {
-    if (pack2) attn_split_kernel<128, 1, 2, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
-    else attn_split_kernel<128, 1, 1, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    if (pack2) attn_split_kernel<128, 1, 1, 2, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    else attn_split_kernel<128, 1, 1, 1, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   } else {
-    if (pack2) attn_split_kernel<64, 1, 2, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
-    else attn_split_kernel<64, 1, 1, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    if (pack2) attn_split_kernel<64, 1, 1, 2, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    else attn_split_kernel<64, 1, 1, 1, false, true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   }
   return hipGetLastError();
 }

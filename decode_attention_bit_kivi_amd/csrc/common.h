@@ -18,6 +18,7 @@ constexpr int64_t kMaxAttnSeqLen = int64_t(4096) * 1024;  // 1024 splits of at m
 // Problem dimensions after validation.
 struct Dims {
   int B, Hq, Hkv, D, bits, G, W;
+  int vbits;         // bits of the value codes (bits: of the key codes)
   int64_t N, nblk;   // positions and 32-position blocks per slice (the cache's current length)
   int64_t Ns;        // positions per slice the cache buffers are laid out for (>= N)
   int64_t slices() const { return (int64_t)B * Hkv; }

@@ -186,10 +186,10 @@ hipError_t launch_quantize(const Dims& d, const _Float16* k16, const _Float16* v
   const dim3 grid((unsigned)nblocks, (unsigned)d.slices());
   if (d.D == 128) {
     quant_keys_kernel<128><<<grid, 128, 0, s>>>(k16, src_len, k_codes, k_meta, d.Ns, blk0, d.bits);
-    quant_values_kernel<128><<<grid, 128, 0, s>>>(v16, src_len, v_codes, v_meta, d.Ns, blk0, d.bits);
+    quant_values_kernel<128><<<grid, 128, 0, s>>>(v16, src_len, v_codes, v_meta, d.Ns, blk0, d.vbits);
   } else {
     quant_keys_kernel<64><<<grid, 64, 0, s>>>(k16, src_len, k_codes, k_meta, d.Ns, blk0, d.bits);
-    quant_values_kernel<64><<<grid, 64, 0, s>>>(v16, src_len, v_codes, v_meta, d.Ns, blk0, d.bits);
+    quant_values_kernel<64><<<grid, 64, 0, s>>>(v16, src_len, v_codes, v_meta, d.Ns, blk0, d.vbits);
   }
   return hipGetLastError();
 }

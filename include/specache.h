@@ -58,7 +58,10 @@
  *  cache buffers are laid out for (specache_shape.seq_capacity, 0 meaning
  *  Nc = N; a multiple of 32, Nc >= N), T = query tokens per step (1 or 2;
  *  row 0 is the real token T_t, row 1 the speculative token T'_{t+1}),
- *  b = bits per code (1 or 2), g = quantization group = 32, W = D / 32.
+ *  b = bits per code (1 or 2; specache_shape.bits for the keys and
+ *  specache_shape.v_bits, default the same, for the values -- the summary's
+ *  §5 pairs 1- or 2-bit keys with 1- or 2-bit values), g = quantization
+ *  group = 32, W = D / 32.
  *  G * T <= 16.  Every call reads and writes positions [0, N) of the caches;
  *  positions [N, Nc) are room for specache_quantize_append and
  *  specache_offload_fp16 (the decode-time cache update).
@@ -86,17 +89,19 @@
  *  elements in the high half-word (element e is a channel for keys, a token
  *  for values).
  *
- *  k_codes  uint32 [B][Hkv][Nc][b][W]      word (p, j, w) holds plane j of the
+ *  k_codes  uint32 [B][Hkv][Nc][bk][W]     (bk, bv: key and value bits)
+ *                                          word (p, j, w) holds plane j of the
  *                                          codes of token p, channels 32w+e(i).
  *  k_meta   float16[B][Hkv][Nc/32][2][D]   [blk][0][c] = z, [blk][1][c] = s of the
  *                                          key group (tokens 32blk..32blk+31, channel c).
- *  v_codes  uint32 [B][Hkv][Nc/32][b][D]   word (blk, j, c) holds plane j of the
+ *  v_codes  uint32 [B][Hkv][Nc/32][bv][D]  word (blk, j, c) holds plane j of the
  *                                          codes of channel c, tokens 32blk+e(i).
  *  v_meta   float16[B][Hkv][Nc/32][2][W][32] [blk][0][w][t] = z, [blk][1][w][t] = s of
  *                                          the value group (token 32blk+t, channels
  *                                          32w..32w+31).
- *  Bytes per position per KV head: (b*D/8 + 4*D/32) for keys and the same for
- *  values -- 64 B at D = 128, b = 1 (one eighth of float16), 96 B at b = 2.
+ *  Bytes per position per KV head: (bk*D/8 + 4*D/32) for keys and
+ *  (bv*D/8 + 4*D/32) for values -- 64 B at D = 128 with 1-bit keys and
+ *  values (one eighth of float16), 96 B with 2 bits for both.
  *
  * ------------------------------------------------------------------------
  * Other tensors
@@ -119,7 +124,7 @@
 extern "C" {
 #endif
 
-#define SPECACHE_ABI_VERSION 3
+#define SPECACHE_ABI_VERSION 4
 
 typedef enum specache_status {
   SPECACHE_OK = 0,
@@ -140,6 +145,8 @@ typedef struct specache_shape {
   int32_t bits;
   int32_t group;
   int64_t seq_capacity;  /* Nc: positions the cache buffers hold; 0 = seq_len */
+  int32_t v_bits;        /* bits of the value codes; 0 = bits (then bits is both) */
+  int32_t reserved;      /* 0 */
 } specache_shape;
 
 /* The four device buffers of C' (layouts above). */

@@ -104,6 +104,35 @@ def test_quantize_bit_exact(gpu, name, over):
     _assert_quantize_exact(cache, ref, cfg.bits)
 
 
+@pytest.mark.parametrize("kbits,vbits", [(2, 1), (1, 2)])
+def test_mixed_key_value_bits(gpu, kbits, vbits):
+    """Keys and values with different code widths: codes bit-exact, attention and the fused
+    step against the oracle with each half dequantized at its own width."""
+    cfg = get_config("llama8k").with_(bits=kbits, seed=7, seq_len=4096 + 64)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), kbits, v_bits=vbits)
+    torch.cuda.synchronize()
+    kc, kz, ks = oracle.quantize_keys(K, kbits)
+    vc, vz, vs = oracle.quantize_values(V, vbits)
+    gk, gkz, gks = unpack_keys(_np(cache.k_codes), _np(cache.k_meta), kbits)
+    gv, gvz, gvs = unpack_values(_np(cache.v_codes), _np(cache.v_meta), vbits)
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    for got, want in ((gkz, kz), (gks, ks), (gvz, vz), (gvs, vs)):
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    kh, vh = oracle.dequantize_keys(kc, kz, ks), oracle.dequantize_values(vc, vz, vs)
+    rng = np.random.default_rng(3)
+    idx = _random_idx(rng, cfg.batch, cfg.n_kv_heads, cfg.seq_len, cfg.top_k)
+    sk, sv = oracle.gather_rows(K, V, idx)
+    o = decode_attn(_dev(Q), cache, _dev(idx), _dev(sk), _dev(sv))
+    of, nxt = decode_step(_dev(Q), cache, cfg.top_k, idx=_dev(idx), k_sel=_dev(sk), v_sel=_dev(sv))
+    torch.cuda.synchronize()
+    ref = oracle.mixed_attention(Q, kh, vh, idx, sk, sv, sm_scale=cfg.sm_scale)
+    assert _attn_err(_np(o), ref) <= ATTN_TOL
+    assert torch.equal(of.view(torch.int16), o.view(torch.int16))
+    r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
+    _assert_topk(_np(nxt), r_ref, cfg.top_k, [(0, h) for h in range(cfg.n_kv_heads)])
+
+
 @pytest.mark.parametrize("bits", [1, 2])
 def test_quantize_adversarial_values(gpu, bits):
     """Exact ties, constant groups, signed zeros, float16 extremes and subnormals."""

@@ -178,6 +178,18 @@ def test_capacity_sizes_the_buffers_and_bounds_append_and_offload(lib):
     assert off(0, 0) == _lib.SPECACHE_OK
 
 
+def test_mixed_bit_widths_size_the_value_planes(lib):
+    kc, km, vc, vm = [ctypes.c_size_t() for _ in range(4)]
+    s = _shape(bits=1, v_bits=2, batch=2, seq_len=2048)
+    total = lib.specache_lowbit_bytes(ctypes.byref(s), ctypes.byref(kc), ctypes.byref(km), ctypes.byref(vc),
+                                      ctypes.byref(vm))
+    shapes = lowbit_sizes(2, 2, 2048, 128, 1, v_bits=2)
+    assert [kc.value, km.value, vc.value, vm.value] == [4 * np.prod(shapes[0]), 2 * np.prod(shapes[1]),
+                                                       4 * np.prod(shapes[2]), 2 * np.prod(shapes[3])]
+    assert total / (2 * 2 * 2048) == (1 * 128 / 8 + 4 * 128 / 32) + (2 * 128 / 8 + 4 * 128 / 32)
+    assert lib.specache_lowbit_bytes(ctypes.byref(_shape(v_bits=3)), None, None, None, None) == 0
+
+
 def test_compression_ratio_matches_pages():
     """SpeCache summary, Figure 4 caption: at g = 32 and 1 bit the GPU copy is 0.13
     (Mistral, 32K) and 0.14 (LLaMA-3, 8K) of the 16-bit cache, with the §4 setup of
