@@ -70,37 +70,39 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, cuda: bool = True):
 def lowbit_sizes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, bits: int, group: int = 32,
                  v_bits: int | None = None):
     """(k_codes, k_meta, v_codes, v_meta) element shapes of C' (see include/specache.h); bits
-    of the keys, v_bits (default bits) of the values."""
-    W = head_dim // 32
-    nblk = seq_len // group
+    of the keys, v_bits (default bits) of the values, quantization group 32 or 64."""
+    nblk = seq_len // 32
     vb = v_bits or bits
-    return ((batch, n_kv_heads, seq_len, bits, W), (batch, n_kv_heads, nblk, 2, head_dim),
-            (batch, n_kv_heads, nblk, vb, head_dim), (batch, n_kv_heads, nblk, 2, W, 32))
+    return ((batch, n_kv_heads, seq_len, bits, head_dim // 32), (batch, n_kv_heads, seq_len // group, 2, head_dim),
+            (batch, n_kv_heads, nblk, vb, head_dim), (batch, n_kv_heads, nblk, 2, head_dim // group, 32))
 
 
 def empty_cache(batch, n_kv_heads, seq_len, head_dim, bits, device="cuda", capacity: int | None = None,
-                v_bits: int | None = None) -> LowBitCache:
+                v_bits: int | None = None, group: int = 32) -> LowBitCache:
     cap = capacity or seq_len
-    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, cap, head_dim, bits, v_bits=v_bits)
+    kc, km, vc, vm = lowbit_sizes(batch, n_kv_heads, cap, head_dim, bits, group=group, v_bits=v_bits)
     return LowBitCache(torch.empty(kc, dtype=torch.int32, device=device),
                        torch.empty(km, dtype=torch.float16, device=device),
                        torch.empty(vc, dtype=torch.int32, device=device),
                        torch.empty(vm, dtype=torch.float16, device=device),
-                       batch, n_kv_heads, seq_len, head_dim, bits, capacity=cap, v_bits=v_bits or bits)
+                       batch, n_kv_heads, seq_len, head_dim, bits, group=group, capacity=cap,
+                       v_bits=v_bits or bits)
 
 
 def quantize_pack(k16: torch.Tensor, v16: torch.Tensor, bits: int, out: LowBitCache | None = None,
-                  seq_len: int | None = None, stream=None, v_bits: int | None = None) -> LowBitCache:
+                  seq_len: int | None = None, stream=None, v_bits: int | None = None,
+                  group: int = 32) -> LowBitCache:
     """specache_quantize_pack: K, V [B, Hkv, Nc, D] float16 (device) -> C' laid out for Nc
     positions, of which the first seq_len (default Nc) are quantized; keys with `bits`, values
-    with `v_bits` (default `bits`)."""
+    with `v_bits` (default `bits`), in groups of `group` (32 or 64) tokens / channels."""
     _need(k16, "k16", torch.float16, 4)
     _need(v16, "v16", torch.float16, 4)
     if k16.shape != v16.shape:
         raise ValueError("k16 and v16 must have the same shape")
     B, Hkv, Nc, D = k16.shape
     N = Nc if seq_len is None else int(seq_len)
-    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device, capacity=Nc, v_bits=v_bits)
+    cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device, capacity=Nc, v_bits=v_bits,
+                                                    group=group)
     lib = _lib.load()
     if out is not None:
         cache.seq_len = N

@@ -20,6 +20,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
   if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 || s->seq_len <= 0 ||
       s->n_q_heads % s->n_kv_heads != 0 || s->seq_len % kGroup != 0 || s->batch > 65535 ||
       (int64_t)s->batch * s->n_kv_heads > 65535 || cap < s->seq_len || cap % kGroup != 0 ||
+      (s->group == 64 && (s->seq_len % 64 != 0 || cap % 64 != 0)) ||
       cap > (int64_t(1) << 31) - 1) {
     *err = SPECACHE_ERR_INVALID;
     return false;
@@ -29,7 +30,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
     *err = SPECACHE_ERR_INVALID;
     return false;
   }
-  if (s->group != kGroup || (s->head_dim != 64 && s->head_dim != 128) ||
+  if ((s->group != 32 && s->group != 64) || (s->head_dim != 64 && s->head_dim != 128) ||
       s->n_q_heads / s->n_kv_heads > kMaxRows) {
     *err = SPECACHE_ERR_UNSUPPORTED;
     return false;
@@ -40,6 +41,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
   d->D = s->head_dim;
   d->bits = s->bits;
   d->vbits = vbits;
+  d->group = s->group;
   d->G = s->n_q_heads / s->n_kv_heads;
   d->W = s->head_dim / 32;
   d->N = s->seq_len;
@@ -138,9 +140,9 @@ size_t specache_lowbit_bytes(const specache_shape* shape, size_t* k_codes, size_
   const size_t pos = (size_t)d.slices() * d.Ns;  // laid out for the capacity
   const size_t nb = (size_t)d.Ns / kGroup;
   const size_t kc = pos * d.bits * d.W * 4;
-  const size_t km = (size_t)d.slices() * nb * 2 * d.D * 2;
+  const size_t km = (size_t)d.slices() * (d.Ns / d.group) * 2 * d.D * 2;
   const size_t vc = (size_t)d.slices() * nb * d.vbits * d.D * 4;
-  const size_t vm = (size_t)d.slices() * nb * 2 * d.W * 32 * 2;
+  const size_t vm = (size_t)d.slices() * nb * 2 * (d.D / d.group) * 32 * 2;
   if (k_codes) *k_codes = kc;
   if (k_meta) *k_meta = km;
   if (v_codes) *v_codes = vc;
@@ -165,7 +167,7 @@ int specache_quantize_append(const specache_shape* shape, const void* k16_new, c
   Dims d;
   int err;
   if (!make_dims(shape, &d, &err)) return err;
-  if (n_new < 0 || n_new % kGroup != 0 || d.N + n_new > d.Ns) return SPECACHE_ERR_INVALID;
+  if (n_new < 0 || n_new % d.group != 0 || d.N + n_new > d.Ns) return SPECACHE_ERR_INVALID;
   if (n_new == 0) return SPECACHE_OK;
   if (!k16_new || !v16_new || !lowbit_ok(cache)) return SPECACHE_ERR_INVALID;
   return hip_status(launch_quantize(d, static_cast<const _Float16*>(k16_new), static_cast<const _Float16*>(v16_new),
@@ -324,6 +326,7 @@ int fill_attn_args(const Dims& d, const void* q16, int n_tokens, const specache_
   a->v_codes = static_cast<const uint32_t*>(cache->v_codes);
   a->v_meta = static_cast<const _Float16*>(cache->v_meta);
   a->seq_stride = d.Ns;
+  a->group = d.group;
   a->idx = idx;
   a->k = k;
   a->k_sel = static_cast<const _Float16*>(k_sel);

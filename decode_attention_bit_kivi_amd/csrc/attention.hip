@@ -143,7 +143,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   for (int ct = 0; ct < CPL; ++ct) Oacc[ct] = zero4();
   f32x4 Ozs = zero4();
 
-  const int wv_grp = (CPL * n16) / 32;  // value group of this lane's channels
+  const int gshift = a.group == 64 ? 1 : 0;  // groups of 64 (keys: tokens, values: channels)
+  const int Wg = W >> gshift;                 // value groups per token
+  const int wv_grp = (CPL * n16) >> (5 + gshift);  // value group of this lane's channels
   const int arow = PACK == 2 ? (n16 & 7) : n16;  // query row of this lane's logits
   const bool rank_lane = RANK && arow < R && (arow % T) == a.rank_row;
   // token (within a block) of A/B k-slot j for k-group g: j < 4 -> 4g + j, else 16 + 4g + j - 4
@@ -211,10 +213,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   const int64_t Ns = a.seq_stride, nblk_s = a.seq_stride / 32;  // the cache's layout stride
   const uint32_t* kc_slice = a.k_codes + slice * Ns * KB * W;
   const uint32_t* vc_slice = a.v_codes + slice * nblk_s * VB * D;
-  const _Float16* vm_slice = a.v_meta + slice * nblk_s * 2 * W * 32;
-  const _Float16* km_slice = a.k_meta + slice * nblk_s * 2 * D;
-  const int zrow = n16 < 2 * W ? n16 : 0;  // value-metadata row of the zero-point / scale column
-  const bool zs_lane = n16 < 2 * W;
+  const _Float16* vm_slice = a.v_meta + slice * nblk_s * 2 * Wg * 32;
+  const _Float16* km_slice = a.k_meta + slice * (nblk_s >> gshift) * 2 * D;
+  const int zrow = n16 < 2 * Wg ? n16 : 0;  // value-metadata row of the zero-point / scale column
+  const bool zs_lane = n16 < 2 * Wg;
   // All loads are unconditional (clamped to valid blocks) so that they issue back to back.
   auto load_block = [&](int jj) {
     BlockData bd;
@@ -227,9 +229,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     const uint32_t* vc = vc_slice + blk * VB * D;
 #pragma unroll
     for (int pl = 0; pl < VB; ++pl) bd.vw[pl] = load_words<CPL>(vc + pl * D + CPL * n16);
-    const _Float16* vm = vm_slice + blk * 2 * W * 32;
-    bd.vs_lo = load_u2(vm + W * 32 + wv_grp * 32 + 4 * g);
-    bd.vs_hi = load_u2(vm + W * 32 + wv_grp * 32 + 16 + 4 * g);
+    const _Float16* vm = vm_slice + blk * 2 * Wg * 32;
+    bd.vs_lo = load_u2(vm + Wg * 32 + wv_grp * 32 + 4 * g);
+    bd.vs_hi = load_u2(vm + Wg * 32 + wv_grp * 32 + 16 + 4 * g);
     // rows 0..W-1 of the value metadata are the zero-points of groups 0..W-1, rows W..2W-1 the scales
     bd.zs_lo = load_u2(vm + zrow * 32 + 4 * g);
     bd.zs_hi = load_u2(vm + zrow * 32 + 16 + 4 * g);
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   Frag pz[W], ps[W];
   auto prepass_load = [&](int jj) {
     const int bi = jj + 4 * n16;
-    const _Float16* km = km_slice + (blk0 + (bi < nb ? bi : jj)) * 2 * D;
+    const _Float16* km = km_slice + ((blk0 + (bi < nb ? bi : jj)) >> gshift) * 2 * D;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       pz[w].v = load_u4(km + 32 * w + 8 * g);
@@ -561,7 +563,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
     const bool keep = PACK == 2 ? (g < 2) : true;
     if (keep) {
-      if (n16 < 2 * W) sm.u.comb.zs[wave][r][n16] = zsv;
+      if (n16 < 2 * Wg) sm.u.comb.zs[wave][r][n16] = zsv;
 #pragma unroll
       for (int ct = 0; ct < CPL; ++ct) sm.u.comb.o[wave][r][CPL * n16 + ct] = ov[ct];
     }
@@ -575,12 +577,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) M = fmaxf(M, sm.u.comb.m[w4][r]);
     float lsum = 0.0f, o = 0.0f;
-    const int gv = c / 32;
+    const int gv = c >> (5 + gshift);
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
       const float e4 = __builtin_amdgcn_exp2f(sm.u.comb.m[w4][r] - M);
       lsum += e4 * sm.u.comb.l[w4][r];
-      o += e4 * (-0.5f * sm.u.comb.o[w4][r][c] + sm.u.comb.zs[w4][r][gv] + hV * sm.u.comb.zs[w4][r][W + gv]);
+      o += e4 * (-0.5f * sm.u.comb.o[w4][r][c] + sm.u.comb.zs[w4][r][gv] + hV * sm.u.comb.zs[w4][r][Wg + gv]);
     }
     const int64_t row = row0 + r;
     a.part_acc[(row * S + split) * D + c] = o;

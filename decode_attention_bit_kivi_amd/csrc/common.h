@@ -7,7 +7,7 @@
 
 namespace specache {
 
-constexpr int kGroup = 32;        // quantization group (tokens for keys, channels for values)
+constexpr int kGroup = 32;        // code block: 32 tokens (the smaller quantization group)
 constexpr int kMaxRows = 16;      // G * T query rows per KV head handled by one workgroup
 constexpr int kMaxTail = 64;
 // The runtime only accepts a compute-unit mask that leaves at least one unit on
@@ -19,6 +19,7 @@ constexpr int64_t kMaxAttnSeqLen = int64_t(4096) * 1024;  // 1024 splits of at m
 struct Dims {
   int B, Hq, Hkv, D, bits, G, W;
   int vbits;         // bits of the value codes (bits: of the key codes)
+  int group;         // quantization group: 32 or 64 (key tokens, value channels)
   int64_t N, nblk;   // positions and 32-position blocks per slice (the cache's current length)
   int64_t Ns;        // positions per slice the cache buffers are laid out for (>= N)
   int64_t slices() const { return (int64_t)B * Hkv; }
@@ -147,6 +148,7 @@ struct AttnArgs {
   const uint32_t* v_codes;
   const _Float16* v_meta;
   int64_t seq_stride;  // positions per slice the low-bit cache is laid out for
+  int group;           // quantization group (32 or 64)
   const int32_t* idx;
   int k;
   const _Float16* k_sel;

@@ -32,7 +32,7 @@ template <int D, int BITS, int PACK>
 __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restrict__ q16, int T, int rank_row,
                                                        const uint32_t* __restrict__ k_codes,
                                                        const _Float16* __restrict__ k_meta, int64_t N, int64_t Ns,
-                                                       int G,
+                                                       int gshift, int G,
                                                        int Hkv, float sm_scale, int64_t L, int S,
                                                        float* __restrict__ logits, float* __restrict__ part_m,
                                                        float* __restrict__ part_l, uint32_t* __restrict__ hist) {
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
   const int64_t slice = blockIdx.y;
   const int64_t b = slice / Hkv, h = slice % Hkv;
   const int Hq = Hkv * G;
-  const int64_t nblk_s = Ns / 32;  // the cache's layout stride in blocks
+  const int64_t ngrp_s = Ns >> (5 + gshift);  // the cache's layout stride in key groups (32 << gshift)
   const int64_t p0 = (int64_t)split * L;
   const int64_t p1 = p0 + L < N ? p0 + L : N;
   const int nb = (int)((p1 - p0) / 32);
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int pl = 0; pl < BITS; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * BITS + pl) * W);
-    const _Float16* kms = k_meta + ((slice * nblk_s + blk) * 2 + 1) * D;
+    const _Float16* kms = k_meta + ((slice * ngrp_s + (blk >> gshift)) * 2 + 1) * D;
 #pragma unroll
     for (int w = 0; w < W; ++w) bd.ks[w] = load_u4(kms + 32 * w + 8 * g);
     return bd;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
     Frag az[W], as[W];
     if (prepass) {
       const int bi = jj + 4 * n16;
-      const _Float16* km = k_meta + (slice * nblk_s + blk0 + (bi < nb ? bi : jj)) * 2 * D;
+      const _Float16* km = k_meta + (slice * ngrp_s + ((blk0 + (bi < nb ? bi : jj)) >> gshift)) * 2 * D;
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         az[w].v = load_u4(km + 32 * w + 8 * g);
@@ -213,10 +213,10 @@ void launch_score_t(const Dims& d, const ScorePlan& plan, const _Float16* q16, i
                     float* part_l, uint32_t* hist, hipStream_t s) {
   const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
   if (d.G <= 8)
-    score_kernel<D, BITS, 2><<<grid, 256, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.Ns, d.G, d.Hkv,
+    score_kernel<D, BITS, 2><<<grid, 256, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.Ns, d.group == 64 ? 1 : 0, d.G, d.Hkv,
                                                   sm_scale, plan.L, plan.S, logits, part_m, part_l, hist);
   else
-    score_kernel<D, BITS, 1><<<grid, 256, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.Ns, d.G, d.Hkv,
+    score_kernel<D, BITS, 1><<<grid, 256, 0, s>>>(q16, n_tokens, rank_row, k_codes, k_meta, d.N, d.Ns, d.group == 64 ? 1 : 0, d.G, d.Hkv,
                                                   sm_scale, plan.L, plan.S, logits, part_m, part_l, hist);
 }
 

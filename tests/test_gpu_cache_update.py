@@ -37,8 +37,8 @@ def _np(t):
 def _codes(cache, N):
     """Codes and metadata of positions [0, N) of a (possibly larger) cache."""
     kc, kz, ks = unpack_keys(_np(cache.k_codes), _np(cache.k_meta), cache.bits)
-    vc, vz, vs = unpack_values(_np(cache.v_codes), _np(cache.v_meta), cache.bits)
-    nb = N // 32
+    vc, vz, vs = unpack_values(_np(cache.v_codes), _np(cache.v_meta), cache.v_bits or cache.bits)
+    nb = N // cache.group
     return (kc[:, :, :N], kz[:, :, :nb], ks[:, :, :nb], vc[:, :, :N], vz[:, :, :N], vs[:, :, :N])
 
 
@@ -75,25 +75,25 @@ def test_cache_with_spare_capacity_gives_the_same_results():
     assert torch.equal(f_t.view(torch.int16), f_r.view(torch.int16)) and torch.equal(n_t, n_r)
 
 
-@pytest.mark.parametrize("bits", [1, 2])
-def test_append_equals_quantizing_the_whole_sequence(bits):
-    cfg = get_config("llama8k").with_(seq_len=2048 + 96, bits=bits, seed=5)
+@pytest.mark.parametrize("bits,group", [(1, 32), (2, 32), (1, 64)])
+def test_append_equals_quantizing_the_whole_sequence(bits, group):
+    cfg = get_config("llama8k").with_(seq_len=2048 + 3 * group, bits=bits, seed=5)
     K, V, Q, _, _, _ = generate_all(cfg)
     N0, cap = 2048, 4096
     cache = quantize_pack(_dev(_with_room(K[:, :, :N0], cap)), _dev(_with_room(V[:, :, :N0], cap)), bits,
-                          seq_len=N0)
-    quantize_append(cache, _dev(K[:, :, N0:N0 + 64]), _dev(V[:, :, N0:N0 + 64]))
-    quantize_append(cache, _dev(K[:, :, N0 + 64:]), _dev(V[:, :, N0 + 64:]))
+                          seq_len=N0, group=group)
+    quantize_append(cache, _dev(K[:, :, N0:N0 + 2 * group]), _dev(V[:, :, N0:N0 + 2 * group]))
+    quantize_append(cache, _dev(K[:, :, N0 + 2 * group:]), _dev(V[:, :, N0 + 2 * group:]))
     torch.cuda.synchronize()
     N = cfg.seq_len
     assert cache.seq_len == N
-    kc, kz, ks = oracle.quantize_keys(K, bits)
-    vc, vz, vs = oracle.quantize_values(V, bits)
+    kc, kz, ks = oracle.quantize_keys(K, bits, group)
+    vc, vz, vs = oracle.quantize_values(V, bits, group)
     got = _codes(cache, N)
     for g, w in zip(got, (kc, kz, ks, vc, vz, vs)):
         assert np.array_equal(g.view(np.uint8) if g.dtype != np.float16 else g.view(np.uint16),
                               w.view(np.uint8) if w.dtype != np.float16 else w.view(np.uint16))
-    whole = quantize_pack(_dev(K), _dev(V), bits)
+    whole = quantize_pack(_dev(K), _dev(V), bits, group=group)
     q = _dev(Q)
     o_a = decode_attn(q, cache)
     o_w = decode_attn(q, whole)

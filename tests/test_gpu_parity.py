@@ -104,6 +104,40 @@ def test_quantize_bit_exact(gpu, name, over):
     _assert_quantize_exact(cache, ref, cfg.bits)
 
 
+@pytest.mark.parametrize("bits,D", [(1, 128), (2, 128), (1, 64)])
+def test_group_64(gpu, bits, D):
+    """Quantization groups of 64 (keys: 64 tokens per channel, values: 64 channels per
+    token): codes and metadata bit-exact, ranking and attention against the oracle."""
+    cfg = get_config("llama8k").with_(bits=bits, head_dim=D, seq_len=4096 + 64, seed=8)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), bits, group=64)
+    kc, kz, ks = oracle.quantize_keys(K, bits, 64)
+    vc, vz, vs = oracle.quantize_values(V, bits, 64)
+    gk, gkz, gks = unpack_keys(_np(cache.k_codes), _np(cache.k_meta), bits)
+    gv, gvz, gvs = unpack_values(_np(cache.v_codes), _np(cache.v_meta), bits)
+    assert np.array_equal(gk, kc) and np.array_equal(gv, vc)
+    for got, want in ((gkz, kz), (gks, ks), (gvz, vz), (gvs, vs)):
+        assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    kh = oracle.dequantize_keys(kc, kz, ks, 64)
+    vh = oracle.dequantize_values(vc, vz, vs, 64)
+    rng = np.random.default_rng(4)
+    idx = _random_idx(rng, cfg.batch, cfg.n_kv_heads, cfg.seq_len, cfg.top_k)
+    sk, sv = oracle.gather_rows(K, V, idx)
+    rk = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    sel = score_topk(_dev(Q), cache, cfg.top_k, rank_key_out=rk)
+    o = decode_attn(_dev(Q), cache, _dev(idx), _dev(sk), _dev(sv))
+    of, nxt = decode_step(_dev(Q), cache, cfg.top_k, idx=_dev(idx), k_sel=_dev(sk), v_sel=_dev(sv))
+    torch.cuda.synchronize()
+    r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
+    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    slices = [(0, h) for h in range(cfg.n_kv_heads)]
+    _assert_topk(_np(sel), r_ref, cfg.top_k, slices)
+    _assert_topk(_np(nxt), r_ref, cfg.top_k, slices)
+    ref = oracle.mixed_attention(Q, kh, vh, idx, sk, sv, sm_scale=cfg.sm_scale)
+    assert _attn_err(_np(o), ref) <= ATTN_TOL
+    assert torch.equal(of.view(torch.int16), o.view(torch.int16))
+
+
 @pytest.mark.parametrize("kbits,vbits", [(2, 1), (1, 2)])
 def test_mixed_key_value_bits(gpu, kbits, vbits):
     """Keys and values with different code widths: codes bit-exact, attention and the fused

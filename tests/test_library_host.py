@@ -57,7 +57,8 @@ def _shape(**kw):
     (dict(bits=3), _lib.SPECACHE_ERR_INVALID),
     (dict(n_q_heads=7), _lib.SPECACHE_ERR_INVALID),           # not a multiple of Hkv
     (dict(head_dim=96), _lib.SPECACHE_ERR_UNSUPPORTED),
-    (dict(group=64), _lib.SPECACHE_ERR_UNSUPPORTED),
+    (dict(group=16), _lib.SPECACHE_ERR_UNSUPPORTED),
+    (dict(group=64, seq_len=1056), _lib.SPECACHE_ERR_INVALID),  # not whole 64-token groups
     (dict(batch=0), _lib.SPECACHE_ERR_INVALID),
     (dict(n_q_heads=2 * 17), _lib.SPECACHE_ERR_UNSUPPORTED),  # G = 17 > 16
 ])
@@ -176,6 +177,19 @@ def test_capacity_sizes_the_buffers_and_bounds_append_and_offload(lib):
     assert off(2, 4095) == _lib.SPECACHE_ERR_INVALID
     assert off(1, -1) == _lib.SPECACHE_ERR_INVALID
     assert off(0, 0) == _lib.SPECACHE_OK
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_group_sizes_the_metadata(lib, group):
+    s = _shape(group=group, batch=2, seq_len=2048)
+    out = [ctypes.c_size_t() for _ in range(4)]
+    lib.specache_lowbit_bytes(ctypes.byref(s), *[ctypes.byref(o) for o in out])
+    shapes = lowbit_sizes(2, 2, 2048, 128, 1, group=group)
+    assert [o.value for o in out] == [4 * np.prod(shapes[0]), 2 * np.prod(shapes[1]),
+                                      4 * np.prod(shapes[2]), 2 * np.prod(shapes[3])]
+    # metadata: 2 float16 per key group per channel, 2 per value group per token
+    assert out[1].value == 2 * 2 * (2048 // group) * 2 * 128 * 2
+    assert out[3].value == 2 * 2 * 2048 * 2 * (128 // group) * 2
 
 
 def test_mixed_bit_widths_size_the_value_planes(lib):

@@ -142,22 +142,38 @@ def test_codes_are_round_half_up_of_exact_ratio(bits, direction):
     assert off_by_rounding <= 0.01 * 2 * len(groups)
 
 
-def test_group_directions():
+@pytest.mark.parametrize("group", [32, 64])
+def test_group_directions(group):
     """SemKV §2.1: keys are grouped per channel along tokens, values per token
-    along channels.  Changing one element moves only its own group's metadata."""
+    along channels (SpeCache §4: groups of 32 or 64).  Changing one element moves
+    only its own group's metadata."""
     rng = np.random.default_rng(3)
-    x = rng.standard_normal((64, 64)).astype(np.float16)
-    _, zk, sk = oracle.quantize_keys(x, 2)
-    _, zv, sv = oracle.quantize_values(x, 2)
+    x = rng.standard_normal((128, 128)).astype(np.float16)
+    _, zk, sk = oracle.quantize_keys(x, 2, group)
+    _, zv, sv = oracle.quantize_values(x, 2, group)
+    assert sk.shape == (128 // group, 128) and sv.shape == (128, 128 // group)
     y = x.copy()
-    y[37, 5] = np.float16(50.0)                 # new maximum of its groups
-    _, zk2, sk2 = oracle.quantize_keys(y, 2)
-    _, zv2, sv2 = oracle.quantize_values(y, 2)
+    y[77, 40] = np.float16(50.0)                # new maximum of its groups
+    _, zk2, sk2 = oracle.quantize_keys(y, 2, group)
+    _, zv2, sv2 = oracle.quantize_values(y, 2, group)
     changed_k = np.argwhere(sk2 != sk)
     changed_v = np.argwhere(sv2 != sv)
-    assert changed_k.tolist() == [[37 // 32, 5]]
-    assert changed_v.tolist() == [[37, 5 // 32]]
+    assert changed_k.tolist() == [[77 // group, 40]]
+    assert changed_v.tolist() == [[77, 40 // group]]
     assert np.array_equal(zk2, zk) and np.array_equal(zv2, zv)
+
+
+def test_group_64_is_the_min_max_of_its_two_halves():
+    """A 64-group's 1-bit zero-point and scale are those of the min and max over both of its
+    32-element halves (SpeCache §3's formula applied to the larger group)."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((64, 8)).astype(np.float16)
+    _, z64, s64 = oracle.quantize_keys(x, 1, 64)
+    mn = np.minimum(x[:32].min(0), x[32:].min(0)).astype(np.float32)
+    mx = np.maximum(x[:32].max(0), x[32:].max(0)).astype(np.float32)
+    z, s = oracle.zero_point_scale(mn, mx, 1)
+    assert np.array_equal(z64[0].view(np.uint16), z.view(np.uint16))
+    assert np.array_equal(s64[0].view(np.uint16), s.view(np.uint16))
 
 
 def test_constant_group_and_signed_zero():
