@@ -300,8 +300,10 @@ def main():
             step(st, i, reuse)
         torch.cuda.synchronize()
         t_start.record(comp)
+        h0 = time.perf_counter()
         for i in range(args.steps):
             step(st, args.warmup + i, reuse)
+        host_enqueue_us.append((time.perf_counter() - h0) / args.steps * 1e6)  # host time to enqueue a step
         comp.wait_stream(side)
         t_end.record(comp)
         torch.cuda.synchronize()
@@ -318,6 +320,7 @@ def main():
         g_us = np.array([e["g0"].elapsed_time(e["g1"]) for e in evs]) * 1e3
         return ms, d_us, g_us, fetched
 
+    host_enqueue_us = []
     modes = ["reuse", "full"] if args.reuse else ["full"]
     runs = {}
     for m in modes:
@@ -423,6 +426,7 @@ def main():
             "step_compute_only_four_call": unfused_us,
             "exposed_gather": max(0.0, ms_step * 1e3 - fused_us),
             "quantize_pack_prefill": quant_us,
+            "host_enqueue_per_step": host_enqueue_us[0],
         },
         "bandwidth_GBs": {
             "decode_step_in_pipeline": achieved,
