@@ -77,14 +77,28 @@ __device__ __forceinline__ Words<NW> load_words(const uint32_t* p) {
 __device__ __forceinline__ uint2 load_u2(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ uint4 load_u4(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Reductions over the four k-groups of a wave (lanes l, l^16, l^32, l^48).
+// Reductions over the four k-groups of a wave (lanes l, l^16, l^32, l^48) on gfx950's
+// cross-row swaps, with no LDS round trip.  Swapping a register with a copy of itself leaves
+// the values of lanes l and l^16 (permlane16) or l and l^32 (permlane32) in the two registers
+// (in a lane-dependent order), so a symmetric operation of the pair reduces over the partners.
+// Written as inline assembly: the compiler's builtins for these swaps fold the second result
+// away when it is combined with the first.  The wait states around the swap are those the
+// compiler itself places next to it.
+#define SPECACHE_SWAP_OP(SWAP, OP) "s_nop 1\n\t" SWAP " %0, %1\n\ts_nop 1\n\t" OP " %0, %0, %1"
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  float y = x;
+  asm(SPECACHE_SWAP_OP("v_permlane16_swap_b32", "v_max_f32") : "+v"(x), "+v"(y));
+  y = x;
+  asm(SPECACHE_SWAP_OP("v_permlane32_swap_b32", "v_max_f32") : "+v"(x), "+v"(y));
+  return x;
 }
 __device__ __forceinline__ float sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  float y = x;
+  asm(SPECACHE_SWAP_OP("v_permlane16_swap_b32", "v_add_f32") : "+v"(x), "+v"(y));
+  y = x;
+  asm(SPECACHE_SWAP_OP("v_permlane32_swap_b32", "v_add_f32") : "+v"(x), "+v"(y));
+  return x;
 }
+#undef SPECACHE_SWAP_OP
 
 }  // namespace specache
