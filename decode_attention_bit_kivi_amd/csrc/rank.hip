@@ -20,7 +20,12 @@
 //                whose set bits one prefix sum turns into the ascending output.
 //                A bin too large for LDS falls back to the radix select over
 //                all keys (three sweeps).  Every sweep reads 4096 consecutive
-//                values per step, a float4 per thread.
+//                values per step, a float4 per thread.  A slice of at most
+//                32768 positions is read once and kept in registers (32 keys
+//                a thread) for every step, and a bin of at most 64 keys is
+//                resolved by one wave counting, without the radix passes.
+//                The bin's value interval comes from a 64-way search by one
+//                wave.
 //   The exact selection compares order-preserving 32-bit integer keys of the
 //   float r.
 #include "common.h"
@@ -58,24 +63,28 @@ __device__ __forceinline__ uint32_t coarse_bin(float r, float r_lo) {
   return (uint32_t)x;
 }
 
+// Inclusive prefix sum over a wave with DPP lane moves (no LDS round trips): shifts by 1, 2, 4
+// and 8 within each row of 16 lanes, then the last lane of row 0 (of rows 0-1) added to rows 1
+// and 3 (2 and 3).  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return (uint32_t)v;
+}
+
 // Exclusive prefix sum over the 1024-thread workgroup; returns the exclusive value, writes the total.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) scratch[wv] = x;
   __syncthreads();
   if (wv == 0) {
-    uint32_t s = lane < kSelWaves ? scratch[lane] : 0u;
-#pragma unroll
-    for (int off = 1; off < kSelWaves; off <<= 1) {
-      const uint32_t y = __shfl_up(s, off);
-      if (lane >= off) s += y;
-    }
+    const uint32_t s = wave_inclusive_scan(lane < kSelWaves ? scratch[lane] : 0u);
     if (lane < kSelWaves) scratch[kSelWaves + lane] = s;  // inclusive wave prefix
   }
   __syncthreads();
@@ -231,8 +240,8 @@ __device__ __forceinline__ int64_t sweep_pos(int64_t base, int i) {
 
 // The digit of hist[0, nbins) holding the krem-th largest element, counted from the top, and the
 // number of elements in the digits above it.
-__device__ __forceinline__ void pick_digit(SelectSmem& sm, int nbins, uint32_t krem, uint32_t& digit,
-                                           uint32_t& above) {
+template <typename Smem>
+__device__ __forceinline__ void pick_digit(Smem& sm, int nbins, uint32_t krem, uint32_t& digit, uint32_t& above) {
   const int t = threadIdx.x;
   if (t == 0) {
     sm.sel_digit = 0u;
@@ -261,9 +270,9 @@ __device__ __forceinline__ void pick_digit(SelectSmem& sm, int nbins, uint32_t k
 // (key thr, number of keys equal to thr to take, number of keys equal to thr).
 // count(shift, nbins, prefix, mask) adds every key u with (u & mask) == prefix to
 // sm.hist[(u >> shift) & (nbins - 1)].
-template <typename Count>
-__device__ __forceinline__ void radix_select(SelectSmem& sm, uint32_t krem, Count count, uint32_t& thr,
-                                             uint32_t& need_eq, uint32_t& n_eq) {
+template <typename Smem, typename Count>
+__device__ __forceinline__ void radix_select(Smem& sm, uint32_t krem, Count count, uint32_t& thr, uint32_t& need_eq,
+                                             uint32_t& n_eq) {
   const int t = threadIdx.x;
   uint32_t prefix = 0u, mask = 0u;
   for (int pass = 0; pass < 3; ++pass) {  // digits: bits 31..21, 20..10, 9..0
@@ -284,13 +293,36 @@ __device__ __forceinline__ void radix_select(SelectSmem& sm, uint32_t krem, Coun
   need_eq = krem;
 }
 
-// Smallest order key of a non-NaN value whose coarse bin is >= b, for b < kBins.  Between the
-// keys of -inf and +inf the bins are non-decreasing in the key, and bin(+inf) = kBins - 1 >= b.
-__device__ uint32_t first_key_of_bin(uint32_t b, float r_lo) {
-  uint32_t lo = 0x007fffffu, hi = 0xff800000u;  // order keys of -inf and +inf
+// Smallest order key of a non-NaN value whose coarse bin is >= b, for b < kBins, found by one
+// wave.  Between the keys of -inf and +inf the bins are non-decreasing in the key, and bin(+inf) =
+// kBins - 1 >= b.  Each round probes 64 evenly spaced keys of [lo, hi] (the answer is in it, and
+// the condition holds at hi): the answer lies at or below the first probe where it holds and
+// above the probe before.
+__device__ uint32_t first_key_of_bin_wave(uint32_t b, float r_lo) {
+  const int lane = threadIdx.x & 63;
+  uint32_t lo = 0x007fffffu, hi = 0xff800000u;
+  if (b == 0u) return lo;  // every value is in a bin >= 0
+  {
+    // the bin starts at about r_lo + b / kBinScale: probe the 64 keys around that value first
+    const uint32_t c = order_key(r_lo + (float)b / kBinScale);
+    const uint32_t x = c - 32u + (uint32_t)lane;
+    const uint64_t m = __ballot(coarse_bin(key_value(x), r_lo) >= b);
+    if (m != 0u && !(m & 1u)) return c - 32u + (uint32_t)__builtin_ctzll(m);  // the answer is inside
+  }
   while (lo < hi) {
-    const uint32_t mid = lo + (hi - lo) / 2u;
-    if (coarse_bin(key_value(mid), r_lo) >= b) hi = mid; else lo = mid + 1u;
+    const uint64_t step = ((uint64_t)(hi - lo) + 63u) / 64u;
+    uint64_t x = (uint64_t)lo + (uint64_t)lane * step;
+    if (x > hi) x = hi;
+    const uint64_t m = __ballot(coarse_bin(key_value((uint32_t)x), r_lo) >= b);
+    if (m == 0u) {  // every probe below the answer (the last one is then below hi)
+      lo = (uint32_t)(lo + 63u * step) + 1u;
+      continue;
+    }
+    const int j = __builtin_ctzll(m);
+    if (j == 0) break;  // the answer is lo
+    const uint64_t xj = (uint64_t)lo + (uint64_t)j * step;
+    hi = (uint32_t)(xj < hi ? xj : hi);
+    lo = (uint32_t)((uint64_t)lo + (uint64_t)(j - 1) * step) + 1u;
   }
   return lo;
 }
@@ -314,8 +346,13 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* _
   // the threshold bin as an interval of values [lo, hi) (the top bin runs to +inf), found by two
   // binary searches over the keys.  The ranks hold no -0 and no NaN, so comparing the floats
   // orders them as their keys do.
-  if (t == 0) bin_vals[0] = key_value(first_key_of_bin(bin, r_lo));
-  if (t == 64) bin_vals[1] = bin + 1 < (uint32_t)kBins ? key_value(first_key_of_bin(bin + 1, r_lo)) : INFINITY;
+  if (t < 64) {
+    const uint32_t key = first_key_of_bin_wave(bin, r_lo);
+    if (t == 0) bin_vals[0] = key_value(key);
+  } else if (t < 128) {
+    const float vb = bin + 1 < (uint32_t)kBins ? key_value(first_key_of_bin_wave(bin + 1, r_lo)) : INFINITY;
+    if (t == 64) bin_vals[1] = vb;
+  }
   __syncthreads();
   const float va = bin_vals[0], vb = bin_vals[1];
   const bool top_open = bin + 1 >= (uint32_t)kBins;
@@ -331,12 +368,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* _
       if (!__any(mine != 0u)) return;
       // slots: one prefix sum over the wave and one LDS atomic per wave
       const uint32_t n = __popc(mine);
-      uint32_t incl = n;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
+      const uint32_t incl = wave_inclusive_scan(n);
       uint32_t base_slot = 0u;
       if (lane == 63) base_slot = atomicAdd(&sm.n_cand, incl);
       base_slot = __shfl(base_slot, 63);
@@ -434,6 +466,209 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* _
   }
 }
 
+// ---- rank_select for slices of at most kResidentN positions: the keys stay in registers
+// (one coalesced read), the threshold bin's interval comes from two one-wave searches, a bin of
+// at most 64 keys is resolved by one wave counting, and the compaction builds one bitmap word
+// per thread from mark bytes.
+constexpr int64_t kResidentN = (int64_t)kSelThreads * 4 * kSweepU;
+constexpr int kResidentWords = (int)(kResidentN / 32);
+
+static_assert(kBins == 2 * kSelThreads, "two histogram bins per thread");
+static_assert(kResidentWords == kSelThreads, "one bitmap word per thread");
+static_assert(kSweepU == 8, "eight mark bytes per bitmap word");
+
+struct ResidentSmem {
+  uint32_t hist[kBins];
+  uint32_t scan_scratch[2 * kSelWaves];
+  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t res[4];  // small-bin selection: thr, need_eq, n_eq, found
+  float bin_vals[2];
+  // marks of positions 4n .. 4n + 3: bit e selected (above the threshold, or equal to it when all
+  // equal keys are taken), bit 4 + e equal to the threshold otherwise
+  alignas(16) uint8_t marks[kResidentN / 4];
+  uint32_t cand[kCand];
+};
+
+__global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const float* __restrict__ rkey,
+                                                                           const uint32_t* __restrict__ ghist,
+                                                                           int64_t N, int k, float r_lo,
+                                                                           int32_t* __restrict__ idx_out) {
+  __shared__ ResidentSmem sm;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t slice = blockIdx.x;
+  const float* ky = rkey + slice * N;
+  const uint32_t* gh = ghist + slice * kBins;
+  // the histogram's loads first and then the keys', all unconditional (clamped addresses), so
+  // that waiting for the histogram leaves the keys in flight; the empty statement with a memory
+  // clobber keeps every load above the first barrier
+  const uint32_t h0 = gh[t], h1 = gh[t + kSelThreads];
+  float4 f[kSweepU];
+#pragma unroll
+  for (int u = 0; u < kSweepU; ++u) {
+    const int64_t p = 4 * ((int64_t)t + u * kSelThreads);
+    f[u] = *reinterpret_cast<const float4*>(ky + (p < N ? p : 0));
+  }
+  asm volatile("" ::: "memory");
+  sm.hist[t] = h0;
+  sm.hist[t + kSelThreads] = h1;
+  // v[4u + e]: position 4 * (t + u * kSelThreads) + e, -inf past N (N is a multiple of 32)
+  float v[4 * kSweepU];
+#pragma unroll
+  for (int u = 0; u < kSweepU; ++u) {
+    const bool in = 4 * ((int64_t)t + u * kSelThreads) < N;
+    v[4 * u] = in ? f[u].x : -INFINITY;
+    v[4 * u + 1] = in ? f[u].y : -INFINITY;
+    v[4 * u + 2] = in ? f[u].z : -INFINITY;
+    v[4 * u + 3] = in ? f[u].w : -INFINITY;
+  }
+  // N <= kResidentN: positions fit 32 bits; a float4 is wholly in range or wholly past N
+  auto in_range = [&](int u) { return 4 * (t + u * kSelThreads) < (int)N; };
+  if (t == 0) {
+    sm.n_cand = 0u;
+    sm.res[3] = 0u;
+  }
+  __syncthreads();
+
+  uint32_t bin, above;
+  pick_digit(sm, kBins, (uint32_t)k, bin, above);
+  const uint32_t in_bin = sm.hist[bin];
+  if (wave == 0) {
+    const uint32_t key = first_key_of_bin_wave(bin, r_lo);
+    if (lane == 0) sm.bin_vals[0] = key_value(key);
+  } else if (wave == 1) {
+    const float vb = bin + 1 < (uint32_t)kBins ? key_value(first_key_of_bin_wave(bin + 1, r_lo)) : INFINITY;
+    if (lane == 0) sm.bin_vals[1] = vb;
+  }
+  __syncthreads();
+  const float va = sm.bin_vals[0], vb = sm.bin_vals[1];
+  const bool top_open = bin + 1 >= (uint32_t)kBins;
+
+  uint32_t thr, need_eq, n_thr;
+  if (in_bin <= (uint32_t)kCand) {
+    // the threshold bin's keys into LDS (any order): one prefix sum and one LDS atomic per wave
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int u = 0; u < kSweepU; ++u)
+      if (in_range(u))
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = v[4 * u + e];
+          mine |= (x >= va && (top_open || x < vb)) ? (1u << (4 * u + e)) : 0u;
+        }
+    if (__any(mine != 0u)) {
+      const uint32_t n = __popc(mine);
+      const uint32_t incl = wave_inclusive_scan(n);
+      uint32_t base_slot = 0u;
+      if (lane == 63) base_slot = atomicAdd(&sm.n_cand, incl);
+      base_slot = __shfl(base_slot, 63);
+      uint32_t slot = base_slot + incl - n;
+#pragma unroll
+      for (int i = 0; i < 4 * kSweepU; ++i)
+        if ((mine >> i) & 1u) {
+          if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[i]);
+          ++slot;
+        }
+    }
+    __syncthreads();
+    const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
+    const uint32_t krem = (uint32_t)k - above;
+    if (nc <= 64u) {
+      if (wave == 0) {
+        // lane j: how many of the bin's keys are above / equal to key j; key j is the threshold
+        // when the krem-th largest falls among its equals
+        const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
+        uint32_t gt = 0u, eq = 0u;
+        for (uint32_t j = 0; j < nc; ++j) {
+          const uint32_t o = sm.cand[j];
+          gt += o > c ? 1u : 0u;
+          eq += o == c ? 1u : 0u;
+        }
+        const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
+        if (m != 0u && lane == __builtin_ctzll(m)) {
+          sm.res[0] = c;
+          sm.res[1] = krem - gt;
+          sm.res[2] = eq;
+          sm.res[3] = 1u;
+        }
+      }
+      __syncthreads();
+    }
+    if (sm.res[3]) {
+      thr = sm.res[0];
+      need_eq = sm.res[1];
+      n_thr = sm.res[2];
+    } else {
+      radix_select(sm, krem,
+                   [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+                     for (uint32_t i = t; i < nc; i += kSelThreads) {
+                       const uint32_t u = sm.cand[i];
+                       if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                     }
+                   },
+                   thr, need_eq, n_thr);
+    }
+  } else {
+    radix_select(sm, (uint32_t)k,
+                 [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+#pragma unroll
+                   for (int i = 0; i < 4 * kSweepU; ++i) {
+                     const uint32_t u = order_key(v[i]);
+                     if (in_range(i >> 2) && (u & mask) == prefix)
+                       atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                   }
+                 },
+                 thr, need_eq, n_thr);
+  }
+
+  // Every key above thr and the first need_eq equal to it, in position order: a mark byte per
+  // float4, then thread t gathers the eight bytes of positions 32t .. 32t + 31 into two words
+  // (selected, equal) and one prefix sum over the words orders the output.
+  const float vthr = key_value(thr);
+  const bool all_eq = need_eq == n_thr;  // every key equal to thr is taken
+#pragma unroll
+  for (int u = 0; u < kSweepU; ++u) {
+    uint32_t mk = 0u;
+    if (in_range(u))
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = v[4 * u + e];
+        mk |= (x > vthr || (all_eq && x == vthr)) ? (1u << e) : 0u;
+        mk |= (!all_eq && x == vthr) ? (16u << e) : 0u;
+      }
+    sm.marks[t + u * kSelThreads] = (uint8_t)mk;
+  }
+  __syncthreads();
+  uint32_t m = 0u, e = 0u;
+  {
+    const uint2 b8 = *reinterpret_cast<const uint2*>(&sm.marks[8 * t]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t byte = ((j < 4 ? b8.x : b8.y) >> (8 * (j & 3))) & 0xffu;
+      m |= (byte & 15u) << (4 * j);
+      e |= (byte >> 4) << (4 * j);
+    }
+  }
+  uint32_t tot;
+  if (!all_eq) {
+    const uint32_t ne = __popc(e);
+    const uint32_t eq_before = block_exclusive_scan(ne, sm.scan_scratch, tot);
+    uint32_t eq_take = eq_before >= need_eq ? 0u : (need_eq - eq_before < ne ? need_eq - eq_before : ne);
+    while (eq_take > 0u) {  // the lowest equal positions first
+      const uint32_t low = e & (0u - e);
+      m |= low;
+      e ^= low;
+      --eq_take;
+    }
+  }
+  uint32_t out = block_exclusive_scan(__popc(m), sm.scan_scratch, tot);
+  while (m != 0u) {
+    const int b = __builtin_ctz(m);
+    m &= m - 1u;
+    if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(32 * t + b);
+    ++out;
+  }
+}
+
 template <int GM>
 void launch_keys(const Dims& d, int S, const float* logits, const float* part_m, const float* part_l, float r_lo,
                  float* keys, uint32_t* hist, hipStream_t s) {
@@ -453,7 +688,10 @@ hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const f
     launch_keys<8>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
   else
     launch_keys<16>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
-  rank_select_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out);
+  if (d.N <= kResidentN)
+    rank_select_resident_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out);
+  else
+    rank_select_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out);
   return hipGetLastError();
 }
 
