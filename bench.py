@@ -42,7 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_step_mistral32k_traffic.json")
-STEP_SOURCES = ("attention.hip", "rank.hip", "mfma_frag.h", "common.h")
+STEP_SOURCES = ("attention.hip", "rank.hip", "merge.h", "mfma_frag.h", "common.h")
 
 
 def step_sources_hash() -> str:

@@ -229,7 +229,7 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
                               static_cast<const uint32_t*>(cache->k_codes), static_cast<const _Float16*>(cache->k_meta),
                               sm_scale, logits, part_m, part_l, hist, s);
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
-  e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, hist, idx_out, s);
+  e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, hist, idx_out, nullptr, s);
   return hip_status(e);
 }
 
@@ -446,12 +446,11 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
   a.rank_l = reinterpret_cast<float*>(base + ws.rank_l);
   a.rank_hist = reinterpret_cast<uint32_t*>(base + ws.hist);
   float* keys = rank_key_out ? rank_key_out : reinterpret_cast<float*>(base + ws.keys);
-  // the ranking first: the prefetch of the next set waits on it, the merge does not
+  // the split merge runs inside the selection's launch, on the compute units it leaves idle
   if (launch_attn_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
-  if (launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys, a.rank_hist, idx_next_out, s) !=
-      hipSuccess)
-    return SPECACHE_ERR_HIP;
-  return hip_status(launch_attn_merge(d, plan, a, s));
+  const MergeJob merge{a.part_ml, a.part_acc, plan.S, (int64_t)d.B * d.Hq * n_tokens, a.out16};
+  return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys, a.rank_hist,
+                                       idx_next_out, &merge, s));
 }
 
 namespace {

@@ -27,6 +27,7 @@
 // Softmax maxima are kept per accumulator row and only rescaled when a new
 // logit exceeds the running maximum by more than 2^8 (probabilities up to 256
 // stay exact enough in float16 and cannot overflow).
+#include "merge.h"
 #include "mfma_frag.h"
 
 namespace specache {
@@ -34,7 +35,7 @@ namespace specache {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kEmpty = -1.0e30f;   // running max of a row that has seen nothing
+constexpr float kEmpty = kMergeEmpty;  // running max of a row that has seen nothing
 constexpr float kRescale = 8.0f;     // lazy-rescale threshold (log2 units)
 constexpr int kMaxBlocksPerSplit = 128;
 
@@ -600,63 +601,13 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   }
 }
 
-// One workgroup per query row: weights 2^(m_s - M) of the S split partials in
-// LDS, then each thread sums its channel over the splits with all loads in flight.
+// Four query rows per workgroup, one wave each.
 template <int D>
-__global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__ part_ml,
-                                                       const float* __restrict__ part_acc, int S,
-                                                       _Float16* __restrict__ out) {
-  constexpr int kMaxS = 1024;
-  __shared__ float wts[kMaxS];
-  __shared__ float red[D / 64];
-  __shared__ float Mrow, Lrow;
-  const int64_t row = blockIdx.x;
-  const int c = threadIdx.x;
-  const float* ml = part_ml + row * S * 2;
-  float M = kEmpty;
-  for (int s = c; s < S; s += D) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if ((c & 63) == 0) red[c >> 6] = M;
-  __syncthreads();
-  if (c == 0) {
-    float m = red[0];
-#pragma unroll
-    for (int i = 1; i < D / 64; ++i) m = fmaxf(m, red[i]);
-    Mrow = m;
-  }
-  __syncthreads();
-  M = Mrow;
-  float l = 0.0f;
-  for (int s = c; s < S; s += D) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    wts[s] = w;
-    l = fmaf(ml[2 * s + 1], w, l);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-  __syncthreads();
-  if ((c & 63) == 0) red[c >> 6] = l;
-  __syncthreads();
-  if (c == 0) {
-    float t = 0.0f;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) t += red[i];
-    Lrow = t;
-  }
-  __syncthreads();
-  const float* acc = part_acc + row * S * D + c;
-  float o = 0.0f;
-  int s = 0;
-  for (; s + 8 <= S; s += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = acc[(int64_t)(s + u) * D];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) o = fmaf(v[u], wts[s + u], o);
-  }
-  for (; s < S; ++s) o = fmaf(acc[(int64_t)s * D], wts[s], o);
-  out[row * D + c] = (_Float16)(o / Lrow);
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_ml,
+                                                         const float* __restrict__ part_acc, int S, int64_t rows,
+                                                         _Float16* __restrict__ out) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row < rows) merge_row_wave<D>(part_ml, part_acc, S, out, row);
 }
 
 template <int D, int KB, int VB, bool RANK>
@@ -703,11 +654,12 @@ hipError_t launch_attn16_split(const Dims& d, const AttnPlan& plan, const AttnAr
 }
 
 hipError_t launch_attn_merge(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
-  const unsigned rows = (unsigned)((int64_t)d.B * d.Hq * a.T);
+  const int64_t rows = (int64_t)d.B * d.Hq * a.T;
+  const unsigned blocks = (unsigned)ceil_div(rows, 4);
   if (d.D == 128)
-    attn_merge_kernel<128><<<rows, 128, 0, s>>>(a.part_ml, a.part_acc, plan.S, a.out16);
+    attn_merge_kernel<128><<<blocks, 256, 0, s>>>(a.part_ml, a.part_acc, plan.S, rows, a.out16);
   else
-    attn_merge_kernel<64><<<rows, 64, 0, s>>>(a.part_ml, a.part_acc, plan.S, a.out16);
+    attn_merge_kernel<64><<<blocks, 256, 0, s>>>(a.part_ml, a.part_acc, plan.S, rows, a.out16);
   return hipGetLastError();
 }
 

@@ -126,10 +126,21 @@ hipError_t launch_score(const Dims& d, const ScorePlan& plan, const _Float16* q1
                         int rank_row, const uint32_t* k_codes, const _Float16* k_meta, float sm_scale,
                         float* logits, float* part_m, float* part_l, uint32_t* hist, hipStream_t s);
 
+// The attention's split merge, run by extra workgroups of the selection launch (they use the
+// compute units the per-slice selection leaves idle).
+struct MergeJob {
+  const float* part_ml;   // [rows][S][2]
+  const float* part_acc;  // [rows][S][D]
+  int S;
+  int64_t rows;
+  _Float16* out16;        // [rows][D]
+};
+
 // part_m / part_l: [slices][G][S] per-split (max, sum 2^(x - max)) of the logits, log2 units.
+// merge: null, or the attention merge to run alongside the selection.
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
-                              hipStream_t s);
+                              const MergeJob* merge, hipStream_t s);
 
 // skip_negative: rows with a negative index are left untouched (resident-set reuse).
 hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,

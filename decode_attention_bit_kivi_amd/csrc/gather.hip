@@ -84,10 +84,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t* __restrict__
 // Resident-set reuse: row i of the new selection whose position is also in the previous
 // selection (at row j) is copied from the previous rows (device to device); the others are
 // marked for fetching: fetch_idx[i] = position, or -1 for a copied row.  A position outside
-// [0, N) is marked with N, so that the fetch writes a NaN row for it.  Grid: (row chunks of
-// kReuseRows, slices); the previous selection of the slice is searched in LDS.
-constexpr int kReuseRows = 64;
-constexpr int kPrevLds = 8192;
+// [0, N) is marked with N, so that the fetch writes a NaN row for it.  Grid: (chunks of 256 /
+// (D/8) rows, slices); one lane group per row, so each lane's work is one chain: index load,
+// search of the previous selection (staged in LDS when it has at most kPrevLds entries), copy.
+constexpr int kPrevLds = 4096;
 
 template <int D>
 __global__ __launch_bounds__(256) void reuse_kernel(const int32_t* __restrict__ idx, int k,
@@ -96,36 +96,35 @@ __global__ __launch_bounds__(256) void reuse_kernel(const int32_t* __restrict__ 
                                                     const uint4* __restrict__ v_prev_rows, uint4* __restrict__ k_sel,
                                                     uint4* __restrict__ v_sel, int32_t* __restrict__ fetch_idx) {
   constexpr int kLanesPerRow = D * 2 / 16;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
   __shared__ int32_t prev[kPrevLds];
   const int tid = threadIdx.x;
   const int64_t slice = blockIdx.y;
+  const int i = blockIdx.x * kRowsPerBlock + tid / kLanesPerRow;  // this lane group's entry
+  const int part = tid % kLanesPerRow;
+  const int32_t p = i < k ? idx[slice * k + i] : 0;  // in flight while the previous selection is staged
   const int32_t* ip = idx_prev + slice * k_prev;
   const bool in_lds = k_prev <= kPrevLds;
   if (in_lds)
-    for (int i = tid; i < k_prev; i += 256) prev[i] = ip[i];
+    for (int j = tid; j < k_prev; j += 256) prev[j] = ip[j];
   __syncthreads();
-  const int part = tid % kLanesPerRow;
-  const int i0 = blockIdx.x * kReuseRows;
-  for (int r = tid / kLanesPerRow; r < kReuseRows; r += 256 / kLanesPerRow) {
-    const int i = i0 + r;
-    if (i >= k) break;
-    const int32_t p = idx[slice * k + i];
-    int lo = 0, hi = k_prev;  // first entry of the previous selection >= p
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      const int32_t v = in_lds ? prev[mid] : ip[mid];
-      if (v < p) lo = mid + 1; else hi = mid;
-    }
-    const bool valid = p >= 0 && p < N;
-    const bool found = valid && lo < k_prev && (in_lds ? prev[lo] : ip[lo]) == p;
-    if (found) {
-      const int64_t src = (slice * k_prev + lo) * kLanesPerRow + part;
-      const int64_t dst = (slice * k + i) * kLanesPerRow + part;
-      k_sel[dst] = k_prev_rows[src];
-      v_sel[dst] = v_prev_rows[src];
-    }
-    if (part == 0) fetch_idx[slice * k + i] = found ? -1 : (valid ? p : (int32_t)N);
+  if (i >= k) return;
+  int lo = 0, hi = k_prev;  // first entry of the previous selection >= p
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int32_t v = in_lds ? prev[mid] : ip[mid];
+    if (v < p) lo = mid + 1; else hi = mid;
   }
+  const bool valid = p >= 0 && p < N;
+  const bool found = valid && lo < k_prev && (in_lds ? prev[lo] : ip[lo]) == p;
+  if (found) {
+    const int64_t src = (slice * k_prev + lo) * kLanesPerRow + part;
+    const int64_t dst = (slice * k + i) * kLanesPerRow + part;
+    const uint4 kr = k_prev_rows[src], vr = v_prev_rows[src];
+    k_sel[dst] = kr;
+    v_sel[dst] = vr;
+  }
+  if (part == 0) fetch_idx[slice * k + i] = found ? -1 : (valid ? p : (int32_t)N);
 }
 
 // The fetch of the rows a reuse pass left (index >= 0; negative = resident, untouched): each
@@ -218,7 +217,7 @@ hipError_t launch_reuse(const Dims& d, const int32_t* idx, int k, const int32_t*
                         const _Float16* k_prev_rows, const _Float16* v_prev_rows, _Float16* k_sel, _Float16* v_sel,
                         int32_t* fetch_idx, hipStream_t s) {
   if (d.slices() * k == 0) return hipSuccess;
-  const dim3 grid((unsigned)ceil_div(k, kReuseRows), (unsigned)d.slices());
+  const dim3 grid((unsigned)ceil_div(k, 256 / (d.D * 2 / 16)), (unsigned)d.slices());
   auto u4 = [](const _Float16* p) { return reinterpret_cast<const uint4*>(p); };
   auto w4 = [](_Float16* p) { return reinterpret_cast<uint4*>(p); };
   if (d.D == 128)

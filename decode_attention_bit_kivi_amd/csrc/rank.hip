@@ -28,7 +28,7 @@
 //                wave.
 //   The exact selection compares order-preserving 32-bit integer keys of the
 //   float r.
-#include "common.h"
+#include "merge.h"
 
 namespace specache {
 
@@ -327,9 +327,16 @@ __device__ uint32_t first_key_of_bin_wave(uint32_t b, float r_lo) {
   return lo;
 }
 
+template <int D>
 __global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* __restrict__ rkey,
                                                                   const uint32_t* __restrict__ ghist, int64_t N,
-                                                                  int k, float r_lo, int32_t* __restrict__ idx_out) {
+                                                                  int k, float r_lo, int32_t* __restrict__ idx_out,
+                                                                  unsigned n_sel, MergeJob mj) {
+  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
+    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
+    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
+    return;
+  }
   __shared__ SelectSmem sm;
   __shared__ float bin_vals[2];
   const int t = threadIdx.x, lane = t & 63;
@@ -489,10 +496,17 @@ struct ResidentSmem {
   uint32_t cand[kCand];
 };
 
+template <int D>
 __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const float* __restrict__ rkey,
                                                                            const uint32_t* __restrict__ ghist,
                                                                            int64_t N, int k, float r_lo,
-                                                                           int32_t* __restrict__ idx_out) {
+                                                                           int32_t* __restrict__ idx_out,
+                                                                           unsigned n_sel, MergeJob mj) {
+  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
+    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
+    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
+    return;
+  }
   __shared__ ResidentSmem sm;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t slice = blockIdx.x;
@@ -676,11 +690,22 @@ void launch_keys(const Dims& d, int S, const float* logits, const float* part_m,
   rank_keys_kernel<GM><<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, S, d.N, r_lo, keys, hist);
 }
 
+template <int D>
+void launch_select(const Dims& d, int k, float r_lo, const float* keys, const uint32_t* hist, int32_t* idx_out,
+                   const MergeJob& mj, hipStream_t s) {
+  const unsigned n_sel = (unsigned)d.slices();
+  const unsigned grid = n_sel + (unsigned)ceil_div(mj.rows, kSelWaves);
+  if (d.N <= kResidentN)
+    rank_select_resident_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel, mj);
+  else
+    rank_select_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel, mj);
+}
+
 }  // namespace
 
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
-                              hipStream_t s) {
+                              const MergeJob* merge, hipStream_t s) {
   const float r_lo = logf((float)d.G) - kBinSpan;  // the same value for both kernels
   if (d.G <= 4)
     launch_keys<4>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
@@ -688,10 +713,12 @@ hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const f
     launch_keys<8>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
   else
     launch_keys<16>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
-  if (d.N <= kResidentN)
-    rank_select_resident_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out);
+  const MergeJob none{nullptr, nullptr, 0, 0, nullptr};
+  const MergeJob& mj = merge ? *merge : none;
+  if (d.D == 64)
+    launch_select<64>(d, k, r_lo, keys, hist, idx_out, mj, s);
   else
-    rank_select_kernel<<<(unsigned)d.slices(), kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out);
+    launch_select<128>(d, k, r_lo, keys, hist, idx_out, mj, s);
   return hipGetLastError();
 }
 
