@@ -83,6 +83,9 @@ def parse():
                     help="fetch only the rows of the new top-k not already resident (the step time of "
                          "fetching every row is reported beside it)")
     ap.add_argument("--top-k", type=int, default=0, help="override the workload's top-k (latency-vs-k sweeps)")
+    ap.add_argument("--sync-every", type=int, default=2, choices=(1, 2),
+                    help="steps per cross-stream synchronisation of the pipeline (2 at most with 4 layers "
+                         "in turn: the gathers of a pair of steps must land before the pair's layers return)")
     ap.add_argument("--rank", choices=("lowbit", "mixed"), default="lowbit",
                     help="lowbit: rank against C'; mixed: by the attention row itself (fetched rows and tail in)")
     ap.add_argument("--compute-reserve", type=int, default=32,
@@ -181,6 +184,10 @@ def main():
                                    "slice with no exchange, see the design notes", "n_gpus": args.gpus}))
         sys.exit(2)
 
+    if args.steps % args.sync_every or args.warmup % args.sync_every:
+        print(json.dumps({"error": "--steps and --warmup must be multiples of --sync-every"}))
+        sys.exit(2)
+
     import torch
     from decode_attention_bit_kivi_amd import (
         quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, empty_cache,
@@ -242,11 +249,12 @@ def main():
     mixed = args.rank == "mixed"
     gathered = [torch.cuda.Event() for _ in range(layers)]
     stepped = [torch.cuda.Event() for _ in range(layers)]
+    sync_every = args.sync_every  # steps per cross-stream synchronisation (a divisor of the layers)
 
     def new_state():
         """Per layer: two selections and two row buffers in turn (the step reads one pair and
         its ranking fills the other), seeded by a pre-decoding score_topk + gather."""
-        st = {"occ": [0] * layers, "idx": [], "sel": [], "fetch": []}
+        st = {"occ": [0] * layers, "idx": [], "sel": [], "fetch": [], "pending": []}
         for l in range(layers):
             i0 = score_topk(qs[n_q - 1], caches[l], k, rank_row=1, workspace=ws_s)
             st["idx"].append([i0, torch.empty_like(i0)])
@@ -259,6 +267,10 @@ def main():
         return st
 
     def step(st, i, reuse, ev=None):
+        """Step i of the pipeline (layer i mod layers).  The streams synchronise once per
+        sync_every steps: the compute stream waits for the gathers of the group of steps two
+        groups back (the gather stream runs in order, so the group's event covers each of them),
+        and after the group's last step the gather stream fetches the rows of the whole group."""
         def mark(name, stream):
             if ev and name in ev:
                 ev[name].record(stream)
@@ -269,7 +281,9 @@ def main():
         cur, nxt = r % 2, 1 - r % 2
         idx_c, idx_n = st["idx"][l][cur], st["idx"][l][nxt]
         sel_c, sel_n = st["sel"][l][cur], st["sel"][l][nxt]
-        comp.wait_event(gathered[l])
+        grp = (i // sync_every) % (layers // sync_every)  # event slot of this group
+        if i % sync_every == 0:
+            comp.wait_event(gathered[grp])
         mark("d0", comp)
         decode_step(qs[r % n_q], caches[l], k, rank_row=1, rank_mixed=mixed, idx=idx_c, k_sel=sel_c[0],
                     v_sel=sel_c[1], out=out, idx_next_out=idx_n, workspace=ws)
@@ -277,15 +291,20 @@ def main():
         if reuse:  # rows of the new set already resident: device copy on the compute stream
             gather_reuse(idx_n, idx_c, sel_c[0], sel_c[1], N, k_sel=sel_n[0], v_sel=sel_n[1],
                          fetch_idx=st["fetch"][l])
-        stepped[l].record(comp)
-        side.wait_event(stepped[l])
+        st["pending"].append((l, idx_n, sel_n))
+        if i % sync_every != sync_every - 1:
+            return
+        stepped[grp].record(comp)
+        side.wait_event(stepped[grp])
         mark("g0", side)
-        if reuse:
-            gather_fp16_missing(st["fetch"][l], hk, hv, sel_n[0], sel_n[1], cfg.bits, stream=side)
-        else:
-            gather_fp16(idx_n, hk, hv, cfg.bits, sel_n[0], sel_n[1], stream=side)
+        for (pl, pidx, psel) in st["pending"]:
+            if reuse:
+                gather_fp16_missing(st["fetch"][pl], hk, hv, psel[0], psel[1], cfg.bits, stream=side)
+            else:
+                gather_fp16(pidx, hk, hv, cfg.bits, psel[0], psel[1], stream=side)
         mark("g1", side)
-        gathered[l].record(side)
+        st["pending"] = []
+        gathered[grp].record(side)
 
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -317,7 +336,9 @@ def main():
             step(st, args.warmup + args.steps + i, reuse, ev)
         torch.cuda.synchronize()
         d_us = np.array([e["d0"].elapsed_time(e["d1"]) for e in evs]) * 1e3
-        g_us = np.array([e["g0"].elapsed_time(e["g1"]) for e in evs]) * 1e3
+        # gathers are issued per group of sync_every steps, bracketed at the group's last step
+        g_us = np.array([evs[j]["g0"].elapsed_time(evs[j]["g1"]) for j in range(len(evs))
+                         if (args.warmup + args.steps + j) % sync_every == sync_every - 1]) * 1e3 / sync_every
         return ms, d_us, g_us, fetched
 
     host_enqueue_us = []
@@ -399,7 +420,7 @@ def main():
                         f"top-k {k} per KV head gathered from pinned host memory; {layers} layers in turn",
             "batch": B, "seq_len": N, "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "bits": cfg.bits,
             "top_k": k, "n_tokens": T, "layers_rotated": layers, "gather_stream_cus": args.gather_cus,
-            "compute_stream": args.compute_stream, "rank": args.rank,
+            "compute_stream": args.compute_stream, "rank": args.rank, "sync_every": args.sync_every,
             "fetch": "resident rows reused, only new top-k rows fetched" if args.reuse else "every top-k row fetched",
             "queries": f"fresh draws every step ({n_q} in turn), planted peak shared",
             "compute_stream_reserved_cus": max(args.compute_reserve, args.gather_cus)

@@ -97,9 +97,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // ---------------------------------------------------------------- rank_keys
 
 template <int GM>  // GM >= G: the heads' logits of a run are held in registers
-__global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* __restrict__ logits,
-                                                                const float* __restrict__ part_m,
-                                                                const float* __restrict__ part_l, int G, int S,
+__global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* logits, const float* part_m,
+                                                                const float* part_l, int G, int S,
                                                                 int64_t N, float r_lo, float* __restrict__ rkey,
                                                                 uint32_t* __restrict__ ghist) {
   __shared__ float lse2[GM];  // log2-sum-exp2 of each head, in log2 units
@@ -107,17 +106,41 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* __r
   const int t = threadIdx.x;
   const int64_t slice = blockIdx.y;
   const int64_t c0 = (int64_t)blockIdx.x * kKeyChunk;
+
+  // Each head's log-sum-exp comes from the split statistics (max, sum 2^(x - max)), log2 units:
+  // kKeyThreads / GM threads per head read the splits in parallel and merge across lanes.  Their
+  // first split's loads are issued before anything else (clamped, unconditional), so that waiting
+  // for them leaves the logits' loads in flight.
+  constexpr int TPH = kKeyThreads / GM;  // 64, 32 or 16: within one wave
+  const int hg = t / TPH, hj = t % TPH;
+  const int64_t st0 = (slice * G + (hg < G ? hg : 0)) * S + (hj < S ? hj : 0);
+  const float m_first = part_m[st0], l_first = part_l[st0];
+  // keeps these two loads ahead of the logits' loads (the inputs are not restrict-qualified, so
+  // that the compiler cannot treat the loads as invariant and move them past such points)
+  asm volatile("" ::: "memory");
+  // Each thread: 4 runs of 4 consecutive positions (a float4 per head), NB runs in flight (all
+  // four for up to 4 heads), with clamped addresses.
+  constexpr int NB = GM <= 4 ? 4 : 2;
+  const float* lg = logits + slice * G * N;
+  float4 x[NB][GM];
+  auto load = [&](int rr, float4 (&dst)[GM]) {
+    int64_t p = c0 + 4 * (t + rr * kKeyThreads);
+    if (p >= N) p = c0;  // past the end: a valid address, the values go unused
+#pragma unroll
+    for (int g = 0; g < GM; ++g)
+      dst[g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + p);
+    asm volatile("" ::: "memory");  // runs issue in order, so each run waits only for its own loads
+  };
+#pragma unroll
+  for (int rr = 0; rr < NB; ++rr) load(rr, x[rr]);
   {
-    // Each head's log-sum-exp from the split statistics (max, sum 2^(x - max)), log2 units:
-    // kKeyThreads / GM threads per head load the splits in parallel and merge by shuffles.
-    constexpr int TPH = kKeyThreads / GM;  // 64, 32 or 16: within one wave
-    const int g = t / TPH, j = t % TPH;
+    const int g = hg, j = hj;
     float M = -INFINITY, L = 0.0f;
     if (g < G) {
       const float* pm = part_m + (slice * G + g) * S;
       const float* pl = part_l + (slice * G + g) * S;
       for (int s = j; s < S; s += TPH) {
-        const float m = pm[s], l = pl[s];
+        const float m = s == j ? m_first : pm[s], l = s == j ? l_first : pl[s];
         const float mn = fmaxf(M, m);
         L = (M == -INFINITY ? 0.0f : L * exp2f(M - mn)) + (m == -INFINITY ? 0.0f : l * exp2f(m - mn));
         M = mn;
@@ -133,25 +156,10 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* __r
     if (g < G && j == 0) lse2[g] = M + log2f(L);
   }
   for (int i = t; i < kBins; i += kKeyThreads) hist[i] = 0u;
-
-  // each thread: 4 runs of 4 consecutive positions (a float4 per head); NB runs' loads are in
-  // flight at a time (all four for up to 4 heads)
-  constexpr int NB = GM <= 4 ? 4 : 2;
-  const float* lg = logits + slice * G * N;
-  float4 x[NB][GM];
-  auto load = [&](int rr, float4 (&dst)[GM]) {
-    const int64_t p = c0 + 4 * (t + rr * kKeyThreads);
-#pragma unroll
-    for (int g = 0; g < GM; ++g)
-      if (g < G && p < N) dst[g] = *reinterpret_cast<const float4*>(lg + (int64_t)g * N + p);
-  };
-#pragma unroll
-  for (int rr = 0; rr < NB - 1; ++rr) load(rr, x[rr]);
   __syncthreads();
   uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    if (rr + NB - 1 < 4) load(rr + NB - 1, x[(rr + NB - 1) % NB]);
     const int64_t p = c0 + 4 * (t + rr * kKeyThreads);
     if (p < N) {  // N is a multiple of 32: the whole float4 is in range
       float r[4];
@@ -184,6 +192,7 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* __r
         ++cur_cnt;
       }
     }
+    if (rr + NB < 4) load(rr + NB, x[rr % NB]);  // the slot just consumed takes a later run
   }
   if (cur_cnt) atomicAdd(&hist[cur_bin], cur_cnt);
   __syncthreads();
