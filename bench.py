@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="layers (C' copies) in turn (0: enough for >= 512 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle sample")
-    ap.add_argument("--gather-cus", type=int, default=8, help="compute units of the gather stream")
+    ap.add_argument("--gather-cus", type=int, default=16, help="compute units of the gather stream")
     ap.add_argument("--compute-stream", choices=("exclusive", "shared"), default="exclusive",
                     help="exclusive: the compute runs on the compute units the gather stream does not use")
     ap.add_argument("--reuse", action=argparse.BooleanOptionalAction, default=True,

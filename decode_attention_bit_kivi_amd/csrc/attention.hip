@@ -37,7 +37,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kEmpty = kMergeEmpty;  // running max of a row that has seen nothing
 constexpr float kRescale = 8.0f;     // lazy-rescale threshold (log2 units)
-constexpr int kMaxBlocksPerSplit = 128;
+constexpr int kMaxBlocksPerSplit = kAttnMaxBlocks;
 
 template <int D, int PACK>
 struct AttnSmem {

@@ -60,7 +60,7 @@ struct AttnPlan {
 
 constexpr int kPlanMaxCUs = 256;     // compute units the attention plans are sized for at most
 constexpr int kAttnWGsPerCU = 2;     // resident attention workgroups per compute unit
-constexpr int kAttnMaxBlocks = 128;  // 32-position blocks per split (the kernel's kappa bitmask)
+constexpr int kAttnMaxBlocks = 256;  // 32-position blocks per split (the kernel's kappa bitmask)
 constexpr int kAttnMaxSplits = 1024; // splits per slice (the merge kernel's weight table)
 
 inline int64_t attn_min_splits(const Dims& d) { return ceil_div(d.nblk, kAttnMaxBlocks); }
