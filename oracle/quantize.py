@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 What it follows:
   * [SpeCache] §3 "original KIVI quantization": Q(X) = round((X - z_X) / s_X),
     X' = Q(X) * s_X + z_X, with z_X = min X and s_X = (max X - min X) / (2^B - 1);
-    the rounding is "四舍五入", i.e. round half up.
+    the rounding the page names is ordinary round-to-nearest, read as round half up.
   * [SpeCache] §3 "improved 1-bit quantization" (also the quick-read equation):
     at one bit, z_X = (3 min X + max X) / 4 and s_X = (max X - min X) / 2, so the
     two codes land on the midpoints of [min, mid) and (mid, max].
