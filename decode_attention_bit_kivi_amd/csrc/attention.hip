@@ -73,7 +73,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   __shared__ AttnSmem<D, PACK> sm;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a wave-uniform (scalar) value: block indices and the address arithmetic
+  // derived from it then run on the scalar unit, beside the VALU
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
   const int64_t slice = blockIdx.y;
@@ -219,23 +221,38 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   const int zrow = n16 < 2 * Wg ? n16 : 0;  // value-metadata row of the zero-point / scale column
   const bool zs_lane = n16 < 2 * Wg;
   // All loads are unconditional (clamped to valid blocks) so that they issue back to back.
+  // the rank row's logits of this slice ([G][N] floats): lane offset of the lane's head row
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rl_buf =
+      make_rsrc(RANK && a.rank_logits ? static_cast<const void*>(a.rank_logits + slice * G * N)
+                                      : static_cast<const void*>(a.q16),
+                RANK && a.rank_logits ? (uint32_t)(G * N * 4) : 0u);
+  const uint32_t rl_lane = (uint32_t)((arow / T) * N * 4);
+  // A block's base addresses are wave-uniform (scalar); each lane adds a loop-invariant unsigned
+  // 32-bit offset.  The codes are read through raw buffers over the slice (scalar block offset,
+  // per-lane offset), the value metadata through the scalar base of the block.
+  const __amdgpu_buffer_rsrc_t kc_buf = make_rsrc(kc_slice, (uint32_t)(Ns * KB * W * 4));
+  const __amdgpu_buffer_rsrc_t vc_buf = make_rsrc(vc_slice, (uint32_t)(nblk_s * VB * D * 4));
+  const uint32_t off_k = (uint32_t)(n16 * KB * W * 4), off_v = (uint32_t)(CPL * n16 * 4);
+  const uint32_t off_vs = (uint32_t)(Wg * 32 + wv_grp * 32 + 4 * g), off_zs = (uint32_t)(zrow * 32 + 4 * g);
   auto load_block = [&](int jj) {
     BlockData bd;
     const int64_t blk = blk0 + jj;
-    const uint32_t* kc = kc_slice + blk * 32 * KB * W;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int pl = 0; pl < KB; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * KB + pl) * W);
-    const uint32_t* vc = vc_slice + blk * VB * D;
+      for (int pl = 0; pl < KB; ++pl)
+        bd.kw[tau][pl] = buffer_words<W>(kc_buf, off_k + (uint32_t)((16 * tau * KB + pl) * W * 4),
+                                         (uint32_t)(blk * 32 * KB * W * 4));
 #pragma unroll
-    for (int pl = 0; pl < VB; ++pl) bd.vw[pl] = load_words<CPL>(vc + pl * D + CPL * n16);
+    for (int pl = 0; pl < VB; ++pl)
+      bd.vw[pl] = buffer_words<CPL>(vc_buf, off_v + (uint32_t)(pl * D * 4), (uint32_t)(blk * VB * D * 4));
     const _Float16* vm = vm_slice + blk * 2 * Wg * 32;
-    bd.vs_lo = load_u2(vm + Wg * 32 + wv_grp * 32 + 4 * g);
-    bd.vs_hi = load_u2(vm + Wg * 32 + wv_grp * 32 + 16 + 4 * g);
+    bd.vs_lo = load_u2(vm + off_vs);
+    bd.vs_hi = load_u2(vm + 16 + off_vs);
     // rows 0..W-1 of the value metadata are the zero-points of groups 0..W-1, rows W..2W-1 the scales
-    bd.zs_lo = load_u2(vm + zrow * 32 + 4 * g);
-    bd.zs_hi = load_u2(vm + zrow * 32 + 16 + 4 * g);
+    bd.zs_lo = load_u2(vm + off_zs);
+    bd.zs_hi = load_u2(vm + 16 + off_zs);
     return bd;
   };
   // Prepass over the wave's next 16 blocks: zero-points and scales of the keys against the
@@ -311,15 +328,21 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
           if (!((kmw >> tok) & 1u)) dst[tok] = xa[i] * kLn2;
         }
       } else if (rank_lane) {
-        float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
+        // through the raw buffer over the slice's logits: the block offset is scalar
         constexpr float kLn2 = 0.69314718055994531f;
+        const uint32_t soff = (uint32_t)((blk0 + jj) * 32 * 4);
+        typedef float f4_t __attribute__((ext_vector_type(4)));
         if constexpr (PACK == 2) {
-          *reinterpret_cast<float4*>(dst + 16 * (n16 >> 3) + 4 * g) =
-              make_float4(xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2);
+          const f4_t v = {xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
+                                                 (int)(rl_lane + 4 * (16 * (n16 >> 3) + 4 * g)), (int)soff, 0);
         } else {
-          *reinterpret_cast<float4*>(dst + 4 * g) = make_float4(xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2);
-          *reinterpret_cast<float4*>(dst + 16 + 4 * g) =
-              make_float4(xa[4] * kLn2, xa[5] * kLn2, xa[6] * kLn2, xa[7] * kLn2);
+          const f4_t v0 = {xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2};
+          const f4_t v1 = {xa[4] * kLn2, xa[5] * kLn2, xa[6] * kLn2, xa[7] * kLn2};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v0), rl_buf, (int)(rl_lane + 16 * g),
+                                                 (int)soff, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v1), rl_buf,
+                                                 (int)(rl_lane + 4 * (16 + 4 * g)), (int)soff, 0);
         }
       }
     }

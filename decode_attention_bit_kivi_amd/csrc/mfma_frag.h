@@ -74,6 +74,33 @@ __device__ __forceinline__ Words<NW> load_words(const uint32_t* p) {
   return r;
 }
 
+// Raw buffer over `bytes` bytes at `p` (gfx9 descriptor: untyped, no swizzle).  A load through it
+// adds a wave-uniform byte offset (scalar register) to a per-lane byte offset, so the address
+// arithmetic of a loop whose base moves uniformly stays off the VALU; bytes past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// NW consecutive 32-bit words at byte voff + soff of the buffer (4*NW-byte aligned).
+template <int NW>
+__device__ __forceinline__ Words<NW> buffer_words(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  Words<NW> w;
+  if constexpr (NW == 8 || NW == 4) {
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16 * h), (int)soff, 0);
+      w.w[4 * h] = x[0]; w.w[4 * h + 1] = x[1]; w.w[4 * h + 2] = x[2]; w.w[4 * h + 3] = x[3];
+    }
+  } else if constexpr (NW == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    w.w[0] = x[0]; w.w[1] = x[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w.w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * i), (int)soff, 0);
+  }
+  return w;
+}
+
 __device__ __forceinline__ uint2 load_u2(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 __device__ __forceinline__ uint4 load_u4(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
