@@ -219,7 +219,6 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   const _Float16* vm_slice = a.v_meta + slice * nblk_s * 2 * Wg * 32;
   const _Float16* km_slice = a.k_meta + slice * (nblk_s >> gshift) * 2 * D;
   const int zrow = n16 < 2 * Wg ? n16 : 0;  // value-metadata row of the zero-point / scale column
-  const bool zs_lane = n16 < 2 * Wg;
   // All loads are unconditional (clamped to valid blocks) so that they issue back to back.
   // the rank row's logits of this slice ([G][N] floats): lane offset of the lane's head row
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -394,11 +393,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
         Oacc[ct] = mma(pl == 0 ? Ap : Ap2, Bv, Oacc[ct]);
       }
     }
+    // columns n16 >= 2 Wg carry another row's (finite) metadata: their outputs are never read
     Frag Bzs;
-    Bzs.u[0] = zs_lane ? bd.zs_lo.x : 0u;
-    Bzs.u[1] = zs_lane ? bd.zs_lo.y : 0u;
-    Bzs.u[2] = zs_lane ? bd.zs_hi.x : 0u;
-    Bzs.u[3] = zs_lane ? bd.zs_hi.y : 0u;
+    Bzs.u[0] = bd.zs_lo.x;
+    Bzs.u[1] = bd.zs_lo.y;
+    Bzs.u[2] = bd.zs_hi.x;
+    Bzs.u[3] = bd.zs_hi.y;
     Ozs = mma(Ap, Bzs, Ozs);
   };
 

@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
   __shared__ float red_m[4][16], red_l[4][16];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a wave-uniform (scalar) value: block indices and base offsets stay scalar
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
   const int split = blockIdx.x;
   const int64_t slice = blockIdx.y;
@@ -77,23 +78,34 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
     Words<W> kw[2][BITS];
     uint4 ks[W];
   };
+  // Raw buffers over the slice's codes and key metadata: a block's offset is scalar, each lane
+  // adds a loop-invariant offset.
+  const __amdgpu_buffer_rsrc_t kc_buf = make_rsrc(k_codes + slice * Ns * BITS * W, (uint32_t)(Ns * BITS * W * 4));
+  const __amdgpu_buffer_rsrc_t km_buf = make_rsrc(k_meta + slice * ngrp_s * 2 * D, (uint32_t)(ngrp_s * 2 * D * 2));
+  const uint32_t off_k = (uint32_t)(n16 * BITS * W * 4), off_m = (uint32_t)((D + 8 * g) * 2);
   auto load_block = [&](int jj) {
     BlockData bd;
     const int64_t blk = blk0 + jj;
-    const uint32_t* kc = k_codes + (slice * Ns + blk * 32) * BITS * W;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int pl = 0; pl < BITS; ++pl) bd.kw[tau][pl] = load_words<W>(kc + ((16 * tau + n16) * BITS + pl) * W);
-    const _Float16* kms = k_meta + ((slice * ngrp_s + (blk >> gshift)) * 2 + 1) * D;
+      for (int pl = 0; pl < BITS; ++pl)
+        bd.kw[tau][pl] = buffer_words<W>(kc_buf, off_k + (uint32_t)((16 * tau * BITS + pl) * W * 4),
+                                         (uint32_t)(blk * 32 * BITS * W * 4));
+    const uint32_t moff = (uint32_t)((blk >> gshift) * 2 * D * 2);  // the group's zero-points; scales follow
 #pragma unroll
-    for (int w = 0; w < W; ++w) bd.ks[w] = load_u4(kms + 32 * w + 8 * g);
+    for (int w = 0; w < W; ++w) {
+      const Words<4> v = buffer_words<4>(km_buf, off_m + (uint32_t)(32 * w * 2), moff);
+      bd.ks[w] = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+    }
     return bd;
   };
 
   float m2 = -INFINITY, l2 = 0.0f;   // this lane's running (max, sum 2^(x - max)) in log2 units
   const int head = PACK == 2 ? (n16 & 7) : n16;
   const bool writer = head < G;
+  const __amdgpu_buffer_rsrc_t lg_buf = make_rsrc(logits + slice * G * N, (uint32_t)(G * N * 4));
+  const uint32_t lg_lane = (uint32_t)((writer ? head : 0) * N * 4);
 
   BlockData cur;
   if (wave < nb) cur = load_block(wave);
@@ -153,14 +165,20 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
       const float s = BITS == 1 ? -0.5f * acc[tau][0][i & 3] : -0.5f * acc[tau][0][i & 3] - acc[tau][BITS - 1][i & 3];
       x[i] = sm_scale * (c0 + s);
     }
-    const int64_t pos = (blk0 + jj) * 32;
-    if (writer) {
-      float* dst = logits + (slice * G + head) * N + pos;
+    if (writer) {  // through the raw buffer over the slice's logits (block offset scalar)
+      const uint32_t soff = (uint32_t)((blk0 + jj) * 32 * 4);
+      typedef float f4_t __attribute__((ext_vector_type(4)));
+      typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
       if constexpr (PACK == 2) {
-        *reinterpret_cast<float4*>(dst + 16 * (n16 >> 3) + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+        const f4_t v = {x[0], x[1], x[2], x[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), lg_buf,
+                                               (int)(lg_lane + 4 * (16 * (n16 >> 3) + 4 * g)), (int)soff, 0);
       } else {
-        *reinterpret_cast<float4*>(dst + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4*>(dst + 16 + 4 * g) = make_float4(x[4], x[5], x[6], x[7]);
+        const f4_t v0 = {x[0], x[1], x[2], x[3]}, v1 = {x[4], x[5], x[6], x[7]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v0), lg_buf, (int)(lg_lane + 16 * g),
+                                               (int)soff, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v1), lg_buf, (int)(lg_lane + 4 * (16 + 4 * g)),
+                                               (int)soff, 0);
       }
     }
     float bm = x[0];
