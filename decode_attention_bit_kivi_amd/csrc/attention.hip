@@ -208,8 +208,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   };
 
   // ================= low-bit blocks =================
-  struct BlockData {
+  // A block's key codes and value data load on separate schedules (each one block ahead of its use).
+  struct KData {
     Words<W> kw[2][KB];
+  };
+  struct VData {
     Words<CPL> vw[VB];
     uint2 vs_lo, vs_hi, zs_lo, zs_hi;
   };
@@ -234,15 +237,20 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   const __amdgpu_buffer_rsrc_t vc_buf = make_rsrc(vc_slice, (uint32_t)(nblk_s * VB * D * 4));
   const uint32_t off_k = (uint32_t)(n16 * KB * W * 4), off_v = (uint32_t)(CPL * n16 * 4);
   const uint32_t off_vs = (uint32_t)(Wg * 32 + wv_grp * 32 + 4 * g), off_zs = (uint32_t)(zrow * 32 + 4 * g);
-  auto load_block = [&](int jj) {
-    BlockData bd;
+  auto load_k = [&](int jj) {
+    KData kd;
     const int64_t blk = blk0 + jj;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int pl = 0; pl < KB; ++pl)
-        bd.kw[tau][pl] = buffer_words<W>(kc_buf, off_k + (uint32_t)((16 * tau * KB + pl) * W * 4),
+        kd.kw[tau][pl] = buffer_words<W>(kc_buf, off_k + (uint32_t)((16 * tau * KB + pl) * W * 4),
                                          (uint32_t)(blk * 32 * KB * W * 4));
+    return kd;
+  };
+  auto load_v = [&](int jj) {
+    VData bd;
+    const int64_t blk = blk0 + jj;
 #pragma unroll
     for (int pl = 0; pl < VB; ++pl)
       bd.vw[pl] = buffer_words<CPL>(vc_buf, off_v + (uint32_t)(pl * D * 4), (uint32_t)(blk * VB * D * 4));
@@ -279,9 +287,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     lds_fence();
   };
 
-  auto compute_block = [&](const BlockData& bd, int jj, int step) {
-    // scores
-    f32x4 acc[2][KB];
+  // scores of a block: the key codes expanded against the queries on the matrix cores
+  auto score_block = [&](const KData& kd, int step, f32x4 (&acc)[2][KB]) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
         for (int pl = 0; pl < KB; ++pl) {
           Frag A;
 #pragma unroll
-          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(bd.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
+          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(kd.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
           if constexpr (PACK == 2)
             acc[0][pl] = mma(A, tau == 0 ? B0[w] : B1[w], acc[0][pl]);
           else
@@ -304,7 +311,10 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
         }
       }
     }
-    const float c0 = sm.cst[wave][step & 15][PACK == 2 ? (n16 & 7) : n16];
+  };
+  auto block_const = [&](int step) { return sm.cst[wave][step & 15][PACK == 2 ? (n16 & 7) : n16]; };
+  // the rest of a block: logits, softmax, ranking outputs, values.  c0: the block's constant.
+  auto finish_block = [&](const VData& bd, const f32x4 (&acc)[2][KB], float c0, int jj) {
     const float c0m = c0 - m_used;
     float xr[NX], xa[NX];
 #pragma unroll
@@ -402,20 +412,47 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     Ozs = mma(Ap, Bzs, Ozs);
   };
 
-  // Two block buffers in turn: the next block's loads are in flight while one is computed.
+  // Software pipeline over this wave's blocks (jj = wave + 4 i, i = 0 .. nw - 1): iteration i
+  // issues block i + 1's score MFMAs before finishing block i (softmax, values), so the matrix
+  // cores work on one block while the VALU finishes the other; key codes load two blocks ahead,
+  // value data one.  A block's constant is read right after the prepass that covers it (the next
+  // prepass rewrites the LDS slots).
   if constexpr (!F16) {
-    BlockData b0, b1;
-    if (wave < nb) b0 = load_block(wave);
-    for (int jj = wave; jj < nb; jj += 8) {
-      const int step = (jj - wave) >> 2;  // even; a prepass step every 16 of this wave's blocks
-      const bool pre = (step & 15) == 0;
-      if (pre) prepass_load(jj);
-      b1 = load_block(jj + 4 < nb ? jj + 4 : jj);
-      if (pre) prepass_finish();
-      compute_block(b0, jj, step);
-      if (jj + 4 >= nb) break;
-      b0 = load_block(jj + 8 < nb ? jj + 8 : jj + 4);
-      compute_block(b1, jj + 4, step + 1);
+    const int nw = wave < nb ? (nb - wave + 3) / 4 : 0;
+    auto blk = [&](int i) { return wave + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
+    if (nw > 0) {
+      KData k0 = load_k(blk(0)), k1 = load_k(blk(1));
+      VData v0 = load_v(blk(0)), v1;
+      f32x4 acc0[2][KB], acc1[2][KB];
+      prepass_load(blk(0));
+      prepass_finish();
+      score_block(k0, 0, acc0);
+      float c0_0 = block_const(0), c0_1 = 0.0f;
+      for (int i = 0; i < nw; i += 2) {
+        k0 = load_k(blk(i + 2));
+        v1 = load_v(blk(i + 1));
+        if (i + 1 < nw) {
+          if (((i + 1) & 15) == 0) {
+            prepass_load(blk(i + 1));
+            prepass_finish();
+          }
+          score_block(k1, i + 1, acc1);
+          c0_1 = block_const(i + 1);
+        }
+        finish_block(v0, acc0, c0_0, blk(i));
+        if (i + 1 >= nw) break;
+        k1 = load_k(blk(i + 3));
+        v0 = load_v(blk(i + 2));
+        if (i + 2 < nw) {
+          if (((i + 2) & 15) == 0) {
+            prepass_load(blk(i + 2));
+            prepass_finish();
+          }
+          score_block(k0, i + 2, acc0);
+          c0_0 = block_const(i + 2);
+        }
+        finish_block(v1, acc1, c0_1, blk(i + 1));
+      }
     }
   }
 
