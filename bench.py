@@ -32,6 +32,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -91,9 +92,11 @@ def parse():
     ap.add_argument("--compute-reserve", type=int, default=32,
                     help="with an exclusive compute stream: the low compute units kept from it (the "
                          "gather's among them); 32 leaves every shader engine the same number of units")
-    ap.add_argument("--mode", choices=("step", "copy"), default="step",
+    ap.add_argument("--mode", choices=("step", "copy", "traffic-record"), default="step",
                     help="copy: a plain 1 GiB device-to-device copy, the reference for scaling the "
-                         "profiler's HBM byte counters")
+                         "profiler's HBM byte counters; traffic-record: write the HBM traffic record "
+                         "from the four counter runs under --pmc-root (see TRAFFIC_COMMANDS)")
+    ap.add_argument("--pmc-root", default="gpurun_out", help="directory holding the counter runs")
     return ap.parse_args()
 
 
@@ -114,6 +117,91 @@ def copy_reference(reps: int = 5):
     us = e0.elapsed_time(e1) * 1e3 / reps
     print(json.dumps({"mode": "copy", "bytes_read": n, "bytes_written": n, "us": us,
                       "GBs": 2 * n / (us * 1e-6) / 1e9}), flush=True)
+
+
+TRAFFIC_KERNELS = "attn_split|rank_keys|rank_select|attn_merge"
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_fetch -o run -- python -u bench.py --mode copy",
+    "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o run -- python -u bench.py --mode copy",
+    f"rocprofv3 --kernel-include-regex '{TRAFFIC_KERNELS}' --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch "
+    "-o run -- python -u bench.py --steps 4 --warmup 2 --no-cpu-baseline",
+    f"rocprofv3 --kernel-include-regex '{TRAFFIC_KERNELS}' --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write "
+    "-o run -- python -u bench.py --steps 4 --warmup 2 --no-cpu-baseline",
+    "python bench.py --mode traffic-record --pmc-root gpurun_out",
+]
+
+
+def _counter_rows(root: str, run: str, counter: str):
+    """(queue, dispatch id, kernel name, value) of every dispatch in one rocprofv3 counter run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(root, run, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter collection under {os.path.join(root, run)}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Queue_Id"], int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort(key=lambda x: x[1])
+    return rows
+
+
+def write_traffic_record(root: str, workload: str = "mistral32k"):
+    """HBM bytes per decode_step call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for the plain 1 GiB copy.  A call is the fused-step
+    split dispatch and the rank_keys and rank_select dispatches that follow it on its queue."""
+    import statistics
+    cal = {}
+    for counter, run in (("FETCH_SIZE", "pmc_copy_fetch"), ("WRITE_SIZE", "pmc_copy_write")):
+        vals = [v for _, _, name, v in _counter_rows(root, run, counter) if "copy" in name.lower()]
+        cal[counter] = statistics.median(vals)
+    n = 1 << 30
+    scale = {"FETCH_SIZE": n / (cal["FETCH_SIZE"] * 1024), "WRITE_SIZE": n / (cal["WRITE_SIZE"] * 1024)}
+    per = {}
+    for counter, run in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
+        after_split = {}
+        for queue, _, name, v in _counter_rows(root, run, counter):
+            if "attn_split_kernel" in name and ", true, false>" in name:
+                kind = re.search(r"attn_split_kernel<[^>]*>", name).group(0)
+                after_split[queue] = True
+            elif after_split.get(queue) and ("rank_keys" in name or "rank_select" in name):
+                kind = "rank_keys_kernel" if "rank_keys" in name else "rank_select_kernel (with the split merge)"
+                if "rank_select" in name:
+                    after_split[queue] = False
+            else:
+                if "attn_split" in name:
+                    after_split[queue] = False
+                continue
+            per.setdefault(kind, {}).setdefault(counter, []).append(v)
+    out = {}
+    total = 0.0
+    for kind, d in per.items():
+        f_kib = statistics.mean(d["FETCH_SIZE"])
+        w_kib = statistics.mean(d["WRITE_SIZE"])
+        fb, wb = f_kib * 1024 * scale["FETCH_SIZE"], w_kib * 1024 * scale["WRITE_SIZE"]
+        out[kind] = {"dispatches": len(d["FETCH_SIZE"]), "fetch_kib_raw": round(f_kib), "write_kib": round(w_kib),
+                     "fetch_bytes": round(fb), "write_bytes": round(wb)}
+        total += fb + wb
+    from workloads import get_config
+    rec = {
+        "workload": workload,
+        "what": "HBM bytes per specache_decode_step call: the three kernels it launches, each dispatch taken "
+                "right after a fused-step split dispatch on its queue; rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                "per dispatch, scaled by the same counters' reading for a plain 1 GiB device copy",
+        "commands": TRAFFIC_COMMANDS,
+        "calibration": {"copy_bytes_read": n, "copy_bytes_written": n,
+                        "FETCH_SIZE_kib": round(cal["FETCH_SIZE"]), "WRITE_SIZE_kib": round(cal["WRITE_SIZE"]),
+                        "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4)},
+        "per_kernel": out,
+        "traffic_bytes_per_launch": round(total),
+        "algorithmic_bytes_per_launch": algorithmic_bytes_step(get_config(workload)),
+        "sources_sha256": step_sources_hash(),
+    }
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({"traffic_bytes_per_launch": rec["traffic_bytes_per_launch"], "per_kernel": out}))
 
 
 def algorithmic_bytes_step(cfg) -> int:
@@ -178,6 +266,9 @@ def main():
     args = parse()
     if args.mode == "copy":
         copy_reference()
+        return
+    if args.mode == "traffic-record":
+        write_traffic_record(args.pmc_root, args.workload)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; the path shards per (batch, KV head) "

@@ -162,10 +162,11 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   // than 2^kRescale.  xr holds logits relative to the current maximum; on a rescale they are
   // recomputed from the absolute values xa.
   auto online_update = [&](float (&xr)[NX], const float (&xa)[NX]) {
+    // the wave-wide vote needs no per-row maximum: some row's maximum exceeds the threshold
+    // exactly when some lane's does
     float bm = xr[0];
 #pragma unroll
     for (int i = 1; i < NX; ++i) bm = fmaxf(bm, xr[i]);
-    bm = max_over_groups(bm);
     if (__any(bm > kRescale)) {
       float ba = xa[0];
 #pragma unroll
@@ -326,28 +327,27 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
     const uint32_t kmw = sm.kmask[jj];
     if constexpr (RANK) {
-      // the rank row's logits against C' (before any kappa masking), natural units; when ranking
+      // the rank row's logits against C' (before any kappa masking), log2 units; when ranking
       // by the mixed cache the kappa positions are written by the 16-bit pass instead
       if (rank_lane && a.rank_mixed && kmw) {
         float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
-        constexpr float kLn2 = 0.69314718055994531f;
 #pragma unroll
         for (int i = 0; i < NX; ++i) {
           const int tok = PACK == 2 ? (16 * (n16 >> 3) + 4 * g + i) : (16 * (i >> 2) + 4 * g + (i & 3));
-          if (!((kmw >> tok) & 1u)) dst[tok] = xa[i] * kLn2;
+          if (!((kmw >> tok) & 1u)) dst[tok] = xa[i];
         }
       } else if (rank_lane) {
-        // through the raw buffer over the slice's logits: the block offset is scalar
-        constexpr float kLn2 = 0.69314718055994531f;
-        const uint32_t soff = (uint32_t)((blk0 + jj) * 32 * 4);
+        // through the raw buffer over the slice's logits: the block offset is scalar (read from
+        // the first lane, so that the compiler keeps it in a scalar register)
+        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((blk0 + jj) * 32 * 4));
         typedef float f4_t __attribute__((ext_vector_type(4)));
         if constexpr (PACK == 2) {
-          const f4_t v = {xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2};
+          const f4_t v = {xa[0], xa[1], xa[2], xa[3]};
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
                                                  (int)(rl_lane + 4 * (16 * (n16 >> 3) + 4 * g)), (int)soff, 0);
         } else {
-          const f4_t v0 = {xa[0] * kLn2, xa[1] * kLn2, xa[2] * kLn2, xa[3] * kLn2};
-          const f4_t v1 = {xa[4] * kLn2, xa[5] * kLn2, xa[6] * kLn2, xa[7] * kLn2};
+          const f4_t v0 = {xa[0], xa[1], xa[2], xa[3]};
+          const f4_t v1 = {xa[4], xa[5], xa[6], xa[7]};
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v0), rl_buf, (int)(rl_lane + 16 * g),
                                                  (int)soff, 0);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v1), rl_buf,
@@ -428,7 +428,17 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       prepass_finish();
       score_block(k0, 0, acc0);
       float c0_0 = block_const(0), c0_1 = 0.0f;
+      // Issue priority by the blocks this wave has left: two workgroups share each compute
+      // unit, and the SIMD arbiter otherwise favours the older one, which then finishes long
+      // before the younger and leaves one wave per SIMD for the rest.  A wave that has got
+      // ahead drops below the waves behind it, so the waves of a SIMD finish together.
+      const int pr1 = nw / 16 + 1, pr2 = nw / 6 + 1, pr3 = nw / 3 + 1;
       for (int i = 0; i < nw; i += 2) {
+        const int rem = nw - i;
+        if (rem > pr3) __builtin_amdgcn_s_setprio(3);
+        else if (rem > pr2) __builtin_amdgcn_s_setprio(2);
+        else if (rem > pr1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         k0 = load_k(blk(i + 2));
         v1 = load_v(blk(i + 1));
         if (i + 1 < nw) {
@@ -455,6 +465,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       }
     }
   }
+
+  __builtin_amdgcn_s_setprio(3);  // the rest of the workgroup is a chain of latencies: let it through
 
   // ranking statistics over C' = the low-bit positions processed so far, kappa positions included
   float rank_m_lane = m_used, rank_l_lane = l_part;
@@ -528,7 +540,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
         // ranking by the mixed cache: a fetched row's logit replaces its low-bit one
         if (a.rank_mixed && rank_lane && !tail && ok) {
           const int64_t pos = a.idx[slice * a.k + base + tok];
-          a.rank_logits[(slice * G + arow / T) * N + pos] = v * 0.69314718055994531f;
+          a.rank_logits[(slice * G + arow / T) * N + pos] = v;
         }
       }
       if (tail) ok = ok && (base + tok <= a.tail - T + tq);

@@ -174,7 +174,7 @@ struct AttnArgs {
   // Ranking outputs of the fused step (all null / unused for plain attention):
   int rank_row;
   int rank_mixed;        // 0: rank against C'; 1: rank by the row of the mixed-cache attention
-  float* rank_logits;    // [slices][G][N]: the rank row's logits (natural units)
+  float* rank_logits;    // [slices][G][N]: the rank row's logits (log2 units)
   float* rank_m;         // [slices][G][S]: per-split max of its softmax (log2 units)
   float* rank_l;         // [slices][G][S]: per-split sum of 2^(x - max)
   uint32_t* rank_hist;   // [slices][2048]: zeroed by the split kernel for the rank kernels

@@ -43,7 +43,6 @@ constexpr float kBinSpan = 32.0f;              // r window of the coarse bins, b
 constexpr float kBinScale = kBins / kBinSpan;  // bins per unit of r (a power of two: exact)
 constexpr int kCand = 16384;                   // keys of the threshold bin held in LDS
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint32_t order_key(float r) {
   const uint32_t f = __float_as_uint(r);
@@ -172,7 +171,7 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
           if (g < G) {
             const float4 v4 = x[rr % NB][g];
             const float v = e == 0 ? v4.x : (e == 1 ? v4.y : (e == 2 ? v4.z : v4.w));
-            lp[g] = fmaf(v, kLog2e, -lse2[g]);  // log2 of the head's probability
+            lp[g] = v - lse2[g];  // log2 of the head's probability (the logits are in log2 units)
             mx = fmaxf(mx, lp[g]);
           }
         float sum = 0.0f;

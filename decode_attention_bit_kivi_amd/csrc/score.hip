@@ -18,7 +18,8 @@
 // Layout: grid (splits, slices), 256 threads = 4 waves; a wave owns every
 // 4th 32-position block of its split.  With at most 8 heads the two 16-token
 // tiles of a block share one accumulator (heads in columns 0-7 for tile 0,
-// 8-15 for tile 1).  Logits go to [slice][head][position] as float32; the
+// 8-15 for tile 1).  Logits go to [slice][head][position] as float32 in log2
+// units (natural-unit logit times log2 e); the
 // per-split statistics are (max, sum of 2^(x - max)) in log2 units.
 #include "mfma_frag.h"
 
@@ -38,6 +39,7 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
                                                        float* __restrict__ part_l, uint32_t* __restrict__ hist) {
   constexpr int W = D / 32;
   constexpr float hK = BITS == 1 ? 0.5f : 1.5f;
+  const float qscale = sm_scale * kLog2e;  // the logits are written in log2 units
   constexpr int NX = PACK == 2 ? 4 : 8;
   __shared__ float cst[4][16][16];
   __shared__ float red_m[4][16], red_l[4][16];
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
     for (int i = 0; i < NX; ++i) {
       const int tau = PACK == 2 ? 0 : i / 4;
       const float s = BITS == 1 ? -0.5f * acc[tau][0][i & 3] : -0.5f * acc[tau][0][i & 3] - acc[tau][BITS - 1][i & 3];
-      x[i] = sm_scale * (c0 + s);
+      x[i] = qscale * (c0 + s);  // log2 units
     }
     if (writer) {  // through the raw buffer over the slice's logits (block offset scalar)
       const uint32_t soff = (uint32_t)((blk0 + jj) * 32 * 4);
@@ -184,10 +186,10 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
     float bm = x[0];
 #pragma unroll
     for (int i = 1; i < NX; ++i) bm = fmaxf(bm, x[i]);
-    const float mn = fmaxf(m2, bm * kLog2e);
+    const float mn = fmaxf(m2, bm);
     float add = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NX; ++i) add += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mn));
+    for (int i = 0; i < NX; ++i) add += __builtin_amdgcn_exp2f(x[i] - mn);
     l2 = l2 * __builtin_amdgcn_exp2f(m2 - mn) + add;
     m2 = mn;
     cur = nxt;
