@@ -137,7 +137,8 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   }
 
   float m_used = kEmpty;   // running max (log2 units) of accumulator row n16
-  float l_part = 0.0f;     // this lane's share of that row's sum of exponentials
+  float l_part = 0.0f;     // this lane's share of that row's sum of exponentials (low-bit positions)
+  float l16 = 0.0f;        // the same over the 16-bit rows (fetched and tail), kept apart for the ranking
   // ranking: the C' terms of kappa positions (masked out of the attention), kept relative to
   // their own running max m_corr (row-uniform) so that the attention's arithmetic is untouched
   float m_corr = kEmpty, l_corr = 0.0f;
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
       m_used = mn;
       l_part *= alpha;
+      l16 *= alpha;
 #pragma unroll
       for (int i = 0; i < NX; ++i) xr[i] = xa[i] - mn;
 #pragma unroll
@@ -412,76 +414,18 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     Ozs = mma(Ap, Bzs, Ozs);
   };
 
-  // Software pipeline over this wave's blocks (jj = wave + 4 i, i = 0 .. nw - 1): iteration i
-  // issues block i + 1's score MFMAs before finishing block i (softmax, values), so the matrix
-  // cores work on one block while the VALU finishes the other; key codes load two blocks ahead,
-  // value data one.  A block's constant is read right after the prepass that covers it (the next
-  // prepass rewrites the LDS slots).
-  if constexpr (!F16) {
-    const int nw = wave < nb ? (nb - wave + 3) / 4 : 0;
-    auto blk = [&](int i) { return wave + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
-    if (nw > 0) {
-      KData k0 = load_k(blk(0)), k1 = load_k(blk(1));
-      VData v0 = load_v(blk(0)), v1;
-      f32x4 acc0[2][KB], acc1[2][KB];
-      prepass_load(blk(0));
-      prepass_finish();
-      score_block(k0, 0, acc0);
-      float c0_0 = block_const(0), c0_1 = 0.0f;
-      // Issue priority by the blocks this wave has left: two workgroups share each compute
-      // unit, and the SIMD arbiter otherwise favours the older one, which then finishes long
-      // before the younger and leaves one wave per SIMD for the rest.  A wave that has got
-      // ahead drops below the waves behind it, so the waves of a SIMD finish together.
-      const int pr1 = nw / 16 + 1, pr2 = nw / 6 + 1, pr3 = nw / 3 + 1;
-      for (int i = 0; i < nw; i += 2) {
-        const int rem = nw - i;
-        if (rem > pr3) __builtin_amdgcn_s_setprio(3);
-        else if (rem > pr2) __builtin_amdgcn_s_setprio(2);
-        else if (rem > pr1) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
-        k0 = load_k(blk(i + 2));
-        v1 = load_v(blk(i + 1));
-        if (i + 1 < nw) {
-          if (((i + 1) & 15) == 0) {
-            prepass_load(blk(i + 1));
-            prepass_finish();
-          }
-          score_block(k1, i + 1, acc1);
-          c0_1 = block_const(i + 1);
-        }
-        finish_block(v0, acc0, c0_0, blk(i));
-        if (i + 1 >= nw) break;
-        k1 = load_k(blk(i + 3));
-        v0 = load_v(blk(i + 2));
-        if (i + 2 < nw) {
-          if (((i + 2) & 15) == 0) {
-            prepass_load(blk(i + 2));
-            prepass_finish();
-          }
-          score_block(k0, i + 2, acc0);
-          c0_0 = block_const(i + 2);
-        }
-        finish_block(v1, acc1, c0_1, blk(i + 1));
-      }
-    }
-  }
-
-  __builtin_amdgcn_s_setprio(3);  // the rest of the workgroup is a chain of latencies: let it through
-
-  // ranking statistics over C' = the low-bit positions processed so far, kappa positions included
-  float rank_m_lane = m_used, rank_l_lane = l_part;
-  if constexpr (RANK) {
-    rank_m_lane = fmaxf(m_used, m_corr);
-    rank_l_lane = l_part * __builtin_amdgcn_exp2f(m_used - rank_m_lane) +
-                  l_corr * __builtin_amdgcn_exp2f(m_corr - rank_m_lane);
-  }
-
-  // ================= 16-bit rows: fetched kappa rows of this split, then the tail =================
+  // ================= 16-bit rows: the fetched kappa rows of this split, then the tail =================
+  // Block q of a wave's share (q = wave, wave + 4, ...): the fetched rows' blocks run before the
+  // low-bit blocks, so that their loads and transposes overlap the other waves' low-bit work (the
+  // wave then has more low-bit blocks left than the others and takes the issue priority until it
+  // has caught up); the tail's blocks run after them.  Their exponentials go to l16, so the
+  // low-bit sums l_part stay the ranking statistics over C'.
   const int n_sel = i1 - i0;
   const bool has_tail = (split == S - 1) && a.tail > 0;
   const int n_sel_blk = (n_sel + 31) / 32;
   const int n_tail_blk = has_tail ? (a.tail + 31) / 32 : 0;
-  for (int q = wave; q < n_sel_blk + n_tail_blk; q += 4) {
+  const int first_tail_q = n_sel_blk + ((wave - n_sel_blk) % 4 + 4) % 4;  // first q >= n_sel_blk of this wave
+  auto f16_block = [&](int q) {
     const bool tail = q >= n_sel_blk;
     const int base = tail ? 32 * (q - n_sel_blk) : i0 + 32 * q;
     const int lim = tail ? a.tail : i1;
@@ -552,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       p[i] = __builtin_amdgcn_exp2f(xr[i]);
-      l_part += p[i];
+      l16 += p[i];
     }
     const Frag Ap2 = make_p(p, -2.0f);  // the value accumulator is scaled by -1/2 at the end
     lds_fence();
@@ -569,10 +513,78 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       Oacc[ct] = mma(Ap2, Bv, Oacc[ct]);
     }
     lds_fence();
+  };
+  for (int q = wave; q < n_sel_blk; q += 4) f16_block(q);
+
+  // Software pipeline over this wave's blocks (jj = wave + 4 i, i = 0 .. nw - 1): iteration i
+  // issues block i + 1's score MFMAs before finishing block i (softmax, values), so the matrix
+  // cores work on one block while the VALU finishes the other; key codes load two blocks ahead,
+  // value data one.  A block's constant is read right after the prepass that covers it (the next
+  // prepass rewrites the LDS slots).
+  if constexpr (!F16) {
+    const int nw = wave < nb ? (nb - wave + 3) / 4 : 0;
+    auto blk = [&](int i) { return wave + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
+    if (nw > 0) {
+      KData k0 = load_k(blk(0)), k1 = load_k(blk(1));
+      VData v0 = load_v(blk(0)), v1;
+      f32x4 acc0[2][KB], acc1[2][KB];
+      prepass_load(blk(0));
+      prepass_finish();
+      score_block(k0, 0, acc0);
+      float c0_0 = block_const(0), c0_1 = 0.0f;
+      // Issue priority by the blocks this wave has left: two workgroups share each compute
+      // unit, and the SIMD arbiter otherwise favours the older one, which then finishes long
+      // before the younger and leaves one wave per SIMD for the rest.  A wave that has got
+      // ahead drops below the waves behind it, so the waves of a SIMD finish together.
+      const int pr1 = nw / 16 + 1, pr2 = nw / 6 + 1, pr3 = nw / 3 + 1;
+      for (int i = 0; i < nw; i += 2) {
+        const int rem = nw - i;
+        if (rem > pr3) __builtin_amdgcn_s_setprio(3);
+        else if (rem > pr2) __builtin_amdgcn_s_setprio(2);
+        else if (rem > pr1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+        k0 = load_k(blk(i + 2));
+        v1 = load_v(blk(i + 1));
+        if (i + 1 < nw) {
+          if (((i + 1) & 15) == 0) {
+            prepass_load(blk(i + 1));
+            prepass_finish();
+          }
+          score_block(k1, i + 1, acc1);
+          c0_1 = block_const(i + 1);
+        }
+        finish_block(v0, acc0, c0_0, blk(i));
+        if (i + 1 >= nw) break;
+        k1 = load_k(blk(i + 3));
+        v0 = load_v(blk(i + 2));
+        if (i + 2 < nw) {
+          if (((i + 2) & 15) == 0) {
+            prepass_load(blk(i + 2));
+            prepass_finish();
+          }
+          score_block(k0, i + 2, acc0);
+          c0_0 = block_const(i + 2);
+        }
+        finish_block(v1, acc1, c0_1, blk(i + 1));
+      }
+    }
   }
 
+  __builtin_amdgcn_s_setprio(3);  // the rest of the workgroup is a chain of latencies: let it through
+
+  // ranking statistics over C' = the low-bit positions processed so far, kappa positions included
+  float rank_m_lane = m_used, rank_l_lane = l_part;
+  if constexpr (RANK) {
+    rank_m_lane = fmaxf(m_used, m_corr);
+    rank_l_lane = l_part * __builtin_amdgcn_exp2f(m_used - rank_m_lane) +
+                  l_corr * __builtin_amdgcn_exp2f(m_corr - rank_m_lane);
+  }
+
+  // ================= 16-bit rows of the tail (the fetched rows went first) =================
+  for (int q = first_tail_q; q < n_sel_blk + n_tail_blk; q += 4) f16_block(q);
+
   // ================= wave epilogue =================
-  const float l_row = sum_over_groups(l_part);  // row n16
+  const float l_row = sum_over_groups(l_part + l16);  // row n16
   float fin_m = m_used, fin_l = l_row;          // final (m, l) of row (n16 & 7) or n16
   float f_self = 1.0f, f_other = 0.0f;          // weights of rows n16 and n16 ^ 8
   if constexpr (PACK == 2) {
