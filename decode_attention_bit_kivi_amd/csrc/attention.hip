@@ -514,16 +514,21 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
     lds_fence();
   };
+  __builtin_amdgcn_s_setprio(3);  // a chain of latencies: issue it ahead of the other waves' loops
   for (int q = wave; q < n_sel_blk; q += 4) f16_block(q);
 
-  // Software pipeline over this wave's blocks (jj = wave + 4 i, i = 0 .. nw - 1): iteration i
+  // Software pipeline over this wave's blocks (jj = vw + 4 i, i = 0 .. nw - 1): iteration i
   // issues block i + 1's score MFMAs before finishing block i (softmax, values), so the matrix
   // cores work on one block while the VALU finishes the other; key codes load two blocks ahead,
   // value data one.  A block's constant is read right after the prepass that covers it (the next
   // prepass rewrites the LDS slots).
   if constexpr (!F16) {
-    const int nw = wave < nb ? (nb - wave + 3) / 4 : 0;
-    auto blk = [&](int i) { return wave + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
+    // low-bit blocks jj = vw + 4 i: the waves that took one 16-bit block more than the others
+    // take the last places of the rotation, which get one low-bit block fewer when the split's
+    // block count is not a multiple of 4
+    const int vw = (wave - n_sel_blk) & 3;
+    const int nw = vw < nb ? (nb - vw + 3) / 4 : 0;
+    auto blk = [&](int i) { return vw + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
     if (nw > 0) {
       KData k0 = load_k(blk(0)), k1 = load_k(blk(1));
       VData v0 = load_v(blk(0)), v1;
