@@ -296,22 +296,31 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int pl = 0; pl < KB; ++pl) acc[tau][pl] = zero4();
+    // chunks w and w + 1 expand together (one 64-bit shift per pair of words); the products
+    // accumulate in the order w, tau as for one chunk at a time
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const uint4 ksv = sm.kscale[wave][step & 15][g][w];
-      const uint32_t mag[4] = {ksv.x, ksv.y, ksv.z, ksv.w};
+    for (int w = 0; w < W; w += 2) {
+      const uint4 ka = sm.kscale[wave][step & 15][g][w], kb = sm.kscale[wave][step & 15][g][w + 1];
+      const uint32_t ma[4] = {ka.x, ka.y, ka.z, ka.w}, mb[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
+      for (int pl = 0; pl < KB; ++pl) {
+        Frag A0[2], A1[2];  // [tau]: chunk w, chunk w + 1
 #pragma unroll
-        for (int pl = 0; pl < KB; ++pl) {
-          Frag A;
+        for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(kd.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
-          if constexpr (PACK == 2)
-            acc[0][pl] = mma(A, tau == 0 ? B0[w] : B1[w], acc[0][pl]);
-          else
-            acc[tau][pl] = mma(A, B0[w], acc[tau][pl]);
-        }
+          for (int d = 0; d < 4; ++d)
+            signed_pairs2(kd.kw[tau][pl].w[w], kd.kw[tau][pl].w[w + 1], 15 - 4 * g - d, ma[d], mb[d], A0[tau].u[d],
+                          A1[tau].u[d]);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau) {
+            const Frag& A = h2 == 0 ? A0[tau] : A1[tau];
+            if constexpr (PACK == 2)
+              acc[0][pl] = mma(A, tau == 0 ? B0[w + h2] : B1[w + h2], acc[0][pl]);
+            else
+              acc[tau][pl] = mma(A, B0[w + h2], acc[tau][pl]);
+          }
       }
     }
   };
@@ -396,13 +405,15 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     // values
     const uint32_t vmag[4] = {bd.vs_lo.x, bd.vs_lo.y, bd.vs_hi.x, bd.vs_hi.y};
 #pragma unroll
-    for (int ct = 0; ct < CPL; ++ct) {
+    for (int ct = 0; ct < CPL; ct += 2) {
 #pragma unroll
       for (int pl = 0; pl < VB; ++pl) {
-        Frag Bv;
+        Frag Bv0, Bv1;  // channel tiles ct and ct + 1, one 64-bit shift per pair of words
 #pragma unroll
-        for (int d = 0; d < 4; ++d) Bv.u[d] = signed_pair(bd.vw[pl].w[ct], shv[d], vmag[d]);
-        Oacc[ct] = mma(pl == 0 ? Ap : Ap2, Bv, Oacc[ct]);
+        for (int d = 0; d < 4; ++d)
+          signed_pairs2(bd.vw[pl].w[ct], bd.vw[pl].w[ct + 1], shv[d], vmag[d], vmag[d], Bv0.u[d], Bv1.u[d]);
+        Oacc[ct] = mma(pl == 0 ? Ap : Ap2, Bv0, Oacc[ct]);
+        Oacc[ct + 1] = mma(pl == 0 ? Ap : Ap2, Bv1, Oacc[ct + 1]);
       }
     }
     // columns n16 >= 2 Wg carry another row's (finite) metadata: their outputs are never read
