@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   float l_part = 0.0f;     // this lane's share of that row's sum of exponentials (low-bit positions)
   float l16 = 0.0f;        // the same over the 16-bit rows (fetched and tail), kept apart for the ranking
   // ranking: the C' terms of kappa positions (masked out of the attention), kept relative to
-  // their own running max m_corr (row-uniform) so that the attention's arithmetic is untouched
+  // their own running max m_corr (per lane) so that the attention's arithmetic is untouched
   float m_corr = kEmpty, l_corr = 0.0f;
   f32x4 Oacc[CPL];
 #pragma unroll
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
         float cm = xc[0];
 #pragma unroll
         for (int i = 1; i < NX; ++i) cm = fmaxf(cm, xc[i]);
-        const float mn = fmaxf(m_corr, max_over_groups(cm));
+        const float mn = fmaxf(m_corr, cm);
         l_corr *= __builtin_amdgcn_exp2f(m_corr - mn);
         m_corr = mn;
 #pragma unroll
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
   // ranking statistics over C' = the low-bit positions processed so far, kappa positions included
   float rank_m_lane = m_used, rank_l_lane = l_part;
   if constexpr (RANK) {
-    rank_m_lane = fmaxf(m_used, m_corr);
+    rank_m_lane = max_over_groups(fmaxf(m_used, m_corr));  // the same for the four lanes of a row
     rank_l_lane = l_part * __builtin_amdgcn_exp2f(m_used - rank_m_lane) +
                   l_corr * __builtin_amdgcn_exp2f(m_corr - rank_m_lane);
   }

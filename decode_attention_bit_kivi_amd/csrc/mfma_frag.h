@@ -11,11 +11,11 @@
 // around the group's midpoint, so the operand value is +-s: the code bit
 // becomes the float16 sign bit of s (a set bit gives -s, so the operand is
 // -(2b - 1) s and the kernels scale its products by -1/2).  The packed layout keeps the two
-// elements of an operand dword 16 bit positions apart, so one shift moves
-// both bits into the two sign positions and one and-or attaches the
-// magnitudes -- two VALU operations per two elements, or three per four when
-// one 64-bit shift serves two words -- and every product with a float16
-// query element is exact in the float32 accumulator.
+// elements of an operand dword 16 bit positions apart, so a shift moves both
+// bits into the two sign positions and one and-or attaches the magnitudes;
+// one 64-bit shift serves two code words, so the expansion costs three VALU
+// operations per four elements, and every product with a float16 query
+// element is exact in the float32 accumulator.
 #pragma once
 
 #include "common.h"
@@ -37,15 +37,10 @@ __device__ __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// Elements whose bits sit at positions p and p + 16 of `word`, with
-// shift = 15 - p: returns the float16 pair (+-mag.lo, +-mag.hi).
-__device__ __forceinline__ uint32_t signed_pair(uint32_t word, int shift, uint32_t mag) {
-  return ((word << shift) & 0x80008000u) | mag;
-}
-
-// Two words expanded with one 64-bit shift: shifting the pair (w1:w0) left by shift <= 15 moves
-// bits p and p + 16 of each word to bits 15 and 31 of its own half; what w0 pushes into the high
-// half lands below bit `shift`, where the mask drops it.  Three VALU operations per two pairs.
+// Elements whose bits sit at positions p and p + 16 of w0 and of w1, with shift = 15 - p: the
+// float16 pairs (+-mag0.lo, +-mag0.hi) and (+-mag1.lo, +-mag1.hi).  Shifting the pair (w1:w0) left
+// by shift <= 15 moves bits p and p + 16 of each word to bits 15 and 31 of its own half; what w0
+// pushes into the high half lands below bit `shift`, where the mask drops it.
 __device__ __forceinline__ void signed_pairs2(uint32_t w0, uint32_t w1, int shift, uint32_t mag0, uint32_t mag1,
                                               uint32_t& out0, uint32_t& out1) {
   const uint64_t x = ((((uint64_t)w1) << 32) | (uint64_t)w0) << shift;

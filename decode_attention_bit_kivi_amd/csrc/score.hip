@@ -142,21 +142,31 @@ __global__ __launch_bounds__(256, 2) void score_kernel(const _Float16* __restric
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int pl = 0; pl < BITS; ++pl) acc[tau][pl] = zero4();
+    // chunks w and w + 1 expand together (one 64-bit shift per pair of words); the products
+    // accumulate in the order w, tau as for one chunk at a time
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const uint32_t* mag = reinterpret_cast<const uint32_t*>(&cur.ks[w]);
+    for (int w = 0; w < W; w += 2) {
+      const uint32_t* ma = reinterpret_cast<const uint32_t*>(&cur.ks[w]);
+      const uint32_t* mb = reinterpret_cast<const uint32_t*>(&cur.ks[w + 1]);
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
+      for (int pl = 0; pl < BITS; ++pl) {
+        Frag A0[2], A1[2];  // [tau]: chunk w, chunk w + 1
 #pragma unroll
-        for (int pl = 0; pl < BITS; ++pl) {
-          Frag A;
+        for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int d = 0; d < 4; ++d) A.u[d] = signed_pair(cur.kw[tau][pl].w[w], 15 - 4 * g - d, mag[d]);
-          if constexpr (PACK == 2)
-            acc[0][pl] = mma(A, tau == 0 ? B0[w] : B1[w], acc[0][pl]);
-          else
-            acc[tau][pl] = mma(A, B0[w], acc[tau][pl]);
-        }
+          for (int d = 0; d < 4; ++d)
+            signed_pairs2(cur.kw[tau][pl].w[w], cur.kw[tau][pl].w[w + 1], 15 - 4 * g - d, ma[d], mb[d], A0[tau].u[d],
+                          A1[tau].u[d]);
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau) {
+            const Frag& A = h2 == 0 ? A0[tau] : A1[tau];
+            if constexpr (PACK == 2)
+              acc[0][pl] = mma(A, tau == 0 ? B0[w + h2] : B1[w + h2], acc[0][pl]);
+            else
+              acc[tau][pl] = mma(A, B0[w + h2], acc[tau][pl]);
+          }
       }
     }
     const float c0 = cst[wave][step & 15][head];
