@@ -84,9 +84,9 @@ def parse():
                     help="fetch only the rows of the new top-k not already resident (the step time of "
                          "fetching every row is reported beside it)")
     ap.add_argument("--top-k", type=int, default=0, help="override the workload's top-k (latency-vs-k sweeps)")
-    ap.add_argument("--sync-every", type=int, default=2, choices=(1, 2),
-                    help="steps per cross-stream synchronisation of the pipeline (2 at most with 4 layers "
-                         "in turn: the gathers of a pair of steps must land before the pair's layers return)")
+    ap.add_argument("--sync-every", type=int, default=2, choices=(1, 2, 4),
+                    help="steps per cross-stream synchronisation of the pipeline (at most half the layers "
+                         "in turn: the gathers of a group of steps must land before the group's layers return)")
     ap.add_argument("--rank", choices=("lowbit", "mixed"), default="lowbit",
                     help="lowbit: rank against C'; mixed: by the attention row itself (fetched rows and tail in)")
     ap.add_argument("--compute-reserve", type=int, default=32,
@@ -372,6 +372,7 @@ def main():
     quant_us = e0.elapsed_time(e1) * 1e3 / nq
 
     layers = args.copies or max(3, cfg.n_layers, math.ceil(512e6 / cache0.nbytes()))
+    layers = max(layers, 2 * args.sync_every)  # a group's gathers land while the next group computes
     layers = -(-layers // args.sync_every) * args.sync_every  # whole synchronisation groups
     caches = [cache0] + [quantize_pack(k16, v16, cfg.bits) for _ in range(layers - 1)]
     torch.cuda.synchronize()
