@@ -1,0 +1,69 @@
+"""Host checks of bench.py's bookkeeping (no GPU): the HBM traffic record built from
+rocprofv3 counter runs, the algorithmic byte count, and the one-GPU refusal."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from workloads import get_config  # noqa: E402
+
+SPLIT = "void specache::(anonymous namespace)::attn_split_kernel<128, 1, 1, 2, true, false>(specache::AttnArgs, int)"
+KEYS = "void specache::(anonymous namespace)::rank_keys_kernel<4>(float const*)"
+SELECT = "void specache::(anonymous namespace)::rank_select_resident_kernel<128>(float const*)"
+
+
+def _write(root, run, rows):
+    d = os.path.join(root, run, "host", "123")
+    os.makedirs(d)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Queue_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writerows(rows)
+
+
+def test_traffic_record_scales_counters_and_keeps_only_fused_step_dispatches(tmp_path, monkeypatch):
+    root = str(tmp_path)
+    # the plain 1 GiB copy reads as 512 MiB of FETCH_SIZE and 1 GiB of WRITE_SIZE (KiB units)
+    _write(root, "pmc_copy_fetch", [[1, 1, "fill", "FETCH_SIZE", 0], [2, 1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288]])
+    _write(root, "pmc_copy_write", [[1, 1, "fill", "WRITE_SIZE", 1048576],
+                                    [2, 1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576]])
+    for counter, run, vals in (("FETCH_SIZE", "pmc_fetch", (1000, 100, 10)), ("WRITE_SIZE", "pmc_write", (500, 50, 5))):
+        rows, did = [], 1
+        for _ in range(3):
+            for name, v in ((SPLIT, vals[0]), (KEYS, vals[1]), (SELECT, vals[2])):
+                rows.append([did, 2, name, counter, v])
+                did += 1
+            rows.append([did, 2, KEYS, counter, 10 ** 6])  # a score_topk's rank_keys: not part of the step
+            did += 1
+        _write(root, run, rows)
+    out = tmp_path / "record.json"
+    monkeypatch.setattr(bench, "TRAFFIC_RECORD", str(out))
+    bench.write_traffic_record(root)
+    rec = json.loads(out.read_text())
+    assert rec["calibration"]["fetch_scale"] == 2.0 and rec["calibration"]["write_scale"] == 1.0
+    per = rec["per_kernel"]
+    assert per["rank_keys_kernel"]["dispatches"] == 3
+    want = 1024 * (2 * (1000 + 100 + 10) + (500 + 50 + 5))
+    assert rec["traffic_bytes_per_launch"] == want
+    assert rec["sources_sha256"] == bench.step_sources_hash()
+    assert rec["algorithmic_bytes_per_launch"] == bench.algorithmic_bytes_step(get_config("mistral32k"))
+
+
+def test_algorithmic_bytes_of_the_32k_step():
+    cfg = get_config("mistral32k")
+    slices, N, k = 8 * 8, 32768, 328
+    want = slices * (64 * N + 516 * k + 4 * k) + 2 * (8 * 32 * 2) * 128 * 2
+    assert bench.algorithmic_bytes_step(cfg) == want == 145395712
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout
