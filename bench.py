@@ -536,6 +536,15 @@ def main():
 
     serial_us = compute_loop(serial_step)
 
+    # the host link's contiguous rate: one pinned-host-to-device copy of as many bytes as the
+    # gather of every top-k row moves (the pages found scattered row copies several times slower
+    # than one contiguous copy)
+    n_gather = 2 * B * Hkv * k * D * 2
+    h_blk = torch.empty(n_gather, dtype=torch.uint8).pin_memory()
+    d_blk = torch.empty(n_gather, dtype=torch.uint8, device=dev)
+    h2d_us = compute_loop(lambda i: d_blk.copy_(h_blk, non_blocking=True))
+    del h_blk, d_blk
+
     step_bytes = algorithmic_bytes_step(cfg)
     step_avg_s = float(step_us.mean()) * 1e-6
     achieved = step_bytes / step_avg_s / 1e9
@@ -607,8 +616,13 @@ def main():
             "step_speedup_vs_fp16_attention": fp16_us / (ms_step * 1e3),
             "serial_fetch_step_us": serial_us,
             "step_speedup_vs_serial_fetch": serial_us / (ms_step * 1e3),
+            "contiguous_h2d_us": h2d_us,
+            "contiguous_h2d_GBs": n_gather / (h2d_us * 1e-6) / 1e9,
+            "gather_full_fetch_vs_contiguous_h2d": float(np.median(runs["full"][2])) / h2d_us
+            if "full" in runs else None,
             "what": "fp16: attention over the whole 16-bit cache in HBM (decode_attn_fp16); serial: rank "
-                    "with the real token against C', fetch its top-k without overlap, attend",
+                    "with the real token against C', fetch its top-k without overlap, attend; contiguous "
+                    "h2d: one pinned-host-to-device copy of the bytes of every top-k row",
         },
     }
     if not args.no_cpu_baseline:
