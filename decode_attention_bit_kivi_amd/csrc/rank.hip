@@ -37,7 +37,7 @@ namespace {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kKeyThreads = 256;
-constexpr int kKeyChunk = kKeyThreads * 16;    // positions per rank_keys workgroup
+constexpr int kKeyChunk = kKeyThreads * 8;     // positions per rank_keys workgroup
 constexpr int kBins = 2048;
 constexpr float kBinSpan = 32.0f;              // r window of the coarse bins, below log G
 constexpr float kBinScale = kBins / kBinSpan;  // bins per unit of r (a power of two: exact)
@@ -117,9 +117,11 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
   // keeps these two loads ahead of the logits' loads (the inputs are not restrict-qualified, so
   // that the compiler cannot treat the loads as invariant and move them past such points)
   asm volatile("" ::: "memory");
-  // Each thread: 4 runs of 4 consecutive positions (a float4 per head), NB runs in flight (all
-  // four for up to 4 heads), with clamped addresses.
-  constexpr int NB = GM <= 4 ? 4 : 2;
+  // Each thread: kRuns runs of 4 consecutive positions (a float4 per head), NB runs in flight
+  // (all of them for up to 4 heads), with clamped addresses.  Small chunks (two runs a thread)
+  // keep more workgroups, and so more of the logits' loads, in flight at once.
+  constexpr int kRuns = kKeyChunk / (4 * kKeyThreads);
+  constexpr int NB = GM <= 4 ? kRuns : (kRuns < 2 ? kRuns : 2);
   const float* lg = logits + slice * G * N;
   float4 x[NB][GM];
   auto load = [&](int rr, float4 (&dst)[GM]) {
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
   __syncthreads();
   uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
+  for (int rr = 0; rr < kRuns; ++rr) {
     const int64_t p = c0 + 4 * (t + rr * kKeyThreads);
     if (p < N) {  // N is a multiple of 32: the whole float4 is in range
       float r[4];
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
         ++cur_cnt;
       }
     }
-    if (rr + NB < 4) load(rr + NB, x[rr % NB]);  // the slot just consumed takes a later run
+    if (rr + NB < kRuns) load(rr + NB, x[rr % NB]);  // the slot just consumed takes a later run
   }
   if (cur_cnt) atomicAdd(&hist[cur_bin], cur_cnt);
   __syncthreads();
