@@ -518,21 +518,30 @@ def test_fused_step_next_selection_may_alias_current(gpu):
     _assert_topk(_np(want_next), r_ref, cfg.top_k, slices)
 
 
-@pytest.mark.parametrize("name,mixed", [("mistral32k", False), ("long128k", False), ("mistral32k", True)])
-def test_fused_step_full_size_sampled(gpu, name, mixed):
-    """The fused step at full size, in the benchmark's launch configuration: score_topk
-    seeds the selection, the step gathers its rows from pinned host memory and returns the
-    next selection (ranked against C', or by the mixed-cache attention row)."""
+@pytest.mark.parametrize("name,mixed,stream", [("mistral32k", False, "device"), ("long128k", False, "device"),
+                                               ("mistral32k", True, "device"), ("mistral32k", False, "bench")])
+def test_fused_step_full_size_sampled(gpu, name, mixed, stream):
+    """The fused step at full size: score_topk seeds the selection, the step gathers its rows
+    from pinned host memory and returns the next selection (ranked against C', or by the
+    mixed-cache attention row).  stream = "bench": on the compute stream bench.py times (every
+    compute unit but 32, so the split plan is the benchmark's); "device": the whole device."""
     cfg = get_config(name)
     sl = _sampled(cfg, 3)
     K, V, Q, _, _, _ = generate_all(cfg, slices=sl)
-    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
-    q = _dev(Q)
+    cs = ComputeStream(32) if stream == "bench" else None
+    comp = cs.torch if cs else torch.cuda.current_stream()
+    comp.wait_stream(torch.cuda.current_stream())
     hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
-    idx = score_topk(q, cache, cfg.top_k)
-    ks, vs = gather_fp16(idx, hk, hv)
-    out, nxt = decode_step(q, cache, cfg.top_k, rank_mixed=mixed, idx=idx, k_sel=ks, v_sel=vs)
+    with torch.cuda.stream(comp):
+        cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+        q = _dev(Q)
+        idx = score_topk(q, cache, cfg.top_k)
+        ks, vs = gather_fp16(idx, hk, hv)
+        out, nxt = decode_step(q, cache, cfg.top_k, rank_mixed=mixed, idx=idx, k_sel=ks, v_sel=vs)
+        comp.synchronize()
     idx_np, out, nxt = _np(idx), _np(out), _np(nxt)
+    if cs:
+        cs.close()
     G = cfg.gqa
     for (b, h) in sl:
         q1 = Q[b:b + 1, h * G:(h + 1) * G]
