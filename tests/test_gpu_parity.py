@@ -188,6 +188,26 @@ def test_quantize_adversarial_values(gpu, bits):
     _assert_quantize_exact(cache, ref, bits)
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered")  # the oracle's dequantized 0 * inf
+@pytest.mark.parametrize("bits", [1, 2])
+def test_quantize_infinite_scale_groups(gpu, bits):
+    """Groups holding +inf have an infinite scale: the kernels then decide the codes by the
+    correctly rounded division instead of the division-free comparisons (every code 0, the
+    zero-point +inf), as the oracle's division does; the other groups are unaffected."""
+    rng = np.random.default_rng(91 + bits)
+    B, H, N, D = 1, 2, 128, 64
+    K = rng.standard_normal((B, H, N, D)).astype(np.float16)
+    V = rng.standard_normal((B, H, N, D)).astype(np.float16)
+    K[0, 0, 5, 3] = np.float16(np.inf)      # key group (tokens 0-31, channel 3)
+    K[0, 1, 70, 10] = np.float16(np.inf)
+    V[0, 0, 9, 40] = np.float16(np.inf)     # value group (token 9, channels 32-63)
+    V[0, 1, 100, 0] = np.float16(np.inf)
+    cache = quantize_pack(_dev(K), _dev(V), bits)
+    torch.cuda.synchronize()
+    ref, _, _ = _reference_cache(K, V, bits)
+    _assert_quantize_exact(cache, ref, bits)
+
+
 @pytest.mark.parametrize("name", ["mistral32k", "long128k"])
 def test_quantize_full_size_sampled(gpu, name):
     cfg = get_config(name)
