@@ -544,6 +544,17 @@ def main():
     d_blk = torch.empty(n_gather, dtype=torch.uint8, device=dev)
     h2d_us = compute_loop(lambda i: d_blk.copy_(h_blk, non_blocking=True))
     del h_blk, d_blk
+    # offloading the whole layer instead (the pages' full-offload comparison): the layer's 16-bit
+    # K and V copied from pinned host memory into HBM
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k16.copy_(hk, non_blocking=True)
+    e0.record(comp)
+    for _ in range(2):
+        k16.copy_(hk, non_blocking=True)
+        v16.copy_(hv, non_blocking=True)
+    e1.record(comp)
+    torch.cuda.synchronize()
+    full_layer_us = e0.elapsed_time(e1) * 1e3 / 2
 
     step_bytes = algorithmic_bytes_step(cfg)
     step_avg_s = float(step_us.mean()) * 1e-6
@@ -592,6 +603,8 @@ def main():
             "step_full_fetch": runs["full"][0] * 1e3,
             "decode_step_in_pipeline": float(np.median(step_us)),
             "decode_step_in_pipeline_mean": float(step_us.mean()),
+            "decode_step_in_pipeline_p10": float(np.percentile(step_us, 10)),
+            "decode_step_in_pipeline_p90": float(np.percentile(step_us, 90)),
             "gather_fp16_side_stream": float(np.median(gather_us)),
             "gather_full_fetch": float(np.median(runs["full"][2])),
             "step_compute_only_fused": fused_us,
@@ -617,12 +630,15 @@ def main():
             "serial_fetch_step_us": serial_us,
             "step_speedup_vs_serial_fetch": serial_us / (ms_step * 1e3),
             "contiguous_h2d_us": h2d_us,
+            "full_layer_h2d_us": full_layer_us,
+            "full_layer_h2d_vs_step": full_layer_us / (ms_step * 1e3),
             "contiguous_h2d_GBs": n_gather / (h2d_us * 1e-6) / 1e9,
             "gather_full_fetch_vs_contiguous_h2d": float(np.median(runs["full"][2])) / h2d_us
             if "full" in runs else None,
             "what": "fp16: attention over the whole 16-bit cache in HBM (decode_attn_fp16); serial: rank "
                     "with the real token against C', fetch its top-k without overlap, attend; contiguous "
-                    "h2d: one pinned-host-to-device copy of the bytes of every top-k row",
+                    "h2d: one pinned-host-to-device copy of the bytes of every top-k row; full layer h2d: "
+                    "the layer's whole 16-bit K and V copied from pinned host memory",
         },
     }
     if not args.no_cpu_baseline:
