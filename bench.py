@@ -646,6 +646,16 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg, K, V, Q, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
+    # torch's pinned-memory allocator records an event on every stream a pinned block was
+    # copied on when the block is freed (hk and hv were, by the full-layer copy): free them
+    # while the library's streams still exist, then destroy the streams
+    del hk, hv
+    torch.cuda.synchronize()
+    torch.cuda.set_stream(torch.cuda.default_stream())
+    if args.compute_stream == "exclusive":
+        compute_stream.close()
+    gather_stream.close()
+
 
 if __name__ == "__main__":
     main()
