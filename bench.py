@@ -153,7 +153,8 @@ def _counter_rows(root: str, run: str, counter: str):
 def write_traffic_record(root: str, workload: str = "mistral32k"):
     """HBM bytes per decode_step call from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
     scaled by what the same counter reads for the plain 1 GiB copy.  A call is the fused-step
-    split dispatch and the rank_keys and rank_select dispatches that follow it on its queue."""
+    split dispatch and the selection dispatches that follow it on its queue (rank_keys, for
+    slices that one selection workgroup cannot hold, then rank_select)."""
     import statistics
     cal = {}
     for counter, run in (("FETCH_SIZE", "pmc_copy_fetch"), ("WRITE_SIZE", "pmc_copy_write")):
@@ -189,8 +190,10 @@ def write_traffic_record(root: str, workload: str = "mistral32k"):
     from workloads import get_config
     rec = {
         "workload": workload,
-        "what": "HBM bytes per specache_decode_step call: the three kernels it launches, each dispatch taken "
-                "right after a fused-step split dispatch on its queue; rocprofv3 FETCH_SIZE and WRITE_SIZE "
+        "what": "HBM bytes per specache_decode_step call: the kernels it launches (the split, then the "
+                "selection: rank_select alone, or rank_keys and rank_select for slices longer than one "
+                "selection workgroup holds), each dispatch taken right after a fused-step split dispatch on "
+                "its queue; rocprofv3 FETCH_SIZE and WRITE_SIZE "
                 "per dispatch, scaled by the same counters' reading for a plain 1 GiB device copy",
         "commands": TRAFFIC_COMMANDS,
         "calibration": {"copy_bytes_read": n, "copy_bytes_written": n,
@@ -589,7 +592,9 @@ def main():
             if args.compute_stream == "exclusive" else 0,
         },
         "roofline": {
-            "kernel": "decode_step (attn_split_kernel with ranking + rank_keys + rank_select + attn_merge)",
+            "kernel": "decode_step (attn_split_kernel with ranking + " + (
+                "rank_select forming r(p) and merging the splits)" if N <= 32768 and Hq // Hkv <= 4 else
+                "rank_keys + rank_select merging the splits)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

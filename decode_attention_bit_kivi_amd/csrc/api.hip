@@ -229,7 +229,8 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
                               static_cast<const uint32_t*>(cache->k_codes), static_cast<const _Float16*>(cache->k_meta),
                               sm_scale, logits, part_m, part_l, hist, s);
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
-  e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, hist, idx_out, nullptr, s);
+  e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, rank_key_out != nullptr, hist, idx_out,
+                         nullptr, s);
   return hip_status(e);
 }
 
@@ -449,8 +450,8 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
   // the split merge runs inside the selection's launch, on the compute units it leaves idle
   if (launch_attn_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
   const MergeJob merge{a.part_ml, a.part_acc, plan.S, (int64_t)d.B * d.Hq * n_tokens, a.out16};
-  return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys, a.rank_hist,
-                                       idx_next_out, &merge, s));
+  return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys,
+                                       rank_key_out != nullptr, a.rank_hist, idx_next_out, &merge, s));
 }
 
 namespace {

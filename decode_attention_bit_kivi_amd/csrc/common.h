@@ -137,10 +137,12 @@ struct MergeJob {
 };
 
 // part_m / part_l: [slices][G][S] per-split (max, sum 2^(x - max)) of the logits, log2 units.
-// merge: null, or the attention merge to run alongside the selection.
+// merge: null, or the attention merge to run alongside the selection.  keys: where r(p) goes
+// (the caller's output when keys_wanted, else workspace a slice too large for one workgroup's
+// registers uses between its two kernels).
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
-                              const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
-                              const MergeJob* merge, hipStream_t s);
+                              const float* part_l, int k, float* keys, bool keys_wanted, uint32_t* hist,
+                              int32_t* idx_out, const MergeJob* merge, hipStream_t s);
 
 // skip_negative: rows with a negative index are left untouched (resident-set reuse).
 hipError_t launch_gather(const Dims& d, const int32_t* idx, int k, const _Float16* k_src,

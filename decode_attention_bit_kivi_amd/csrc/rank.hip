@@ -93,6 +93,49 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + x - v;
 }
 
+// Merge of two (max, sum 2^(x - max)) pairs of one head, log2 units.
+__device__ __forceinline__ void merge_stat(float& M, float& L, float m, float l) {
+  const float mn = fmaxf(M, m);
+  L = (M == -INFINITY ? 0.0f : L * exp2f(M - mn)) + (m == -INFINITY ? 0.0f : l * exp2f(m - mn));
+  M = mn;
+}
+
+// One head's log2-sum-exp2 from its S split statistics, read by TPH lanes of one wave (lane j
+// takes splits j, j + TPH, ...; its first pair, m_first / l_first, already loaded), merged across
+// the lanes.  Every lane returns the head's value.
+template <int TPH>
+__device__ __forceinline__ float head_lse2(const float* pm, const float* pl, int S, int j, float m_first,
+                                           float l_first) {
+  float M = -INFINITY, L = 0.0f;
+  for (int s = j; s < S; s += TPH) merge_stat(M, L, s == j ? m_first : pm[s], s == j ? l_first : pl[s]);
+#pragma unroll
+  for (int off = 1; off < TPH; off <<= 1) merge_stat(M, L, __shfl_xor(M, off), __shfl_xor(L, off));
+  return M + log2f(L);
+}
+
+// r of the position held in component e of x[g] (head g's logit, log2 units):
+// log sum_g exp(s_g - LSE_g), in natural-log units.
+template <int GM>
+__device__ __forceinline__ float rank_of(const float4 (&x)[GM], int e, const float* lse2, int G) {
+  float lp[GM];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+    if (g < G) {
+      const float4 v4 = x[g];
+      const float v = e == 0 ? v4.x : (e == 1 ? v4.y : (e == 2 ? v4.z : v4.w));
+      lp[g] = v - lse2[g];  // log2 of the head's probability (the logits are in log2 units)
+      mx = fmaxf(mx, lp[g]);
+    }
+  float sum = 0.0f;
+#pragma unroll
+  for (int g = 0; g < GM; ++g)
+    if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
+  // v_log_f32 is log2; adding +0 turns a -0 into +0, so that comparing the floats and comparing
+  // their order-preserving keys agree
+  return (mx + __builtin_amdgcn_logf(sum)) * kLn2 + 0.0f;
+}
+
 // ---------------------------------------------------------------- rank_keys
 
 template <int GM>  // GM >= G: the heads' logits of a run are held in registers
@@ -135,26 +178,10 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
 #pragma unroll
   for (int rr = 0; rr < NB; ++rr) load(rr, x[rr]);
   {
-    const int g = hg, j = hj;
-    float M = -INFINITY, L = 0.0f;
-    if (g < G) {
-      const float* pm = part_m + (slice * G + g) * S;
-      const float* pl = part_l + (slice * G + g) * S;
-      for (int s = j; s < S; s += TPH) {
-        const float m = s == j ? m_first : pm[s], l = s == j ? l_first : pl[s];
-        const float mn = fmaxf(M, m);
-        L = (M == -INFINITY ? 0.0f : L * exp2f(M - mn)) + (m == -INFINITY ? 0.0f : l * exp2f(m - mn));
-        M = mn;
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < TPH; off <<= 1) {
-      const float m = __shfl_xor(M, off), l = __shfl_xor(L, off);
-      const float mn = fmaxf(M, m);
-      L = (M == -INFINITY ? 0.0f : L * exp2f(M - mn)) + (m == -INFINITY ? 0.0f : l * exp2f(m - mn));
-      M = mn;
-    }
-    if (g < G && j == 0) lse2[g] = M + log2f(L);
+    const int g = hg < G ? hg : 0;  // the lanes of heads past G merge head 0 again, unused
+    const float l2 = head_lse2<TPH>(part_m + (slice * G + g) * S, part_l + (slice * G + g) * S, S, hj, m_first,
+                                    l_first);
+    if (hg < G && hj == 0) lse2[hg] = l2;
   }
   for (int i = t; i < kBins; i += kKeyThreads) hist[i] = 0u;
   __syncthreads();
@@ -165,25 +192,7 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
     if (p < N) {  // N is a multiple of 32: the whole float4 is in range
       float r[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float lp[GM];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int g = 0; g < GM; ++g)
-          if (g < G) {
-            const float4 v4 = x[rr % NB][g];
-            const float v = e == 0 ? v4.x : (e == 1 ? v4.y : (e == 2 ? v4.z : v4.w));
-            lp[g] = v - lse2[g];  // log2 of the head's probability (the logits are in log2 units)
-            mx = fmaxf(mx, lp[g]);
-          }
-        float sum = 0.0f;
-#pragma unroll
-        for (int g = 0; g < GM; ++g)
-          if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
-        // v_log_f32 is log2; adding +0 turns a -0 into +0, so that comparing the floats and
-        // comparing their order-preserving keys agree
-        r[e] = (mx + __builtin_amdgcn_logf(sum)) * kLn2 + 0.0f;
-      }
+      for (int e = 0; e < 4; ++e) r[e] = rank_of<GM>(x[rr % NB], e, lse2, G);
       *reinterpret_cast<float4*>(rkey + slice * N + p) = make_float4(r[0], r[1], r[2], r[3]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -506,12 +515,27 @@ struct ResidentSmem {
   uint32_t cand[kCand];
 };
 
-template <int D>
+// Inputs of the resident selection when it forms r(p) itself (FUSED): the rank row's logits and
+// the split statistics, as rank_keys takes them, for G <= kFusedG heads.  keys_out, if not null,
+// receives r as rank_keys would write it.
+struct FusedRank {
+  const float* logits;  // [slices][G][N], log2 units
+  const float* part_m;  // [slices][G][S]
+  const float* part_l;
+  int G, S;
+  float* keys_out;
+};
+
+constexpr int kFusedG = 4;   // heads per slice the fused form holds in registers
+constexpr int kFusedNB = 3;  // float4 runs (of every head) a thread has in flight
+
+template <int D, bool FUSED>
 __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const float* __restrict__ rkey,
                                                                            const uint32_t* __restrict__ ghist,
                                                                            int64_t N, int k, float r_lo,
                                                                            int32_t* __restrict__ idx_out,
-                                                                           unsigned n_sel, MergeJob mj) {
+                                                                           unsigned n_sel, MergeJob mj,
+                                                                           FusedRank fr) {
   if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
     const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
     if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
@@ -520,38 +544,101 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
   __shared__ ResidentSmem sm;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t slice = blockIdx.x;
-  const float* ky = rkey + slice * N;
-  const uint32_t* gh = ghist + slice * kBins;
-  // the histogram's loads first and then the keys', all unconditional (clamped addresses), so
-  // that waiting for the histogram leaves the keys in flight; the empty statement with a memory
-  // clobber keeps every load above the first barrier
-  const uint32_t h0 = gh[t], h1 = gh[t + kSelThreads];
-  float4 f[kSweepU];
-#pragma unroll
-  for (int u = 0; u < kSweepU; ++u) {
-    const int64_t p = 4 * ((int64_t)t + u * kSelThreads);
-    f[u] = *reinterpret_cast<const float4*>(ky + (p < N ? p : 0));
-  }
-  asm volatile("" ::: "memory");
-  sm.hist[t] = h0;
-  sm.hist[t + kSelThreads] = h1;
-  // v[4u + e]: position 4 * (t + u * kSelThreads) + e, -inf past N (N is a multiple of 32)
-  float v[4 * kSweepU];
-#pragma unroll
-  for (int u = 0; u < kSweepU; ++u) {
-    const bool in = 4 * ((int64_t)t + u * kSelThreads) < N;
-    v[4 * u] = in ? f[u].x : -INFINITY;
-    v[4 * u + 1] = in ? f[u].y : -INFINITY;
-    v[4 * u + 2] = in ? f[u].z : -INFINITY;
-    v[4 * u + 3] = in ? f[u].w : -INFINITY;
-  }
   // N <= kResidentN: positions fit 32 bits; a float4 is wholly in range or wholly past N
   auto in_range = [&](int u) { return 4 * (t + u * kSelThreads) < (int)N; };
-  if (t == 0) {
-    sm.n_cand = 0u;
-    sm.res[3] = 0u;
+  // v[4u + e]: position 4 * (t + u * kSelThreads) + e, -inf past N (N is a multiple of 32)
+  float v[4 * kSweepU];
+  if constexpr (FUSED) {
+    // r(p) formed here (the arithmetic of rank_keys, shared with it): each head's log-sum-exp
+    // from the split statistics by one wave per head, then the float4 runs of the G heads'
+    // logits, kFusedNB runs in flight (issued before the statistics, clamped addresses), and the
+    // coarse histogram with LDS atomics
+    __shared__ float lse2[kFusedG];
+    const int G = fr.G, S = fr.S;
+    const float* lg = fr.logits + slice * G * N;
+    float4 x[kFusedNB][kFusedG];
+    auto load = [&](int u, float4 (&dst)[kFusedG]) {
+      int64_t p = 4 * ((int64_t)t + u * kSelThreads);
+      if (p >= N) p = 0;  // past the end: a valid address, the values go unused
+#pragma unroll
+      for (int g = 0; g < kFusedG; ++g)
+        dst[g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + p);
+      asm volatile("" ::: "memory");  // runs issue in order, so each run waits only for its own loads
+    };
+    const int hw = wave < G ? wave : 0;  // waves past G merge head 0 again, unused
+    const int64_t sb = (slice * G + hw) * S;
+    const int j0 = lane < S ? lane : 0;
+    const float m_first = fr.part_m[sb + j0], l_first = fr.part_l[sb + j0];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < kFusedNB; ++u) load(u, x[u]);
+    sm.hist[t] = 0u;
+    sm.hist[t + kSelThreads] = 0u;
+    if (wave < kFusedG) {
+      const float l2 = head_lse2<64>(fr.part_m + sb, fr.part_l + sb, S, lane, m_first, l_first);
+      if (wave < G && lane == 0) lse2[wave] = l2;
+    }
+    if (t == 0) {
+      sm.n_cand = 0u;
+      sm.res[3] = 0u;
+    }
+    __syncthreads();
+    uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
+#pragma unroll
+    for (int u = 0; u < kSweepU; ++u) {
+      if (in_range(u)) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = rank_of<kFusedG>(x[u % kFusedNB], e, lse2, G);
+        if (fr.keys_out)
+          *reinterpret_cast<float4*>(fr.keys_out + slice * N + 4 * (t + u * kSelThreads)) =
+              make_float4(r[0], r[1], r[2], r[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[4 * u + e] = r[e];
+          const uint32_t b = coarse_bin(r[e], r_lo);
+          if (cur_cnt != 0u && b != cur_bin) atomicAdd(&sm.hist[cur_bin], cur_cnt), cur_cnt = 0u;
+          cur_bin = b;
+          ++cur_cnt;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * u + e] = -INFINITY;
+      }
+      if (u + kFusedNB < kSweepU) load(u + kFusedNB, x[u % kFusedNB]);  // the slot just consumed
+    }
+    if (cur_cnt) atomicAdd(&sm.hist[cur_bin], cur_cnt);
+    __syncthreads();
+  } else {
+    const float* ky = rkey + slice * N;
+    const uint32_t* gh = ghist + slice * kBins;
+    // the histogram's loads first and then the keys', all unconditional (clamped addresses), so
+    // that waiting for the histogram leaves the keys in flight; the empty statement with a memory
+    // clobber keeps every load above the first barrier
+    const uint32_t h0 = gh[t], h1 = gh[t + kSelThreads];
+    float4 f[kSweepU];
+#pragma unroll
+    for (int u = 0; u < kSweepU; ++u) {
+      const int64_t p = 4 * ((int64_t)t + u * kSelThreads);
+      f[u] = *reinterpret_cast<const float4*>(ky + (p < N ? p : 0));
+    }
+    asm volatile("" ::: "memory");
+    sm.hist[t] = h0;
+    sm.hist[t + kSelThreads] = h1;
+#pragma unroll
+    for (int u = 0; u < kSweepU; ++u) {
+      const bool in = in_range(u);
+      v[4 * u] = in ? f[u].x : -INFINITY;
+      v[4 * u + 1] = in ? f[u].y : -INFINITY;
+      v[4 * u + 2] = in ? f[u].z : -INFINITY;
+      v[4 * u + 3] = in ? f[u].w : -INFINITY;
+    }
+    if (t == 0) {
+      sm.n_cand = 0u;
+      sm.res[3] = 0u;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   uint32_t bin, above;
   pick_digit(sm, kBins, (uint32_t)k, bin, above);
@@ -702,11 +789,16 @@ void launch_keys(const Dims& d, int S, const float* logits, const float* part_m,
 
 template <int D>
 void launch_select(const Dims& d, int k, float r_lo, const float* keys, const uint32_t* hist, int32_t* idx_out,
-                   const MergeJob& mj, hipStream_t s) {
+                   const MergeJob& mj, const FusedRank* fr, hipStream_t s) {
   const unsigned n_sel = (unsigned)d.slices();
   const unsigned grid = n_sel + (unsigned)ceil_div(mj.rows, kSelWaves);
-  if (d.N <= kResidentN)
-    rank_select_resident_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel, mj);
+  const FusedRank none{nullptr, nullptr, nullptr, 0, 0, nullptr};
+  if (fr)
+    rank_select_resident_kernel<D, true><<<grid, kSelThreads, 0, s>>>(nullptr, nullptr, d.N, k, r_lo, idx_out,
+                                                                      n_sel, mj, *fr);
+  else if (d.N <= kResidentN)
+    rank_select_resident_kernel<D, false><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel,
+                                                                       mj, none);
   else
     rank_select_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel, mj);
 }
@@ -714,21 +806,29 @@ void launch_select(const Dims& d, int k, float r_lo, const float* keys, const ui
 }  // namespace
 
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
-                              const float* part_l, int k, float* keys, uint32_t* hist, int32_t* idx_out,
-                              const MergeJob* merge, hipStream_t s) {
+                              const float* part_l, int k, float* keys, bool keys_wanted, uint32_t* hist,
+                              int32_t* idx_out, const MergeJob* merge, hipStream_t s) {
   const float r_lo = logf((float)d.G) - kBinSpan;  // the same value for both kernels
+  const MergeJob none{nullptr, nullptr, 0, 0, nullptr};
+  const MergeJob& mj = merge ? *merge : none;
+  if (d.N <= kResidentN && d.G <= kFusedG) {  // one launch: the selection forms r(p) itself
+    const FusedRank fr{logits, part_m, part_l, d.G, S, keys_wanted ? keys : nullptr};
+    if (d.D == 64)
+      launch_select<64>(d, k, r_lo, nullptr, nullptr, idx_out, mj, &fr, s);
+    else
+      launch_select<128>(d, k, r_lo, nullptr, nullptr, idx_out, mj, &fr, s);
+    return hipGetLastError();
+  }
   if (d.G <= 4)
     launch_keys<4>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
   else if (d.G <= 8)
     launch_keys<8>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
   else
     launch_keys<16>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
-  const MergeJob none{nullptr, nullptr, 0, 0, nullptr};
-  const MergeJob& mj = merge ? *merge : none;
   if (d.D == 64)
-    launch_select<64>(d, k, r_lo, keys, hist, idx_out, mj, s);
+    launch_select<64>(d, k, r_lo, keys, hist, idx_out, mj, nullptr, s);
   else
-    launch_select<128>(d, k, r_lo, keys, hist, idx_out, mj, s);
+    launch_select<128>(d, k, r_lo, keys, hist, idx_out, mj, nullptr, s);
   return hipGetLastError();
 }
 
