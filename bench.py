@@ -210,10 +210,12 @@ def write_traffic_record(root: str, workload: str = "mistral32k"):
 
 
 class HipEvent:
-    """A HIP timing event created with hipEventDisableSystemFence: recording it adds no
-    system-scope release fence (an L2 write-back) to the stream, so it perturbs the calls it
-    brackets far less than a default event; its timestamp is taken at the same point of the
-    stream.  Called through the HIP runtime the process has loaded (torch's)."""
+    """A HIP event created with hipEventDisableSystemFence: recording it adds no system-scope
+    release fence (an L2 write-back for the host's sake) to the stream, only the device-scope
+    one, which is all another stream of the same GPU needs.  As a timing event it perturbs the
+    calls it brackets far less than a default event (its timestamp is taken at the same point
+    of the stream); with timing=False it orders streams (wait).  Called through the HIP runtime
+    the process has loaded (torch's)."""
     _hip = None
 
     @classmethod
@@ -226,11 +228,12 @@ class HipEvent:
             cls._hip = ctypes.CDLL(paths[0])
         return cls._hip
 
-    def __init__(self):
+    def __init__(self, timing: bool = True):
         import ctypes
         self._c = ctypes
         self.ev = ctypes.c_void_p()
-        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(0x20000000))
+        flags = 0x20000000 | (0 if timing else 0x2)  # hipEventDisableSystemFence [| hipEventDisableTiming]
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(flags))
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
 
@@ -238,6 +241,12 @@ class HipEvent:
         rc = self._runtime().hipEventRecord(self.ev, self._c.c_void_p(stream.cuda_stream))
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def wait(self, stream):
+        """Work enqueued on `stream` after this call waits for the event's last record."""
+        rc = self._runtime().hipStreamWaitEvent(self._c.c_void_p(stream.cuda_stream), self.ev, self._c.c_uint(0))
+        if rc != 0:
+            raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
 
     def elapsed_time(self, end) -> float:
         """Milliseconds from this event to `end` (both completed)."""
@@ -390,8 +399,10 @@ def main():
     qs_np = generate_step_queries(cfg, n_q)
     qs = [torch.from_numpy(qs_np[i]).to(dev) for i in range(n_q)]
     mixed = args.rank == "mixed"
-    gathered = [torch.cuda.Event() for _ in range(layers)]
-    stepped = [torch.cuda.Event() for _ in range(layers)]
+    # the streams' synchronisation events: device-scope release only (both streams are on this
+    # GPU); a default event's system-scope fence cost the step ~1.3 µs
+    gathered = [HipEvent(timing=False) for _ in range(layers)]
+    stepped = [HipEvent(timing=False) for _ in range(layers)]
     sync_every = args.sync_every  # steps per cross-stream synchronisation (a divisor of the layers)
 
     def new_state():
@@ -426,7 +437,7 @@ def main():
         sel_c, sel_n = st["sel"][l][cur], st["sel"][l][nxt]
         grp = (i // sync_every) % (layers // sync_every)  # event slot of this group
         if i % sync_every == 0:
-            comp.wait_event(gathered[grp])
+            gathered[grp].wait(comp)
         mark("d0", comp)
         decode_step(qs[r % n_q], caches[l], k, rank_row=1, rank_mixed=mixed, idx=idx_c, k_sel=sel_c[0],
                     v_sel=sel_c[1], out=out, idx_next_out=idx_n, workspace=ws)
@@ -438,7 +449,7 @@ def main():
         if i % sync_every != sync_every - 1:
             return
         stepped[grp].record(comp)
-        side.wait_event(stepped[grp])
+        stepped[grp].wait(side)
         mark("g0", side)
         for (pl, pidx, psel) in st["pending"]:
             if reuse:
@@ -530,10 +541,10 @@ def main():
         c = caches[i % layers]
         score_topk(qs[i % n_q], c, k, rank_row=0, idx_out=serial_idx, workspace=ws_s)
         stepped[0].record(comp)
-        side.wait_event(stepped[0])
+        stepped[0].wait(side)
         gather_fp16(serial_idx, hk, hv, cfg.bits, *serial_rows[i % 2], stream=side)
         gathered[0].record(side)
-        comp.wait_event(gathered[0])
+        gathered[0].wait(comp)
         decode_attn(qs[i % n_q], c, serial_idx, serial_rows[i % 2][0], serial_rows[i % 2][1], out=out,
                     workspace=ws_a)
 
