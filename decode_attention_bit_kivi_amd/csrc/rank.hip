@@ -26,6 +26,11 @@
 //                resolved by one wave counting, without the radix passes.
 //                The bin's value interval comes from a 64-way search by one
 //                wave.
+//   For a slice of at most 32768 positions and at most 4 heads per KV head
+//   there is one launch: the register-resident rank_select forms r(p) and the
+//   coarse histogram itself, with the arithmetic of rank_keys (shared
+//   functions, so the keys are the same bits), and no key buffer is written
+//   unless the caller asks for r.
 //   The exact selection compares order-preserving 32-bit integer keys of the
 //   float r.
 #include "merge.h"

@@ -268,6 +268,26 @@ def test_score_topk_crowded_and_tied_ranks(gpu, qscale):
     assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
 
 
+@pytest.mark.parametrize("seq_len", [32768, 32768 + 64])
+def test_selection_same_with_and_without_key_output(gpu, seq_len):
+    """r(p) is written only when the caller asks for it (up to 32768 positions the selection
+    forms the keys itself, beyond that a separate pass writes them to workspace): the selected
+    sets do not depend on it, for score_topk and for the fused step (each against itself: the
+    two compute the logits in different kernels)."""
+    cfg = get_config("llama8k").with_(seq_len=seq_len, top_k=328, bits=1, seed=5)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    q = _dev(Q)
+    rk = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    a = score_topk(q, cache, cfg.top_k, rank_key_out=rk)
+    b = score_topk(q, cache, cfg.top_k)
+    rk2 = torch.empty_like(rk)
+    _, na = decode_step(q, cache, cfg.top_k, rank_key_out=rk2)
+    _, nb = decode_step(q, cache, cfg.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(na, nb)
+
+
 @pytest.mark.parametrize("name", ["mistral32k", "long128k"])
 def test_score_topk_full_size_sampled(gpu, name):
     cfg = get_config(name)
