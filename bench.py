@@ -342,7 +342,7 @@ def main():
     from decode_attention_bit_kivi_amd import (
         quantize_pack, score_topk, gather_fp16, decode_attn, decode_step, empty_cache,
         score_topk_workspace_size, decode_attn_workspace_size, decode_step_workspace_size, GatherStream,
-        ComputeStream, gather_reuse, gather_fp16_missing, decode_attn_fp16,
+        ComputeStream, gather_reuse, gather_fp16_missing, decode_attn_fp16, flag_set, flag_wait,
     )
     from workloads import get_config, generate_all, generate_step_queries
 
@@ -399,10 +399,21 @@ def main():
     qs_np = generate_step_queries(cfg, n_q)
     qs = [torch.from_numpy(qs_np[i]).to(dev) for i in range(n_q)]
     mixed = args.rank == "mixed"
-    # the streams' synchronisation events: device-scope release only (both streams are on this
-    # GPU); a default event's system-scope fence cost the step ~1.3 µs
+    # the compute stream waits for the gathers through events recorded without the system-scope
+    # fence (device scope is all a second stream of this GPU needs; a default event's fence cost
+    # the step ~1.3 µs); the gather stream waits for the compute stream's selections on a flag
+    # (a kernel polling a sequence number in device memory starts the gathers sooner than a
+    # queue barrier does)
     gathered = [HipEvent(timing=False) for _ in range(layers)]
-    stepped = [HipEvent(timing=False) for _ in range(layers)]
+    sync_flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    flag_timeouts = torch.zeros(1, dtype=torch.int32, device=dev)
+    flag_seq = [0]
+
+    def compute_then_side():
+        """Later work on the gather stream runs after everything enqueued on the compute stream."""
+        flag_seq[0] += 1
+        flag_set(sync_flag, flag_seq[0], stream=comp)
+        flag_wait(sync_flag, flag_seq[0], flag_timeouts, stream=side)
     sync_every = args.sync_every  # steps per cross-stream synchronisation (a divisor of the layers)
 
     def new_state():
@@ -448,8 +459,7 @@ def main():
         st["pending"].append((l, idx_n, sel_n))
         if i % sync_every != sync_every - 1:
             return
-        stepped[grp].record(comp)
-        stepped[grp].wait(side)
+        compute_then_side()
         mark("g0", side)
         for (pl, pidx, psel) in st["pending"]:
             if reuse:
@@ -540,8 +550,7 @@ def main():
         """Rank with the real token against C', fetch its top-k (no overlap), then attend."""
         c = caches[i % layers]
         score_topk(qs[i % n_q], c, k, rank_row=0, idx_out=serial_idx, workspace=ws_s)
-        stepped[0].record(comp)
-        stepped[0].wait(side)
+        compute_then_side()
         gather_fp16(serial_idx, hk, hv, cfg.bits, *serial_rows[i % 2], stream=side)
         gathered[0].record(side)
         gathered[0].wait(comp)
@@ -570,6 +579,8 @@ def main():
     torch.cuda.synchronize()
     full_layer_us = e0.elapsed_time(e1) * 1e3 / 2
 
+    if int(flag_timeouts.item()) != 0:  # a gather ran without its selection: the timings are void
+        raise SystemExit(f"{int(flag_timeouts.item())} stream flag wait(s) ended at their time limit")
     step_bytes = algorithmic_bytes_step(cfg)
     step_avg_s = float(step_us.mean()) * 1e-6
     achieved = step_bytes / step_avg_s / 1e9

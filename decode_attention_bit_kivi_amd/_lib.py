@@ -14,7 +14,7 @@ import threading
 LIB_PATH = os.environ.get("SPECACHE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libspecache.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SPECACHE_OK = 0
 SPECACHE_ERR_INVALID = 1
@@ -42,6 +42,8 @@ EXPORTED = (
     "specache_gather_stream_create",
     "specache_compute_stream_create",
     "specache_stream_destroy",
+    "specache_flag_set",
+    "specache_flag_wait",
     "specache_status_string",
     "specache_abi_version",
 )
@@ -112,6 +114,8 @@ def load() -> ctypes.CDLL:
             "specache_gather_stream_create": (I, [I, ctypes.POINTER(P)]),
             "specache_compute_stream_create": (I, [I, ctypes.POINTER(P)]),
             "specache_stream_destroy": (I, [P]),
+            "specache_flag_set": (I, [P, ctypes.c_uint32, P]),
+            "specache_flag_wait": (I, [P, ctypes.c_uint32, ctypes.c_uint32, P, P]),
             "specache_status_string": (ctypes.c_char_p, [I]),
             "specache_abi_version": (I, []),
         }

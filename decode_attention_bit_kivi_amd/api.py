@@ -295,6 +295,28 @@ class ComputeStream(CUStream):
     _create = "specache_compute_stream_create"
 
 
+def _flag_word(t: torch.Tensor, name: str):
+    if not (t.is_cuda and t.dtype in (torch.int32, torch.uint32) and t.numel() >= 1 and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous int32 or uint32 CUDA tensor (its first element is used)")
+    return t.data_ptr()
+
+
+def flag_set(flag: torch.Tensor, value: int, stream=None) -> None:
+    """specache_flag_set: once the stream's earlier work is done, store `value` (uint32) into
+    flag[0] with device-scope release ordering."""
+    _lib.check(_lib.load().specache_flag_set(_flag_word(flag, "flag"), value & 0xFFFFFFFF, _stream(stream)),
+               "specache_flag_set")
+
+
+def flag_wait(flag: torch.Tensor, value: int, timeouts: torch.Tensor, max_wait_us: int = 2_000_000,
+              stream=None) -> None:
+    """specache_flag_wait: hold the stream until flag[0] has reached `value` (bounded by
+    max_wait_us; a wait that ends on the bound adds 1 to timeouts[0])."""
+    _lib.check(_lib.load().specache_flag_wait(_flag_word(flag, "flag"), value & 0xFFFFFFFF, max_wait_us,
+                                              _flag_word(timeouts, "timeouts"), _stream(stream)),
+               "specache_flag_wait")
+
+
 def decode_attn_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int, k: int, tail_len: int = 0) -> int:
     shape = cache.shape(n_q_heads)
     return int(_lib.load().specache_decode_attn_workspace_size(ctypes.byref(shape), n_tokens, k, tail_len))

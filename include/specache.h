@@ -124,7 +124,7 @@
 extern "C" {
 #endif
 
-#define SPECACHE_ABI_VERSION 4
+#define SPECACHE_ABI_VERSION 5
 
 typedef enum specache_status {
   SPECACHE_OK = 0,
@@ -293,6 +293,33 @@ int specache_gather_stream_create(int n_cus, void** stream_out);
  */
 int specache_compute_stream_create(int reserved_cus, void** stream_out);
 int specache_stream_destroy(void* stream);
+
+/*
+ * Ordering between two streams of one GPU through a flag in device memory, for
+ * the overlapped loop of §3 "decoding" (the prefetch stream waits for the
+ * selection it fetches, then runs beside the other layers' compute) without a
+ * queue barrier between the streams.
+ *
+ * specache_flag_set enqueues on `stream` a kernel that, once every earlier
+ * command on that stream has completed, stores `value` into *flag (uint32 in
+ * device memory, caller-owned) with release ordering at device scope.
+ * specache_flag_wait enqueues on `stream` a one-wave kernel that polls *flag
+ * (acquire at device scope) until it has reached `value` (flag - value taken
+ * as a signed 32-bit distance, so a sequence number may wrap); work enqueued
+ * on `stream` after it sees everything the setter's stream published.  The
+ * wait is bounded: after max_wait_us microseconds (1 <= max_wait_us) it stops
+ * waiting and adds 1 to *timeouts (uint32 in device memory, caller-owned and
+ * zeroed by the caller), so the caller can detect a flag that was never set.
+ * The flag only ever needs to grow: use increasing sequence numbers rather
+ * than clearing it.  The two streams must not share a hardware queue (the
+ * library's gather and compute streams each have their own): a wait that
+ * blocks the queue of its own setter ends only at the time limit.
+ * Returns SPECACHE_ERR_INVALID for a null pointer or max_wait_us == 0,
+ * SPECACHE_ERR_HIP if the launch fails.
+ */
+int specache_flag_set(uint32_t* flag, uint32_t value, void* stream);
+int specache_flag_wait(const uint32_t* flag, uint32_t value, uint32_t max_wait_us, uint32_t* timeouts,
+                       void* stream);
 
 /*
  * O = Attn([T_t, T'_{t+1}], C' U C_kappa) (the summary's quick read, third

@@ -219,3 +219,12 @@ def test_compression_ratio_matches_pages():
         fp16_rows = (fig["residual"] + fig["top_k"]) * 2 * 128 * 2
         ratio = (lowbit + fp16_rows) / (N * 2 * 128 * 2)
         assert round(ratio, 2) == case["ratio"], (N, ratio)
+
+
+def test_flag_argument_validation(lib):
+    """Null flag or timeout words and a zero bound are refused before any launch."""
+    inv = _lib.SPECACHE_ERR_INVALID
+    assert lib.specache_flag_set(None, 1, None) == inv
+    assert lib.specache_flag_wait(None, 1, 100, 1, None) == inv
+    assert lib.specache_flag_wait(1, 1, 100, None, None) == inv
+    assert lib.specache_flag_wait(1, 1, 0, 1, None) == inv
