@@ -1,7 +1,7 @@
 // Ordering between two streams of one GPU through a flag in device memory instead of a queue
 // barrier: the producer stream stores a sequence number once its earlier work is done, and a
 // one-wave kernel on the consumer stream holds that stream until it reads a number at least as
-// large.  In the overlapped decode loop the gather stream waits this way for the compute
+// large.  In the overlapped decode loop the gather stream can wait this way for the compute
 // stream's selection: a queue barrier between two streams releases the waiting stream ~11 µs
 // after the work it waits for has ended, while the stream behind a polling kernel starts its
 // next kernel within ~2 µs of the store.  The setter pays for its release instead (the

@@ -311,9 +311,11 @@ int specache_stream_destroy(void* stream);
  * waiting and adds 1 to *timeouts (uint32 in device memory, caller-owned and
  * zeroed by the caller), so the caller can detect a flag that was never set.
  * The flag only ever needs to grow: use increasing sequence numbers rather
- * than clearing it.  The two streams must not share a hardware queue (the
- * library's gather and compute streams each have their own): a wait that
- * blocks the queue of its own setter ends only at the time limit.
+ * than clearing it.  The setter must be able to run while the wait runs: the
+ * two streams must not share a hardware queue (the library's gather and
+ * compute streams each have their own), and where kernel dispatches are
+ * serialised (a profiler collecting per-dispatch counters does this) a wait
+ * whose setter comes later ends only at the time limit.
  * Returns SPECACHE_ERR_INVALID for a null pointer or max_wait_us == 0,
  * SPECACHE_ERR_HIP if the launch fails.
  */
