@@ -562,12 +562,16 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
     const int G = fr.G, S = fr.S;
     const float* lg = fr.logits + slice * G * N;
     float4 x[kFusedNB][kFusedG];
+    // the logits are read once: non-temporal loads (measured ~0.5 µs faster per call)
+    typedef float f4v __attribute__((ext_vector_type(4)));
     auto load = [&](int u, float4 (&dst)[kFusedG]) {
       int64_t p = 4 * ((int64_t)t + u * kSelThreads);
       if (p >= N) p = 0;  // past the end: a valid address, the values go unused
 #pragma unroll
-      for (int g = 0; g < kFusedG; ++g)
-        dst[g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + p);
+      for (int g = 0; g < kFusedG; ++g) {
+        const f4v w = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(lg + (int64_t)(g < G ? g : 0) * N + p));
+        dst[g] = make_float4(w.x, w.y, w.z, w.w);
+      }
       asm volatile("" ::: "memory");  // runs issue in order, so each run waits only for its own loads
     };
     const int hw = wave < G ? wave : 0;  // waves past G merge head 0 again, unused
