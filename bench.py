@@ -68,7 +68,29 @@ def recorded_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def parse():
+def round_up(x: int, m: int) -> int:
+    return -(-x // m) * m
+
+
+def pipeline_schedule(warmup: int, steps: int, sync_every: int):
+    """Step indices of the three passes of the pipeline: (warm-up, timed, instrumented).
+
+    A step's index picks its layer and its synchronisation group (sync_every consecutive
+    indices, whose gathers are issued together after the group's last step).  Any counts are
+    accepted: a pass that ends inside a group flushes that group's gathers at its end, so the
+    timed pass covers exactly `steps` steps and all of their gathers; the next pass starts at
+    the next whole group.  The instrumented pass (per-call events) runs whole groups only."""
+    if warmup < 0 or steps < 1 or sync_every < 1:
+        raise ValueError("need warmup >= 0, steps >= 1 and sync_every >= 1")
+    w = list(range(warmup))
+    t0 = round_up(warmup, sync_every)
+    t = list(range(t0, t0 + steps))
+    i0 = round_up(t0 + steps, sync_every)
+    n_i = round_up(steps, sync_every)
+    return w, t, list(range(i0, i0 + n_i))
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -97,7 +119,7 @@ def parse():
                          "profiler's HBM byte counters; traffic-record: write the HBM traffic record "
                          "from the four counter runs under --pmc-root (see TRAFFIC_COMMANDS)")
     ap.add_argument("--pmc-root", default="gpurun_out", help="directory holding the counter runs")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def copy_reference(reps: int = 5):
@@ -340,9 +362,7 @@ def main():
                                    "slice with no exchange, see the design notes", "n_gpus": args.gpus}))
         sys.exit(2)
 
-    if args.steps % args.sync_every or args.warmup % args.sync_every:
-        print(json.dumps({"error": "--steps and --warmup must be multiples of --sync-every"}))
-        sys.exit(2)
+    warm_idx, timed_idx, instr_idx = pipeline_schedule(args.warmup, args.steps, args.sync_every)
 
     import torch
     from decode_attention_bit_kivi_amd import (
@@ -461,16 +481,27 @@ def main():
             gather_reuse(idx_n, idx_c, sel_c[0], sel_c[1], N, k_sel=sel_n[0], v_sel=sel_n[1],
                          fetch_idx=st["fetch"][l])
         st["pending"].append((l, idx_n, sel_n))
-        if i % sync_every != sync_every - 1:
+        st["grp"] = grp
+        if i % sync_every == sync_every - 1:
+            flush(st, reuse, ev)
+
+    def flush(st, reuse, ev=None):
+        """The gathers of the steps enqueued since the last flush, on the gather stream after
+        the compute stream's work: at the end of every group of sync_every steps, and at the
+        end of a pass that stops inside a group."""
+        if not st["pending"]:
             return
+        grp = st["grp"]
         compute_then_side(grp)
-        mark("g0", side)
+        if ev and "g0" in ev:
+            ev["g0"].record(side)
         for (pl, pidx, psel) in st["pending"]:
             if reuse:
                 gather_fp16_missing(st["fetch"][pl], hk, hv, psel[0], psel[1], cfg.bits, stream=side)
             else:
                 gather_fp16(pidx, hk, hv, cfg.bits, psel[0], psel[1], stream=side)
-        mark("g1", side)
+        if ev and "g1" in ev:
+            ev["g1"].record(side)
         st["pending"] = []
         gathered[grp].record(side)
 
@@ -484,29 +515,31 @@ def main():
         (fence-free HipEvents),
         the same schedule with events around every decode_step and every gather."""
         st = new_state()
-        for i in range(args.warmup):
+        for i in warm_idx:
             step(st, i, reuse)
+        flush(st, reuse)
         torch.cuda.synchronize()
         t_start.record(comp)
         h0 = time.perf_counter()
-        for i in range(args.steps):
-            step(st, args.warmup + i, reuse)
-        host_enqueue_us.append((time.perf_counter() - h0) / args.steps * 1e6)  # host time to enqueue a step
+        for i in timed_idx:
+            step(st, i, reuse)
+        flush(st, reuse)   # a last group cut short: its gathers are part of the timed steps
+        host_enqueue_us.append((time.perf_counter() - h0) / len(timed_idx) * 1e6)  # host time to enqueue a step
         comp.wait_stream(side)
         t_end.record(comp)
         torch.cuda.synchronize()
-        ms = t_start.elapsed_time(t_end) / args.steps
+        ms = t_start.elapsed_time(t_end) / len(timed_idx)
         fetched = None
         if reuse:
             fetched = float(np.mean([(f >= 0).float().mean().item() for f in st["fetch"]]))
-        evs = [{n: HipEvent() for n in ("d0", "d1", "g0", "g1")} for _ in range(args.steps)]
-        for i, ev in enumerate(evs):
-            step(st, args.warmup + args.steps + i, reuse, ev)
+        evs = [{n: HipEvent() for n in ("d0", "d1", "g0", "g1")} for _ in instr_idx]
+        for i, ev in zip(instr_idx, evs):
+            step(st, i, reuse, ev)
         torch.cuda.synchronize()
         d_us = np.array([e["d0"].elapsed_time(e["d1"]) for e in evs]) * 1e3
         # gathers are issued per group of sync_every steps, bracketed at the group's last step
-        g_us = np.array([evs[j]["g0"].elapsed_time(evs[j]["g1"]) for j in range(len(evs))
-                         if (args.warmup + args.steps + j) % sync_every == sync_every - 1]) * 1e3 / sync_every
+        g_us = np.array([ev["g0"].elapsed_time(ev["g1"]) for i, ev in zip(instr_idx, evs)
+                         if i % sync_every == sync_every - 1]) * 1e3 / sync_every
         return ms, d_us, g_us, fetched
 
     host_enqueue_us = []
@@ -600,7 +633,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # float16 operands on the matrix cores (queries, fetched rows, expanded codes) with float32
+        # accumulation; K/V stored as cfg.bits-bit codes with float16 zero-points and scales
+        "dtype": "f16",
+        "precision": {"queries_outputs_fetched_rows": "float16",
+                      "kv_cache": f"{cfg.bits}-bit codes, float16 zero-point/scale per group of {cfg.group}",
+                      "accumulation": "float32"},
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {MODEL_SHAPE.get(cfg.name, 'synthetic')} layer, batch {B}, {Hq} query / {Hkv} KV heads, "

@@ -43,6 +43,20 @@ class LowBitCache:
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_meta, self.v_codes, self.v_meta))
 
+    def check(self) -> None:
+        """The four buffers have the shapes, types and layout the C ABI assumes for this
+        cache's dimensions (raises ValueError / TypeError before any kernel sees them)."""
+        cap = self.capacity or self.seq_len
+        if self.seq_len <= 0 or self.seq_len > cap:
+            raise ValueError(f"cache seq_len {self.seq_len} outside (0, capacity {cap}]")
+        sizes = lowbit_sizes(self.batch, self.n_kv_heads, cap, self.head_dim, self.bits, group=self.group,
+                             v_bits=self.v_bits or self.bits)
+        for name, t, dt, shp in (("k_codes", self.k_codes, torch.int32, sizes[0]),
+                                 ("k_meta", self.k_meta, torch.float16, sizes[1]),
+                                 ("v_codes", self.v_codes, torch.int32, sizes[2]),
+                                 ("v_meta", self.v_meta, torch.float16, sizes[3])):
+            _need(t, f"cache.{name}", dt, shp)
+
 
 def _stream(stream) -> int:
     if stream is None:
@@ -54,17 +68,61 @@ def _stream(stream) -> int:
     return int(stream)
 
 
-def _need(t: torch.Tensor, name: str, dtype, ndim: int, cuda: bool = True):
+def _need(t: torch.Tensor, name: str, dtype, shape):
+    """t is a contiguous tensor of `dtype` whose shape matches `shape` (a tuple whose None
+    entries match any size, or an int: only the number of dimensions is fixed).  The device is
+    checked separately (_on_gpu), after every shape: a mismatch never reaches the library, whose
+    kernels take raw pointers and would read or write out of bounds."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    ndim = shape if isinstance(shape, int) else len(shape)
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not isinstance(shape, int):
+        for got, want in zip(t.shape, shape):
+            if want is not None and got != want:
+                raise ValueError(f"{name} must have shape {tuple('*' if w is None else w for w in shape)}, "
+                                 f"got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if cuda and not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _on_gpu(**tensors):
+    """Every named tensor (None entries skipped) is on one GPU."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+
+
+def _host_readable(t: torch.Tensor, name: str):
+    """A gather / offload endpoint: device memory or pinned host memory."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+
+
+def _workspace(ws, need: int, device):
+    """The caller's workspace (any dtype, contiguous, at least `need` bytes, on the operands'
+    GPU), or a new one."""
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def lowbit_sizes(batch: int, n_kv_heads: int, seq_len: int, head_dim: int, bits: int, group: int = 32,
@@ -96,33 +154,37 @@ def quantize_pack(k16: torch.Tensor, v16: torch.Tensor, bits: int, out: LowBitCa
     positions, of which the first seq_len (default Nc) are quantized; keys with `bits`, values
     with `v_bits` (default `bits`), in groups of `group` (32 or 64) tokens / channels."""
     _need(k16, "k16", torch.float16, 4)
-    _need(v16, "v16", torch.float16, 4)
-    if k16.shape != v16.shape:
-        raise ValueError("k16 and v16 must have the same shape")
     B, Hkv, Nc, D = k16.shape
+    _need(v16, "v16", torch.float16, (B, Hkv, Nc, D))
     N = Nc if seq_len is None else int(seq_len)
+    if out is not None:
+        out.check()
+        if (out.batch, out.n_kv_heads, out.capacity or out.seq_len, out.head_dim, out.bits, out.group) != \
+                (B, Hkv, Nc, D, bits, group) or (v_bits is not None and (out.v_bits or out.bits) != v_bits):
+            raise ValueError("out cache shape does not match the inputs")
+        _on_gpu(k16=k16, v16=v16, k_codes=out.k_codes, k_meta=out.k_meta, v_codes=out.v_codes, v_meta=out.v_meta)
+    else:
+        _on_gpu(k16=k16, v16=v16)
     cache = out if out is not None else empty_cache(B, Hkv, N, D, bits, k16.device, capacity=Nc, v_bits=v_bits,
                                                     group=group)
-    lib = _lib.load()
-    if out is not None:
-        cache.seq_len = N
-    shape = cache.shape()
-    if (cache.batch, cache.n_kv_heads, cache.capacity or cache.seq_len, cache.head_dim, cache.bits) != \
-            (B, Hkv, Nc, D, bits):
-        raise ValueError("out cache shape does not match the inputs")
-    _lib.check(lib.specache_quantize_pack(ctypes.byref(shape), k16.data_ptr(), v16.data_ptr(),
-                                          ctypes.byref(cache.c_struct()), _stream(stream)),
+    cache.seq_len = N
+    _lib.check(_lib.load().specache_quantize_pack(ctypes.byref(cache.shape()), k16.data_ptr(), v16.data_ptr(),
+                                                  ctypes.byref(cache.c_struct()), _stream(stream)),
                "specache_quantize_pack")
     return cache
+
+
+def _cache_on_gpu(cache: LowBitCache, **others):
+    _on_gpu(k_codes=cache.k_codes, k_meta=cache.k_meta, v_codes=cache.v_codes, v_meta=cache.v_meta, **others)
 
 
 def quantize_append(cache: LowBitCache, k16_new: torch.Tensor, v16_new: torch.Tensor, stream=None) -> LowBitCache:
     """specache_quantize_append: quantize K, V [B, Hkv, n_new, D] (n_new a multiple of 32) into
     positions [seq_len, seq_len + n_new) of the cache; cache.seq_len grows by n_new."""
-    _need(k16_new, "k16_new", torch.float16, 4)
-    _need(v16_new, "v16_new", torch.float16, 4)
-    if k16_new.shape != v16_new.shape:
-        raise ValueError("k16_new and v16_new must have the same shape")
+    cache.check()
+    _need(k16_new, "k16_new", torch.float16, (cache.batch, cache.n_kv_heads, None, cache.head_dim))
+    _need(v16_new, "v16_new", torch.float16, tuple(k16_new.shape))
+    _cache_on_gpu(cache, k16_new=k16_new, v16_new=v16_new)
     n_new = k16_new.shape[2]
     _lib.check(_lib.load().specache_quantize_append(ctypes.byref(cache.shape()), k16_new.data_ptr(),
                                                     v16_new.data_ptr(), n_new, ctypes.byref(cache.c_struct()),
@@ -136,11 +198,14 @@ def offload_fp16(k16_new: torch.Tensor, v16_new: torch.Tensor, k16_cache: torch.
                  pos0: int, stream=None):
     """specache_offload_fp16: rows [B, Hkv, n_new, D] (device) -> positions pos0.. of the 16-bit
     cache [B, Hkv, Nc, D] (pinned host or device)."""
-    _need(k16_new, "k16_new", torch.float16, 4)
-    _need(v16_new, "v16_new", torch.float16, 4)
-    _need(k16_cache, "k16_cache", torch.float16, 4, cuda=False)
-    _need(v16_cache, "v16_cache", torch.float16, 4, cuda=False)
+    _need(k16_cache, "k16_cache", torch.float16, 4)
     B, Hkv, Nc, D = k16_cache.shape
+    _need(v16_cache, "v16_cache", torch.float16, (B, Hkv, Nc, D))
+    _need(k16_new, "k16_new", torch.float16, (B, Hkv, None, D))
+    _need(v16_new, "v16_new", torch.float16, tuple(k16_new.shape))
+    _on_gpu(k16_new=k16_new, v16_new=v16_new)
+    _host_readable(k16_cache, "k16_cache")
+    _host_readable(v16_cache, "v16_cache")
     n_new = k16_new.shape[2]
     shape = _lib.Shape(B, Hkv, Hkv, D, Nc, 1, 32, Nc)   # only the layout (Nc) matters here
     _lib.check(_lib.load().specache_offload_fp16(ctypes.byref(shape), k16_new.data_ptr(), v16_new.data_ptr(), n_new,
@@ -153,35 +218,52 @@ def score_topk_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int,
     return int(_lib.load().specache_score_topk_workspace_size(ctypes.byref(shape), n_tokens, k))
 
 
+def _queries(q16: torch.Tensor, cache: LowBitCache):
+    """q16 [B, Hq, T, D] for this cache: (B, Hq, T, D)."""
+    cache.check()
+    _need(q16, "q16", torch.float16, (cache.batch, None, None, cache.head_dim))
+    B, Hq, T, D = q16.shape
+    if Hq % cache.n_kv_heads:
+        raise ValueError(f"q16 has {Hq} heads, not a multiple of the cache's {cache.n_kv_heads} KV heads")
+    return B, Hq, T, D
+
+
 def score_topk(q16: torch.Tensor, cache: LowBitCache, k: int, rank_row: int = 1, sm_scale: float | None = None,
                idx_out: torch.Tensor | None = None, rank_key_out: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """specache_score_topk: idx [B, Hkv, k] int32 (ascending) of the top-k positions
     by the rank row's attention over C'.  rank_key_out, if given ([B, Hkv, N]
     float32), receives r(p)."""
-    _need(q16, "q16", torch.float16, 4)
-    B, Hq, T, D = q16.shape
+    B, Hq, T, D = _queries(q16, cache)
+    Hkv, N = cache.n_kv_heads, cache.seq_len
+    if idx_out is not None:
+        _need(idx_out, "idx_out", torch.int32, (B, Hkv, k))
+    if rank_key_out is not None:
+        _need(rank_key_out, "rank_key_out", torch.float32, (B, Hkv, N))
     sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     lib = _lib.load()
     shape = cache.shape(Hq)
     need = lib.specache_score_topk_workspace_size(ctypes.byref(shape), T, k)
     if need == 0:
         raise ValueError("invalid score_topk arguments (shape, n_tokens or k)")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    _cache_on_gpu(cache, q16=q16, idx_out=idx_out, rank_key_out=rank_key_out, workspace=workspace)
+    workspace = _workspace(workspace, need, q16.device)
     if idx_out is None:
-        idx_out = torch.empty((B, cache.n_kv_heads, k), dtype=torch.int32, device=q16.device)
-    _need(idx_out, "idx_out", torch.int32, 3)
-    rk = 0
-    if rank_key_out is not None:
-        _need(rank_key_out, "rank_key_out", torch.float32, 3)
-        rk = rank_key_out.data_ptr()
+        idx_out = torch.empty((B, Hkv, k), dtype=torch.int32, device=q16.device)
+    rk = 0 if rank_key_out is None else rank_key_out.data_ptr()
     _lib.check(lib.specache_score_topk(ctypes.byref(shape), q16.data_ptr(), T, rank_row,
                                        ctypes.byref(cache.c_struct()), sm_scale, k, idx_out.data_ptr(), rk,
-                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                       _stream(stream)),
+                                       workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
                "specache_score_topk")
     return idx_out
+
+
+def _rows_out(t, name, shape, device):
+    """A caller's row buffer of `shape` (float16, GPU), or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=torch.float16, device=device)
+    _need(t, name, torch.float16, shape)
+    return t
 
 
 def gather_fp16(idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor, bits: int = 1,
@@ -189,19 +271,19 @@ def gather_fp16(idx: torch.Tensor, k16_src: torch.Tensor, v16_src: torch.Tensor,
                 seq_len: int | None = None):
     """specache_gather_fp16: rows idx of the 16-bit cache (pinned host or device,
     [B, Hkv, Nc, D], positions [0, seq_len) in use) -> (k_sel, v_sel) [B, Hkv, k, D]."""
-    _need(idx, "idx", torch.int32, 3)
-    _need(k16_src, "k16_src", torch.float16, 4, cuda=False)
-    _need(v16_src, "v16_src", torch.float16, 4, cuda=False)
-    for name, t in (("k16_src", k16_src), ("v16_src", v16_src)):
-        if not (t.is_cuda or t.is_pinned()):
-            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    _need(k16_src, "k16_src", torch.float16, 4)
     B, Hkv, Nc, D = k16_src.shape
+    _need(v16_src, "v16_src", torch.float16, (B, Hkv, Nc, D))
+    _need(idx, "idx", torch.int32, (B, Hkv, None))
     k = idx.shape[2]
-    dev = idx.device
-    if k_sel is None:
-        k_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
-    if v_sel is None:
-        v_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
+    for name, t in (("k_sel", k_sel), ("v_sel", v_sel)):
+        if t is not None:
+            _need(t, name, torch.float16, (B, Hkv, k, D))
+    _on_gpu(idx=idx, k_sel=k_sel, v_sel=v_sel)
+    _host_readable(k16_src, "k16_src")
+    _host_readable(v16_src, "v16_src")
+    k_sel = _rows_out(k_sel, "k_sel", (B, Hkv, k, D), idx.device)
+    v_sel = _rows_out(v_sel, "v_sel", (B, Hkv, k, D), idx.device)
     shape = _lib.Shape(B, Hkv, Hkv, D, Nc if seq_len is None else seq_len, bits, 32, Nc)
     _lib.check(_lib.load().specache_gather_fp16(ctypes.byref(shape), idx.data_ptr(), k, k16_src.data_ptr(),
                                                 v16_src.data_ptr(), k_sel.data_ptr(), v_sel.data_ptr(),
@@ -216,17 +298,21 @@ def gather_reuse(idx: torch.Tensor, idx_prev: torch.Tensor, k_sel_prev: torch.Te
     """specache_gather_reuse: rows of idx also in idx_prev are copied from the previous
     rows; returns (k_sel, v_sel, fetch_idx) with fetch_idx = -1 for the copied rows."""
     _need(idx, "idx", torch.int32, 3)
-    _need(idx_prev, "idx_prev", torch.int32, 3)
-    _need(k_sel_prev, "k_sel_prev", torch.float16, 4)
-    _need(v_sel_prev, "v_sel_prev", torch.float16, 4)
     B, Hkv, k = idx.shape
+    _need(idx_prev, "idx_prev", torch.int32, (B, Hkv, None))
     k_prev = idx_prev.shape[2]
+    _need(k_sel_prev, "k_sel_prev", torch.float16, (B, Hkv, k_prev, None))
     D = k_sel_prev.shape[3]
-    dev = idx.device
-    if k_sel is None:
-        k_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
-    if v_sel is None:
-        v_sel = torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev)
+    _need(v_sel_prev, "v_sel_prev", torch.float16, (B, Hkv, k_prev, D))
+    for name, t in (("k_sel", k_sel), ("v_sel", v_sel)):
+        if t is not None:
+            _need(t, name, torch.float16, (B, Hkv, k, D))
+    if fetch_idx is not None:
+        _need(fetch_idx, "fetch_idx", torch.int32, (B, Hkv, k))
+    _on_gpu(idx=idx, idx_prev=idx_prev, k_sel_prev=k_sel_prev, v_sel_prev=v_sel_prev, k_sel=k_sel, v_sel=v_sel,
+            fetch_idx=fetch_idx)
+    k_sel = _rows_out(k_sel, "k_sel", (B, Hkv, k, D), idx.device)
+    v_sel = _rows_out(v_sel, "v_sel", (B, Hkv, k, D), idx.device)
     if fetch_idx is None:
         fetch_idx = torch.empty_like(idx)
     shape = _lib.Shape(B, Hkv, Hkv, D, seq_len, 1, 32)
@@ -241,16 +327,16 @@ def gather_fp16_missing(fetch_idx: torch.Tensor, k16_src: torch.Tensor, v16_src:
                         k_sel: torch.Tensor, v_sel: torch.Tensor, bits: int = 1, stream=None,
                         seq_len: int | None = None):
     """specache_gather_fp16_missing: fetch the rows fetch_idx marks (>= 0) into k_sel / v_sel."""
-    _need(fetch_idx, "fetch_idx", torch.int32, 3)
-    _need(k16_src, "k16_src", torch.float16, 4, cuda=False)
-    _need(v16_src, "v16_src", torch.float16, 4, cuda=False)
-    _need(k_sel, "k_sel", torch.float16, 4)
-    _need(v_sel, "v_sel", torch.float16, 4)
-    for name, t in (("k16_src", k16_src), ("v16_src", v16_src)):
-        if not (t.is_cuda or t.is_pinned()):
-            raise ValueError(f"{name} must be a GPU tensor or pinned host memory")
+    _need(k16_src, "k16_src", torch.float16, 4)
     B, Hkv, Nc, D = k16_src.shape
+    _need(v16_src, "v16_src", torch.float16, (B, Hkv, Nc, D))
+    _need(fetch_idx, "fetch_idx", torch.int32, (B, Hkv, None))
     k = fetch_idx.shape[2]
+    _need(k_sel, "k_sel", torch.float16, (B, Hkv, k, D))
+    _need(v_sel, "v_sel", torch.float16, (B, Hkv, k, D))
+    _on_gpu(fetch_idx=fetch_idx, k_sel=k_sel, v_sel=v_sel)
+    _host_readable(k16_src, "k16_src")
+    _host_readable(v16_src, "v16_src")
     shape = _lib.Shape(B, Hkv, Hkv, D, Nc if seq_len is None else seq_len, bits, 32, Nc)
     _lib.check(_lib.load().specache_gather_fp16_missing(ctypes.byref(shape), fetch_idx.data_ptr(), k,
                                                         k16_src.data_ptr(), v16_src.data_ptr(), k_sel.data_ptr(),
@@ -259,9 +345,18 @@ def gather_fp16_missing(fetch_idx: torch.Tensor, k16_src: torch.Tensor, v16_src:
     return k_sel, v_sel
 
 
+# Library streams that close() has retired.  torch's pinned-host allocator records an event on
+# every stream a pinned block was copied on when that block is freed, which may happen long after
+# the stream's last use (a pinned tensor that outlives the stream object); a destroyed stream
+# there crashes the process.  So a closed stream keeps its HIP handle until the process ends.
+_RETIRED_STREAMS: list = []
+
+
 class CUStream:
-    """A HIP stream limited to a set of compute units (created by the library,
-    released by close()).  `.torch` is a torch stream view of it."""
+    """A HIP stream limited to a set of compute units (created by the library).  `.torch` is a
+    torch stream view of it.  close() waits for the stream's work and retires it: no work may be
+    enqueued on it afterwards, but the HIP stream itself is released only when the process ends
+    (see _RETIRED_STREAMS), so that freeing a pinned tensor that was copied on it stays safe."""
 
     _create = None
 
@@ -274,8 +369,8 @@ class CUStream:
 
     def close(self):
         if self.handle:
-            torch.cuda.synchronize()
-            _lib.check(_lib.load().specache_stream_destroy(self.handle), "specache_stream_destroy")
+            self.torch.synchronize()
+            _RETIRED_STREAMS.append((self.handle, self.torch))
             self.handle = None
 
     def __del__(self):
@@ -322,25 +417,34 @@ def decode_attn_workspace_size(cache: LowBitCache, n_q_heads: int, n_tokens: int
     return int(_lib.load().specache_decode_attn_workspace_size(ctypes.byref(shape), n_tokens, k, tail_len))
 
 
-def _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail):
-    _need(q16, "q16", torch.float16, 4)
+def _attn_operands(q16, cache, idx, k_sel, v_sel, k_tail, v_tail, out):
+    """Shapes of the attention operands against q16 [B, Hq, T, D] and the cache:
+    idx [B, Hkv, k], k_sel / v_sel [B, Hkv, k, D], k_tail / v_tail [B, Hkv, R, D], out like q16."""
+    B, Hq, T, D = _queries(q16, cache)
+    Hkv = cache.n_kv_heads
     k = 0
-    ip = kp = vp = 0
     if idx is not None:
-        _need(idx, "idx", torch.int32, 3)
+        _need(idx, "idx", torch.int32, (B, Hkv, None))
         k = idx.shape[2]
         if k > 0:
-            _need(k_sel, "k_sel", torch.float16, 4)
-            _need(v_sel, "v_sel", torch.float16, 4)
-            ip, kp, vp = idx.data_ptr(), k_sel.data_ptr(), v_sel.data_ptr()
+            _need(k_sel, "k_sel", torch.float16, (B, Hkv, k, D))
+            _need(v_sel, "v_sel", torch.float16, (B, Hkv, k, D))
     R = 0
-    ktp = vtp = 0
     if k_tail is not None:
-        _need(k_tail, "k_tail", torch.float16, 4)
-        _need(v_tail, "v_tail", torch.float16, 4)
+        _need(k_tail, "k_tail", torch.float16, (B, Hkv, None, D))
+        _need(v_tail, "v_tail", torch.float16, tuple(k_tail.shape))
         R = k_tail.shape[2]
-        ktp, vtp = k_tail.data_ptr(), v_tail.data_ptr()
-    return k, ip, kp, vp, R, ktp, vtp
+    elif v_tail is not None:
+        raise ValueError("v_tail given without k_tail")
+    if out is not None:
+        _need(out, "out", torch.float16, (B, Hq, T, D))
+    return k, R
+
+
+def _ptrs(k, idx, k_sel, v_sel, R, k_tail, v_tail):
+    ip, kp, vp = (idx.data_ptr(), k_sel.data_ptr(), v_sel.data_ptr()) if k > 0 else (0, 0, 0)
+    ktp, vtp = (k_tail.data_ptr(), v_tail.data_ptr()) if R > 0 else (0, 0)
+    return ip, kp, vp, ktp, vtp
 
 
 def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None = None,
@@ -350,7 +454,7 @@ def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None 
                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """specache_decode_attn: O [B, Hq, T, D] float16 = Attn(q, C' with rows idx replaced by
     k_sel / v_sel, then the optional tail)."""
-    k, ip, kp, vp, R, ktp, vtp = _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail)
+    k, R = _attn_operands(q16, cache, idx, k_sel, v_sel, k_tail, v_tail, out)
     B, Hq, T, D = q16.shape
     sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     lib = _lib.load()
@@ -358,14 +462,15 @@ def decode_attn(q16: torch.Tensor, cache: LowBitCache, idx: torch.Tensor | None 
     need = lib.specache_decode_attn_workspace_size(ctypes.byref(shape), T, k, R)
     if need == 0:
         raise ValueError("invalid decode_attn arguments (shape, n_tokens, k or tail length)")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    _cache_on_gpu(cache, q16=q16, idx=idx if k else None, k_sel=k_sel if k else None, v_sel=v_sel if k else None,
+                  k_tail=k_tail, v_tail=v_tail, out=out, workspace=workspace)
+    workspace = _workspace(workspace, need, q16.device)
     if out is None:
         out = torch.empty_like(q16)
+    ip, kp, vp, ktp, vtp = _ptrs(k, idx, k_sel, v_sel, R, k_tail, v_tail)
     _lib.check(lib.specache_decode_attn(ctypes.byref(shape), q16.data_ptr(), T, ctypes.byref(cache.c_struct()),
                                         ip, k, kp, vp, ktp, vtp, R, sm_scale, out.data_ptr(),
-                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                        _stream(stream)),
+                                        workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
                "specache_decode_attn")
     return out
 
@@ -376,32 +481,37 @@ def decode_attn_fp16(q16: torch.Tensor, k16: torch.Tensor, v16: torch.Tensor, se
                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """specache_decode_attn_fp16: the 16-bit comparator, attention over the full float16 cache
     k16 / v16 [B, Hkv, Nc, D] (positions [0, seq_len) used) and the optional tail."""
-    _need(q16, "q16", torch.float16, 4)
-    _need(k16, "k16", torch.float16, 4, cuda=False)
-    _need(v16, "v16", torch.float16, 4, cuda=False)
-    B, Hq, T, D = q16.shape
-    _, Hkv, Nc, _ = k16.shape
+    _need(k16, "k16", torch.float16, 4)
+    B, Hkv, Nc, D = k16.shape
+    _need(v16, "v16", torch.float16, (B, Hkv, Nc, D))
+    _need(q16, "q16", torch.float16, (B, None, None, D))
+    _, Hq, T, _ = q16.shape
+    if Hq % Hkv:
+        raise ValueError(f"q16 has {Hq} heads, not a multiple of the cache's {Hkv} KV heads")
     N = Nc if seq_len is None else int(seq_len)
     sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     R = 0
-    ktp = vtp = 0
     if k_tail is not None:
-        _need(k_tail, "k_tail", torch.float16, 4)
-        _need(v_tail, "v_tail", torch.float16, 4)
+        _need(k_tail, "k_tail", torch.float16, (B, Hkv, None, D))
+        _need(v_tail, "v_tail", torch.float16, tuple(k_tail.shape))
         R = k_tail.shape[2]
-        ktp, vtp = k_tail.data_ptr(), v_tail.data_ptr()
+    if out is not None:
+        _need(out, "out", torch.float16, (B, Hq, T, D))
     lib = _lib.load()
     shape = _lib.Shape(B, Hq, Hkv, D, N, 1, 32, Nc)
     need = lib.specache_decode_attn_fp16_workspace_size(ctypes.byref(shape), T, R)
     if need == 0:
         raise ValueError("invalid decode_attn_fp16 arguments (shape, n_tokens or tail length)")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    _on_gpu(q16=q16, k_tail=k_tail, v_tail=v_tail, out=out, workspace=workspace)
+    _host_readable(k16, "k16")
+    _host_readable(v16, "v16")
+    workspace = _workspace(workspace, need, q16.device)
     if out is None:
         out = torch.empty_like(q16)
+    ktp, vtp = (k_tail.data_ptr(), v_tail.data_ptr()) if R > 0 else (0, 0)
     _lib.check(lib.specache_decode_attn_fp16(ctypes.byref(shape), q16.data_ptr(), T, k16.data_ptr(), v16.data_ptr(),
                                              ktp, vtp, R, sm_scale, out.data_ptr(), workspace.data_ptr(),
-                                             workspace.numel() * workspace.element_size(), _stream(stream)),
+                                             _nbytes(workspace), _stream(stream)),
                "specache_decode_attn_fp16")
     return out
 
@@ -423,29 +533,32 @@ def decode_step(q16: torch.Tensor, cache: LowBitCache, k_next: int, rank_row: in
     """specache_decode_step: (O, idx_next) -- decode_attn's output and the next selection
     for row rank_row from one pass over C': ranked against C' (score_topk's ranking), or
     with rank_mixed by that row of the attention itself (fetched rows and tail included)."""
-    k, ip, kp, vp, R, ktp, vtp = _attn_operands(q16, idx, k_sel, v_sel, k_tail, v_tail)
+    k, R = _attn_operands(q16, cache, idx, k_sel, v_sel, k_tail, v_tail, out)
     B, Hq, T, D = q16.shape
+    Hkv, N = cache.n_kv_heads, cache.seq_len
+    if idx_next_out is not None:
+        _need(idx_next_out, "idx_next_out", torch.int32, (B, Hkv, k_next))
+    if rank_key_out is not None:
+        _need(rank_key_out, "rank_key_out", torch.float32, (B, Hkv, N))
     sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
     lib = _lib.load()
     shape = cache.shape(Hq)
     need = lib.specache_decode_step_workspace_size(ctypes.byref(shape), T, k, R, k_next)
     if need == 0:
         raise ValueError("invalid decode_step arguments (shape, n_tokens, k, tail length or k_next)")
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q16.device)
+    _cache_on_gpu(cache, q16=q16, idx=idx if k else None, k_sel=k_sel if k else None, v_sel=v_sel if k else None,
+                  k_tail=k_tail, v_tail=v_tail, out=out, idx_next_out=idx_next_out, rank_key_out=rank_key_out,
+                  workspace=workspace)
+    workspace = _workspace(workspace, need, q16.device)
     if out is None:
         out = torch.empty_like(q16)
     if idx_next_out is None:
-        idx_next_out = torch.empty((B, cache.n_kv_heads, k_next), dtype=torch.int32, device=q16.device)
-    _need(idx_next_out, "idx_next_out", torch.int32, 3)
-    rk = 0
-    if rank_key_out is not None:
-        _need(rank_key_out, "rank_key_out", torch.float32, 3)
-        rk = rank_key_out.data_ptr()
+        idx_next_out = torch.empty((B, Hkv, k_next), dtype=torch.int32, device=q16.device)
+    rk = 0 if rank_key_out is None else rank_key_out.data_ptr()
+    ip, kp, vp, ktp, vtp = _ptrs(k, idx, k_sel, v_sel, R, k_tail, v_tail)
     _lib.check(lib.specache_decode_step(ctypes.byref(shape), q16.data_ptr(), T, rank_row, int(bool(rank_mixed)),
                                         ctypes.byref(cache.c_struct()), ip, k, kp, vp, ktp, vtp, R, sm_scale,
                                         out.data_ptr(), k_next, idx_next_out.data_ptr(), rk,
-                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                        _stream(stream)),
+                                        workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
                "specache_decode_step")
     return out, idx_next_out

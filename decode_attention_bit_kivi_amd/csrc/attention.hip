@@ -190,9 +190,9 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
     }
   };
 
-  auto pack2 = [](float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-  };
+  // round to nearest even (one v_cvt_pk_f16_f32): the sums l_part / l16 hold the unrounded p, so
+  // the rounding of the value product's operand must not lean one way
+  auto pack2 = [](float a, float b) { return pack_half2(a, b); };
   // P (float32) -> float16 A fragment; slots j < 4 hold tile-0 tokens, j >= 4 tile-1 tokens.
   auto make_p = [&](const float (&p)[NX], float mul) {
     Frag A;

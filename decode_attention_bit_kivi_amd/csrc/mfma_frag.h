@@ -48,9 +48,11 @@ __device__ __forceinline__ void signed_pairs2(uint32_t w0, uint32_t w1, int shif
   out1 = ((uint32_t)(x >> 32) & 0x80008000u) | mag1;
 }
 
+// Two floats to a float16 pair, each rounded to nearest even (gfx950: one v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  typedef float float2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, half2_t));
 }
 
 template <int NW>

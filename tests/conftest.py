@@ -27,3 +27,26 @@ def gpu():
         pytest.fail("GPU test selected but no GPU is visible")
     import torch
     return torch.device("cuda:0")
+
+
+def pytest_terminal_summary(terminalreporter):
+    from tests import parity_log
+    if not parity_log.RECORDS:
+        return
+    tr = terminalreporter
+    tr.section("measured parity margins (value / bound)")
+    worst = {}
+    for r in parity_log.RECORDS:
+        key = r["kind"]
+        if key not in worst or r["value"] / r["bound"] > worst[key]["value"] / worst[key]["bound"]:
+            worst[key] = r
+    for r in parity_log.RECORDS:
+        tr.write_line(f"{r['kind']:<18} {r['value']:.3e} / {r['bound']:.0e}  {r['test']} {r['what']}")
+    for k, r in worst.items():
+        tr.write_line(f"worst {k}: {r['value']:.3e} of {r['bound']:.0e} ({r['test']} {r['what']})")
+    path = os.environ.get("SPECACHE_PARITY_LOG")
+    if path:
+        import json
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(parity_log.RECORDS, f, indent=1)

@@ -67,3 +67,22 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stdout
+
+
+@pytest.mark.parametrize("steps,warmup,sync", [(20, 5, 2), (50, 10, 2), (7, 0, 4), (1, 3, 2), (21, 5, 4), (5, 5, 1)])
+def test_schedule_times_exactly_the_requested_steps(steps, warmup, sync):
+    """Any --steps / --warmup pair is accepted (for example --steps 20 --warmup 5 with the
+    default --sync-every 2): the timed pass holds exactly `steps` steps, the passes do not
+    overlap, and every pass but a cut-short one starts on a whole synchronisation group."""
+    w, t, i = bench.pipeline_schedule(warmup, steps, sync)
+    assert len(w) == warmup and len(t) == steps and len(i) >= steps and len(i) % sync == 0
+    assert t[0] % sync == 0 and i[0] % sync == 0
+    assert all(b == a + 1 for a, b in zip(t, t[1:])) and all(b == a + 1 for a, b in zip(i, i[1:]))
+    assert (not w or w[-1] < t[0]) and t[-1] < i[0]
+
+
+def test_steps_20_warmup_5_are_accepted():
+    args = bench.parse(["--gpus", "1", "--steps", "20", "--warmup", "5"])
+    assert (args.gpus, args.steps, args.warmup, args.sync_every) == (1, 20, 5, 2)
+    w, t, i = bench.pipeline_schedule(args.warmup, args.steps, args.sync_every)
+    assert len(t) == 20 and t[0] == 6

@@ -59,3 +59,25 @@ def test_flag_wait_ends_at_its_bound(gpu):
     flag_wait(flag, 4, tmo, max_wait_us=200)           # not reached: a second timeout
     torch.cuda.synchronize()
     assert tmo.item() == 2
+
+
+def test_pinned_tensor_freed_after_its_copy_stream_is_closed(gpu):
+    """torch's pinned-host allocator records an event on every stream a pinned block was copied
+    on when the block is freed; close() therefore retires a library stream without releasing
+    it, so a pinned tensor copied on the stream may outlive the stream object."""
+    import gc
+    for cls in (GatherStream, ComputeStream):
+        st = cls(16)
+        pinned = torch.arange(1 << 20, dtype=torch.float32).pin_memory()
+        dst = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(st.torch):
+            dst.copy_(pinned, non_blocking=True)
+        st.close()
+        assert st.handle is None
+        del st, pinned
+        gc.collect()
+        torch.cuda.synchronize()
+        assert torch.equal(dst.cpu(), torch.arange(1 << 20, dtype=torch.float32))
+    # the freed pinned blocks are reused by later allocations and copies
+    again = torch.ones(1 << 20, dtype=torch.float32).pin_memory()
+    assert float(again.cuda().sum().item()) == float(1 << 20)

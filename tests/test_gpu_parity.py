@@ -27,6 +27,7 @@ from decode_attention_bit_kivi_amd import (
     SpecacheError, gather_reuse, gather_fp16_missing, decode_attn_fp16,
 )
 from tests.layout import unpack_keys, unpack_values
+from tests.parity_log import record
 from workloads import get_config, generate_all
 
 pytestmark = pytest.mark.gpu
@@ -70,19 +71,40 @@ def _assert_quantize_exact(cache, ref, bits, slices=None):
         assert np.array_equal(got[sel].view(np.uint16), want[sel].view(np.uint16)), "metadata differs"
 
 
-def _assert_topk(idx_gpu, r_ref, k, slices):
+def _assert_topk(idx_gpu, r_ref, k, slices, what=""):
+    """Same count, strictly ascending, and every position in the symmetric difference with the
+    oracle's set within the tie band of the k-th largest oracle rank.  Records the widest
+    distance from the k-th rank over the symmetric difference (0 when the sets are equal)."""
+    widest, n_diff = 0.0, 0
     for (b, h) in slices:
         got = idx_gpu[b, h]
         assert len(got) == k and np.all(np.diff(got) > 0), "not strictly ascending"
         want = oracle.topk_positions(r_ref[b:b + 1, h:h + 1], k)[0, 0]
         kth = np.sort(r_ref[b, h])[::-1][k - 1]
         diff = np.setxor1d(got, want)
-        bad = [p for p in diff if abs(r_ref[b, h, p] - kth) >= TIE_BAND]
+        n_diff += len(diff)
+        dist = [abs(r_ref[b, h, p] - kth) for p in diff]
+        widest = max([widest] + dist)
+        bad = [p for p, d in zip(diff, dist) if d >= TIE_BAND]
         assert not bad, f"slice {(b, h)}: positions {bad[:8]} outside the tie band"
+    record("topk_tie_distance", widest, TIE_BAND, f"{what} ({n_diff} positions differ over {len(slices)} slices)")
 
 
 def _attn_err(o_gpu, o_ref):
     return float(np.max(np.abs(o_gpu.astype(np.float64) - o_ref)) / np.max(np.abs(o_ref)))
+
+
+def _check_attn(o_gpu, o_ref, what=""):
+    """max |O_gpu - O_ref| / max |O_ref| within ATTN_TOL; the measured error is recorded."""
+    err = _attn_err(o_gpu, o_ref)
+    record("attention_rel_err", err, ATTN_TOL, what)
+    assert err <= ATTN_TOL, f"attention relative error {err:.3e} > {ATTN_TOL} {what}"
+
+
+def _check_rank_keys(rk_gpu, r_ref, what=""):
+    err = float(np.max(np.abs(rk_gpu - r_ref)))
+    record("rank_key_abs_err", err, 1e-4, what)
+    assert err < 1e-4, f"r(p) error {err:.3e} {what}"
 
 
 # ---------------------------------------------------------------- quantize_pack
@@ -129,12 +151,12 @@ def test_group_64(gpu, bits, D):
     of, nxt = decode_step(_dev(Q), cache, cfg.top_k, idx=_dev(idx), k_sel=_dev(sk), v_sel=_dev(sv))
     torch.cuda.synchronize()
     r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
-    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    _check_rank_keys(_np(rk), r_ref)
     slices = [(0, h) for h in range(cfg.n_kv_heads)]
     _assert_topk(_np(sel), r_ref, cfg.top_k, slices)
     _assert_topk(_np(nxt), r_ref, cfg.top_k, slices)
     ref = oracle.mixed_attention(Q, kh, vh, idx, sk, sv, sm_scale=cfg.sm_scale)
-    assert _attn_err(_np(o), ref) <= ATTN_TOL
+    _check_attn(_np(o), ref)
     assert torch.equal(of.view(torch.int16), o.view(torch.int16))
 
 
@@ -161,7 +183,7 @@ def test_mixed_key_value_bits(gpu, kbits, vbits):
     of, nxt = decode_step(_dev(Q), cache, cfg.top_k, idx=_dev(idx), k_sel=_dev(sk), v_sel=_dev(sv))
     torch.cuda.synchronize()
     ref = oracle.mixed_attention(Q, kh, vh, idx, sk, sv, sm_scale=cfg.sm_scale)
-    assert _attn_err(_np(o), ref) <= ATTN_TOL
+    _check_attn(_np(o), ref)
     assert torch.equal(of.view(torch.int16), o.view(torch.int16))
     r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
     _assert_topk(_np(nxt), r_ref, cfg.top_k, [(0, h) for h in range(cfg.n_kv_heads)])
@@ -208,10 +230,13 @@ def test_quantize_infinite_scale_groups(gpu, bits):
     _assert_quantize_exact(cache, ref, bits)
 
 
-@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
+FULL_SIZE_SLICES = 4   # seeded (batch, KV head) slices filled and checked per full-size workload
+
+
+@pytest.mark.parametrize("name", ["mistral32k", "long128k", "layers32"])
 def test_quantize_full_size_sampled(gpu, name):
     cfg = get_config(name)
-    sl = _sampled(cfg, 3)
+    sl = _sampled(cfg, FULL_SIZE_SLICES)
     K, V, _, _, _, _ = generate_all(cfg, slices=sl)
     cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
     torch.cuda.synchronize()
@@ -245,7 +270,7 @@ def test_score_topk_matches_oracle(gpu, name, over):
     r_ref = oracle.rank_scores(Q, kh, row, cfg.sm_scale)
     slices = [(b, h) for b in range(cfg.batch) for h in range(cfg.n_kv_heads)]
     _assert_topk(_np(idx), r_ref, cfg.top_k, slices)
-    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    _check_rank_keys(_np(rk), r_ref)
 
 
 @pytest.mark.parametrize("qscale", [0.0, 1e-3, 1.0])
@@ -265,7 +290,7 @@ def test_score_topk_crowded_and_tied_ranks(gpu, qscale):
     if qscale == 0.0:
         assert np.array_equal(idx, np.broadcast_to(np.arange(cfg.top_k, dtype=np.int32), idx.shape))
     _assert_topk(idx, r_ref, cfg.top_k, slices)
-    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    _check_rank_keys(_np(rk), r_ref)
 
 
 @pytest.mark.parametrize("seq_len", [32768, 32768 + 64])
@@ -288,19 +313,20 @@ def test_selection_same_with_and_without_key_output(gpu, seq_len):
     assert torch.equal(a, b) and torch.equal(na, nb)
 
 
-@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
-def test_score_topk_full_size_sampled(gpu, name):
+@pytest.mark.parametrize("name,rank_row", [("mistral32k", 1), ("long128k", 1), ("layers32", 1),
+                                           ("mistral32k", 0)])   # row 0 of two: the serial comparator's ranking
+def test_score_topk_full_size_sampled(gpu, name, rank_row):
     cfg = get_config(name)
-    sl = _sampled(cfg, 3)
+    sl = _sampled(cfg, FULL_SIZE_SLICES)
     K, V, Q, planted, _, _ = generate_all(cfg, slices=sl)
     cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
-    idx = _np(score_topk(_dev(Q), cache, cfg.top_k))
+    idx = _np(score_topk(_dev(Q), cache, cfg.top_k, rank_row=rank_row))
     for (b, h) in sl:
         G = cfg.gqa
         q = Q[b:b + 1, h * G:(h + 1) * G]
         _, kh, _ = _reference_cache(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], cfg.bits)
-        r_ref = oracle.rank_scores(q, kh, 1, cfg.sm_scale)
-        _assert_topk(idx[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)])
+        r_ref = oracle.rank_scores(q, kh, rank_row, cfg.sm_scale)
+        _assert_topk(idx[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)], f"{name} row {rank_row} slice {(b, h)}")
         if cfg.n_planted:
             assert np.isin(planted[b, h], idx[b, h]).mean() >= 0.9
 
@@ -444,8 +470,7 @@ def test_decode_attn_matches_oracle(gpu, name, over, mode):
                       None if KT is None else _dev(KT), None if VT is None else _dev(VT))
     torch.cuda.synchronize()
     ref = oracle.mixed_attention(Q, kh, vh, idx, ks, vs, KT, VT, sm_scale=cfg.sm_scale)
-    err = _attn_err(_np(out), ref)
-    assert err <= ATTN_TOL, err
+    _check_attn(_np(out), ref, f"{name} {over} {mode}")
 
 
 @pytest.mark.parametrize("name,over,mode", [
@@ -488,9 +513,9 @@ def test_fused_step_matches_separate_calls(gpu, name, over, mode):
     r_ref = oracle.rank_scores(Q, kh, row, cfg.sm_scale)
     slices = [(b, h) for b in range(B) for h in range(Hkv)]
     _assert_topk(_np(idx_next), r_ref, cfg.top_k, slices)
-    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    _check_rank_keys(_np(rk), r_ref)
     ref = oracle.mixed_attention(Q, kh, vh, idx, ks, vs, KT, VT, sm_scale=cfg.sm_scale)
-    assert _attn_err(_np(o_fused), ref) <= ATTN_TOL
+    _check_attn(_np(o_fused), ref)
 
 
 @pytest.mark.parametrize("name,over,mode", [
@@ -534,7 +559,7 @@ def test_fused_step_mixed_cache_rank(gpu, name, over, mode):
     _, kh, _ = _reference_cache(K, V, cfg.bits)
     r_ref = oracle.rank_scores_mixed(Q, kh, row, cfg.sm_scale, idx=idx, k_sel=ks, k_tail=KT)
     _assert_topk(_np(idx_next), r_ref, cfg.top_k, [(b, h) for b in range(B) for h in range(Hkv)])
-    assert np.max(np.abs(_np(rk) - r_ref)) < 1e-4
+    _check_rank_keys(_np(rk), r_ref)
 
 
 def test_fused_step_next_selection_may_alias_current(gpu):
@@ -558,15 +583,17 @@ def test_fused_step_next_selection_may_alias_current(gpu):
     _assert_topk(_np(want_next), r_ref, cfg.top_k, slices)
 
 
-@pytest.mark.parametrize("name,mixed,stream", [("mistral32k", False, "device"), ("long128k", False, "device"),
-                                               ("mistral32k", True, "device"), ("mistral32k", False, "bench")])
-def test_fused_step_full_size_sampled(gpu, name, mixed, stream):
+@pytest.mark.parametrize("name,mixed,stream,rank_row", [
+    ("mistral32k", False, "device", 1), ("long128k", False, "device", 1), ("mistral32k", True, "device", 1),
+    ("mistral32k", False, "bench", 1), ("layers32", False, "bench", 1), ("mistral32k", False, "bench", 0)])
+def test_fused_step_full_size_sampled(gpu, name, mixed, stream, rank_row):
     """The fused step at full size: score_topk seeds the selection, the step gathers its rows
     from pinned host memory and returns the next selection (ranked against C', or by the
-    mixed-cache attention row).  stream = "bench": on the compute stream bench.py times (every
-    compute unit but 32, so the split plan is the benchmark's); "device": the whole device."""
+    mixed-cache attention row; by the speculative row, or by the real one).  stream = "bench":
+    on the compute stream bench.py times (every compute unit but 32, so the split plan is the
+    benchmark's); "device": the whole device."""
     cfg = get_config(name)
-    sl = _sampled(cfg, 3)
+    sl = _sampled(cfg, FULL_SIZE_SLICES)
     K, V, Q, _, _, _ = generate_all(cfg, slices=sl)
     cs = ComputeStream(32) if stream == "bench" else None
     comp = cs.torch if cs else torch.cuda.current_stream()
@@ -577,7 +604,8 @@ def test_fused_step_full_size_sampled(gpu, name, mixed, stream):
         q = _dev(Q)
         idx = score_topk(q, cache, cfg.top_k)
         ks, vs = gather_fp16(idx, hk, hv)
-        out, nxt = decode_step(q, cache, cfg.top_k, rank_mixed=mixed, idx=idx, k_sel=ks, v_sel=vs)
+        out, nxt = decode_step(q, cache, cfg.top_k, rank_row=rank_row, rank_mixed=mixed, idx=idx, k_sel=ks,
+                               v_sel=vs)
         comp.synchronize()
     idx_np, out, nxt = _np(idx), _np(out), _np(nxt)
     if cs:
@@ -589,12 +617,13 @@ def test_fused_step_full_size_sampled(gpu, name, mixed, stream):
         i = idx_np[b:b + 1, h:h + 1]
         rks, rvs = oracle.gather_rows(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], i)
         ref = oracle.mixed_attention(q1, kh, vh, i, rks, rvs, sm_scale=cfg.sm_scale)
-        assert _attn_err(out[b:b + 1, h * G:(h + 1) * G], ref) <= ATTN_TOL
+        what = f"{name} {'mixed' if mixed else 'lowbit'} {stream} row {rank_row} slice {(b, h)}"
+        _check_attn(out[b:b + 1, h * G:(h + 1) * G], ref, what)
         if mixed:
-            r_ref = oracle.rank_scores_mixed(q1, kh, 1, cfg.sm_scale, idx=i, k_sel=rks)
+            r_ref = oracle.rank_scores_mixed(q1, kh, rank_row, cfg.sm_scale, idx=i, k_sel=rks)
         else:
-            r_ref = oracle.rank_scores(q1, kh, 1, cfg.sm_scale)
-        _assert_topk(nxt[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)])
+            r_ref = oracle.rank_scores(q1, kh, rank_row, cfg.sm_scale)
+        _assert_topk(nxt[b:b + 1, h:h + 1], r_ref, cfg.top_k, [(0, 0)], what)
 
 
 @pytest.mark.parametrize("name,over", [
@@ -617,7 +646,7 @@ def test_fp16_comparator_matches_oracle(gpu, name, over):
     torch.cuda.synchronize()
     ref = oracle.mixed_attention(Q, K.astype(np.float64), V.astype(np.float64), sm_scale=cfg.sm_scale, k_tail=KT,
                                  v_tail=VT)
-    assert _attn_err(_np(out), ref) <= ATTN_TOL
+    _check_attn(_np(out), ref)
     cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
     idx = np.broadcast_to(np.arange(N, dtype=np.int32), (B, H, N)).copy()
     o_all = decode_attn(_dev(Q), cache, _dev(idx), _dev(K), _dev(V), kt, vt)
@@ -625,18 +654,27 @@ def test_fp16_comparator_matches_oracle(gpu, name, over):
     assert _attn_err(_np(out), _np(o_all).astype(np.float64)) <= 1e-3
 
 
-@pytest.mark.parametrize("name", ["mistral32k", "long128k"])
-def test_decode_step_full_size_sampled(gpu, name):
-    """The whole step at full size: score_topk -> gather from pinned host -> decode_attn."""
+@pytest.mark.parametrize("name,stream", [("mistral32k", "device"), ("long128k", "device"), ("layers32", "bench"),
+                                         ("mistral32k", "bench")])
+def test_decode_step_full_size_sampled(gpu, name, stream):
+    """The whole step at full size in four calls: score_topk -> gather from pinned host ->
+    decode_attn (stream as in test_fused_step_full_size_sampled)."""
     cfg = get_config(name)
-    sl = _sampled(cfg, 3)
+    sl = _sampled(cfg, FULL_SIZE_SLICES)
     K, V, Q, _, _, _ = generate_all(cfg, slices=sl)
-    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
-    idx = score_topk(_dev(Q), cache, cfg.top_k)
+    cs = ComputeStream(32) if stream == "bench" else None
+    comp = cs.torch if cs else torch.cuda.current_stream()
+    comp.wait_stream(torch.cuda.current_stream())
     hk, hv = torch.from_numpy(K).pin_memory(), torch.from_numpy(V).pin_memory()
-    ks, vs = gather_fp16(idx, hk, hv)
-    out = _np(decode_attn(_dev(Q), cache, idx, ks, vs))
-    idx = _np(idx)
+    with torch.cuda.stream(comp):
+        cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+        idx = score_topk(_dev(Q), cache, cfg.top_k)
+        ks, vs = gather_fp16(idx, hk, hv)
+        out = decode_attn(_dev(Q), cache, idx, ks, vs)
+        comp.synchronize()
+    out, idx = _np(out), _np(idx)
+    if cs:
+        cs.close()
     G = cfg.gqa
     for (b, h) in sl:
         q = Q[b:b + 1, h * G:(h + 1) * G]
@@ -644,7 +682,9 @@ def test_decode_step_full_size_sampled(gpu, name):
         i = idx[b:b + 1, h:h + 1]
         rks, rvs = oracle.gather_rows(K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], i)
         ref = oracle.mixed_attention(q, kh, vh, i, rks, rvs, sm_scale=cfg.sm_scale)
-        assert _attn_err(out[b:b + 1, h * G:(h + 1) * G], ref) <= ATTN_TOL
+        _check_attn(out[b:b + 1, h * G:(h + 1) * G], ref, f"{name} {stream} slice {(b, h)}")
+        r_ref = oracle.rank_scores(q, kh, 1, cfg.sm_scale)
+        _assert_topk(i, r_ref, cfg.top_k, [(0, 0)], f"{name} {stream} slice {(b, h)}")
 
 
 def test_gather_on_cu_limited_stream(gpu):
