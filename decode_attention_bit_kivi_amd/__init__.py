@@ -9,7 +9,7 @@ from .api import (
     LowBitCache, empty_cache, lowbit_sizes, quantize_pack, score_topk, score_topk_workspace_size,
     gather_fp16, decode_attn, decode_attn_workspace_size, decode_step, decode_step_workspace_size,
     GatherStream, ComputeStream, gather_reuse, gather_fp16_missing, quantize_append, offload_fp16,
-    decode_attn_fp16, flag_set, flag_wait,
+    decode_attn_fp16, flag_set, flag_wait, decode_step_noalloc,
 )
 from ._lib import SpecacheError
 
@@ -17,6 +17,6 @@ __all__ = [
     "LowBitCache", "empty_cache", "lowbit_sizes", "quantize_pack", "score_topk",
     "score_topk_workspace_size", "gather_fp16", "decode_attn", "decode_attn_workspace_size",
     "decode_step", "decode_step_workspace_size", "GatherStream", "ComputeStream", "gather_reuse", "gather_fp16_missing",
-    "quantize_append", "offload_fp16", "decode_attn_fp16", "flag_set", "flag_wait",
+    "quantize_append", "offload_fp16", "decode_attn_fp16", "flag_set", "flag_wait", "decode_step_noalloc",
     "SpecacheError",
 ]

@@ -14,7 +14,7 @@ import threading
 LIB_PATH = os.environ.get("SPECACHE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libspecache.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 SPECACHE_OK = 0
 SPECACHE_ERR_INVALID = 1
@@ -22,6 +22,8 @@ SPECACHE_ERR_UNSUPPORTED = 2
 SPECACHE_ERR_WORKSPACE = 3
 SPECACHE_ERR_NOT_PINNED = 4
 SPECACHE_ERR_HIP = 5
+SPECACHE_ERR_TOO_LARGE = 6
+NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SPECACHE_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "specache_lowbit_bytes",
@@ -39,6 +41,7 @@ EXPORTED = (
     "specache_decode_attn_fp16",
     "specache_decode_step_workspace_size",
     "specache_decode_step",
+    "specache_decode_step_noalloc",
     "specache_gather_stream_create",
     "specache_compute_stream_create",
     "specache_stream_destroy",
@@ -111,6 +114,7 @@ def load() -> ctypes.CDLL:
             "specache_decode_attn_fp16": (I, [SP, P, I, P, P, P, P, I, F, P, P, SZ, P]),
             "specache_decode_step_workspace_size": (SZ, [SP, I, I, I, I]),
             "specache_decode_step": (I, [SP, P, I, I, I, LP, P, I, P, P, P, P, I, F, P, I, P, P, P, SZ, P]),
+            "specache_decode_step_noalloc": (I, [SP, P, I, I, I, LP, P, I, P, P, P, P, I, F, P, I, P, P, P]),
             "specache_gather_stream_create": (I, [I, ctypes.POINTER(P)]),
             "specache_compute_stream_create": (I, [I, ctypes.POINTER(P)]),
             "specache_stream_destroy": (I, [P]),

@@ -562,3 +562,33 @@ def decode_step(q16: torch.Tensor, cache: LowBitCache, k_next: int, rank_row: in
                                         workspace.data_ptr(), _nbytes(workspace), _stream(stream)),
                "specache_decode_step")
     return out, idx_next_out
+
+
+def decode_step_noalloc(q16: torch.Tensor, cache: LowBitCache, k_next: int, rank_row: int = 1,
+                        rank_mixed: bool = False, idx: torch.Tensor | None = None, k_sel: torch.Tensor | None = None,
+                        v_sel: torch.Tensor | None = None, k_tail: torch.Tensor | None = None,
+                        v_tail: torch.Tensor | None = None, sm_scale: float | None = None,
+                        out: torch.Tensor = None, idx_next_out: torch.Tensor = None,
+                        rank_key_out: torch.Tensor | None = None, stream=None):
+    """specache_decode_step_noalloc: decode_step with its scratch in the library's static device
+    array (no workspace; out and idx_next_out are the caller's, so nothing is allocated here
+    either).  Calls that overlap on one GPU race on the array."""
+    k, R = _attn_operands(q16, cache, idx, k_sel, v_sel, k_tail, v_tail, out)
+    B, Hq, T, D = q16.shape
+    Hkv, N = cache.n_kv_heads, cache.seq_len
+    if out is None or idx_next_out is None:
+        raise ValueError("decode_step_noalloc allocates nothing: pass out and idx_next_out")
+    _need(idx_next_out, "idx_next_out", torch.int32, (B, Hkv, k_next))
+    if rank_key_out is not None:
+        _need(rank_key_out, "rank_key_out", torch.float32, (B, Hkv, N))
+    sm_scale = 1.0 / math.sqrt(D) if sm_scale is None else float(sm_scale)
+    _cache_on_gpu(cache, q16=q16, idx=idx if k else None, k_sel=k_sel if k else None, v_sel=v_sel if k else None,
+                  k_tail=k_tail, v_tail=v_tail, out=out, idx_next_out=idx_next_out, rank_key_out=rank_key_out)
+    rk = 0 if rank_key_out is None else rank_key_out.data_ptr()
+    ip, kp, vp, ktp, vtp = _ptrs(k, idx, k_sel, v_sel, R, k_tail, v_tail)
+    _lib.check(_lib.load().specache_decode_step_noalloc(
+        ctypes.byref(cache.shape(Hq)), q16.data_ptr(), T, rank_row, int(bool(rank_mixed)),
+        ctypes.byref(cache.c_struct()), ip, k, kp, vp, ktp, vtp, R, sm_scale, out.data_ptr(), k_next,
+        idx_next_out.data_ptr(), rk, _stream(stream)),
+        "specache_decode_step_noalloc")
+    return out, idx_next_out

@@ -1,7 +1,9 @@
 // The C ABI declared in include/specache.h: argument validation on the host,
 // workspace carving, and dispatch to the kernel launchers.  Nothing here
-// allocates memory or keeps state.
+// allocates memory; the only state is the per-device address of the
+// no-allocation decode step's static scratch array.
 #include <cstring>
+#include <mutex>
 
 #include "../../include/specache.h"
 #include "common.h"
@@ -419,11 +421,15 @@ size_t specache_decode_step_workspace_size(const specache_shape* shape, int n_to
   return attn_ws(d, n_tokens).total_step;
 }
 
-int specache_decode_step(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
-                         int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k, const void* k_sel,
-                         const void* v_sel, const void* k_tail, const void* v_tail, int tail_len, float sm_scale,
-                         void* out16, int k_next, int32_t* idx_next_out, float* rank_key_out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_step_impl(const specache_shape* shape, const void* q16, int n_tokens, int rank_row, int rank_mixed,
+                     const specache_lowbit* cache, const int32_t* idx, int k, const void* k_sel, const void* v_sel,
+                     const void* k_tail, const void* v_tail, int tail_len, float sm_scale, void* out16, int k_next,
+                     int32_t* idx_next_out, float* rank_key_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   Dims d;
   int err;
   if (!make_dims(shape, &d, &err)) return err;
@@ -452,6 +458,76 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
   const MergeJob merge{a.part_ml, a.part_acc, plan.S, (int64_t)d.B * d.Hq * n_tokens, a.out16};
   return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys,
                                        rank_key_out != nullptr, a.rank_hist, idx_next_out, &merge, s));
+}
+
+// The no-allocation decode step's scratch: one array per GPU, in the library's code object, held
+// until the process ends.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in for the symbol); the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SPECACHE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's scratch address, or null (status in *err).
+void* scratch_address(int* err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *err = SPECACHE_ERR_HIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = SPECACHE_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    if (slot.err != hipSuccess) slot.ptr = nullptr;
+  });
+  if (slot.err != hipSuccess || !slot.ptr) {
+    *err = SPECACHE_ERR_HIP;
+    return nullptr;
+  }
+  *err = SPECACHE_OK;
+  return slot.ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int specache_decode_step(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
+                         int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k, const void* k_sel,
+                         const void* v_sel, const void* k_tail, const void* v_tail, int tail_len, float sm_scale,
+                         void* out16, int k_next, int32_t* idx_next_out, float* rank_key_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_step_impl(shape, q16, n_tokens, rank_row, rank_mixed, cache, idx, k, k_sel, v_sel, k_tail, v_tail,
+                          tail_len, sm_scale, out16, k_next, idx_next_out, rank_key_out, workspace, workspace_bytes,
+                          stream);
+}
+
+int specache_decode_step_noalloc(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
+                                 int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k,
+                                 const void* k_sel, const void* v_sel, const void* k_tail, const void* v_tail,
+                                 int tail_len, float sm_scale, void* out16, int k_next, int32_t* idx_next_out,
+                                 float* rank_key_out, void* stream) {
+  const size_t need = specache_decode_step_workspace_size(shape, n_tokens, k, tail_len, k_next);
+  if (need > SPECACHE_NOALLOC_SCRATCH_BYTES) return SPECACHE_ERR_TOO_LARGE;
+  int err = SPECACHE_OK;
+  void* ws = nullptr;
+  if (need > 0) {  // else the arguments are invalid: decode_step_impl names the error
+    ws = scratch_address(&err);
+    if (!ws) return err;
+  }
+  return decode_step_impl(shape, q16, n_tokens, rank_row, rank_mixed, cache, idx, k, k_sel, v_sel, k_tail, v_tail,
+                          tail_len, sm_scale, out16, k_next, idx_next_out, rank_key_out, ws,
+                          ws ? (size_t)SPECACHE_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 namespace {
@@ -501,6 +577,8 @@ const char* specache_status_string(int status) {
     case SPECACHE_ERR_WORKSPACE: return "workspace missing or too small";
     case SPECACHE_ERR_NOT_PINNED: return "gather source is neither device memory nor pinned host memory";
     case SPECACHE_ERR_HIP: return "HIP runtime error";
+    case SPECACHE_ERR_TOO_LARGE:
+      return "problem needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }

@@ -35,7 +35,9 @@
  *    them.  Ordering across streams is the caller's job (HIP events).
  *  - The library keeps no state and allocates nothing: scratch space comes
  *    from a caller-provided workspace whose size the *_workspace_size
- *    functions return.
+ *    functions return.  (One exception: specache_decode_step_noalloc, for
+ *    callers that cannot allocate, keeps its scratch in a static array of the
+ *    library's device code.)
  *  - The attention calls split the positions of each slice over a number of
  *    workgroups chosen for the compute units `stream` may use (its CU mask,
  *    else the whole device).  Results are deterministic for a given stream
@@ -124,7 +126,7 @@
 extern "C" {
 #endif
 
-#define SPECACHE_ABI_VERSION 5
+#define SPECACHE_ABI_VERSION 6
 
 typedef enum specache_status {
   SPECACHE_OK = 0,
@@ -132,7 +134,8 @@ typedef enum specache_status {
   SPECACHE_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128, group != 32, G*T > 16 */
   SPECACHE_ERR_WORKSPACE = 3,   /* workspace null or smaller than the *_workspace_size value */
   SPECACHE_ERR_NOT_PINNED = 4,  /* gather source is neither device memory nor pinned host memory */
-  SPECACHE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+  SPECACHE_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed */
+  SPECACHE_ERR_TOO_LARGE = 6    /* specache_decode_step_noalloc: scratch needed beyond its static buffer */
 } specache_status;
 
 /* Shape of one layer's cache.  group must be 32. */
@@ -385,6 +388,29 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
                          const void* v_tail, int tail_len, float sm_scale, void* out16,
                          int k_next, int32_t* idx_next_out, float* rank_key_out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * specache_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same call and result
+ * (same kernels; out16 and idx_next_out identical to specache_decode_step's on the same stream)
+ * with its scratch in a static device array of the library instead of a caller workspace.
+ * Allocates nothing: no hipMalloc / hipFree on any call.
+ *
+ * The array holds SPECACHE_NOALLOC_SCRATCH_BYTES per GPU (every GPU the library runs on keeps its
+ * own copy until the process ends); a problem whose specache_decode_step_workspace_size exceeds
+ * it returns SPECACHE_ERR_TOO_LARGE before anything is enqueued (96 MiB holds, for example, the
+ * 32K-context step at batch 16 with 8 KV heads, 32 query heads and k = 328).  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents (no part of it needs to start
+ * at zero: the kernels clear what they accumulate into).  Calls on one stream are ordered; calls
+ * that overlap on one GPU (several streams, or several host threads) race on the array and give
+ * undefined results.  Other arguments and errors as for specache_decode_step.
+ */
+#define SPECACHE_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+int specache_decode_step_noalloc(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
+                                 int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k,
+                                 const void* k_sel, const void* v_sel, const void* k_tail, const void* v_tail,
+                                 int tail_len, float sm_scale, void* out16, int k_next, int32_t* idx_next_out,
+                                 float* rank_key_out, void* stream);
 
 /*
  * The 16-bit comparator: O = Attn(q, C) over the full 16-bit cache held in

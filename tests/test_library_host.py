@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.specache_abi_version() == _lib.ABI_VERSION
-    for code in range(6):
+    for code in range(7):
         assert lib.specache_status_string(code)
     assert lib.specache_status_string(99) == b"unknown status"
 
@@ -228,3 +228,19 @@ def test_flag_argument_validation(lib):
     assert lib.specache_flag_wait(None, 1, 100, 1, None) == inv
     assert lib.specache_flag_wait(1, 1, 100, None, None) == inv
     assert lib.specache_flag_wait(1, 1, 0, 1, None) == inv
+
+
+def test_noalloc_step_refuses_sizes_beyond_its_scratch_before_any_hip_call(lib):
+    """The no-allocation decode step checks the scratch it would need against its static array
+    on the host: too large -> SPECACHE_ERR_TOO_LARGE, bad arguments -> their own status."""
+    big = _shape(batch=32, n_q_heads=32, n_kv_heads=8, seq_len=32768)
+    need = lib.specache_decode_step_workspace_size(ctypes.byref(big), 2, 328, 0, 328)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    lb = _lib.LowBit(1, 1, 1, 1)
+    call = lambda s, k_next=328, T=2: lib.specache_decode_step_noalloc(  # noqa: E731
+        ctypes.byref(s), 1, T, 1, 0, ctypes.byref(lb), 1, 328, 1, 1, None, None, 0, 0.1, 1, k_next, 1, None, None)
+    assert call(big) == _lib.SPECACHE_ERR_TOO_LARGE
+    small = _shape(batch=2, n_q_heads=32, n_kv_heads=8, seq_len=4096)
+    assert call(small, k_next=0) == _lib.SPECACHE_ERR_INVALID        # k_next < 1: invalid, not "too large"
+    assert call(small, T=3) == _lib.SPECACHE_ERR_INVALID
+    assert lib.specache_decode_step_workspace_size(ctypes.byref(small), 2, 328, 0, 328) <= _lib.NOALLOC_SCRATCH_BYTES
