@@ -77,7 +77,7 @@ ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
 struct AttnWs {
   size_t ml, acc, total;
   // fused step only:
-  size_t logits, rank_m, rank_l, keys, hist, total_step;
+  size_t logits, rank_m, rank_l, keys, hist, gmax, total_step;
 };
 
 // Sized for attn_max_splits, the most splits any launch plan uses.
@@ -99,6 +99,8 @@ AttnWs attn_ws(const Dims& d, int T) {
   off += align256(sizeof(float) * (size_t)d.slices() * d.N);
   w.hist = off;
   off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
+  w.gmax = off;  // per-16-position logit maxima of the pruned selection
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / 16));
   w.total_step = off;
   return w;
 }
@@ -453,11 +455,17 @@ int decode_step_impl(const specache_shape* shape, const void* q16, int n_tokens,
   a.rank_l = reinterpret_cast<float*>(base + ws.rank_l);
   a.rank_hist = reinterpret_cast<uint32_t*>(base + ws.hist);
   float* keys = rank_key_out ? rank_key_out : reinterpret_cast<float*>(base + ws.keys);
+  // bounds for the pruned selection: ranking against C' (the mixed-cache ranking replaces the
+  // fetched rows' logits after they are written), no key output, one bound group per selected
+  // position at most (G * T <= 8 follows from G <= 4)
+  if (!rank_mixed && !rank_key_out && rank_select_prunable(d, k_next))
+    a.rank_gmax = reinterpret_cast<float*>(base + ws.gmax);
   // the split merge runs inside the selection's launch, on the compute units it leaves idle
   if (launch_attn_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
   const MergeJob merge{a.part_ml, a.part_acc, plan.S, (int64_t)d.B * d.Hq * n_tokens, a.out16};
   return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys,
-                                       rank_key_out != nullptr, a.rank_hist, idx_next_out, &merge, s));
+                                       rank_key_out != nullptr, a.rank_hist, idx_next_out, &merge, s,
+                                       a.rank_gmax));
 }
 
 // The no-allocation decode step's scratch: one array per GPU, in the library's code object, held

@@ -789,6 +789,299 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
   }
 }
 
+// ---- rank_select from per-16-position bounds (the fused step, slices of at most kResidentN
+// positions, at most kFusedG heads).  r(p) is non-decreasing in every head's logit, so with M_g
+// the maximum of head g's logits over a group of 16 positions:
+//   U = r(M_1, .., M_G)             bounds r from above over the group, and
+//   L = max_g (M_g - LSE_g)         from below at the position holding that maximum (r is at
+//                                   least any one head's log-probability);
+// at least k positions therefore have r >= the k-th largest L, and only a group whose U reaches
+// that value can hold a selected position.  The kernel reads the bounds, the logits of those
+// groups only, and selects among their positions exactly as the resident selection does.
+constexpr int kGrp = 16;                            // positions per bound group
+constexpr int kMaxGroups = (int)(kResidentN / kGrp);  // 2048: two groups per thread
+constexpr float kBoundMargin = 1e-3f;               // slack on U for the rounding of its arithmetic
+
+static_assert(kMaxGroups == 2 * kSelThreads, "two bound groups per thread");
+
+struct PrunedSmem {
+  uint32_t hist[kBins];
+  uint32_t scan_scratch[2 * kSelWaves];
+  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t res[4];  // small-bin selection: thr, need_eq, n_eq, found
+  float bin_vals[2];
+  float lse2[kFusedG];
+  uint32_t n_grp;
+  uint16_t grp[kMaxGroups];  // candidate groups, ascending
+  uint32_t cand[kCand];
+};
+
+struct PrunedRank {
+  const float* logits;  // [slices][G][N], log2 units
+  const float* part_m;  // [slices][G][S]
+  const float* part_l;
+  const float* gmax;    // [slices][G][N / 16], log2 units
+  int G, S;
+};
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t N, int k, float r_lo,
+                                                                         int32_t* __restrict__ idx_out,
+                                                                         unsigned n_sel, MergeJob mj, PrunedRank pr) {
+  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
+    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
+    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
+    return;
+  }
+  __shared__ PrunedSmem sm;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t slice = blockIdx.x;
+  const int G = pr.G, S = pr.S;
+  const int ngrp = (int)(N / kGrp);  // N is a multiple of 32 and at most kResidentN
+
+  // the bounds of groups 2t and 2t + 1 (a float2 per head) and the first split statistics are
+  // loaded before anything waits
+  float2 gm[kFusedG];
+  {
+    const float* gp = pr.gmax + slice * G * ngrp;
+    const int i0 = 2 * t < ngrp ? 2 * t : 0;
+#pragma unroll
+    for (int g = 0; g < kFusedG; ++g) gm[g] = *reinterpret_cast<const float2*>(gp + (g < G ? g : 0) * ngrp + i0);
+  }
+  const int hw = wave < G ? wave : 0;
+  const int64_t sb = (slice * G + hw) * S;
+  const int j0 = lane < S ? lane : 0;
+  const float m_first = pr.part_m[sb + j0], l_first = pr.part_l[sb + j0];
+  asm volatile("" ::: "memory");
+  sm.hist[t] = 0u;
+  sm.hist[t + kSelThreads] = 0u;
+  if (wave < kFusedG) {
+    const float l2 = head_lse2<64>(pr.part_m + sb, pr.part_l + sb, S, lane, m_first, l_first);
+    if (wave < G && lane == 0) sm.lse2[wave] = l2;
+  }
+  if (t == 0) {
+    sm.n_cand = 0u;
+    sm.res[3] = 0u;
+  }
+  __syncthreads();
+  float lse2[kFusedG];
+#pragma unroll
+  for (int g = 0; g < kFusedG; ++g) lse2[g] = g < G ? sm.lse2[g] : 0.0f;
+
+  // U and L of the two groups (the arithmetic of rank_of, on the maxima)
+  float U[2], L[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float lp[kFusedG];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < kFusedG; ++g)
+      if (g < G) {
+        lp[g] = (s == 0 ? gm[g].x : gm[g].y) - lse2[g];
+        mx = fmaxf(mx, lp[g]);
+      }
+    float sum = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kFusedG; ++g)
+      if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
+    U[s] = (mx + __builtin_amdgcn_logf(sum)) * kLn2 + kBoundMargin;
+    L[s] = mx * kLn2 + 0.0f;
+  }
+  const bool gv0 = 2 * t < ngrp, gv1 = 2 * t + 1 < ngrp;
+
+  // tau_lo: below the k-th largest L (the lower edge of the coarse bin holding it, one bin down)
+  float tau_lo = -INFINITY;
+  if (k <= ngrp) {
+    if (gv0) atomicAdd(&sm.hist[coarse_bin(L[0], r_lo)], 1u);
+    if (gv1) atomicAdd(&sm.hist[coarse_bin(L[1], r_lo)], 1u);
+    __syncthreads();
+    uint32_t bin, above;
+    pick_digit(sm, kBins, (uint32_t)k, bin, above);
+    if (bin > 0u) tau_lo = r_lo + (float)(bin - 1u) / kBinScale;
+    sm.hist[t] = 0u;
+    sm.hist[t + kSelThreads] = 0u;
+  }
+  // candidate groups, compacted in ascending order
+  const bool c0 = gv0 && U[0] >= tau_lo, c1 = gv1 && U[1] >= tau_lo;
+  {
+    uint32_t tot;
+    uint32_t off = block_exclusive_scan((c0 ? 1u : 0u) + (c1 ? 1u : 0u), sm.scan_scratch, tot);
+    if (c0) sm.grp[off++] = (uint16_t)(2 * t);
+    if (c1) sm.grp[off] = (uint16_t)(2 * t + 1);
+    if (t == 0) sm.n_grp = tot;
+  }
+  __syncthreads();
+  const uint32_t n_grp = sm.n_grp;
+
+  // r of the candidates' positions: thread t holds candidate t (v[0..15]) and candidate
+  // t + kSelThreads (v[16..31]), positions ascending within each; -inf where there is none
+  const float* lg = pr.logits + slice * G * N;
+  float v[32];
+  uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
+  int grp_of[2] = {-1, -1};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t j = (uint32_t)t + (uint32_t)s * kSelThreads;
+    if (j < n_grp) {
+      const int c = sm.grp[j];
+      grp_of[s] = c;
+      float4 x[4][kFusedG];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int g = 0; g < kFusedG; ++g)
+          x[q][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + kGrp * c + 4 * q);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float r = rank_of<kFusedG>(x[q], e, lse2, G);
+          v[16 * s + 4 * q + e] = r;
+          const uint32_t b = coarse_bin(r, r_lo);
+          if (cur_cnt != 0u && b != cur_bin) atomicAdd(&sm.hist[cur_bin], cur_cnt), cur_cnt = 0u;
+          cur_bin = b;
+          ++cur_cnt;
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * s + i] = -INFINITY;
+    }
+  }
+  if (cur_cnt) atomicAdd(&sm.hist[cur_bin], cur_cnt);
+  __syncthreads();
+  auto valid = [&](int i) { return grp_of[i >> 4] >= 0; };
+
+  // the exact threshold among the candidates, as the resident selection finds it
+  uint32_t bin, above;
+  pick_digit(sm, kBins, (uint32_t)k, bin, above);
+  const uint32_t in_bin = sm.hist[bin];
+  if (wave == 0) {
+    const uint32_t key = first_key_of_bin_wave(bin, r_lo);
+    if (lane == 0) sm.bin_vals[0] = key_value(key);
+  } else if (wave == 1) {
+    const float vb = bin + 1 < (uint32_t)kBins ? key_value(first_key_of_bin_wave(bin + 1, r_lo)) : INFINITY;
+    if (lane == 0) sm.bin_vals[1] = vb;
+  }
+  __syncthreads();
+  const float va = sm.bin_vals[0], vb = sm.bin_vals[1];
+  const bool top_open = bin + 1 >= (uint32_t)kBins;
+
+  uint32_t thr, need_eq, n_thr;
+  if (in_bin <= (uint32_t)kCand) {
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float x = v[i];
+      mine |= (valid(i) && x >= va && (top_open || x < vb)) ? (1u << i) : 0u;
+    }
+    if (__any(mine != 0u)) {
+      const uint32_t n = __popc(mine);
+      const uint32_t incl = wave_inclusive_scan(n);
+      uint32_t base_slot = 0u;
+      if (lane == 63) base_slot = atomicAdd(&sm.n_cand, incl);
+      base_slot = __shfl(base_slot, 63);
+      uint32_t slot = base_slot + incl - n;
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if ((mine >> i) & 1u) {
+          if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[i]);
+          ++slot;
+        }
+    }
+    __syncthreads();
+    const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
+    const uint32_t krem = (uint32_t)k - above;
+    if (nc <= 64u) {
+      if (wave == 0) {
+        const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
+        uint32_t gt = 0u, eq = 0u;
+        for (uint32_t j = 0; j < nc; ++j) {
+          const uint32_t o = sm.cand[j];
+          gt += o > c ? 1u : 0u;
+          eq += o == c ? 1u : 0u;
+        }
+        const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
+        if (m != 0u && lane == __builtin_ctzll(m)) {
+          sm.res[0] = c;
+          sm.res[1] = krem - gt;
+          sm.res[2] = eq;
+          sm.res[3] = 1u;
+        }
+      }
+      __syncthreads();
+    }
+    if (sm.res[3]) {
+      thr = sm.res[0];
+      need_eq = sm.res[1];
+      n_thr = sm.res[2];
+    } else {
+      radix_select(sm, krem,
+                   [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+                     for (uint32_t i = t; i < nc; i += kSelThreads) {
+                       const uint32_t u = sm.cand[i];
+                       if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                     }
+                   },
+                   thr, need_eq, n_thr);
+    }
+  } else {
+    radix_select(sm, (uint32_t)k,
+                 [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+#pragma unroll
+                   for (int i = 0; i < 32; ++i) {
+                     const uint32_t u = order_key(v[i]);
+                     if (valid(i) && (u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                   }
+                 },
+                 thr, need_eq, n_thr);
+  }
+
+  // Every key above thr and the first need_eq equal to it, in position order: candidate
+  // t's positions precede candidate t + 1's, and every first-slot candidate precedes every
+  // second-slot one, so two prefix sums (first slots, then second slots) order the output.
+  const float vthr = key_value(thr);
+  const bool all_eq = need_eq == n_thr;
+  uint32_t sel[2] = {0u, 0u}, eqm[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (valid(i)) {
+      const float x = v[i];
+      sel[i >> 4] |= (x > vthr || (all_eq && x == vthr)) ? (1u << (i & 15)) : 0u;
+      eqm[i >> 4] |= (!all_eq && x == vthr) ? (1u << (i & 15)) : 0u;
+    }
+  if (!all_eq) {
+    uint32_t tot0, tot1;
+    const uint32_t ne0 = __popc(eqm[0]), ne1 = __popc(eqm[1]);
+    const uint32_t before0 = block_exclusive_scan(ne0, sm.scan_scratch, tot0);
+    const uint32_t before1 = tot0 + block_exclusive_scan(ne1, sm.scan_scratch, tot1);
+    const uint32_t before[2] = {before0, before1}, ne[2] = {ne0, ne1};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint32_t take = before[s] >= need_eq ? 0u : (need_eq - before[s] < ne[s] ? need_eq - before[s] : ne[s]);
+      while (take > 0u) {  // the lowest equal positions first
+        const uint32_t low = eqm[s] & (0u - eqm[s]);
+        sel[s] |= low;
+        eqm[s] ^= low;
+        --take;
+      }
+    }
+  }
+  uint32_t tot0, tot1;
+  const uint32_t o0 = block_exclusive_scan(__popc(sel[0]), sm.scan_scratch, tot0);
+  const uint32_t o1 = tot0 + block_exclusive_scan(__popc(sel[1]), sm.scan_scratch, tot1);
+  const uint32_t out0[2] = {o0, o1};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint32_t m = sel[s], out = out0[s];
+    while (m != 0u) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1u;
+      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(kGrp * grp_of[s] + b);
+      ++out;
+    }
+  }
+}
+
 template <int GM>
 void launch_keys(const Dims& d, int S, const float* logits, const float* part_m, const float* part_l, float r_lo,
                  float* keys, uint32_t* hist, hipStream_t s) {
@@ -814,12 +1107,26 @@ void launch_select(const Dims& d, int k, float r_lo, const float* keys, const ui
 
 }  // namespace
 
+bool rank_select_prunable(const Dims& d, int k) {
+  return d.N <= kResidentN && d.G <= kFusedG && k <= d.N / kGrp;
+}
+
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, bool keys_wanted, uint32_t* hist,
-                              int32_t* idx_out, const MergeJob* merge, hipStream_t s) {
+                              int32_t* idx_out, const MergeJob* merge, hipStream_t s, const float* gmax) {
   const float r_lo = logf((float)d.G) - kBinSpan;  // the same value for both kernels
   const MergeJob none{nullptr, nullptr, 0, 0, nullptr};
   const MergeJob& mj = merge ? *merge : none;
+  if (gmax && !keys_wanted && rank_select_prunable(d, k)) {
+    const PrunedRank pr{logits, part_m, part_l, gmax, d.G, S};
+    const unsigned n_sel = (unsigned)d.slices();
+    const unsigned grid = n_sel + (unsigned)ceil_div(mj.rows, kSelWaves);
+    if (d.D == 64)
+      rank_select_pruned_kernel<64><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, pr);
+    else
+      rank_select_pruned_kernel<128><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, pr);
+    return hipGetLastError();
+  }
   if (d.N <= kResidentN && d.G <= kFusedG) {  // one launch: the selection forms r(p) itself
     const FusedRank fr{logits, part_m, part_l, d.G, S, keys_wanted ? keys : nullptr};
     if (d.D == 64)
