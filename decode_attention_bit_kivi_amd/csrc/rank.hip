@@ -98,6 +98,20 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + x - v;
 }
 
+// For the key c of this lane, among the first nc (<= 64, wave-uniform) lanes' keys: (number
+// above c) | (number equal to c) << 16.  Each key is read from its lane with v_readlane (no LDS
+// round trip per key).
+__device__ __forceinline__ uint32_t count_above_equal(uint32_t c, uint32_t nc) {
+  uint32_t gt = 0u, eq = 0u;
+  const int n = __builtin_amdgcn_readfirstlane((int)nc);
+  for (int j = 0; j < n; ++j) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)c, j);
+    gt += o > c ? 1u : 0u;
+    eq += o == c ? 1u : 0u;
+  }
+  return gt | (eq << 16);
+}
+
 // Merge of two (max, sum 2^(x - max)) pairs of one head, log2 units.
 __device__ __forceinline__ void merge_stat(float& M, float& L, float m, float l) {
   const float mn = fmaxf(M, m);
@@ -697,12 +711,8 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
         // lane j: how many of the bin's keys are above / equal to key j; key j is the threshold
         // when the krem-th largest falls among its equals
         const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
-        uint32_t gt = 0u, eq = 0u;
-        for (uint32_t j = 0; j < nc; ++j) {
-          const uint32_t o = sm.cand[j];
-          gt += o > c ? 1u : 0u;
-          eq += o == c ? 1u : 0u;
-        }
+        const uint32_t gt_eq = count_above_equal(c, nc);
+        const uint32_t gt = gt_eq & 0xffffu, eq = gt_eq >> 16;
         const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
         if (m != 0u && lane == __builtin_ctzll(m)) {
           sm.res[0] = c;
@@ -802,7 +812,11 @@ constexpr int kGrp = 16;                            // positions per bound group
 constexpr int kMaxGroups = (int)(kResidentN / kGrp);  // 2048: two groups per thread
 constexpr float kBoundMargin = 1e-3f;               // slack on U for the rounding of its arithmetic
 
+constexpr int kPassGroups = kSelThreads / 4;             // candidate groups per pass (four lanes each)
+constexpr int kMaxPasses = kMaxGroups / kPassGroups;    // 8
+
 static_assert(kMaxGroups == 2 * kSelThreads, "two bound groups per thread");
+static_assert(4 * kMaxPasses == 32, "32 keys per thread");
 
 struct PrunedSmem {
   uint32_t hist[kBins];
@@ -913,43 +927,55 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
   __syncthreads();
   const uint32_t n_grp = sm.n_grp;
 
-  // r of the candidates' positions: thread t holds candidate t (v[0..15]) and candidate
-  // t + kSelThreads (v[16..31]), positions ascending within each; -inf where there is none
+  // r of the candidates' positions, four lanes per group (lane quad q = t % 4 holds positions
+  // 4q .. 4q + 3 of the group, so that the four lanes read each head's 64 bytes of the group
+  // together): pass s covers candidates 256 s .. 256 s + 255, candidate 256 s + t / 4 in
+  // v[4s .. 4s + 3]; -inf where there is none.  Passes then threads then lanes run in position order.
   const float* lg = pr.logits + slice * G * N;
-  float v[32];
+  const int q4 = t & 3, gj = t >> 2;
+  const int n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
+  float v[4 * kMaxPasses];
+  int grp_of[kMaxPasses];
   uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
-  int grp_of[2] = {-1, -1};
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const uint32_t j = (uint32_t)t + (uint32_t)s * kSelThreads;
-    if (j < n_grp) {
-      const int c = sm.grp[j];
-      grp_of[s] = c;
-      float4 x[4][kFusedG];
+  for (int s0 = 0; s0 < kMaxPasses; s0 += 2) {
+    if (s0 >= n_pass) {  // uniform: no candidates from here on
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int u = 0; u < 2; ++u) {
+        grp_of[s0 + u] = -1;
 #pragma unroll
-        for (int g = 0; g < kFusedG; ++g)
-          x[q][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + kGrp * c + 4 * q);
+        for (int e = 0; e < 4; ++e) v[4 * (s0 + u) + e] = -INFINITY;
+      }
+      continue;
+    }
+    float4 x[2][kFusedG];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t j = (uint32_t)((s0 + u) * kPassGroups + gj);
+      grp_of[s0 + u] = j < n_grp ? (int)sm.grp[j] : -1;
+      const int c = grp_of[s0 + u] >= 0 ? grp_of[s0 + u] : 0;  // a valid address, unused
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float r = rank_of<kFusedG>(x[q], e, lse2, G);
-          v[16 * s + 4 * q + e] = r;
+      for (int g = 0; g < kFusedG; ++g)
+        x[u][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + kGrp * c + 4 * q4);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float r = -INFINITY;
+        if (grp_of[s0 + u] >= 0) {
+          r = rank_of<kFusedG>(x[u], e, lse2, G);
           const uint32_t b = coarse_bin(r, r_lo);
           if (cur_cnt != 0u && b != cur_bin) atomicAdd(&sm.hist[cur_bin], cur_cnt), cur_cnt = 0u;
           cur_bin = b;
           ++cur_cnt;
         }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[16 * s + i] = -INFINITY;
-    }
+        v[4 * (s0 + u) + e] = r;
+      }
   }
   if (cur_cnt) atomicAdd(&sm.hist[cur_bin], cur_cnt);
   __syncthreads();
-  auto valid = [&](int i) { return grp_of[i >> 4] >= 0; };
+  auto valid = [&](int i) { return grp_of[i >> 2] >= 0; };
 
   // the exact threshold among the candidates, as the resident selection finds it
   uint32_t bin, above;
@@ -970,7 +996,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
   if (in_bin <= (uint32_t)kCand) {
     uint32_t mine = 0u;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 4 * kMaxPasses; ++i) {
       const float x = v[i];
       mine |= (valid(i) && x >= va && (top_open || x < vb)) ? (1u << i) : 0u;
     }
@@ -982,7 +1008,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       base_slot = __shfl(base_slot, 63);
       uint32_t slot = base_slot + incl - n;
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
+      for (int i = 0; i < 4 * kMaxPasses; ++i)
         if ((mine >> i) & 1u) {
           if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[i]);
           ++slot;
@@ -994,12 +1020,8 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     if (nc <= 64u) {
       if (wave == 0) {
         const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
-        uint32_t gt = 0u, eq = 0u;
-        for (uint32_t j = 0; j < nc; ++j) {
-          const uint32_t o = sm.cand[j];
-          gt += o > c ? 1u : 0u;
-          eq += o == c ? 1u : 0u;
-        }
+        const uint32_t gt_eq = count_above_equal(c, nc);
+        const uint32_t gt = gt_eq & 0xffffu, eq = gt_eq >> 16;
         const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
         if (m != 0u && lane == __builtin_ctzll(m)) {
           sm.res[0] = c;
@@ -1028,7 +1050,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     radix_select(sm, (uint32_t)k,
                  [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
 #pragma unroll
-                   for (int i = 0; i < 32; ++i) {
+                   for (int i = 0; i < 4 * kMaxPasses; ++i) {
                      const uint32_t u = order_key(v[i]);
                      if (valid(i) && (u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
                    }
@@ -1036,28 +1058,49 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
                  thr, need_eq, n_thr);
   }
 
-  // Every key above thr and the first need_eq equal to it, in position order: candidate
-  // t's positions precede candidate t + 1's, and every first-slot candidate precedes every
-  // second-slot one, so two prefix sums (first slots, then second slots) order the output.
+  // Every key above thr and the first need_eq equal to it, in position order (pass, then thread,
+  // then lane bit).  Per pass a thread has at most 4 such keys; the prefix sums run over two
+  // passes at once, one 16-bit field each (a pass holds at most 4096 keys).
   const float vthr = key_value(thr);
   const bool all_eq = need_eq == n_thr;
-  uint32_t sel[2] = {0u, 0u}, eqm[2] = {0u, 0u};
+  uint32_t sel[kMaxPasses], eqm[kMaxPasses];
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if (valid(i)) {
-      const float x = v[i];
-      sel[i >> 4] |= (x > vthr || (all_eq && x == vthr)) ? (1u << (i & 15)) : 0u;
-      eqm[i >> 4] |= (!all_eq && x == vthr) ? (1u << (i & 15)) : 0u;
+  for (int s = 0; s < kMaxPasses; ++s) {
+    sel[s] = 0u;
+    eqm[s] = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (valid(4 * s + e)) {
+        const float x = v[4 * s + e];
+        sel[s] |= (x > vthr || (all_eq && x == vthr)) ? (1u << e) : 0u;
+        eqm[s] |= (!all_eq && x == vthr) ? (1u << e) : 0u;
+      }
+  }
+  // exclusive prefix over (pass, thread) of per-pass counts: cnt(s) -> before(s)
+  auto pass_prefix = [&](const uint32_t (&m)[kMaxPasses], uint32_t (&before)[kMaxPasses]) {
+    uint32_t carried = 0u;
+#pragma unroll
+    for (int s = 0; s < kMaxPasses; s += 2) {
+      if (s >= n_pass) {  // uniform: nothing from here on
+        before[s] = carried;
+        before[s + 1] = carried;
+        continue;
+      }
+      uint32_t tot;
+      const uint32_t packed = (uint32_t)__popc(m[s]) | ((uint32_t)__popc(m[s + 1]) << 16);
+      const uint32_t ex = block_exclusive_scan(packed, sm.scan_scratch, tot);
+      before[s] = carried + (ex & 0xffffu);
+      before[s + 1] = carried + (tot & 0xffffu) + (ex >> 16);
+      carried += (tot & 0xffffu) + (tot >> 16);
     }
+  };
   if (!all_eq) {
-    uint32_t tot0, tot1;
-    const uint32_t ne0 = __popc(eqm[0]), ne1 = __popc(eqm[1]);
-    const uint32_t before0 = block_exclusive_scan(ne0, sm.scan_scratch, tot0);
-    const uint32_t before1 = tot0 + block_exclusive_scan(ne1, sm.scan_scratch, tot1);
-    const uint32_t before[2] = {before0, before1}, ne[2] = {ne0, ne1};
+    uint32_t before[kMaxPasses];
+    pass_prefix(eqm, before);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint32_t take = before[s] >= need_eq ? 0u : (need_eq - before[s] < ne[s] ? need_eq - before[s] : ne[s]);
+    for (int s = 0; s < kMaxPasses; ++s) {
+      const uint32_t ne = __popc(eqm[s]);
+      uint32_t take = before[s] >= need_eq ? 0u : (need_eq - before[s] < ne ? need_eq - before[s] : ne);
       while (take > 0u) {  // the lowest equal positions first
         const uint32_t low = eqm[s] & (0u - eqm[s]);
         sel[s] |= low;
@@ -1066,17 +1109,15 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       }
     }
   }
-  uint32_t tot0, tot1;
-  const uint32_t o0 = block_exclusive_scan(__popc(sel[0]), sm.scan_scratch, tot0);
-  const uint32_t o1 = tot0 + block_exclusive_scan(__popc(sel[1]), sm.scan_scratch, tot1);
-  const uint32_t out0[2] = {o0, o1};
+  uint32_t out0[kMaxPasses];
+  pass_prefix(sel, out0);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kMaxPasses; ++s) {
     uint32_t m = sel[s], out = out0[s];
     while (m != 0u) {
       const int b = __builtin_ctz(m);
       m &= m - 1u;
-      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(kGrp * grp_of[s] + b);
+      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(kGrp * grp_of[s] + 4 * q4 + b);
       ++out;
     }
   }
