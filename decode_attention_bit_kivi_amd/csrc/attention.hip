@@ -745,6 +745,7 @@ void launch_split_r(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipS
 }  // namespace
 
 hipError_t launch_attn_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  if (attn_stream_serves(d, a)) return launch_attn_stream(d, plan, a, s);
   if (a.rank_logits) launch_split_r<true>(d, plan, a, s); else launch_split_r<false>(d, plan, a, s);
   return hipGetLastError();
 }

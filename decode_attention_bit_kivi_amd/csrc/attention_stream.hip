@@ -1,0 +1,685 @@
+// Split kernel of the mixed attention for its common decode shape -- head_dim 128, 1-bit key and
+// value codes, at most 8 query rows per KV head (G * T <= 8) -- with the low-bit cache streamed
+// through LDS.
+//
+// It computes what attn_split_kernel (attention.hip) computes for this shape, with the same
+// operands and the same order of products (SpeCache summary, quick read (third mechanism) and
+// §3 "decoding": the 16-bit pairs C_kappa replace their low-bit counterparts; §7 Algorithm 3:
+// K = [K' U K_kappa, K_t], A = MaskedSoftmax(Q_t K^T), O = A V), and the same work decomposition:
+// one workgroup of four waves per (split, KV head), wave w taking the split's 32-position blocks
+// w, w + 4, ...; its outputs are the split partials and, in the RANK form, the rank row's logits
+// and statistics (over C', or those of the attention itself when ranking by the mixed cache) and
+// the 16-position maxima.
+//
+// What differs is how a block's bytes reach the matrix-core operands.  The operand layout holds
+// each code word and value-metadata entry in 4 lanes and each key scale in 16, so loading it
+// directly keeps 4 to 16 register bytes per byte in flight, and the bytes a wave can have in
+// flight bound the bandwidth (Little's law at HBM latency).  Here each lane loads 8 bytes of each
+// of a block's four arrays (key codes, key zero-points and scales, value codes, value metadata:
+// 2 KB, every byte once) kStreamAhead blocks before the block's turn; when the turn comes the
+// wave writes them to an LDS slot of its own and reads its operands back from there (LDS
+// accesses of one wave complete in order, so no barrier is involved).  A block's constant
+// sum_c q_c (z_c + h s_c) comes from four MFMAs on the staged zero-points and scales, so there is
+// no separate pass over the key metadata that would wait for its loads.
+#include "merge.h"
+#include "mfma_frag.h"
+
+#include <type_traits>
+
+namespace specache {
+
+namespace {
+
+constexpr int kStD = 128;
+constexpr int kStW = kStD / 32;    // 32-channel chunks
+constexpr int kStCPL = kStD / 16;  // value channel tiles (channels per lane)
+constexpr int kStRS = 36;          // row stride (halves) of the transposed 16-bit value tile
+constexpr int kStreamAhead = 4;    // blocks whose bytes each wave has in flight
+constexpr int kStSlot = 2048;      // bytes of a staged block
+// byte offsets of the four arrays in a staged block
+constexpr int kStKC = 0, kStKM = 512, kStVC = 1024, kStVM = 1536;
+constexpr float kStLog2e = 1.4426950408889634f;
+constexpr float kStRescale = 8.0f;  // lazy-rescale threshold (log2 units)
+
+struct StreamSmem {
+  uint32_t kmask[kAttnMaxBlocks];
+  float rank_m[4][16], rank_l[4][16];  // per wave: ranking statistics of each query row
+  int sel_range[2];
+  // 16-byte aligned: the operands are read back with 16-byte LDS reads
+  union alignas(16) {
+    union {  // per wave: the 16-bit value tile, or (during the low-bit blocks) two staged blocks
+      _Float16 vt[kStD][kStRS];
+      unsigned char stage[2][kStSlot];
+    } w[4];
+    struct {
+      float o[4][8][kStD];
+      float zs[4][8][2 * kStW];
+      float m[4][8];
+      float l[4][8];
+    } comb;
+  } u;
+};
+
+__device__ __forceinline__ void st_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int R>
+using IC = std::integral_constant<int, R>;
+
+template <bool RANK>
+__global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L, int S) {
+  // Only the explicit fmaf calls fuse: the compiler may not contract a product and a sum on its own,
+  // which it could do differently in the two instantiations and so make the attention of the fused
+  // step differ from decode_attn's in the last bit.
+#pragma clang fp contract(off)
+  constexpr int D = kStD, W = kStW, CPL = kStCPL, P = kStreamAhead;
+  constexpr int U = P % 2 == 0 ? P : 2 * P;  // unroll: the stage buffers and the two score sets
+  constexpr float hK = 0.5f, hV = 0.5f;    // 1-bit codes: the operand is the sign of s around z + s/2
+  static_assert(U == 2 || U == 4, "the remainder steps below are written out for U <= 4");
+  __shared__ StreamSmem sm;
+
+  const int tid = threadIdx.x;
+  // the wave index as a wave-uniform (scalar) value: block indices and LDS bases derived from it
+  // stay on the scalar unit
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x;
+  const int64_t slice = blockIdx.y;
+  const int64_t b = slice / Hkv, h = slice % Hkv;
+  const int T = a.T;
+  const int R = G * T;
+  const int Hq = Hkv * G;
+  const int64_t row0 = b * Hq * T + h * G * T;
+  const float qscale = a.sm_scale * kStLog2e;
+  const int64_t p0 = (int64_t)split * L;
+  const int64_t p1 = p0 + L < N ? p0 + L : N;
+  const int nb = (int)((p1 - p0) / 32);
+  const int64_t blk0 = p0 / 32;
+
+  // ---- query fragments: B[k-slot (g, j)][column n] = q[row n & 7][32w + 8g + j], every row in both
+  // halves of the columns.  A 16-token tile's products go to an accumulator of its own, and lane
+  // n16 keeps tile n16 >> 3's (columns 0-7: tile 0, 8-15: tile 1): the values attn_split_kernel
+  // accumulates for these columns, product for product.
+  const int arow = n16 & 7;  // query row of this lane's logits
+  const bool tile1 = n16 >= 8;
+  Frag Bq[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+    Bq[w].v = arow < R ? load_u4(a.q16 + (row0 + arow) * D + 32 * w + 8 * g) : make_uint4(0, 0, 0, 0);
+
+  float m_used = kMergeEmpty;  // running max (log2 units) of accumulator row n16
+  float l_part = 0.0f;         // this lane's share of that row's sum of exponentials (low-bit positions)
+  float l16 = 0.0f;            // the same over the 16-bit rows (fetched and tail)
+  float m_corr = kMergeEmpty, l_corr = 0.0f;  // C' terms of kappa positions (ranking statistics)
+  f32x4 Oacc[CPL];
+#pragma unroll
+  for (int ct = 0; ct < CPL; ++ct) Oacc[ct] = zero4();
+  f32x4 Ozs = zero4();
+
+  const int gshift = a.group == 64 ? 1 : 0;  // groups of 64 (keys: tokens, values: channels)
+  const int Wg = W >> gshift;                 // value groups per token
+  const int wv_grp = (CPL * n16) >> (5 + gshift);  // value group of this lane's channels
+  const bool rank_lane = RANK && arow < R && (arow % T) == a.rank_row;
+  const int shv[4] = {15 - 2 * g, 14 - 2 * g, 7 - 2 * g, 6 - 2 * g};
+  const float k1 = -0.5f * qscale;  // the expanded key operand is -(2b - 1) s
+
+  // Rescale the accumulators of this lane's rows when a block raises a row maximum by more than
+  // 2^kStRescale; xr holds logits relative to the current maximum, recomputed from the absolute
+  // values xa on a rescale.
+  auto online_update = [&](float (&xr)[4], const float (&xa)[4]) {
+    float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
+    if (__any(bm > kStRescale)) {
+      float ba = fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3]));
+      ba = max_over_groups(ba);
+      const float mn = fmaxf(m_used, ba);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - mn);
+      m_used = mn;
+      l_part *= alpha;
+      l16 *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = xa[i] - mn;
+      // whole-accumulator products: the accumulators then keep their registers through this
+      // (rarely taken) branch, where per-element products left register copies on the common path
+      const f32x4 av = {__shfl(alpha, 4 * g), __shfl(alpha, 4 * g + 1), __shfl(alpha, 4 * g + 2),
+                        __shfl(alpha, 4 * g + 3)};
+#pragma unroll
+      for (int ct = 0; ct < CPL; ++ct) Oacc[ct] = Oacc[ct] * av;
+      Ozs = Ozs * av;
+    }
+  };
+  // P (float32, four values of the score layout) -> the value product's A fragment: slots 0-3 hold
+  // tile 0's tokens, slots 4-7 tile 1's; each value rounded to nearest even.
+  auto make_p = [&](const float (&p)[4], float mul) {
+    const uint32_t lo = pack_half2(p[0] * mul, p[1] * mul), hi = pack_half2(p[2] * mul, p[3] * mul);
+    Frag A;
+    A.u[0] = tile1 ? 0u : lo;
+    A.u[1] = tile1 ? 0u : hi;
+    A.u[2] = tile1 ? lo : 0u;
+    A.u[3] = tile1 ? hi : 0u;
+    return A;
+  };
+
+  // ================= low-bit blocks, streamed =================
+  const int64_t Ns = a.seq_stride, nblk_s = a.seq_stride / 32;  // the cache's layout stride
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t kc_buf = make_rsrc(a.k_codes + slice * Ns * W, (uint32_t)(Ns * W * 4));
+  const __amdgpu_buffer_rsrc_t km_buf =
+      make_rsrc(a.k_meta + slice * (nblk_s >> gshift) * 2 * D, (uint32_t)((nblk_s >> gshift) * 2 * D * 2));
+  const __amdgpu_buffer_rsrc_t vc_buf = make_rsrc(a.v_codes + slice * nblk_s * D, (uint32_t)(nblk_s * D * 4));
+  const __amdgpu_buffer_rsrc_t vm_buf =
+      make_rsrc(a.v_meta + slice * nblk_s * 2 * Wg * 32, (uint32_t)(nblk_s * 2 * Wg * 32 * 2));
+  const uint32_t vm_bytes = (uint32_t)(2 * Wg * 32 * 2);  // value metadata of a block: 512 or 256 bytes
+  // lane offsets of the staged block: 8 bytes per lane and array (the value metadata of groups of 64
+  // is 256 bytes; the upper lanes repeat it)
+  const uint32_t off_stage = (uint32_t)(8 * lane), off_stage_vm = off_stage & (vm_bytes - 1);
+  const __amdgpu_buffer_rsrc_t rl_buf =
+      make_rsrc(RANK && a.rank_logits ? static_cast<const void*>(a.rank_logits + slice * G * N)
+                                      : static_cast<const void*>(a.q16),
+                RANK && a.rank_logits ? (uint32_t)(G * N * 4) : 0u);
+  const uint32_t rl_lane = (uint32_t)((arow / T) * N * 4);
+  // LDS byte offsets of this lane's operands in a staged block
+  const int zrow = n16 < 2 * Wg ? n16 : 0;  // value-metadata row of the zero-point / scale column
+  const uint32_t l_kc = (uint32_t)(kStKC + 16 * n16);                         // + 256: tile 1
+  const uint32_t l_ks = (uint32_t)(kStKM + 2 * D + 16 * g);                    // scales, + 64 w
+  const uint32_t l_kzs = (uint32_t)(kStKM + ((n16 & 3) == 1 ? 2 * D : 0) + 16 * g);  // + 64 w
+  const uint32_t l_vc = (uint32_t)(kStVC + 4 * CPL * n16);
+  const uint32_t l_vs = (uint32_t)(kStVM + 2 * (Wg * 32 + wv_grp * 32 + 4 * g));  // + 32: tokens 16..
+  const uint32_t l_zs = (uint32_t)(kStVM + 2 * (zrow * 32 + 4 * g));              // + 32: tokens 16..
+
+  struct Staged {
+    u32x4_t kc_km, vc_vm;  // 8 bytes of each array
+  };
+  auto stage_load = [&](int jj) {
+    const uint32_t blk = (uint32_t)(blk0 + jj);
+    const auto kc = __builtin_amdgcn_raw_buffer_load_b64(kc_buf, (int)off_stage, (int)(blk * 512u), 0);
+    const auto km = __builtin_amdgcn_raw_buffer_load_b64(km_buf, (int)off_stage, (int)((blk >> gshift) * 512u), 0);
+    const auto vc = __builtin_amdgcn_raw_buffer_load_b64(vc_buf, (int)off_stage, (int)(blk * 512u), 0);
+    const auto vm = __builtin_amdgcn_raw_buffer_load_b64(vm_buf, (int)off_stage_vm, (int)(blk * vm_bytes), 0);
+    Staged st;
+    st.kc_km = u32x4_t{kc[0], kc[1], km[0], km[1]};
+    st.vc_vm = u32x4_t{vc[0], vc[1], vm[0], vm[1]};
+    return st;
+  };
+  auto stage_ptr = [&](int slot) { return sm.u.w[wave].stage[slot]; };
+  auto stage_store = [&](const Staged& st, int slot) {
+    unsigned char* p = stage_ptr(slot) + off_stage;
+    *reinterpret_cast<uint2*>(p + kStKC) = make_uint2(st.kc_km[0], st.kc_km[1]);
+    *reinterpret_cast<uint2*>(p + kStKM) = make_uint2(st.kc_km[2], st.kc_km[3]);
+    *reinterpret_cast<uint2*>(p + kStVC) = make_uint2(st.vc_vm[0], st.vc_vm[1]);
+    *reinterpret_cast<uint2*>(p + kStVM) = make_uint2(st.vc_vm[2], st.vc_vm[3]);
+  };
+
+  // Scores of the staged block in `slot`: the key codes expanded against the queries (chunks w and
+  // w + 1 together, one 64-bit shift per pair of words) and the block's constant from four MFMAs
+  // whose A rows 4g' and 4g' + 1 are the zero-points and the scales (accumulator registers 0 and 1
+  // of every lane then hold sum_c q_c z_c and sum_c q_c s_c of its column's row).
+  struct Scores {
+    f32x4 x;   // this lane's logits before scaling (its tile)
+    float c0;  // the block's constant for the lane's row
+  };
+  struct KOps {
+    uint4 kt[2];   // key codes of tokens n16 and 16 + n16
+    uint4 ks[W];   // key scales of the lane's channels, chunk w
+    uint4 kzs[W];  // zero-points or scales (by row) for the constant's MFMAs
+  };
+  auto read_k = [&](int slot) {
+    const unsigned char* p = stage_ptr(slot);
+    KOps ko;
+    ko.kt[0] = *reinterpret_cast<const uint4*>(p + l_kc);
+    ko.kt[1] = *reinterpret_cast<const uint4*>(p + l_kc + 256);
+#pragma unroll
+    for (int w = 0; w < W; ++w) ko.ks[w] = *reinterpret_cast<const uint4*>(p + l_ks + 64 * w);
+#pragma unroll
+    for (int w = 0; w < W; ++w) ko.kzs[w] = *reinterpret_cast<const uint4*>(p + l_kzs + 64 * w);
+    return ko;
+  };
+  auto score = [&](const KOps& ko) {
+    const uint32_t kw[2][4] = {{ko.kt[0].x, ko.kt[0].y, ko.kt[0].z, ko.kt[0].w},
+                               {ko.kt[1].x, ko.kt[1].y, ko.kt[1].z, ko.kt[1].w}};
+    f32x4 acct[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int w = 0; w < W; w += 2) {
+      const uint4 ka = ko.ks[w], kb = ko.ks[w + 1];
+      const uint32_t ma[4] = {ka.x, ka.y, ka.z, ka.w}, mb[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        Frag A0, A1;  // chunks w, w + 1 of tile tau
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          signed_pairs2(kw[tau][w], kw[tau][w + 1], 15 - 4 * g - d, ma[d], mb[d], A0.u[d], A1.u[d]);
+        acct[tau] = mma(A0, Bq[w], acct[tau]);
+        acct[tau] = mma(A1, Bq[w + 1], acct[tau]);
+      }
+    }
+    f32x4 accc = zero4();
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      Frag Z;
+      Z.v = ko.kzs[w];
+      accc = mma(Z, Bq[w], accc);
+    }
+    Scores sc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc.x[i] = tile1 ? acct[1][i] : acct[0][i];
+    sc.c0 = fmaf(hK, accc[1], accc[0]) * qscale;
+    return sc;
+  };
+
+  // The rest of block jj (staged in `slot`, scored into sc): logits, ranking outputs, softmax,
+  // values.
+  struct VOps {
+    uint4 va, vb;                        // value code words of the lane's channels
+    uint2 vs_lo, vs_hi, zs_lo, zs_hi;    // value scales, zero-point / scale columns
+    uint32_t kmw;                        // kappa positions of the block
+  };
+  auto read_v = [&](int slot, int jj) {
+    const unsigned char* q = stage_ptr(slot);
+    VOps vo;
+    vo.va = *reinterpret_cast<const uint4*>(q + l_vc);
+    vo.vb = *reinterpret_cast<const uint4*>(q + l_vc + 16);
+    vo.vs_lo = *reinterpret_cast<const uint2*>(q + l_vs);
+    vo.vs_hi = *reinterpret_cast<const uint2*>(q + l_vs + 32);
+    vo.zs_lo = *reinterpret_cast<const uint2*>(q + l_zs);
+    vo.zs_hi = *reinterpret_cast<const uint2*>(q + l_zs + 32);
+    vo.kmw = sm.kmask[jj];
+    return vo;
+  };
+  auto finish = [&](const VOps& vo, const Scores& sc, int jj) {
+    const float c0 = sc.c0, c0m = c0 - m_used;
+    float xr[4], xa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xr[i] = fmaf(sc.x[i], k1, c0m);
+      xa[i] = fmaf(sc.x[i], k1, c0);
+    }
+    const uint32_t kmw = vo.kmw;
+    if constexpr (RANK) {
+      // the rank row's logits against C' (before any kappa masking), log2 units; when ranking by the
+      // mixed cache the kappa positions are written by the 16-bit blocks instead
+      if (rank_lane && a.rank_mixed && kmw) {
+        float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * (n16 >> 3) + 4 * g + i;
+          if (!((kmw >> tok) & 1u)) dst[tok] = xa[i];
+        }
+      } else if (rank_lane) {
+        // through the raw buffer over the slice's logits (the block offset is scalar)
+        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((blk0 + jj) * 32 * 4));
+        typedef float f4_t __attribute__((ext_vector_type(4)));
+        const f4_t v = {xa[0], xa[1], xa[2], xa[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
+                                               (int)(rl_lane + 4 * (16 * (n16 >> 3) + 4 * g)), (int)soff, 0);
+      }
+      // the bound of each 16-position group for the pruned selection: the four lanes g of n16 hold
+      // tile n16 >> 3 of row arow
+      if (a.rank_gmax) {
+        const float gm = max_over_groups(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
+        if (rank_lane && g == 0) a.rank_gmax[(slice * G + arow / T) * (N >> 4) + (blk0 + jj) * 2 + (n16 >> 3)] = gm;
+      }
+    }
+    float xc[4];  // C' logits of masked positions, for the ranking statistics
+    if (kmw) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * (n16 >> 3) + 4 * g + i;
+        xc[i] = -INFINITY;
+        if ((kmw >> tok) & 1u) {
+          xc[i] = xa[i];
+          xr[i] = -INFINITY;
+          xa[i] = -INFINITY;
+        }
+      }
+    }
+    online_update(xr, xa);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(xr[i]);
+      l_part += p[i];
+    }
+    if constexpr (RANK) {
+      if (kmw) {
+        const float cm = fmaxf(fmaxf(xc[0], xc[1]), fmaxf(xc[2], xc[3]));
+        const float mn = fmaxf(m_corr, cm);
+        l_corr *= __builtin_amdgcn_exp2f(m_corr - mn);
+        m_corr = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_corr += __builtin_amdgcn_exp2f(xc[i] - mn);
+      }
+    }
+    const Frag Ap = make_p(p, 1.0f);
+
+    // values: the value codes expanded against P, plus one MFMA whose columns are the per-token
+    // zero-points and scales
+    const uint32_t vw[CPL] = {vo.va.x, vo.va.y, vo.va.z, vo.va.w, vo.vb.x, vo.vb.y, vo.vb.z, vo.vb.w};
+    const uint2 vs_lo = vo.vs_lo, vs_hi = vo.vs_hi, zs_lo = vo.zs_lo, zs_hi = vo.zs_hi;
+    const uint32_t vmag[4] = {vs_lo.x, vs_lo.y, vs_hi.x, vs_hi.y};
+#pragma unroll
+    for (int ct = 0; ct < CPL; ct += 2) {
+      Frag Bv0, Bv1;  // channel tiles ct and ct + 1, one 64-bit shift per pair of words
+#pragma unroll
+      for (int d = 0; d < 4; ++d) signed_pairs2(vw[ct], vw[ct + 1], shv[d], vmag[d], vmag[d], Bv0.u[d], Bv1.u[d]);
+      Oacc[ct] = mma(Ap, Bv0, Oacc[ct]);
+      Oacc[ct + 1] = mma(Ap, Bv1, Oacc[ct + 1]);
+    }
+    // columns n16 >= 2 Wg carry another row's (finite) metadata: their outputs are never read
+    Frag Bzs;
+    Bzs.u[0] = zs_lo.x;
+    Bzs.u[1] = zs_lo.y;
+    Bzs.u[2] = zs_hi.x;
+    Bzs.u[3] = zs_hi.y;
+    Ozs = mma(Ap, Bzs, Ozs);
+  };
+
+  // low-bit blocks jj = wave + 4 i of this wave; their first P blocks' loads are issued before
+  // anything else, so that they are in flight through the kappa scan and the fetched 16-bit blocks
+  const int vw = wave;
+  const int nw = vw < nb ? (nb - vw + 3) / 4 : 0;
+  auto blk = [&](int i) { return vw + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
+  Staged stg[P];
+  if (nw > 0) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) stg[j] = stage_load(blk(j));
+  }
+
+  if (RANK && split == 0)  // the rank kernels accumulate a per-slice histogram here
+    for (int i = tid; i < 2048; i += 256) a.rank_hist[slice * 2048 + i] = 0u;
+
+  // ---- kappa positions of this split: a bitmask over its blocks and the range [i0, i1) of the
+  // fetched rows whose positions fall in it (idx is ascending)
+  for (int i = tid; i < kAttnMaxBlocks; i += 256) sm.kmask[i] = 0u;
+  if (tid < 2) sm.sel_range[tid] = 0;
+  __syncthreads();
+  {
+    const int32_t* ix = a.idx + slice * a.k;
+    int below0 = 0, below1 = 0;
+    for (int i = tid; i < a.k; i += 256) {
+      const int64_t p = ix[i];
+      below0 += p < p0 ? 1 : 0;
+      below1 += p < p1 ? 1 : 0;
+      if (p >= p0 && p < p1) atomicOr(&sm.kmask[(p - p0) >> 5], 1u << ((p - p0) & 31));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      below0 += __shfl_xor(below0, off);
+      below1 += __shfl_xor(below1, off);
+    }
+    if (lane == 0 && (below0 | below1)) {
+      atomicAdd(&sm.sel_range[0], below0);
+      atomicAdd(&sm.sel_range[1], below1);
+    }
+  }
+  __syncthreads();
+  const int i0 = sm.sel_range[0], i1 = sm.sel_range[1];
+
+  // ================= 16-bit rows: the fetched kappa rows of this split, then the tail =================
+  // 16-bit block q (the fetched rows' blocks, then the tail's) goes to wave 3 - q mod 4: the waves
+  // with the fewest low-bit blocks take them first.  The fetched rows' blocks run before the
+  // low-bit blocks and the tail's after them; their exponentials go to l16, so the low-bit sums
+  // l_part stay the ranking statistics over C'.
+  const int n_sel = i1 - i0;
+  const bool has_tail = (split == S - 1) && a.tail > 0;
+  const int n_sel_blk = (n_sel + 31) / 32;
+  const int n_tail_blk = has_tail ? (a.tail + 31) / 32 : 0;
+  const int first_tail_q = n_sel_blk + ((3 - wave - n_sel_blk) % 4 + 4) % 4;  // first q >= n_sel_blk of this wave
+  auto f16_block = [&](int q) {
+    const bool tail = q >= n_sel_blk;
+    const int base = tail ? 32 * (q - n_sel_blk) : i0 + 32 * q;
+    const int lim = tail ? a.tail : i1;
+    const _Float16* ksrc = tail ? a.k_tail + slice * a.tail * D : a.k_sel + slice * a.k * D;
+    const _Float16* vsrc = tail ? a.v_tail + slice * a.tail * D : a.v_sel + slice * a.k * D;
+    _Float16(*vt)[kStRS] = sm.u.w[wave].vt;
+    Frag vv[2][W], kk[2][W];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int tok = 16 * tau + n16;
+      const int64_t src_row = base + tok < lim ? base + tok : lim - 1;
+#pragma unroll
+      for (int w = 0; w < W; ++w) vv[tau][w].v = load_u4(vsrc + src_row * D + 32 * w + 8 * g);
+#pragma unroll
+      for (int w = 0; w < W; ++w) kk[tau][w].v = load_u4(ksrc + src_row * D + 32 * w + 8 * g);
+    }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int tok = 16 * tau + n16;
+      const bool ok = base + tok < lim;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        Frag v;
+        v.v = ok ? vv[tau][w].v : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vt[32 * w + 8 * g + j][tok] = v.h[j];
+      }
+    }
+    f32x4 acct[2] = {zero4(), zero4()};
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        Frag A;
+        A.v = (base + 16 * tau + n16 < lim) ? kk[tau][w].v : make_uint4(0, 0, 0, 0);
+        acct[tau] = mma(A, Bq[w], acct[tau]);
+      }
+    }
+    float xr[4], xa[4];
+    const int tq = arow % T;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 16 * (n16 >> 3) + 4 * g + i;
+      const float v = (tile1 ? acct[1][i] : acct[0][i]) * qscale;
+      bool ok = base + tok < lim;
+      if constexpr (RANK) {
+        // ranking by the mixed cache: a fetched row's logit replaces its low-bit one
+        if (a.rank_mixed && rank_lane && !tail && ok) {
+          const int64_t pos = a.idx[slice * a.k + base + tok];
+          a.rank_logits[(slice * G + arow / T) * N + pos] = v;
+        }
+      }
+      if (tail) ok = ok && (base + tok <= a.tail - T + tq);
+      xa[i] = ok ? v : -INFINITY;
+      xr[i] = xa[i] - m_used;
+    }
+    online_update(xr, xa);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(xr[i]);
+      l16 += p[i];
+    }
+    const Frag Ap2 = make_p(p, -2.0f);  // the value accumulator is scaled by -1/2 at the end
+    st_lds_fence();
+#pragma unroll
+    for (int ct = 0; ct < CPL; ++ct) {
+      const int c = CPL * n16 + ct;
+      const uint2 lo = load_u2(&vt[c][4 * g]);
+      const uint2 hi = load_u2(&vt[c][16 + 4 * g]);
+      Frag Bv;
+      Bv.u[0] = lo.x;
+      Bv.u[1] = lo.y;
+      Bv.u[2] = hi.x;
+      Bv.u[3] = hi.y;
+      Oacc[ct] = mma(Ap2, Bv, Oacc[ct]);
+    }
+    st_lds_fence();
+  };
+
+  __builtin_amdgcn_s_setprio(3);  // a chain of latencies: issue it ahead of the other waves' loops
+  for (int q = 3 - wave; q < n_sel_blk; q += 4) f16_block(q);
+
+  if (nw > 0) {
+    // Step i (r = i mod U): block i + 1's bytes go to its slot and its buffer takes block
+    // i + 1 + P's loads; block i + 1 is scored while block i is finished, so the matrix cores work
+    // on one block while the VALU finishes the other.  Buffers, slots and score sets are indexed
+    // by r, so that the unrolled steps address fixed registers.
+    Scores sc[2];
+    auto step = [&](int i, auto rc) {
+      constexpr int r = decltype(rc)::value;
+      constexpr int b1 = (r + 1) % P, s1 = (r + 1) & 1, s0 = r & 1;
+      if constexpr (!RANK) {
+        // every LDS read of the step is issued before its arithmetic: block i's value operands
+        // (staged a step ago), then block i + 1's key operands behind its own staging
+        const VOps vo = read_v(s0, blk(i));
+        stage_store(stg[b1], s1);
+        const KOps ko = read_k(s1);
+        stg[b1] = stage_load(blk(i + 1 + P));
+        __builtin_amdgcn_sched_barrier(0);
+        finish(vo, sc[s0], blk(i));
+        if (i + 1 < nw) sc[s1] = score(ko);
+      } else {
+        // the ranking outputs' registers leave no room to hold both blocks' operands: each block's
+        // reads sit next to its arithmetic
+        stage_store(stg[b1], s1);
+        stg[b1] = stage_load(blk(i + 1 + P));
+        if (i + 1 < nw) sc[s1] = score(read_k(s1));
+        finish(read_v(s0, blk(i)), sc[s0], blk(i));
+      }
+    };
+    stage_store(stg[0], 0);
+    stg[0] = stage_load(blk(P));
+    sc[0] = score(read_k(0));
+    // Issue priority by the blocks this wave has left: two workgroups share each compute unit, and
+    // the SIMD arbiter otherwise favours the older one, which then finishes long before the younger
+    // and leaves one wave per SIMD for the rest.
+    const int pr1 = nw / 16 + 1, pr2 = nw / 6 + 1, pr3 = nw / 3 + 1;
+    int i = 0;
+    for (; i + U <= nw; i += U) {
+      const int rem = nw - i;
+      if (rem > pr3) __builtin_amdgcn_s_setprio(3);
+      else if (rem > pr2) __builtin_amdgcn_s_setprio(2);
+      else if (rem > pr1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+      step(i, IC<0>{});
+      step(i + 1, IC<1>{});
+      if constexpr (U == 4) {
+        step(i + 2, IC<2>{});
+        step(i + 3, IC<3>{});
+      }
+    }
+    // the last nw mod U blocks, each step on the path of the one before it
+    __builtin_amdgcn_s_setprio(0);
+    if (i < nw) {
+      step(i, IC<0>{});
+      if constexpr (U == 4) {
+        if (i + 1 < nw) {
+          step(i + 1, IC<1>{});
+          if (i + 2 < nw) step(i + 2, IC<2>{});
+        }
+      }
+    }
+  }
+
+  __builtin_amdgcn_s_setprio(3);  // the rest of the workgroup is a chain of latencies: let it through
+
+  // ranking statistics over C' = the low-bit positions, kappa positions included
+  float rank_m_lane = m_used, rank_l_lane = l_part;
+  if constexpr (RANK) {
+    rank_m_lane = max_over_groups(fmaxf(m_used, m_corr));  // the same for the four lanes of a row
+    rank_l_lane = l_part * __builtin_amdgcn_exp2f(m_used - rank_m_lane) +
+                  l_corr * __builtin_amdgcn_exp2f(m_corr - rank_m_lane);
+  }
+
+  // ================= 16-bit rows of the tail (the fetched rows went first) =================
+  for (int q = first_tail_q; q < n_sel_blk + n_tail_blk; q += 4) f16_block(q);
+
+  // ================= wave epilogue =================
+  // per accumulator row: the final (max, sum); with tile 0's rows in n16 < 8 and tile 1's in
+  // n16 >= 8, fold the two tiles of a query row
+  const float l_row = sum_over_groups(l_part + l16);
+  const float m2 = __shfl_xor(m_used, 8);
+  const float l2 = __shfl_xor(l_row, 8);
+  const float mm = fmaxf(m_used, m2);
+  const float f_self = __builtin_amdgcn_exp2f(m_used - mm);
+  const float f_other = __builtin_amdgcn_exp2f(m2 - mm);
+  if constexpr (RANK) {
+    float rl = sum_over_groups(rank_l_lane), rm = rank_m_lane;
+    const float rm2 = __shfl_xor(rm, 8), rl2 = __shfl_xor(rl, 8);
+    const float rmm = fmaxf(rm, rm2);
+    rl = rl * __builtin_amdgcn_exp2f(rm - rmm) + rl2 * __builtin_amdgcn_exp2f(rm2 - rmm);
+    if (g == 0) {
+      sm.rank_m[wave][n16] = rmm;
+      sm.rank_l[wave][n16] = rl;
+    }
+  }
+  __syncthreads();  // all waves are done with their tiles and slots; the LDS union becomes the combine buffer
+  if constexpr (RANK) {
+    // one thread per head: combine the four waves and write this split's statistics over C'
+    if (!a.rank_mixed && tid < G) {
+      const int r = tid * T + a.rank_row;
+      float M = kMergeEmpty;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) M = fmaxf(M, sm.rank_m[w4][r]);
+      float Ls = 0.0f;
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) Ls += sm.rank_l[w4][r] * __builtin_amdgcn_exp2f(sm.rank_m[w4][r] - M);
+      a.rank_m[(slice * G + tid) * S + split] = M;
+      a.rank_l[(slice * G + tid) * S + split] = Ls;
+    }
+  }
+  if (g == 0 && n16 < 8) {
+    sm.u.comb.m[wave][n16] = mm;
+    sm.u.comb.l[wave][n16] = f_self * l_row + f_other * l2;
+  }
+  // accumulator rows 4g' + i; rows r and r + 8 (lanes g' and g' ^ 2) fold into r (lanes g' < 2)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * g + i;
+    const float ws = __shfl(f_self, r & 7);
+    const float wo = __shfl(f_other, r & 7);
+    const float zsv = ws * Ozs[i] + wo * __shfl_xor(Ozs[i], 32);
+    float ov[CPL];
+#pragma unroll
+    for (int ct = 0; ct < CPL; ++ct) ov[ct] = ws * Oacc[ct][i] + wo * __shfl_xor(Oacc[ct][i], 32);
+    if (g < 2) {
+      if (n16 < 2 * Wg) sm.u.comb.zs[wave][r][n16] = zsv;
+#pragma unroll
+      for (int ct = 0; ct < CPL; ++ct) sm.u.comb.o[wave][r][CPL * n16 + ct] = ov[ct];
+    }
+  }
+  __syncthreads();
+
+  // ================= combine the four waves and write this split's partials =================
+  for (int e = tid; e < R * D; e += 256) {
+    const int r = e / D, c = e % D;
+    float M = kMergeEmpty;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) M = fmaxf(M, sm.u.comb.m[w4][r]);
+    float lsum = 0.0f, o = 0.0f;
+    const int gv = c >> (5 + gshift);
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const float e4 = __builtin_amdgcn_exp2f(sm.u.comb.m[w4][r] - M);
+      lsum += e4 * sm.u.comb.l[w4][r];
+      o += e4 * (-0.5f * sm.u.comb.o[w4][r][c] + sm.u.comb.zs[w4][r][gv] + hV * sm.u.comb.zs[w4][r][Wg + gv]);
+    }
+    const int64_t row = row0 + r;
+    a.part_acc[(row * S + split) * D + c] = o;
+    if (c == 0) {
+      a.part_ml[(row * S + split) * 2] = M;
+      a.part_ml[(row * S + split) * 2 + 1] = lsum;
+      if constexpr (RANK) {
+        // ranking by the mixed cache: the rank row's own softmax statistics of this split
+        if (a.rank_mixed && r % T == a.rank_row) {
+          a.rank_m[(slice * G + r / T) * S + split] = M;
+          a.rank_l[(slice * G + r / T) * S + split] = lsum;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool attn_stream_serves(const Dims& d, const AttnArgs& a) {
+  return d.D == kStD && d.bits == 1 && d.vbits == 1 && d.G * a.T <= 8;
+}
+
+hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
+  if (a.rank_logits)
+    attn_stream_kernel<true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  else
+    attn_stream_kernel<false><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  return hipGetLastError();
+}
+
+}  // namespace specache

@@ -198,6 +198,11 @@ struct AttnArgs {
 // over C' with the fetched rows substituted and the visible tail (rank_mixed = 1).
 hipError_t launch_attn_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_merge(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
+// The split kernel that streams the low-bit cache through LDS (attention_stream.hip), for head_dim
+// 128, 1-bit key and value codes and G * T <= 8; launch_attn_split uses it whenever it serves, with
+// the same plan and outputs.
+bool attn_stream_serves(const Dims& d, const AttnArgs& a);
+hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 // The 16-bit comparator's split kernel: a.k_sel / a.v_sel are the whole 16-bit cache, a.k its
 // positions per slice; partials as launch_attn_split's, merged by launch_attn_merge.
 hipError_t launch_attn16_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);

@@ -562,6 +562,46 @@ def test_fused_step_mixed_cache_rank(gpu, name, over, mode):
     _check_rank_keys(_np(rk), r_ref)
 
 
+@pytest.mark.parametrize("seq_len", [32, 96, 32 * 7, 32 * 29, 8192 + 96])
+@pytest.mark.parametrize("cus", [8, None])
+def test_streamed_split_block_counts(gpu, seq_len, cus):
+    """The LDS-streamed split kernel (head_dim 128, 1-bit codes, G * T = 8) with every count of
+    low-bit blocks per wave it meets: none, fewer than its loads ahead, and each remainder of its
+    four-step loop.  On 8 compute units the plan takes few, long splits; on the device many short
+    ones.  decode_attn against the oracle; the fused step (ranking against C', and by the mixed
+    cache) bit for bit against it, with its next selection against the oracle's ranking."""
+    cfg = get_config("llama8k").with_(bits=1, seq_len=seq_len, top_k=min(64, seq_len), tail_len=3, seed=7)
+    K, V, Q, _, KT, VT = generate_all(cfg)
+    B, Hkv, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
+    rng = np.random.default_rng(seq_len)
+    idx = _random_idx(rng, B, Hkv, N, cfg.top_k)
+    ks, vs = oracle.gather_rows(K, V, idx)
+    gs = GatherStream(cus) if cus else None
+    comp = gs.torch if gs else torch.cuda.current_stream()
+    comp.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(comp):
+        cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+        args = (_dev(Q), cache, _dev(idx), _dev(ks), _dev(vs), _dev(KT), _dev(VT))
+        o_sep = decode_attn(*args)
+        o_c, nxt_c = decode_step(args[0], cache, cfg.top_k, rank_row=1, idx=args[2], k_sel=args[3],
+                                 v_sel=args[4], k_tail=args[5], v_tail=args[6])
+        o_m, nxt_m = decode_step(args[0], cache, cfg.top_k, rank_row=1, rank_mixed=True, idx=args[2],
+                                 k_sel=args[3], v_sel=args[4], k_tail=args[5], v_tail=args[6])
+        comp.synchronize()
+    if gs:
+        gs.close()
+    assert torch.equal(o_c.view(torch.int16), o_sep.view(torch.int16))
+    assert torch.equal(o_m.view(torch.int16), o_sep.view(torch.int16))
+    _, kh, vh = _reference_cache(K, V, cfg.bits)
+    what = f"seq {seq_len} cus {cus}"
+    ref = oracle.mixed_attention(Q, kh, vh, idx, ks, vs, KT, VT, sm_scale=cfg.sm_scale)
+    _check_attn(_np(o_sep), ref, what)
+    slices = [(b, h) for b in range(B) for h in range(Hkv)]
+    _assert_topk(_np(nxt_c), oracle.rank_scores(Q, kh, 1, cfg.sm_scale), cfg.top_k, slices, what + " C'")
+    r_mixed = oracle.rank_scores_mixed(Q, kh, 1, cfg.sm_scale, idx=idx, k_sel=ks, k_tail=KT)
+    _assert_topk(_np(nxt_m), r_mixed, cfg.top_k, slices, what + " mixed")
+
+
 def test_fused_step_next_selection_may_alias_current(gpu):
     cfg = get_config("llama8k").with_(seq_len=4096, seed=7)
     K, V, Q, _, _, _ = generate_all(cfg)
