@@ -35,11 +35,17 @@ constexpr int kStW = kStD / 32;    // 32-channel chunks
 constexpr int kStCPL = kStD / 16;  // value channel tiles (channels per lane)
 constexpr int kStRS = 36;          // row stride (halves) of the transposed 16-bit value tile
 constexpr int kStreamAhead = 4;    // blocks whose bytes each wave has in flight
-constexpr int kStSlot = 2048;      // bytes of a staged block
-// byte offsets of the four arrays in a staged block
-constexpr int kStKC = 0, kStKM = 512, kStVC = 1024, kStVM = 1536;
+// A staged block in LDS: key codes (512 bytes), key zero-points then scales (256 bytes each, 16
+// bytes apart), value codes (16 bytes after every 64 channels' words), value metadata (64-byte rows,
+// 8 bytes apart).  The gaps put the addresses that one operand read sends to the same bank row on
+// different banks: rows 0 and 1 mod 4 of the constant's operand (zero-points, scales), lanes n16 and
+// n16 + 8 of the value codes, the 8 rows of zero-points and scales of the value metadata.
+constexpr int kStKC = 0, kStKM = 512, kStKS = kStKM + 272, kStVC = kStKM + 528, kStVM = kStVC + 528;
+constexpr int kStSlot = kStVM + 8 * 72;  // 2144 bytes, a multiple of 16
+static_assert(kStSlot % 16 == 0 && kStKS % 16 == 0 && kStVC % 16 == 0 && kStVM % 8 == 0, "LDS read alignment");
 constexpr float kStLog2e = 1.4426950408889634f;
 constexpr float kStRescale = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr uint32_t kStDropped = 0x80000000u;  // a buffer offset past every buffer here: the store is dropped
 
 struct StreamSmem {
   uint32_t kmask[kAttnMaxBlocks];
@@ -65,12 +71,15 @@ __device__ __forceinline__ void st_lds_fence() { asm volatile("s_waitcnt lgkmcnt
 template <int R>
 using IC = std::integral_constant<int, R>;
 
-template <bool RANK>
+// MODE 0: attention only; 1: with the rank row's logits, bounds and statistics against C';
+// 2: with the ranking by the mixed-cache attention row.
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L, int S) {
   // Only the explicit fmaf calls fuse: the compiler may not contract a product and a sum on its own,
   // which it could do differently in the two instantiations and so make the attention of the fused
   // step differ from decode_attn's in the last bit.
 #pragma clang fp contract(off)
+  constexpr bool RANK = MODE != 0, MIXED = MODE == 2;
   constexpr int D = kStD, W = kStW, CPL = kStCPL, P = kStreamAhead;
   constexpr int U = P % 2 == 0 ? P : 2 * P;  // unroll: the stage buffers and the two score sets
   constexpr float hK = 0.5f, hV = 0.5f;    // 1-bit codes: the operand is the sign of s around z + s/2
@@ -171,19 +180,28 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   // lane offsets of the staged block: 8 bytes per lane and array (the value metadata of groups of 64
   // is 256 bytes; the upper lanes repeat it)
   const uint32_t off_stage = (uint32_t)(8 * lane), off_stage_vm = off_stage & (vm_bytes - 1);
+  // LDS offsets of this lane's 8 bytes of each array in a staged block
+  const uint32_t s_kc = (uint32_t)(kStKC + 8 * lane);
+  const uint32_t s_km = (uint32_t)(lane < 32 ? kStKM + 8 * lane : kStKS + 8 * (lane - 32));
+  const uint32_t s_vc = (uint32_t)(kStVC + 8 * lane + 16 * (lane >> 5));
+  const uint32_t s_vm = (uint32_t)(kStVM + 72 * (lane >> 3) + 8 * (lane & 7));
   const __amdgpu_buffer_rsrc_t rl_buf =
       make_rsrc(RANK && a.rank_logits ? static_cast<const void*>(a.rank_logits + slice * G * N)
                                       : static_cast<const void*>(a.q16),
                 RANK && a.rank_logits ? (uint32_t)(G * N * 4) : 0u);
   const uint32_t rl_lane = (uint32_t)((arow / T) * N * 4);
+  const __amdgpu_buffer_rsrc_t gm_buf =
+      make_rsrc(RANK && a.rank_gmax ? static_cast<const void*>(a.rank_gmax + slice * G * (N >> 4))
+                                    : static_cast<const void*>(a.q16),
+                RANK && a.rank_gmax ? (uint32_t)(G * (N >> 4) * 4) : 0u);
   // LDS byte offsets of this lane's operands in a staged block
   const int zrow = n16 < 2 * Wg ? n16 : 0;  // value-metadata row of the zero-point / scale column
   const uint32_t l_kc = (uint32_t)(kStKC + 16 * n16);                         // + 256: tile 1
-  const uint32_t l_ks = (uint32_t)(kStKM + 2 * D + 16 * g);                    // scales, + 64 w
-  const uint32_t l_kzs = (uint32_t)(kStKM + ((n16 & 3) == 1 ? 2 * D : 0) + 16 * g);  // + 64 w
-  const uint32_t l_vc = (uint32_t)(kStVC + 4 * CPL * n16);
-  const uint32_t l_vs = (uint32_t)(kStVM + 2 * (Wg * 32 + wv_grp * 32 + 4 * g));  // + 32: tokens 16..
-  const uint32_t l_zs = (uint32_t)(kStVM + 2 * (zrow * 32 + 4 * g));              // + 32: tokens 16..
+  const uint32_t l_ks = (uint32_t)(kStKS + 16 * g);                                 // scales, + 64 w
+  const uint32_t l_kzs = (uint32_t)(((n16 & 3) == 1 ? kStKS : kStKM) + 16 * g);      // + 64 w
+  const uint32_t l_vc = (uint32_t)(kStVC + 4 * CPL * n16 + 16 * (n16 >> 3));         // + 16: channels 4..7
+  const uint32_t l_vs = (uint32_t)(kStVM + 72 * (Wg + wv_grp) + 8 * g);             // + 32: tokens 16..
+  const uint32_t l_zs = (uint32_t)(kStVM + 72 * zrow + 8 * g);                       // + 32: tokens 16..
 
   struct Staged {
     u32x4_t kc_km, vc_vm;  // 8 bytes of each array
@@ -201,11 +219,11 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   };
   auto stage_ptr = [&](int slot) { return sm.u.w[wave].stage[slot]; };
   auto stage_store = [&](const Staged& st, int slot) {
-    unsigned char* p = stage_ptr(slot) + off_stage;
-    *reinterpret_cast<uint2*>(p + kStKC) = make_uint2(st.kc_km[0], st.kc_km[1]);
-    *reinterpret_cast<uint2*>(p + kStKM) = make_uint2(st.kc_km[2], st.kc_km[3]);
-    *reinterpret_cast<uint2*>(p + kStVC) = make_uint2(st.vc_vm[0], st.vc_vm[1]);
-    *reinterpret_cast<uint2*>(p + kStVM) = make_uint2(st.vc_vm[2], st.vc_vm[3]);
+    unsigned char* p = stage_ptr(slot);
+    *reinterpret_cast<uint2*>(p + s_kc) = make_uint2(st.kc_km[0], st.kc_km[1]);
+    *reinterpret_cast<uint2*>(p + s_km) = make_uint2(st.kc_km[2], st.kc_km[3]);
+    *reinterpret_cast<uint2*>(p + s_vc) = make_uint2(st.vc_vm[0], st.vc_vm[1]);
+    *reinterpret_cast<uint2*>(p + s_vm) = make_uint2(st.vc_vm[2], st.vc_vm[3]);
   };
 
   // Scores of the staged block in `slot`: the key codes expanded against the queries (chunks w and
@@ -293,29 +311,37 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
     }
     const uint32_t kmw = vo.kmw;
     if constexpr (RANK) {
-      // the rank row's logits against C' (before any kappa masking), log2 units; when ranking by the
-      // mixed cache the kappa positions are written by the 16-bit blocks instead
-      if (rank_lane && a.rank_mixed && kmw) {
-        float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
+      // the rank row's logits against C' (before any kappa masking), log2 units, through the raw
+      // buffer over the slice's logits (the block offset is scalar)
+      typedef float f4_t __attribute__((ext_vector_type(4)));
+      const f4_t v = {xa[0], xa[1], xa[2], xa[3]};
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((blk0 + jj) * 32 * 4));
+      const uint32_t voff = rl_lane + 4 * (16 * (n16 >> 3) + 4 * g);
+      if constexpr (MIXED) {
+        // the kappa positions are written by the 16-bit blocks instead
+        if (rank_lane && kmw) {
+          float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * (n16 >> 3) + 4 * g + i;
-          if (!((kmw >> tok) & 1u)) dst[tok] = xa[i];
+          for (int i = 0; i < 4; ++i) {
+            const int tok = 16 * (n16 >> 3) + 4 * g + i;
+            if (!((kmw >> tok) & 1u)) dst[tok] = xa[i];
+          }
+        } else if (rank_lane) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf, (int)voff, (int)soff, 0);
         }
-      } else if (rank_lane) {
-        // through the raw buffer over the slice's logits (the block offset is scalar)
-        const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((blk0 + jj) * 32 * 4));
-        typedef float f4_t __attribute__((ext_vector_type(4)));
-        const f4_t v = {xa[0], xa[1], xa[2], xa[3]};
+      } else {
+        // issued by every lane, the lanes without a rank row addressing past the buffer (such a
+        // store is dropped): with no branch around it the compiler counts it, and the waits for
+        // the staged loads stay exact
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
-                                               (int)(rl_lane + 4 * (16 * (n16 >> 3) + 4 * g)), (int)soff, 0);
+                                               (int)(rank_lane ? voff : kStDropped), (int)soff, 0);
       }
-      // the bound of each 16-position group for the pruned selection: the four lanes g of n16 hold
-      // tile n16 >> 3 of row arow
-      if (a.rank_gmax) {
-        const float gm = max_over_groups(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
-        if (rank_lane && g == 0) a.rank_gmax[(slice * G + arow / T) * (N >> 4) + (blk0 + jj) * 2 + (n16 >> 3)] = gm;
-      }
+      // the bound of each 16-position group for the pruned selection (a buffer of size 0 when it
+      // is not wanted): the four lanes g of n16 hold tile n16 >> 3 of row arow
+      const float gm = max_over_groups(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
+      const uint32_t goff = 4u * (uint32_t)((arow / T) * (N >> 4) + (blk0 + jj) * 2 + (n16 >> 3));
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gm), gm_buf,
+                                            (int)(rank_lane && g == 0 ? goff : kStDropped), 0, 0);
     }
     float xc[4];  // C' logits of masked positions, for the ranking statistics
     if (kmw) {
@@ -470,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
       bool ok = base + tok < lim;
       if constexpr (RANK) {
         // ranking by the mixed cache: a fetched row's logit replaces its low-bit one
-        if (a.rank_mixed && rank_lane && !tail && ok) {
+        if (MIXED && rank_lane && !tail && ok) {
           const int64_t pos = a.idx[slice * a.k + base + tok];
           a.rank_logits[(slice * G + arow / T) * N + pos] = v;
         }
@@ -603,7 +629,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   __syncthreads();  // all waves are done with their tiles and slots; the LDS union becomes the combine buffer
   if constexpr (RANK) {
     // one thread per head: combine the four waves and write this split's statistics over C'
-    if (!a.rank_mixed && tid < G) {
+    if (!MIXED && tid < G) {
       const int r = tid * T + a.rank_row;
       float M = kMergeEmpty;
 #pragma unroll
@@ -658,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
       a.part_ml[(row * S + split) * 2 + 1] = lsum;
       if constexpr (RANK) {
         // ranking by the mixed cache: the rank row's own softmax statistics of this split
-        if (a.rank_mixed && r % T == a.rank_row) {
+        if (MIXED && r % T == a.rank_row) {
           a.rank_m[(slice * G + r / T) * S + split] = M;
           a.rank_l[(slice * G + r / T) * S + split] = lsum;
         }
@@ -675,10 +701,12 @@ bool attn_stream_serves(const Dims& d, const AttnArgs& a) {
 
 hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
-  if (a.rank_logits)
-    attn_stream_kernel<true><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  if (!a.rank_logits)
+    attn_stream_kernel<0><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  else if (!a.rank_mixed)
+    attn_stream_kernel<1><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   else
-    attn_stream_kernel<false><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+    attn_stream_kernel<2><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   return hipGetLastError();
 }
 
