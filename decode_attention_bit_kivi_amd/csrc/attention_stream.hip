@@ -58,8 +58,7 @@ struct StreamSmem {
       unsigned char stage[2][kStSlot];
     } w[4];
     struct {
-      float o[4][8][kStD];
-      float zs[4][8][2 * kStW];
+      float o[4][8][kStD];  // per wave: final-form output rows (16-byte aligned for float4 access)
       float m[4][8];
       float l[4][8];
     } comb;
@@ -103,6 +102,14 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   const int64_t p1 = p0 + L < N ? p0 + L : N;
   const int nb = (int)((p1 - p0) / 32);
   const int64_t blk0 = p0 / 32;
+
+  // ---- the kappa indices are loaded before anything else: the scan below then waits for them
+  // alone, with the query and staged loads issued after them still in flight
+  constexpr int kIdxPre = 2;  // indices per thread loaded up front (the rest, when k > 512, in the scan)
+  const int32_t* ix = a.idx + slice * a.k;
+  int32_t ixv[kIdxPre];
+#pragma unroll
+  for (int j = 0; j < kIdxPre; ++j) ixv[j] = tid + 256 * j < a.k ? ix[tid + 256 * j] : 0;
 
   // ---- query fragments: B[k-slot (g, j)][column n] = q[row n & 7][32w + 8g + j], every row in both
   // halves of the columns.  A 16-token tile's products go to an accumulator of its own, and lane
@@ -401,12 +408,12 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   // anything else, so that they are in flight through the kappa scan and the fetched 16-bit blocks
   const int vw = wave;
   const int nw = vw < nb ? (nb - vw + 3) / 4 : 0;
-  auto blk = [&](int i) { return vw + 4 * (i < nw ? i : nw - 1); };  // clamped to the last block
+  // clamped to the last block (block 0 for a wave with none, whose loads are then unused): the
+  // loads are issued unconditionally, so that the waits for the ones before them stay exact
+  auto blk = [&](int i) { return nw > 0 ? vw + 4 * (i < nw ? i : nw - 1) : 0; };
   Staged stg[P];
-  if (nw > 0) {
 #pragma unroll
-    for (int j = 0; j < P; ++j) stg[j] = stage_load(blk(j));
-  }
+  for (int j = 0; j < P; ++j) stg[j] = stage_load(blk(j));
 
   if (RANK && split == 0)  // the rank kernels accumulate a per-slice histogram here
     for (int i = tid; i < 2048; i += 256) a.rank_hist[slice * 2048 + i] = 0u;
@@ -417,14 +424,16 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   if (tid < 2) sm.sel_range[tid] = 0;
   __syncthreads();
   {
-    const int32_t* ix = a.idx + slice * a.k;
     int below0 = 0, below1 = 0;
-    for (int i = tid; i < a.k; i += 256) {
-      const int64_t p = ix[i];
+    auto take = [&](int64_t p) {
       below0 += p < p0 ? 1 : 0;
       below1 += p < p1 ? 1 : 0;
       if (p >= p0 && p < p1) atomicOr(&sm.kmask[(p - p0) >> 5], 1u << ((p - p0) & 31));
-    }
+    };
+#pragma unroll
+    for (int j = 0; j < kIdxPre; ++j)
+      if (tid + 256 * j < a.k) take(ixv[j]);
+    for (int i = tid + 256 * kIdxPre; i < a.k; i += 256) take(ix[i]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       below0 += __shfl_xor(below0, off);
@@ -645,40 +654,55 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
     sm.u.comb.m[wave][n16] = mm;
     sm.u.comb.l[wave][n16] = f_self * l_row + f_other * l2;
   }
-  // accumulator rows 4g' + i; rows r and r + 8 (lanes g' and g' ^ 2) fold into r (lanes g' < 2)
+  // accumulator rows 4g' + i of the lane's channels in final form, -O/2 + Z + h S with Z and S the
+  // zero-point and scale columns of the channels' value group in the metadata product (held by
+  // lanes wv_grp and Wg + wv_grp of the same k-group); then rows r and r + 8 (the two tiles of a
+  // query row, lanes g' and g' ^ 2) fold into r (lanes g' < 2) with their weights
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * g + i;
+    const float zl = __shfl(Ozs[i], 16 * g + wv_grp);
+    const float sl = __shfl(Ozs[i], 16 * g + Wg + wv_grp);
+    const float base = zl + hV * sl;
     const float ws = __shfl(f_self, r & 7);
     const float wo = __shfl(f_other, r & 7);
-    const float zsv = ws * Ozs[i] + wo * __shfl_xor(Ozs[i], 32);
     float ov[CPL];
 #pragma unroll
-    for (int ct = 0; ct < CPL; ++ct) ov[ct] = ws * Oacc[ct][i] + wo * __shfl_xor(Oacc[ct][i], 32);
-    if (g < 2) {
-      if (n16 < 2 * Wg) sm.u.comb.zs[wave][r][n16] = zsv;
+    for (int ct = 0; ct < CPL; ++ct) ov[ct] = -0.5f * Oacc[ct][i] + base;
 #pragma unroll
-      for (int ct = 0; ct < CPL; ++ct) sm.u.comb.o[wave][r][CPL * n16 + ct] = ov[ct];
+    for (int ct = 0; ct < CPL; ++ct) ov[ct] = ws * ov[ct] + wo * __shfl_xor(ov[ct], 32);
+    if (g < 2) {
+      float4* dst = reinterpret_cast<float4*>(&sm.u.comb.o[wave][r][CPL * n16]);
+      dst[0] = make_float4(ov[0], ov[1], ov[2], ov[3]);
+      dst[1] = make_float4(ov[4], ov[5], ov[6], ov[7]);
     }
   }
   __syncthreads();
 
   // ================= combine the four waves and write this split's partials =================
-  for (int e = tid; e < R * D; e += 256) {
-    const int r = e / D, c = e % D;
-    float M = kMergeEmpty;
-#pragma unroll
-    for (int w4 = 0; w4 < 4; ++w4) M = fmaxf(M, sm.u.comb.m[w4][r]);
-    float lsum = 0.0f, o = 0.0f;
-    const int gv = c >> (5 + gshift);
+  // row r = tid / 32, channels 4 (tid mod 32) .. + 3
+  const int r = tid >> 5, c = 4 * (tid & 31);
+  if (r < R) {
+    float mw[4], M = kMergeEmpty;
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
-      const float e4 = __builtin_amdgcn_exp2f(sm.u.comb.m[w4][r] - M);
+      mw[w4] = sm.u.comb.m[w4][r];
+      M = fmaxf(M, mw[w4]);
+    }
+    float lsum = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const float e4 = __builtin_amdgcn_exp2f(mw[w4] - M);
       lsum += e4 * sm.u.comb.l[w4][r];
-      o += e4 * (-0.5f * sm.u.comb.o[w4][r][c] + sm.u.comb.zs[w4][r][gv] + hV * sm.u.comb.zs[w4][r][Wg + gv]);
+      const float4 ow = *reinterpret_cast<const float4*>(&sm.u.comb.o[w4][r][c]);
+      o.x += e4 * ow.x;
+      o.y += e4 * ow.y;
+      o.z += e4 * ow.z;
+      o.w += e4 * ow.w;
     }
     const int64_t row = row0 + r;
-    a.part_acc[(row * S + split) * D + c] = o;
+    *reinterpret_cast<float4*>(&a.part_acc[(row * S + split) * D + c]) = o;
     if (c == 0) {
       a.part_ml[(row * S + split) * 2] = M;
       a.part_ml[(row * S + split) * 2 + 1] = lsum;
