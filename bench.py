@@ -43,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_step_mistral32k_traffic.json")
-STEP_SOURCES = ("attention.hip", "rank.hip", "merge.h", "mfma_frag.h", "common.h")
+STEP_SOURCES = ("attention.hip", "attention_stream.hip", "rank.hip", "merge.h", "mfma_frag.h", "common.h")
 
 
 def step_sources_hash() -> str:
@@ -143,7 +143,7 @@ def copy_reference(reps: int = 5):
 
 MODEL_SHAPE = {"tiny": "tiny", "llama8k": "Llama-3-8B-shaped", "mistral32k": "Mistral-7B-shaped",
                "layers32": "Llama-3-8B-shaped", "long128k": "long-context (Llama/Mistral-shaped heads)"}
-TRAFFIC_KERNELS = "attn_split|rank_keys|rank_select|attn_merge"
+TRAFFIC_KERNELS = "attn_split|attn_stream|rank_keys|rank_select|attn_merge"
 TRAFFIC_COMMANDS = [
     "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_fetch -o run -- python -u bench.py --mode copy",
     "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o run -- python -u bench.py --mode copy",
@@ -188,15 +188,16 @@ def write_traffic_record(root: str, workload: str = "mistral32k"):
     for counter, run in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
         after_split = {}
         for queue, _, name, v in _counter_rows(root, run, counter):
-            if "attn_split_kernel" in name and ", true, false>" in name:
-                kind = re.search(r"attn_split_kernel<[^>]*>", name).group(0)
+            fused = re.search(r"attn_split_kernel<[^>]*, true, false>|attn_stream_kernel<[12]>", name)
+            if fused:  # the split kernel with ranking outputs (the streamed one, or the general one)
+                kind = fused.group(0)
                 after_split[queue] = True
             elif after_split.get(queue) and ("rank_keys" in name or "rank_select" in name):
                 kind = "rank_keys_kernel" if "rank_keys" in name else "rank_select_kernel (with the split merge)"
                 if "rank_select" in name:
                     after_split[queue] = False
             else:
-                if "attn_split" in name:
+                if "attn_split" in name or "attn_stream" in name:
                     after_split[queue] = False
                 continue
             per.setdefault(kind, {}).setdefault(counter, []).append(v)
@@ -654,7 +655,8 @@ def main():
             if args.compute_stream == "exclusive" else 0,
         },
         "roofline": {
-            "kernel": "decode_step (attn_split_kernel with ranking + " + (
+            "kernel": "decode_step (the split kernel with ranking outputs: attn_stream_kernel<1> for 1-bit "
+                      "codes at head_dim 128, attn_split_kernel otherwise; then " + (
                 "rank_select forming r(p) and merging the splits)" if N <= 32768 and Hq // Hkv <= 4 else
                 "rank_keys + rank_select merging the splits)"),
             "bound": "hbm",

@@ -14,6 +14,8 @@ import bench  # noqa: E402
 from workloads import get_config  # noqa: E402
 
 SPLIT = "void specache::(anonymous namespace)::attn_split_kernel<128, 1, 1, 2, true, false>(specache::AttnArgs, int)"
+STREAM = "void specache::(anonymous namespace)::attn_stream_kernel<1>(specache::AttnArgs, int, int, long, long, int)"
+PLAIN = "void specache::(anonymous namespace)::attn_stream_kernel<0>(specache::AttnArgs, int, int, long, long, int)"
 KEYS = "void specache::(anonymous namespace)::rank_keys_kernel<4>(float const*)"
 SELECT = "void specache::(anonymous namespace)::rank_select_resident_kernel<128>(float const*)"
 
@@ -27,7 +29,8 @@ def _write(root, run, rows):
         w.writerows(rows)
 
 
-def test_traffic_record_scales_counters_and_keeps_only_fused_step_dispatches(tmp_path, monkeypatch):
+@pytest.mark.parametrize("split", [SPLIT, STREAM])
+def test_traffic_record_scales_counters_and_keeps_only_fused_step_dispatches(tmp_path, monkeypatch, split):
     root = str(tmp_path)
     # the plain 1 GiB copy reads as 512 MiB of FETCH_SIZE and 1 GiB of WRITE_SIZE (KiB units)
     _write(root, "pmc_copy_fetch", [[1, 1, "fill", "FETCH_SIZE", 0], [2, 1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288]])
@@ -36,10 +39,14 @@ def test_traffic_record_scales_counters_and_keeps_only_fused_step_dispatches(tmp
     for counter, run, vals in (("FETCH_SIZE", "pmc_fetch", (1000, 100, 10)), ("WRITE_SIZE", "pmc_write", (500, 50, 5))):
         rows, did = [], 1
         for _ in range(3):
-            for name, v in ((SPLIT, vals[0]), (KEYS, vals[1]), (SELECT, vals[2])):
+            for name, v in ((split, vals[0]), (KEYS, vals[1]), (SELECT, vals[2])):
                 rows.append([did, 2, name, counter, v])
                 did += 1
             rows.append([did, 2, KEYS, counter, 10 ** 6])  # a score_topk's rank_keys: not part of the step
+            did += 1
+            rows.append([did, 2, PLAIN, counter, 10 ** 6])  # decode_attn's split: not part of the step
+            did += 1
+            rows.append([did, 2, SELECT, counter, 10 ** 6])  # nor a selection that follows no fused split
             did += 1
         _write(root, run, rows)
     out = tmp_path / "record.json"
