@@ -657,8 +657,10 @@ def main():
         "roofline": {
             "kernel": "decode_step (the split kernel with ranking outputs: attn_stream_kernel<1> for 1-bit "
                       "codes at head_dim 128, attn_split_kernel otherwise; then " + (
-                "rank_select forming r(p) and merging the splits)" if N <= 32768 and Hq // Hkv <= 4 else
-                "rank_keys + rank_select merging the splits)"),
+                "rank_select_pruned: r(p) of the position groups whose 16-position bound reaches the k-th "
+                "rank, the top-k and the merge of the splits)" if N <= 32768 and Hq // Hkv <= 4 and k <= N // 16 else
+                "rank_select forming r(p), the top-k and the merge of the splits)" if N <= 32768 and Hq // Hkv <= 4
+                else "rank_keys + rank_select merging the splits)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
