@@ -822,7 +822,6 @@ struct PrunedSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
   uint32_t sel_digit, sel_above, n_cand;
-  uint32_t res[4];  // small-bin selection: thr, need_eq, n_eq, found
   float bin_vals[2];
   float lse2[kFusedG];
   uint32_t n_grp;
@@ -875,7 +874,6 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
   }
   if (t == 0) {
     sm.n_cand = 0u;
-    sm.res[3] = 0u;
   }
   __syncthreads();
   float lse2[kFusedG];
@@ -994,11 +992,17 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
 
   uint32_t thr, need_eq, n_thr;
   if (in_bin <= (uint32_t)kCand) {
+    // the passes past n_pass hold no candidates: their keys are skipped by a uniform branch
     uint32_t mine = 0u;
 #pragma unroll
-    for (int i = 0; i < 4 * kMaxPasses; ++i) {
-      const float x = v[i];
-      mine |= (valid(i) && x >= va && (top_open || x < vb)) ? (1u << i) : 0u;
+    for (int s = 0; s < kMaxPasses; ++s) {
+      if (s >= n_pass) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * s + e;
+        const float x = v[i];
+        mine |= (valid(i) && x >= va && (top_open || x < vb)) ? (1u << i) : 0u;
+      }
     }
     if (__any(mine != 0u)) {
       const uint32_t n = __popc(mine);
@@ -1008,35 +1012,36 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       base_slot = __shfl(base_slot, 63);
       uint32_t slot = base_slot + incl - n;
 #pragma unroll
-      for (int i = 0; i < 4 * kMaxPasses; ++i)
-        if ((mine >> i) & 1u) {
-          if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[i]);
-          ++slot;
-        }
+      for (int s = 0; s < kMaxPasses; ++s) {
+        if (s >= n_pass) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((mine >> (4 * s + e)) & 1u) {
+            if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[4 * s + e]);
+            ++slot;
+          }
+      }
     }
     __syncthreads();
     const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
     const uint32_t krem = (uint32_t)k - above;
+    // at most 64 keys in the bin: every wave finds the exact threshold among them itself (the same
+    // keys, so the same answer in every wave), which saves a barrier to publish it
+    bool found = false;
     if (nc <= 64u) {
-      if (wave == 0) {
-        const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
-        const uint32_t gt_eq = count_above_equal(c, nc);
-        const uint32_t gt = gt_eq & 0xffffu, eq = gt_eq >> 16;
-        const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
-        if (m != 0u && lane == __builtin_ctzll(m)) {
-          sm.res[0] = c;
-          sm.res[1] = krem - gt;
-          sm.res[2] = eq;
-          sm.res[3] = 1u;
-        }
+      const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
+      const uint32_t gt_eq = count_above_equal(c, nc);
+      const uint32_t gt = gt_eq & 0xffffu, eq = gt_eq >> 16;
+      const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
+      if (m != 0u) {
+        const int src = __builtin_ctzll(m);
+        thr = __builtin_amdgcn_readlane(c, src);
+        need_eq = krem - __builtin_amdgcn_readlane(gt, src);
+        n_thr = __builtin_amdgcn_readlane(eq, src);
+        found = true;
       }
-      __syncthreads();
     }
-    if (sm.res[3]) {
-      thr = sm.res[0];
-      need_eq = sm.res[1];
-      n_thr = sm.res[2];
-    } else {
+    if (!found) {
       radix_select(sm, krem,
                    [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
                      for (uint32_t i = t; i < nc; i += kSelThreads) {
@@ -1068,6 +1073,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
   for (int s = 0; s < kMaxPasses; ++s) {
     sel[s] = 0u;
     eqm[s] = 0u;
+    if (s >= n_pass) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (valid(4 * s + e)) {
@@ -1099,6 +1105,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     pass_prefix(eqm, before);
 #pragma unroll
     for (int s = 0; s < kMaxPasses; ++s) {
+      if (s >= n_pass) continue;
       const uint32_t ne = __popc(eqm[s]);
       uint32_t take = before[s] >= need_eq ? 0u : (need_eq - before[s] < ne ? need_eq - before[s] : ne);
       while (take > 0u) {  // the lowest equal positions first
@@ -1113,6 +1120,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
   pass_prefix(sel, out0);
 #pragma unroll
   for (int s = 0; s < kMaxPasses; ++s) {
+    if (s >= n_pass) continue;
     uint32_t m = sel[s], out = out0[s];
     while (m != 0u) {
       const int b = __builtin_ctz(m);
