@@ -105,6 +105,8 @@ def parse(argv=None):
     ap.add_argument("--reuse", action=argparse.BooleanOptionalAction, default=True,
                     help="fetch only the rows of the new top-k not already resident (the step time of "
                          "fetching every row is reported beside it)")
+    ap.add_argument("--host-copies", choices=("per-layer", "shared"), default="per-layer",
+                    help="the 16-bit cache in pinned host memory: a copy per layer in turn, or one shared")
     ap.add_argument("--top-k", type=int, default=0, help="override the workload's top-k (latency-vs-k sweeps)")
     ap.add_argument("--sync-every", type=int, default=2, choices=(1, 2, 4),
                     help="steps per cross-stream synchronisation of the pipeline (at most half the layers "
@@ -417,6 +419,24 @@ def main():
     layers = -(-layers // args.sync_every) * args.sync_every  # whole synchronisation groups
     caches = [cache0] + [quantize_pack(k16, v16, cfg.bits) for _ in range(layers - 1)]
     torch.cuda.synchronize()
+    # each layer's 16-bit K and V in pinned host memory of its own (as a model offloads every
+    # layer); one copy shared by all layers only when pinning that much fails
+    hks, hvs = [hk], [hv]
+    host_copies = "per-layer"
+    if args.host_copies == "per-layer":
+        try:
+            for _ in range(layers - 1):
+                hks.append(torch.empty(hk.shape, dtype=hk.dtype, pin_memory=True).copy_(hk))
+                hvs.append(torch.empty(hv.shape, dtype=hv.dtype, pin_memory=True).copy_(hv))
+        except RuntimeError as e:
+            hks, hvs = [hk], [hv]
+            host_copies = f"shared (pinning a copy per layer failed: {str(e).splitlines()[0][:120]})"
+    else:
+        host_copies = "shared"
+    print(f"[bench] host copies of the 16-bit cache: {host_copies}", file=sys.stderr, flush=True)
+
+    def host_kv(l):
+        return (hks[l], hvs[l]) if len(hks) > 1 else (hk, hv)
 
     ws = torch.empty(decode_step_workspace_size(cache0, Hq, T, k, 0, k), dtype=torch.uint8, device=dev)
     ws_s = torch.empty(score_topk_workspace_size(cache0, Hq, T, k), dtype=torch.uint8, device=dev)
@@ -448,7 +468,7 @@ def main():
         for l in range(layers):
             i0 = score_topk(qs[n_q - 1], caches[l], k, rank_row=1, workspace=ws_s)
             st["idx"].append([i0, torch.empty_like(i0)])
-            st["sel"].append([gather_fp16(i0, hk, hv, cfg.bits),
+            st["sel"].append([gather_fp16(i0, *host_kv(l), cfg.bits),
                               (torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev),
                                torch.empty((B, Hkv, k, D), dtype=torch.float16, device=dev))])
             st["fetch"].append(torch.empty_like(i0))
@@ -498,9 +518,9 @@ def main():
             ev["g0"].record(side)
         for (pl, pidx, psel) in st["pending"]:
             if reuse:
-                gather_fp16_missing(st["fetch"][pl], hk, hv, psel[0], psel[1], cfg.bits, stream=side)
+                gather_fp16_missing(st["fetch"][pl], *host_kv(pl), psel[0], psel[1], cfg.bits, stream=side)
             else:
-                gather_fp16(pidx, hk, hv, cfg.bits, psel[0], psel[1], stream=side)
+                gather_fp16(pidx, *host_kv(pl), cfg.bits, psel[0], psel[1], stream=side)
         if ev and "g1" in ev:
             ev["g1"].record(side)
         st["pending"] = []
@@ -651,6 +671,7 @@ def main():
             "compute_stream": args.compute_stream, "rank": args.rank, "sync_every": args.sync_every,
             "fetch": "resident rows reused, only new top-k rows fetched" if args.reuse else "every top-k row fetched",
             "queries": f"fresh draws every step ({n_q} in turn), planted peak shared",
+            "host_copies": host_copies,
             "compute_stream_reserved_cus": max(args.compute_reserve, args.gather_cus)
             if args.compute_stream == "exclusive" else 0,
         },
@@ -720,7 +741,7 @@ def main():
     # torch's pinned-memory allocator records an event on every stream a pinned block was
     # copied on when the block is freed (hk and hv were, by the full-layer copy): free them
     # while the library's streams still exist, then destroy the streams
-    del hk, hv
+    del hk, hv, hks, hvs
     torch.cuda.synchronize()
     torch.cuda.set_stream(torch.cuda.default_stream())
     if args.compute_stream == "exclusive":
