@@ -357,7 +357,7 @@ int specache_decode_attn(const specache_shape* shape, const void* q16, int n_tok
   err = fill_attn_args(d, q16, n_tokens, cache, idx, k, k_sel, v_sel, k_tail, v_tail, tail_len, sm_scale, out16, &a);
   if (err != SPECACHE_OK) return err;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const AttnPlan plan = attn_plan(d, stream_cus(s));
+  const AttnPlan plan = attn_plan(d, stream_cus(s), attn_split_wgs_per_cu(d, a));
   const AttnWs ws = attn_ws(d, n_tokens);
   if (!workspace || workspace_bytes < ws.total) return SPECACHE_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);
@@ -391,7 +391,7 @@ int specache_decode_attn_fp16(const specache_shape* shape, const void* q16, int 
   const void* vd = device_view(v16);
   if (!kd || !vd) return SPECACHE_ERR_NOT_PINNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const AttnPlan plan = attn_plan(d, stream_cus(s));
+  const AttnPlan plan = attn_plan(d, stream_cus(s), kAttnWGsPerCU);
   const AttnWs ws = attn_ws(d, n_tokens);
   if (!workspace || workspace_bytes < ws.total) return SPECACHE_ERR_WORKSPACE;
   AttnArgs a;
@@ -442,7 +442,7 @@ int decode_step_impl(const specache_shape* shape, const void* q16, int n_tokens,
       (rank_mixed != 0 && rank_mixed != 1))
     return SPECACHE_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const AttnPlan plan = attn_plan(d, stream_cus(s));
+  const AttnPlan plan = attn_plan(d, stream_cus(s), attn_split_wgs_per_cu(d, a));
   const AttnWs ws = attn_ws(d, n_tokens);
   if (!workspace || workspace_bytes < ws.total_step) return SPECACHE_ERR_WORKSPACE;
   char* base = static_cast<char*>(workspace);

@@ -21,6 +21,11 @@
 // accesses of one wave complete in order, so no barrier is involved).  A block's constant
 // sum_c q_c (z_c + h s_c) comes from four MFMAs on the staged zero-points and scales, so there is
 // no separate pass over the key metadata that would wait for its loads.
+//
+// The kernel is held to 168 registers so that three workgroups share a compute unit (three waves
+// per SIMD): the VALU work of expanding the codes, not the bytes, bounds a wave, and a third wave
+// keeps the SIMD issuing while the other two wait on LDS and the matrix cores.  Each wave then
+// streams two blocks ahead.
 #include "merge.h"
 #include "mfma_frag.h"
 
@@ -34,7 +39,7 @@ constexpr int kStD = 128;
 constexpr int kStW = kStD / 32;    // 32-channel chunks
 constexpr int kStCPL = kStD / 16;  // value channel tiles (channels per lane)
 constexpr int kStRS = 36;          // row stride (halves) of the transposed 16-bit value tile
-constexpr int kStreamAhead = 4;    // blocks whose bytes each wave has in flight
+constexpr int kStreamAhead = 2;    // blocks whose bytes each wave has in flight (three waves per SIMD)
 // A staged block in LDS: key codes (512 bytes), key zero-points then scales (256 bytes each, 16
 // bytes apart), value codes (16 bytes after every 64 channels' words), value metadata (64-byte rows,
 // 8 bytes apart).  The gaps put the addresses that one operand read sends to the same bank row on
@@ -52,6 +57,7 @@ struct StreamSmem {
   uint32_t kmask[kAttnMaxBlocks];
   float rank_m[4][16], rank_l[4][16];  // per wave: ranking statistics of each query row
   int sel_range[2];
+  uint4 bq[kStW][64];  // the query fragments (identical in every wave), lane l's at [w][l]
   // 16-byte aligned: the operands are read back with 16-byte LDS reads
   union alignas(16) {
     union {  // per wave: the 16-bit value tile, or (during the low-bit blocks) two staged blocks
@@ -74,7 +80,7 @@ using IC = std::integral_constant<int, R>;
 // MODE 0: attention only; 1: with the rank row's logits, bounds and statistics against C';
 // 2: with the ranking by the mixed-cache attention row.
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L, int S) {
+__global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L, int S) {
   // Only the explicit fmaf calls fuse: the compiler may not contract a product and a sum on its own,
   // which it could do differently in the two instantiations and so make the attention of the fused
   // step differ from decode_attn's in the last bit.
@@ -115,13 +121,20 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
   // ---- query fragments: B[k-slot (g, j)][column n] = q[row n & 7][32w + 8g + j], every row in both
   // halves of the columns.  A 16-token tile's products go to an accumulator of its own, and lane
   // n16 keeps tile n16 >> 3's (columns 0-7: tile 0, 8-15: tile 1): the values attn_split_kernel
-  // accumulates for these columns, product for product.
+  // accumulates for these columns, product for product.  They are the same in every wave and are
+  // read back from LDS at each use: three workgroups share a compute unit, and 16 registers held
+  // through the loop would not leave room for the third.
   const int arow = n16 & 7;  // query row of this lane's logits
   const bool tile1 = n16 >= 8;
-  Frag Bq[W];
+  uint4 bq_ld[W];
 #pragma unroll
   for (int w = 0; w < W; ++w)
-    Bq[w].v = arow < R ? load_u4(a.q16 + (row0 + arow) * D + 32 * w + 8 * g) : make_uint4(0, 0, 0, 0);
+    bq_ld[w] = arow < R ? load_u4(a.q16 + (row0 + arow) * D + 32 * w + 8 * g) : make_uint4(0, 0, 0, 0);
+  auto Bq = [&](int w) {
+    Frag f;
+    f.v = sm.bq[w][lane];
+    return f;
+  };
 
   float m_used = kMergeEmpty;  // running max (log2 units) of accumulator row n16
   float l_part = 0.0f;         // this lane's share of that row's sum of exponentials (low-bit positions)
@@ -272,8 +285,8 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
 #pragma unroll
         for (int d = 0; d < 4; ++d)
           signed_pairs2(kw[tau][w], kw[tau][w + 1], 15 - 4 * g - d, ma[d], mb[d], A0.u[d], A1.u[d]);
-        acct[tau] = mma(A0, Bq[w], acct[tau]);
-        acct[tau] = mma(A1, Bq[w + 1], acct[tau]);
+        acct[tau] = mma(A0, Bq(w), acct[tau]);
+        acct[tau] = mma(A1, Bq(w + 1), acct[tau]);
       }
     }
     f32x4 accc = zero4();
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
     for (int w = 0; w < W; ++w) {
       Frag Z;
       Z.v = ko.kzs[w];
-      accc = mma(Z, Bq[w], accc);
+      accc = mma(Z, Bq(w), accc);
     }
     Scores sc;
 #pragma unroll
@@ -446,6 +459,10 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
       atomicAdd(&sm.sel_range[1], below1);
     }
   }
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) sm.bq[w][lane] = bq_ld[w];
+  }
   __syncthreads();
   const int i0 = sm.sel_range[0], i1 = sm.sel_range[1];
 
@@ -495,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
       for (int tau = 0; tau < 2; ++tau) {
         Frag A;
         A.v = (base + 16 * tau + n16 < lim) ? kk[tau][w].v : make_uint4(0, 0, 0, 0);
-        acct[tau] = mma(A, Bq[w], acct[tau]);
+        acct[tau] = mma(A, Bq(w), acct[tau]);
       }
     }
     float xr[4], xa[4];
@@ -552,31 +569,19 @@ __global__ __launch_bounds__(256, 2) void attn_stream_kernel(AttnArgs a, int Hkv
     auto step = [&](int i, auto rc) {
       constexpr int r = decltype(rc)::value;
       constexpr int b1 = (r + 1) % P, s1 = (r + 1) & 1, s0 = r & 1;
-      if constexpr (!RANK) {
-        // every LDS read of the step is issued before its arithmetic: block i's value operands
-        // (staged a step ago), then block i + 1's key operands behind its own staging
-        const VOps vo = read_v(s0, blk(i));
-        stage_store(stg[b1], s1);
-        const KOps ko = read_k(s1);
-        stg[b1] = stage_load(blk(i + 1 + P));
-        __builtin_amdgcn_sched_barrier(0);
-        finish(vo, sc[s0], blk(i));
-        if (i + 1 < nw) sc[s1] = score(ko);
-      } else {
-        // the ranking outputs' registers leave no room to hold both blocks' operands: each block's
-        // reads sit next to its arithmetic
-        stage_store(stg[b1], s1);
-        stg[b1] = stage_load(blk(i + 1 + P));
-        if (i + 1 < nw) sc[s1] = score(read_k(s1));
-        finish(read_v(s0, blk(i)), sc[s0], blk(i));
-      }
+      // each block's LDS reads sit next to its arithmetic: at three waves per SIMD there is no
+      // room to hold both blocks' operands at once
+      stage_store(stg[b1], s1);
+      stg[b1] = stage_load(blk(i + 1 + P));
+      if (i + 1 < nw) sc[s1] = score(read_k(s1));
+      finish(read_v(s0, blk(i)), sc[s0], blk(i));
     };
     stage_store(stg[0], 0);
     stg[0] = stage_load(blk(P));
     sc[0] = score(read_k(0));
-    // Issue priority by the blocks this wave has left: two workgroups share each compute unit, and
-    // the SIMD arbiter otherwise favours the older one, which then finishes long before the younger
-    // and leaves one wave per SIMD for the rest.
+    // Issue priority by the blocks this wave has left: three workgroups share each compute unit, and
+    // the SIMD arbiter otherwise favours the oldest, which then finishes long before the others and
+    // leaves fewer waves per SIMD for the rest.
     const int pr1 = nw / 16 + 1, pr2 = nw / 6 + 1, pr3 = nw / 3 + 1;
     int i = 0;
     for (; i + U <= nw; i += U) {

@@ -59,14 +59,16 @@ struct AttnPlan {
 };
 
 constexpr int kPlanMaxCUs = 256;     // compute units the attention plans are sized for at most
-constexpr int kAttnWGsPerCU = 2;     // resident attention workgroups per compute unit
+constexpr int kAttnWGsPerCU = 2;     // resident workgroups per compute unit: general attention kernels
+constexpr int kStreamWGsPerCU = 3;   // the same for the streamed split kernel (attention_stream.hip)
 constexpr int kAttnMaxBlocks = 256;  // 32-position blocks per split (the kernel's kappa bitmask)
 constexpr int kAttnMaxSplits = 1024; // splits per slice (the merge kernel's weight table)
 
 inline int64_t attn_min_splits(const Dims& d) { return ceil_div(d.nblk, kAttnMaxBlocks); }
 
-// Most splits per slice any compute-unit count may get: about four rounds of workgroups on
-// kPlanMaxCUs units.  The workspace is sized for it.
+// Most splits per slice any compute-unit count may get: about four rounds of kAttnWGsPerCU
+// workgroups on kPlanMaxCUs units (over two rounds of the streamed kernel's).  The workspace is
+// sized for it.
 inline int64_t attn_max_splits(const Dims& d) {
   int64_t cap = ceil_div(int64_t(4) * kPlanMaxCUs * kAttnWGsPerCU, d.slices());
   if (cap > d.nblk) cap = d.nblk;
@@ -82,13 +84,14 @@ inline AttnPlan attn_plan_splits(const Dims& d, int64_t S) {
   return p;
 }
 
-// Splits per slice for `cus` compute units: the fewest splits whose estimated time is within 3%
-// of the best.  The estimate of S splits is (rounds of the slices * S workgroups over the
-// resident slots) x (blocks of the busiest of a workgroup's four waves).
-inline AttnPlan attn_plan(const Dims& d, int cus) {
+// Splits per slice for `cus` compute units holding `wgs_per_cu` workgroups each: the fewest
+// splits whose estimated time is within 3% of the best.  The estimate of S splits is (rounds of
+// the slices * S workgroups over the resident slots) x (blocks of the busiest of a workgroup's
+// four waves).
+inline AttnPlan attn_plan(const Dims& d, int cus, int wgs_per_cu) {
   if (cus < 8) cus = 8;
   if (cus > kPlanMaxCUs) cus = kPlanMaxCUs;
-  const int64_t slots = (int64_t)cus * kAttnWGsPerCU;
+  const int64_t slots = (int64_t)cus * wgs_per_cu;
   const int64_t lo = attn_min_splits(d), hi = attn_max_splits(d);
   int64_t best = INT64_MAX;
   int64_t cost[kAttnMaxSplits + 1];
@@ -202,6 +205,10 @@ hipError_t launch_attn_merge(const Dims& d, const AttnPlan& plan, const AttnArgs
 // 128, 1-bit key and value codes and G * T <= 8; launch_attn_split uses it whenever it serves, with
 // the same plan and outputs.
 bool attn_stream_serves(const Dims& d, const AttnArgs& a);
+// Resident workgroups per compute unit of the split kernel that serves these arguments.
+inline int attn_split_wgs_per_cu(const Dims& d, const AttnArgs& a) {
+  return attn_stream_serves(d, a) ? kStreamWGsPerCU : kAttnWGsPerCU;
+}
 hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 // The 16-bit comparator's split kernel: a.k_sel / a.v_sel are the whole 16-bit cache, a.k its
 // positions per slice; partials as launch_attn_split's, merged by launch_attn_merge.
