@@ -55,7 +55,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct ScoreWs {
-  size_t logits, part_m, part_l, keys, hist, total;
+  size_t logits, part_m, part_l, keys, hist, kmax, total;
 };
 
 ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
@@ -70,6 +70,8 @@ ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
   off += align256(sizeof(float) * (size_t)d.slices() * d.N);
   w.hist = off;
   off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
+  w.kmax = off;  // per-16-position maxima of r(p) (the two-launch selection)
+  off += align256(sizeof(float) * (size_t)d.slices() * (d.N / 16));
   w.total = off;
   return w;
 }
@@ -99,7 +101,8 @@ AttnWs attn_ws(const Dims& d, int T) {
   off += align256(sizeof(float) * (size_t)d.slices() * d.N);
   w.hist = off;
   off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
-  w.gmax = off;  // per-16-position logit maxima of the pruned selection
+  w.gmax = off;  // per-16-position logit maxima of the pruned selection, or (two-launch form)
+                 // those of r(p)
   off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / 16));
   w.total_step = off;
   return w;
@@ -234,7 +237,7 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
                               sm_scale, logits, part_m, part_l, hist, s);
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
   e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, rank_key_out != nullptr, hist, idx_out,
-                         nullptr, s);
+                         nullptr, s, nullptr, reinterpret_cast<float*>(base + ws.kmax));
   return hip_status(e);
 }
 
@@ -465,7 +468,7 @@ int decode_step_impl(const specache_shape* shape, const void* q16, int n_tokens,
   const MergeJob merge{a.part_ml, a.part_acc, plan.S, (int64_t)d.B * d.Hq * n_tokens, a.out16};
   return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys,
                                        rank_key_out != nullptr, a.rank_hist, idx_next_out, &merge, s,
-                                       a.rank_gmax));
+                                       a.rank_gmax, reinterpret_cast<float*>(base + ws.gmax)));
 }
 
 // The no-allocation decode step's scratch: one array per GPU, in the library's code object, held

@@ -157,11 +157,14 @@ __device__ __forceinline__ float rank_of(const float4 (&x)[GM], int e, const flo
 
 // ---------------------------------------------------------------- rank_keys
 
+// Also the maximum key of every 16 positions into kmax[slice][N / 16] (the four lanes of a group
+// hold its four runs of one step), for the selection from the groups that reach the threshold bin.
 template <int GM>  // GM >= G: the heads' logits of a run are held in registers
 __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* logits, const float* part_m,
                                                                 const float* part_l, int G, int S,
                                                                 int64_t N, float r_lo, float* __restrict__ rkey,
-                                                                uint32_t* __restrict__ ghist) {
+                                                                uint32_t* __restrict__ ghist,
+                                                                float* __restrict__ kmax) {
   __shared__ float lse2[GM];  // log2-sum-exp2 of each head, in log2 units
   __shared__ uint32_t hist[kBins];
   const int t = threadIdx.x;
@@ -213,6 +216,12 @@ __global__ __launch_bounds__(kKeyThreads) void rank_keys_kernel(const float* log
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = rank_of<GM>(x[rr % NB], e, lse2, G);
       *reinterpret_cast<float4*>(rkey + slice * N + p) = make_float4(r[0], r[1], r[2], r[3]);
+      // lanes 4j .. 4j + 3 hold positions 16j' .. 16j' + 15 (p is a multiple of 16 at lane 4j;
+      // N is a multiple of 32, so the four lanes of a group are all in range together)
+      float gm = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
+      gm = fmaxf(gm, __shfl_xor(gm, 1));
+      gm = fmaxf(gm, __shfl_xor(gm, 2));
+      if ((t & 3) == 0) kmax[slice * (N / 16) + p / 16] = gm;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t b = coarse_bin(r[e], r_lo);
@@ -365,20 +374,14 @@ __device__ uint32_t first_key_of_bin_wave(uint32_t b, float r_lo) {
   return lo;
 }
 
-template <int D>
-__global__ __launch_bounds__(kSelThreads) void rank_select_kernel(const float* __restrict__ rkey,
-                                                                  const uint32_t* __restrict__ ghist, int64_t N,
-                                                                  int k, float r_lo, int32_t* __restrict__ idx_out,
-                                                                  unsigned n_sel, MergeJob mj) {
-  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
-    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
-    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
-    return;
-  }
-  __shared__ SelectSmem sm;
-  __shared__ float bin_vals[2];
+// The selection of slice `slice` from every key of the slice (rkey) and their coarse histogram
+// (ghist), in sweeps over the keys: the threshold bin's keys into LDS, the exact threshold among
+// them, then the positions above it (and the first equal ones) in position order, a chunk at a
+// time.  bin_vals: two floats of LDS outside sm.
+__device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* __restrict__ rkey,
+                                 const uint32_t* __restrict__ ghist, int64_t N, int k, float r_lo,
+                                 int32_t* __restrict__ idx_out, int64_t slice) {
   const int t = threadIdx.x, lane = t & 63;
-  const int64_t slice = blockIdx.x;
   const float* ky = rkey + slice * N;
   const uint32_t* gh = ghist + slice * kBins;
   for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
@@ -822,7 +825,6 @@ struct PrunedSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
   uint32_t sel_digit, sel_above, n_cand;
-  float bin_vals[2];
   float lse2[kFusedG];
   uint32_t n_grp;
   uint16_t grp[kMaxGroups];  // candidate groups, ascending
@@ -836,6 +838,170 @@ struct PrunedRank {
   const float* gmax;    // [slices][G][N / 16], log2 units
   int G, S;
 };
+
+// The coarse bin of the k-th largest key in sm.hist, the number of keys in the bins above it and
+// in it.  A key lies in that bin exactly when its own coarse bin is equal to it (the bins are
+// non-decreasing in the key), so the bin's value interval is never needed.
+template <typename Smem>
+__device__ void threshold_bin(Smem& sm, uint32_t k, uint32_t& bin, uint32_t& above, uint32_t& in_bin) {
+  pick_digit(sm, kBins, k, bin, above);
+  in_bin = sm.hist[bin];
+}
+
+// The selection among the keys of a slice's candidate groups of 16 positions, held four lanes a
+// group (lane quad q4 = t % 4 holds positions 4 q4 .. 4 q4 + 3 of it): pass s, kPassGroups groups,
+// in v[4s .. 4s + 3] for group grp_of[s] (-1: none, -inf keys), passes and threads in position
+// order.  sm.hist counts the keys by coarse bin (window from r_lo); `bin` holds the k-th
+// largest (in_bin keys), `above` keys lie in the bins above it, and the candidates include every
+// key of the slice whose bin is `bin` or higher.  Writes the positions of the k largest keys (ties to the lower position)
+// in position order to idx_out[slice * k ..].
+template <typename Smem>
+__device__ void select_in_groups(Smem& sm, const float (&v)[4 * kMaxPasses], const int (&grp_of)[kMaxPasses],
+                                 int n_pass, int k, float r_lo, uint32_t bin, uint32_t above, uint32_t in_bin,
+                                 int64_t slice, int32_t* __restrict__ idx_out) {
+  const int t = threadIdx.x, lane = t & 63, q4 = t & 3;
+  auto valid = [&](int i) { return grp_of[i >> 2] >= 0; };
+
+  uint32_t thr, need_eq, n_thr;
+  if (in_bin <= (uint32_t)kCand) {
+    // the passes past n_pass hold no candidates: their keys are skipped by a uniform branch
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int s = 0; s < kMaxPasses; ++s) {
+      if (s >= n_pass) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * s + e;
+        const float x = v[i];
+        mine |= (valid(i) && coarse_bin(x, r_lo) == bin) ? (1u << i) : 0u;
+      }
+    }
+    if (__any(mine != 0u)) {
+      const uint32_t n = __popc(mine);
+      const uint32_t incl = wave_inclusive_scan(n);
+      uint32_t base_slot = 0u;
+      if (lane == 63) base_slot = atomicAdd(&sm.n_cand, incl);
+      base_slot = __shfl(base_slot, 63);
+      uint32_t slot = base_slot + incl - n;
+#pragma unroll
+      for (int s = 0; s < kMaxPasses; ++s) {
+        if (s >= n_pass) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((mine >> (4 * s + e)) & 1u) {
+            if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[4 * s + e]);
+            ++slot;
+          }
+      }
+    }
+    __syncthreads();
+    const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
+    const uint32_t krem = (uint32_t)k - above;
+    // at most 64 keys in the bin: every wave finds the exact threshold among them itself (the same
+    // keys, so the same answer in every wave), which saves a barrier to publish it
+    bool found = false;
+    if (nc <= 64u) {
+      const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
+      const uint32_t gt_eq = count_above_equal(c, nc);
+      const uint32_t gt = gt_eq & 0xffffu, eq = gt_eq >> 16;
+      const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
+      if (m != 0u) {
+        const int src = __builtin_ctzll(m);
+        thr = __builtin_amdgcn_readlane(c, src);
+        need_eq = krem - __builtin_amdgcn_readlane(gt, src);
+        n_thr = __builtin_amdgcn_readlane(eq, src);
+        found = true;
+      }
+    }
+    if (!found) {
+      radix_select(sm, krem,
+                   [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+                     for (uint32_t i = t; i < nc; i += kSelThreads) {
+                       const uint32_t u = sm.cand[i];
+                       if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                     }
+                   },
+                   thr, need_eq, n_thr);
+    }
+  } else {
+    radix_select(sm, (uint32_t)k,
+                 [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
+#pragma unroll
+                   for (int i = 0; i < 4 * kMaxPasses; ++i) {
+                     const uint32_t u = order_key(v[i]);
+                     if (valid(i) && (u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
+                   }
+                 },
+                 thr, need_eq, n_thr);
+  }
+
+  // Every key above thr and the first need_eq equal to it, in position order (pass, then thread,
+  // then lane bit).  Per pass a thread has at most 4 such keys; the prefix sums run over two
+  // passes at once, one 16-bit field each (a pass holds at most 4096 keys).
+  const float vthr = key_value(thr);
+  const bool all_eq = need_eq == n_thr;
+  uint32_t sel[kMaxPasses], eqm[kMaxPasses];
+#pragma unroll
+  for (int s = 0; s < kMaxPasses; ++s) {
+    sel[s] = 0u;
+    eqm[s] = 0u;
+    if (s >= n_pass) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (valid(4 * s + e)) {
+        const float x = v[4 * s + e];
+        sel[s] |= (x > vthr || (all_eq && x == vthr)) ? (1u << e) : 0u;
+        eqm[s] |= (!all_eq && x == vthr) ? (1u << e) : 0u;
+      }
+  }
+  // exclusive prefix over (pass, thread) of per-pass counts: cnt(s) -> before(s)
+  auto pass_prefix = [&](const uint32_t (&m)[kMaxPasses], uint32_t (&before)[kMaxPasses]) {
+    uint32_t carried = 0u;
+#pragma unroll
+    for (int s = 0; s < kMaxPasses; s += 2) {
+      if (s >= n_pass) {  // uniform: nothing from here on
+        before[s] = carried;
+        before[s + 1] = carried;
+        continue;
+      }
+      uint32_t tot;
+      const uint32_t packed = (uint32_t)__popc(m[s]) | ((uint32_t)__popc(m[s + 1]) << 16);
+      const uint32_t ex = block_exclusive_scan(packed, sm.scan_scratch, tot);
+      before[s] = carried + (ex & 0xffffu);
+      before[s + 1] = carried + (tot & 0xffffu) + (ex >> 16);
+      carried += (tot & 0xffffu) + (tot >> 16);
+    }
+  };
+  if (!all_eq) {
+    uint32_t before[kMaxPasses];
+    pass_prefix(eqm, before);
+#pragma unroll
+    for (int s = 0; s < kMaxPasses; ++s) {
+      if (s >= n_pass) continue;
+      const uint32_t ne = __popc(eqm[s]);
+      uint32_t take = before[s] >= need_eq ? 0u : (need_eq - before[s] < ne ? need_eq - before[s] : ne);
+      while (take > 0u) {  // the lowest equal positions first
+        const uint32_t low = eqm[s] & (0u - eqm[s]);
+        sel[s] |= low;
+        eqm[s] ^= low;
+        --take;
+      }
+    }
+  }
+  uint32_t out0[kMaxPasses];
+  pass_prefix(sel, out0);
+#pragma unroll
+  for (int s = 0; s < kMaxPasses; ++s) {
+    if (s >= n_pass) continue;
+    uint32_t m = sel[s], out = out0[s];
+    while (m != 0u) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1u;
+      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(kGrp * grp_of[s] + 4 * q4 + b);
+      ++out;
+    }
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t N, int k, float r_lo,
@@ -973,174 +1139,124 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
   }
   if (cur_cnt) atomicAdd(&sm.hist[cur_bin], cur_cnt);
   __syncthreads();
-  auto valid = [&](int i) { return grp_of[i >> 2] >= 0; };
 
   // the exact threshold among the candidates, as the resident selection finds it
-  uint32_t bin, above;
-  pick_digit(sm, kBins, (uint32_t)k, bin, above);
-  const uint32_t in_bin = sm.hist[bin];
-  if (wave == 0) {
-    const uint32_t key = first_key_of_bin_wave(bin, r_lo);
-    if (lane == 0) sm.bin_vals[0] = key_value(key);
-  } else if (wave == 1) {
-    const float vb = bin + 1 < (uint32_t)kBins ? key_value(first_key_of_bin_wave(bin + 1, r_lo)) : INFINITY;
-    if (lane == 0) sm.bin_vals[1] = vb;
+  uint32_t bin, above, in_bin;
+  threshold_bin(sm, (uint32_t)k, bin, above, in_bin);
+  select_in_groups(sm, v, grp_of, n_pass, k, r_lo, bin, above, in_bin, slice, idx_out);
+}
+
+// ---- rank_select for slices longer than one selection workgroup holds, from rank_keys' keys and
+// their maxima over every 16 positions.  The global histogram gives the coarse bin of the k-th
+// largest key; every key in that bin or a higher one lies in a group whose maximum is in such a
+// bin (the bins are non-decreasing in the key), so only those groups' keys are read (about k of
+// them), into registers, and the selection among them is the pruned kernel's.  More than
+// kMaxGroups such groups (a crowded threshold bin, or k near kMaxGroups): the sweeps over every
+// key instead.
+struct GroupedSmem {
+  uint32_t hist[kBins];
+  uint32_t scan_scratch[2 * kSelWaves];
+  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t grp[kMaxGroups];  // candidate groups, ascending
+  uint32_t cand[kCand];
+};
+constexpr int kKmaxPre = 8;  // group maxima a thread loads before the histogram is read (128K: all)
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void rank_select_grouped_kernel(const float* __restrict__ rkey,
+                                                                          const float* __restrict__ kmax,
+                                                                          const uint32_t* __restrict__ ghist,
+                                                                          int64_t N, int k, float r_lo,
+                                                                          int32_t* __restrict__ idx_out,
+                                                                          unsigned n_sel, MergeJob mj) {
+  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
+    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
+    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
+    return;
+  }
+  __shared__ union {
+    GroupedSmem g;
+    SelectSmem s;  // the sweeps' layout, after the grouped form has given up
+  } smu;
+  __shared__ float sweep_vals[2];
+  GroupedSmem& sm = smu.g;
+  const int t = threadIdx.x;
+  const int64_t slice = blockIdx.x;
+  // thread t looks at groups [g0, g1) = [t per, (t + 1) per); their maxima are loaded together
+  // with the histogram when they fit in registers
+  const int64_t ngrp = N / kGrp;
+  const float* gx = kmax + slice * ngrp;
+  const int64_t per = (ngrp + kSelThreads - 1) / kSelThreads;
+  const int64_t g0 = (int64_t)t * per, g1 = g0 + per < ngrp ? g0 + per : ngrp;
+  const bool pre = per <= kKmaxPre;  // uniform
+  float gk[kKmaxPre];
+#pragma unroll
+  for (int i = 0; i < kKmaxPre; ++i) gk[i] = pre && g0 + i < g1 ? gx[g0 + i] : 0.0f;
+  const uint32_t* gh = ghist + slice * kBins;
+  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
+  if (t == 0) sm.n_cand = 0u;
+  __syncthreads();
+  uint32_t bin, above, in_bin;
+  threshold_bin(sm, (uint32_t)k, bin, above, in_bin);
+
+  // candidate groups, compacted in ascending order
+  auto reaches = [&](float m) { return coarse_bin(m, r_lo) >= bin; };
+  uint32_t mine = 0u;
+  if (pre) {
+#pragma unroll
+    for (int i = 0; i < kKmaxPre; ++i) mine += g0 + i < g1 && reaches(gk[i]) ? 1u : 0u;
+  } else {
+    for (int64_t g = g0; g < g1; ++g) mine += reaches(gx[g]) ? 1u : 0u;
+  }
+  uint32_t n_grp;
+  uint32_t off = block_exclusive_scan(mine, sm.scan_scratch, n_grp);
+  if (n_grp <= (uint32_t)kMaxGroups && mine != 0u) {
+    if (pre) {
+#pragma unroll
+      for (int i = 0; i < kKmaxPre; ++i)
+        if (g0 + i < g1 && reaches(gk[i])) sm.grp[off++] = (uint32_t)(g0 + i);
+    } else {
+      for (int64_t g = g0; g < g1; ++g)
+        if (reaches(gx[g])) sm.grp[off++] = (uint32_t)g;
+    }
+  }
+  if (n_grp > (uint32_t)kMaxGroups) {  // uniform
+    __syncthreads();  // the grouped form's LDS becomes the sweeps'
+    select_by_sweeps(smu.s, sweep_vals, rkey, ghist, N, k, r_lo, idx_out, slice);
+    return;
   }
   __syncthreads();
-  const float va = sm.bin_vals[0], vb = sm.bin_vals[1];
-  const bool top_open = bin + 1 >= (uint32_t)kBins;
 
-  uint32_t thr, need_eq, n_thr;
-  if (in_bin <= (uint32_t)kCand) {
-    // the passes past n_pass hold no candidates: their keys are skipped by a uniform branch
-    uint32_t mine = 0u;
-#pragma unroll
-    for (int s = 0; s < kMaxPasses; ++s) {
-      if (s >= n_pass) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * s + e;
-        const float x = v[i];
-        mine |= (valid(i) && x >= va && (top_open || x < vb)) ? (1u << i) : 0u;
-      }
-    }
-    if (__any(mine != 0u)) {
-      const uint32_t n = __popc(mine);
-      const uint32_t incl = wave_inclusive_scan(n);
-      uint32_t base_slot = 0u;
-      if (lane == 63) base_slot = atomicAdd(&sm.n_cand, incl);
-      base_slot = __shfl(base_slot, 63);
-      uint32_t slot = base_slot + incl - n;
-#pragma unroll
-      for (int s = 0; s < kMaxPasses; ++s) {
-        if (s >= n_pass) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((mine >> (4 * s + e)) & 1u) {
-            if (slot < (uint32_t)kCand) sm.cand[slot] = order_key(v[4 * s + e]);
-            ++slot;
-          }
-      }
-    }
-    __syncthreads();
-    const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
-    const uint32_t krem = (uint32_t)k - above;
-    // at most 64 keys in the bin: every wave finds the exact threshold among them itself (the same
-    // keys, so the same answer in every wave), which saves a barrier to publish it
-    bool found = false;
-    if (nc <= 64u) {
-      const uint32_t c = (uint32_t)lane < nc ? sm.cand[lane] : 0u;
-      const uint32_t gt_eq = count_above_equal(c, nc);
-      const uint32_t gt = gt_eq & 0xffffu, eq = gt_eq >> 16;
-      const uint64_t m = __ballot((uint32_t)lane < nc && gt < krem && krem <= gt + eq);
-      if (m != 0u) {
-        const int src = __builtin_ctzll(m);
-        thr = __builtin_amdgcn_readlane(c, src);
-        need_eq = krem - __builtin_amdgcn_readlane(gt, src);
-        n_thr = __builtin_amdgcn_readlane(eq, src);
-        found = true;
-      }
-    }
-    if (!found) {
-      radix_select(sm, krem,
-                   [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
-                     for (uint32_t i = t; i < nc; i += kSelThreads) {
-                       const uint32_t u = sm.cand[i];
-                       if ((u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
-                     }
-                   },
-                   thr, need_eq, n_thr);
-    }
-  } else {
-    radix_select(sm, (uint32_t)k,
-                 [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
-#pragma unroll
-                   for (int i = 0; i < 4 * kMaxPasses; ++i) {
-                     const uint32_t u = order_key(v[i]);
-                     if (valid(i) && (u & mask) == prefix) atomicAdd(&sm.hist[(u >> shift) & (uint32_t)(nbins - 1)], 1u);
-                   }
-                 },
-                 thr, need_eq, n_thr);
-  }
-
-  // Every key above thr and the first need_eq equal to it, in position order (pass, then thread,
-  // then lane bit).  Per pass a thread has at most 4 such keys; the prefix sums run over two
-  // passes at once, one 16-bit field each (a pass holds at most 4096 keys).
-  const float vthr = key_value(thr);
-  const bool all_eq = need_eq == n_thr;
-  uint32_t sel[kMaxPasses], eqm[kMaxPasses];
+  // the candidates' keys, four lanes a group: pass s covers candidates kPassGroups s .. + 255
+  const float* ky = rkey + slice * N;
+  const int q4 = t & 3, gj = t >> 2;
+  const int n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
+  float v[4 * kMaxPasses];
+  int grp_of[kMaxPasses];
 #pragma unroll
   for (int s = 0; s < kMaxPasses; ++s) {
-    sel[s] = 0u;
-    eqm[s] = 0u;
-    if (s >= n_pass) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (valid(4 * s + e)) {
-        const float x = v[4 * s + e];
-        sel[s] |= (x > vthr || (all_eq && x == vthr)) ? (1u << e) : 0u;
-        eqm[s] |= (!all_eq && x == vthr) ? (1u << e) : 0u;
-      }
+    const uint32_t j = (uint32_t)(s * kPassGroups + gj);
+    grp_of[s] = s < n_pass && j < n_grp ? (int)sm.grp[j] : -1;
+    float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (grp_of[s] >= 0) x = *reinterpret_cast<const float4*>(ky + (int64_t)kGrp * grp_of[s] + 4 * q4);
+    v[4 * s] = x.x;
+    v[4 * s + 1] = x.y;
+    v[4 * s + 2] = x.z;
+    v[4 * s + 3] = x.w;
   }
-  // exclusive prefix over (pass, thread) of per-pass counts: cnt(s) -> before(s)
-  auto pass_prefix = [&](const uint32_t (&m)[kMaxPasses], uint32_t (&before)[kMaxPasses]) {
-    uint32_t carried = 0u;
-#pragma unroll
-    for (int s = 0; s < kMaxPasses; s += 2) {
-      if (s >= n_pass) {  // uniform: nothing from here on
-        before[s] = carried;
-        before[s + 1] = carried;
-        continue;
-      }
-      uint32_t tot;
-      const uint32_t packed = (uint32_t)__popc(m[s]) | ((uint32_t)__popc(m[s + 1]) << 16);
-      const uint32_t ex = block_exclusive_scan(packed, sm.scan_scratch, tot);
-      before[s] = carried + (ex & 0xffffu);
-      before[s + 1] = carried + (tot & 0xffffu) + (ex >> 16);
-      carried += (tot & 0xffffu) + (tot >> 16);
-    }
-  };
-  if (!all_eq) {
-    uint32_t before[kMaxPasses];
-    pass_prefix(eqm, before);
-#pragma unroll
-    for (int s = 0; s < kMaxPasses; ++s) {
-      if (s >= n_pass) continue;
-      const uint32_t ne = __popc(eqm[s]);
-      uint32_t take = before[s] >= need_eq ? 0u : (need_eq - before[s] < ne ? need_eq - before[s] : ne);
-      while (take > 0u) {  // the lowest equal positions first
-        const uint32_t low = eqm[s] & (0u - eqm[s]);
-        sel[s] |= low;
-        eqm[s] ^= low;
-        --take;
-      }
-    }
-  }
-  uint32_t out0[kMaxPasses];
-  pass_prefix(sel, out0);
-#pragma unroll
-  for (int s = 0; s < kMaxPasses; ++s) {
-    if (s >= n_pass) continue;
-    uint32_t m = sel[s], out = out0[s];
-    while (m != 0u) {
-      const int b = __builtin_ctz(m);
-      m &= m - 1u;
-      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(kGrp * grp_of[s] + 4 * q4 + b);
-      ++out;
-    }
-  }
+  select_in_groups(sm, v, grp_of, n_pass, k, r_lo, bin, above, in_bin, slice, idx_out);
 }
 
 template <int GM>
 void launch_keys(const Dims& d, int S, const float* logits, const float* part_m, const float* part_l, float r_lo,
-                 float* keys, uint32_t* hist, hipStream_t s) {
+                 float* keys, uint32_t* hist, float* kmax, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(d.N, kKeyChunk), (unsigned)d.slices());
-  rank_keys_kernel<GM><<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, S, d.N, r_lo, keys, hist);
+  rank_keys_kernel<GM><<<grid, kKeyThreads, 0, s>>>(logits, part_m, part_l, d.G, S, d.N, r_lo, keys, hist, kmax);
 }
 
 template <int D>
-void launch_select(const Dims& d, int k, float r_lo, const float* keys, const uint32_t* hist, int32_t* idx_out,
-                   const MergeJob& mj, const FusedRank* fr, hipStream_t s) {
+void launch_select(const Dims& d, int k, float r_lo, const float* keys, const uint32_t* hist, const float* kmax,
+                   int32_t* idx_out, const MergeJob& mj, const FusedRank* fr, hipStream_t s) {
   const unsigned n_sel = (unsigned)d.slices();
   const unsigned grid = n_sel + (unsigned)ceil_div(mj.rows, kSelWaves);
   const FusedRank none{nullptr, nullptr, nullptr, 0, 0, nullptr};
@@ -1151,7 +1267,7 @@ void launch_select(const Dims& d, int k, float r_lo, const float* keys, const ui
     rank_select_resident_kernel<D, false><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel,
                                                                        mj, none);
   else
-    rank_select_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel, mj);
+    rank_select_grouped_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, kmax, hist, d.N, k, r_lo, idx_out, n_sel, mj);
 }
 
 }  // namespace
@@ -1162,7 +1278,8 @@ bool rank_select_prunable(const Dims& d, int k) {
 
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, bool keys_wanted, uint32_t* hist,
-                              int32_t* idx_out, const MergeJob* merge, hipStream_t s, const float* gmax) {
+                              int32_t* idx_out, const MergeJob* merge, hipStream_t s, const float* gmax,
+                              float* kmax) {
   const float r_lo = logf((float)d.G) - kBinSpan;  // the same value for both kernels
   const MergeJob none{nullptr, nullptr, 0, 0, nullptr};
   const MergeJob& mj = merge ? *merge : none;
@@ -1179,21 +1296,21 @@ hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const f
   if (d.N <= kResidentN && d.G <= kFusedG) {  // one launch: the selection forms r(p) itself
     const FusedRank fr{logits, part_m, part_l, d.G, S, keys_wanted ? keys : nullptr};
     if (d.D == 64)
-      launch_select<64>(d, k, r_lo, nullptr, nullptr, idx_out, mj, &fr, s);
+      launch_select<64>(d, k, r_lo, nullptr, nullptr, nullptr, idx_out, mj, &fr, s);
     else
-      launch_select<128>(d, k, r_lo, nullptr, nullptr, idx_out, mj, &fr, s);
+      launch_select<128>(d, k, r_lo, nullptr, nullptr, nullptr, idx_out, mj, &fr, s);
     return hipGetLastError();
   }
   if (d.G <= 4)
-    launch_keys<4>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
+    launch_keys<4>(d, S, logits, part_m, part_l, r_lo, keys, hist, kmax, s);
   else if (d.G <= 8)
-    launch_keys<8>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
+    launch_keys<8>(d, S, logits, part_m, part_l, r_lo, keys, hist, kmax, s);
   else
-    launch_keys<16>(d, S, logits, part_m, part_l, r_lo, keys, hist, s);
+    launch_keys<16>(d, S, logits, part_m, part_l, r_lo, keys, hist, kmax, s);
   if (d.D == 64)
-    launch_select<64>(d, k, r_lo, keys, hist, idx_out, mj, nullptr, s);
+    launch_select<64>(d, k, r_lo, keys, hist, kmax, idx_out, mj, nullptr, s);
   else
-    launch_select<128>(d, k, r_lo, keys, hist, idx_out, mj, nullptr, s);
+    launch_select<128>(d, k, r_lo, keys, hist, kmax, idx_out, mj, nullptr, s);
   return hipGetLastError();
 }
 

@@ -313,6 +313,36 @@ def test_selection_same_with_and_without_key_output(gpu, seq_len):
     assert torch.equal(a, b) and torch.equal(na, nb)
 
 
+@pytest.mark.parametrize("k,qscale", [(1, 1.0), (300, 1.0), (1500, 1.0), (3000, 1.0), (300, 0.0), (300, 1e-3)])
+def test_topk_long_slices_grouped_and_swept(gpu, k, qscale):
+    """Slices longer than one selection workgroup holds (40960 + 96 positions): rank_keys writes
+    r(p) and its maximum over every 16 positions, and the selection reads only the groups whose
+    maximum reaches the threshold bin; when more than 2048 groups do (k = 3000, every rank equal,
+    a bin crowded with distinct keys) it sweeps over every key instead.  score_topk and the fused
+    step's next selection against the oracle; with every rank equal, the k lowest positions."""
+    cfg = get_config("llama8k").with_(seq_len=40960 + 96, top_k=k, seed=7)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    Q = (Q.astype(np.float32) * qscale).astype(np.float16)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    q = _dev(Q)
+    rk = torch.empty((cfg.batch, cfg.n_kv_heads, cfg.seq_len), dtype=torch.float32, device="cuda")
+    a = _np(score_topk(q, cache, k, rank_key_out=rk))
+    b = _np(score_topk(q, cache, k))
+    _, nxt = decode_step(q, cache, k)
+    nxt = _np(nxt)
+    _, kh, _ = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
+    slices = [(0, h) for h in range(cfg.n_kv_heads)]
+    what = f"N {cfg.seq_len} k {k} q x{qscale}"
+    assert np.array_equal(a, b), "the selection depends on the key output"
+    _assert_topk(a, r_ref, k, slices, f"score_topk {what}")
+    _assert_topk(nxt, r_ref, k, slices, f"decode_step {what}")
+    _check_rank_keys(_np(rk), r_ref, what)
+    if qscale == 0.0:
+        lowest = np.broadcast_to(np.arange(k, dtype=np.int32), a.shape)
+        assert np.array_equal(a, lowest) and np.array_equal(nxt, lowest)
+
+
 @pytest.mark.parametrize("name,rank_row", [("mistral32k", 1), ("long128k", 1), ("layers32", 1),
                                            ("mistral32k", 0)])   # row 0 of two: the serial comparator's ranking
 def test_score_topk_full_size_sampled(gpu, name, rank_row):
