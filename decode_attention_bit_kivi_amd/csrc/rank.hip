@@ -35,6 +35,8 @@
 //   float r.
 #include "merge.h"
 
+#include <type_traits>
+
 namespace specache {
 
 namespace {
@@ -839,27 +841,247 @@ struct PrunedRank {
   int G, S;
 };
 
-// The coarse bin of the k-th largest key in sm.hist, the number of keys in the bins above it and
-// in it.  A key lies in that bin exactly when its own coarse bin is equal to it (the bins are
-// non-decreasing in the key), so the bin's value interval is never needed.
-template <typename Smem>
-__device__ void threshold_bin(Smem& sm, uint32_t k, uint32_t& bin, uint32_t& above, uint32_t& in_bin) {
-  pick_digit(sm, kBins, k, bin, above);
-  in_bin = sm.hist[bin];
-}
+// The long-slice form (KEYS): slices longer than one selection workgroup holds, from rank_keys'
+// keys, their global histogram and their maxima over every 16 positions.  The histogram gives
+// the coarse bin of the k-th largest key; a key lies in that bin or a higher one exactly when
+// its own bin does (the bins are non-decreasing in the key), so only the groups whose maximum
+// reaches the bin are read (about k of them) and the selection among their keys is the same.
+// More than kMaxGroups such groups (a crowded threshold bin, or k near kMaxGroups): the sweeps
+// over every key instead, in the same workgroup's LDS.
+struct GroupedSmem {
+  uint32_t hist[kBins];
+  uint32_t scan_scratch[2 * kSelWaves];
+  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t grp[kMaxGroups];  // candidate groups, ascending (indices past 65535 at long slices)
+  uint32_t cand[kCand];
+};
+union KeyedSmem {
+  GroupedSmem g;
+  SelectSmem s;  // the sweeps' layout, once the grouped form has given up
+};
+constexpr int kKmaxPre = 8;  // group maxima a thread loads before the histogram is read (128K: all)
 
-// The selection among the keys of a slice's candidate groups of 16 positions, held four lanes a
-// group (lane quad q4 = t % 4 holds positions 4 q4 .. 4 q4 + 3 of it): pass s, kPassGroups groups,
-// in v[4s .. 4s + 3] for group grp_of[s] (-1: none, -inf keys), passes and threads in position
-// order.  sm.hist counts the keys by coarse bin (window from r_lo); `bin` holds the k-th
-// largest (in_bin keys), `above` keys lie in the bins above it, and the candidates include every
-// key of the slice whose bin is `bin` or higher.  Writes the positions of the k largest keys (ties to the lower position)
-// in position order to idx_out[slice * k ..].
-template <typename Smem>
-__device__ void select_in_groups(Smem& sm, const float (&v)[4 * kMaxPasses], const int (&grp_of)[kMaxPasses],
-                                 int n_pass, int k, float r_lo, uint32_t bin, uint32_t above, uint32_t in_bin,
-                                 int64_t slice, int32_t* __restrict__ idx_out) {
-  const int t = threadIdx.x, lane = t & 63, q4 = t & 3;
+struct KeyGroups {
+  const float* rkey;      // [slices][N]: r(p)
+  const float* kmax;      // [slices][N / 16]: their maxima over every 16 positions
+  const uint32_t* ghist;  // [slices][kBins]: their coarse histogram
+};
+
+template <int D, bool KEYS>
+__global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t N, int k, float r_lo,
+                                                                         int32_t* __restrict__ idx_out,
+                                                                         unsigned n_sel, MergeJob mj, PrunedRank pr,
+                                                                         KeyGroups kg) {
+  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
+    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
+    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
+    return;
+  }
+  __shared__ std::conditional_t<KEYS, KeyedSmem, PrunedSmem> smem;
+  __shared__ float sweep_vals[2];
+  auto& sm = [&]() -> auto& {
+    if constexpr (KEYS) return smem.g;
+    else return smem;
+  }();
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, q4 = t & 3;
+  const int64_t slice = blockIdx.x;
+  // the candidates' keys: pass s (kPassGroups groups, four lanes each; lane quad q4 holds
+  // positions 4 q4 .. 4 q4 + 3 of its group) in v[4s .. 4s + 3] for group grp_of[s] (-1 for
+  // none: keys -inf); passes then threads in position order
+  float v[4 * kMaxPasses];
+  int grp_of[kMaxPasses];
+  int n_pass;
+  uint32_t bin, above, in_bin;  // the k-th key's coarse bin, the keys above it and in it
+  if constexpr (!KEYS) {
+    const int G = pr.G, S = pr.S;
+    const int ngrp = (int)(N / kGrp);  // N is a multiple of 32 and at most kResidentN
+
+    // the bounds of groups 2t and 2t + 1 (a float2 per head) and the first split statistics are
+    // loaded before anything waits
+    float2 gm[kFusedG];
+    {
+      const float* gp = pr.gmax + slice * G * ngrp;
+      const int i0 = 2 * t < ngrp ? 2 * t : 0;
+#pragma unroll
+      for (int g = 0; g < kFusedG; ++g) gm[g] = *reinterpret_cast<const float2*>(gp + (g < G ? g : 0) * ngrp + i0);
+    }
+    const int hw = wave < G ? wave : 0;
+    const int64_t sb = (slice * G + hw) * S;
+    const int j0 = lane < S ? lane : 0;
+    const float m_first = pr.part_m[sb + j0], l_first = pr.part_l[sb + j0];
+    asm volatile("" ::: "memory");
+    sm.hist[t] = 0u;
+    sm.hist[t + kSelThreads] = 0u;
+    if (wave < kFusedG) {
+      const float l2 = head_lse2<64>(pr.part_m + sb, pr.part_l + sb, S, lane, m_first, l_first);
+      if (wave < G && lane == 0) sm.lse2[wave] = l2;
+    }
+    if (t == 0) {
+      sm.n_cand = 0u;
+    }
+    __syncthreads();
+    float lse2[kFusedG];
+#pragma unroll
+    for (int g = 0; g < kFusedG; ++g) lse2[g] = g < G ? sm.lse2[g] : 0.0f;
+
+    // U and L of the two groups (the arithmetic of rank_of, on the maxima)
+    float U[2], L[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float lp[kFusedG];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < kFusedG; ++g)
+        if (g < G) {
+          lp[g] = (s == 0 ? gm[g].x : gm[g].y) - lse2[g];
+          mx = fmaxf(mx, lp[g]);
+        }
+      float sum = 0.0f;
+#pragma unroll
+      for (int g = 0; g < kFusedG; ++g)
+        if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
+      U[s] = (mx + __builtin_amdgcn_logf(sum)) * kLn2 + kBoundMargin;
+      L[s] = mx * kLn2 + 0.0f;
+    }
+    const bool gv0 = 2 * t < ngrp, gv1 = 2 * t + 1 < ngrp;
+
+    // tau_lo: below the k-th largest L (the lower edge of the coarse bin holding it, one bin down)
+    float tau_lo = -INFINITY;
+    if (k <= ngrp) {
+      if (gv0) atomicAdd(&sm.hist[coarse_bin(L[0], r_lo)], 1u);
+      if (gv1) atomicAdd(&sm.hist[coarse_bin(L[1], r_lo)], 1u);
+      __syncthreads();
+      uint32_t bin, above;
+      pick_digit(sm, kBins, (uint32_t)k, bin, above);
+      if (bin > 0u) tau_lo = r_lo + (float)(bin - 1u) / kBinScale;
+      sm.hist[t] = 0u;
+      sm.hist[t + kSelThreads] = 0u;
+    }
+    // candidate groups, compacted in ascending order
+    const bool c0 = gv0 && U[0] >= tau_lo, c1 = gv1 && U[1] >= tau_lo;
+    {
+      uint32_t tot;
+      uint32_t off = block_exclusive_scan((c0 ? 1u : 0u) + (c1 ? 1u : 0u), sm.scan_scratch, tot);
+      if (c0) sm.grp[off++] = (uint16_t)(2 * t);
+      if (c1) sm.grp[off] = (uint16_t)(2 * t + 1);
+      if (t == 0) sm.n_grp = tot;
+    }
+    __syncthreads();
+    const uint32_t n_grp = sm.n_grp;
+
+    // r of the candidates' positions, four lanes per group (lane quad q = t % 4 holds positions
+    // 4q .. 4q + 3 of the group, so that the four lanes read each head's 64 bytes of the group
+    // together): pass s covers candidates 256 s .. 256 s + 255, candidate 256 s + t / 4 in
+    // v[4s .. 4s + 3]; -inf where there is none.  Passes then threads then lanes run in position order.
+    const float* lg = pr.logits + slice * G * N;
+    const int gj = t >> 2;
+    n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
+    uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
+#pragma unroll
+    for (int s0 = 0; s0 < kMaxPasses; s0 += 2) {
+      if (s0 >= n_pass) {  // uniform: no candidates from here on
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          grp_of[s0 + u] = -1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * (s0 + u) + e] = -INFINITY;
+        }
+        continue;
+      }
+      float4 x[2][kFusedG];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t j = (uint32_t)((s0 + u) * kPassGroups + gj);
+        grp_of[s0 + u] = j < n_grp ? (int)sm.grp[j] : -1;
+        const int c = grp_of[s0 + u] >= 0 ? grp_of[s0 + u] : 0;  // a valid address, unused
+#pragma unroll
+        for (int g = 0; g < kFusedG; ++g)
+          x[u][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + kGrp * c + 4 * q4);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float r = -INFINITY;
+          if (grp_of[s0 + u] >= 0) {
+            r = rank_of<kFusedG>(x[u], e, lse2, G);
+            const uint32_t b = coarse_bin(r, r_lo);
+            if (cur_cnt != 0u && b != cur_bin) atomicAdd(&sm.hist[cur_bin], cur_cnt), cur_cnt = 0u;
+            cur_bin = b;
+            ++cur_cnt;
+          }
+          v[4 * (s0 + u) + e] = r;
+        }
+    }
+    if (cur_cnt) atomicAdd(&sm.hist[cur_bin], cur_cnt);
+    __syncthreads();
+
+    // the exact threshold among the candidates, as the resident selection finds it
+    pick_digit(sm, kBins, (uint32_t)k, bin, above);
+    in_bin = sm.hist[bin];
+  } else {
+    // thread t looks at groups [g0, g1) = [t per, (t + 1) per); their maxima are loaded together
+    // with the histogram when they fit in registers
+    const int64_t ngrp = N / kGrp;
+    const float* gx = kg.kmax + slice * ngrp;
+    const int64_t per = (ngrp + kSelThreads - 1) / kSelThreads;
+    const int64_t g0 = (int64_t)t * per, g1 = g0 + per < ngrp ? g0 + per : ngrp;
+    const bool pre = per <= kKmaxPre;  // uniform
+    float gk[kKmaxPre];
+#pragma unroll
+    for (int i = 0; i < kKmaxPre; ++i) gk[i] = pre && g0 + i < g1 ? gx[g0 + i] : 0.0f;
+    const uint32_t* gh = kg.ghist + slice * kBins;
+    for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
+    if (t == 0) sm.n_cand = 0u;
+    __syncthreads();
+    pick_digit(sm, kBins, (uint32_t)k, bin, above);
+    in_bin = sm.hist[bin];
+
+    // candidate groups, compacted in ascending order: a key is in the threshold bin or a higher
+    // one exactly when its bin is, so a group that holds one has its maximum there too
+    auto reaches = [&](float m) { return coarse_bin(m, r_lo) >= bin; };
+    uint32_t mine = 0u;
+    if (pre) {
+#pragma unroll
+      for (int i = 0; i < kKmaxPre; ++i) mine += g0 + i < g1 && reaches(gk[i]) ? 1u : 0u;
+    } else {
+      for (int64_t g = g0; g < g1; ++g) mine += reaches(gx[g]) ? 1u : 0u;
+    }
+    uint32_t n_grp;
+    uint32_t off = block_exclusive_scan(mine, sm.scan_scratch, n_grp);
+    if (n_grp <= (uint32_t)kMaxGroups && mine != 0u) {
+      if (pre) {
+#pragma unroll
+        for (int i = 0; i < kKmaxPre; ++i)
+          if (g0 + i < g1 && reaches(gk[i])) sm.grp[off++] = (uint32_t)(g0 + i);
+      } else {
+        for (int64_t g = g0; g < g1; ++g)
+          if (reaches(gx[g])) sm.grp[off++] = (uint32_t)g;
+      }
+    }
+    if (n_grp > (uint32_t)kMaxGroups) {  // uniform
+      __syncthreads();  // this form's LDS becomes the sweeps'
+      select_by_sweeps(smem.s, sweep_vals, kg.rkey, kg.ghist, N, k, r_lo, idx_out, slice);
+      return;
+    }
+    __syncthreads();
+
+    // the candidates' keys, four lanes a group: pass s covers candidates kPassGroups s .. + 255
+    const float* ky = kg.rkey + slice * N;
+    const int gj = t >> 2;
+    n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
+#pragma unroll
+    for (int s = 0; s < kMaxPasses; ++s) {
+      const uint32_t j = (uint32_t)(s * kPassGroups + gj);
+      grp_of[s] = s < n_pass && j < n_grp ? (int)sm.grp[j] : -1;
+      float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (grp_of[s] >= 0) x = *reinterpret_cast<const float4*>(ky + (int64_t)kGrp * grp_of[s] + 4 * q4);
+      v[4 * s] = x.x;
+      v[4 * s + 1] = x.y;
+      v[4 * s + 2] = x.z;
+      v[4 * s + 3] = x.w;
+    }
+  }
   auto valid = [&](int i) { return grp_of[i >> 2] >= 0; };
 
   uint32_t thr, need_eq, n_thr;
@@ -1003,250 +1225,6 @@ __device__ void select_in_groups(Smem& sm, const float (&v)[4 * kMaxPasses], con
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t N, int k, float r_lo,
-                                                                         int32_t* __restrict__ idx_out,
-                                                                         unsigned n_sel, MergeJob mj, PrunedRank pr) {
-  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
-    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
-    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
-    return;
-  }
-  __shared__ PrunedSmem sm;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t slice = blockIdx.x;
-  const int G = pr.G, S = pr.S;
-  const int ngrp = (int)(N / kGrp);  // N is a multiple of 32 and at most kResidentN
-
-  // the bounds of groups 2t and 2t + 1 (a float2 per head) and the first split statistics are
-  // loaded before anything waits
-  float2 gm[kFusedG];
-  {
-    const float* gp = pr.gmax + slice * G * ngrp;
-    const int i0 = 2 * t < ngrp ? 2 * t : 0;
-#pragma unroll
-    for (int g = 0; g < kFusedG; ++g) gm[g] = *reinterpret_cast<const float2*>(gp + (g < G ? g : 0) * ngrp + i0);
-  }
-  const int hw = wave < G ? wave : 0;
-  const int64_t sb = (slice * G + hw) * S;
-  const int j0 = lane < S ? lane : 0;
-  const float m_first = pr.part_m[sb + j0], l_first = pr.part_l[sb + j0];
-  asm volatile("" ::: "memory");
-  sm.hist[t] = 0u;
-  sm.hist[t + kSelThreads] = 0u;
-  if (wave < kFusedG) {
-    const float l2 = head_lse2<64>(pr.part_m + sb, pr.part_l + sb, S, lane, m_first, l_first);
-    if (wave < G && lane == 0) sm.lse2[wave] = l2;
-  }
-  if (t == 0) {
-    sm.n_cand = 0u;
-  }
-  __syncthreads();
-  float lse2[kFusedG];
-#pragma unroll
-  for (int g = 0; g < kFusedG; ++g) lse2[g] = g < G ? sm.lse2[g] : 0.0f;
-
-  // U and L of the two groups (the arithmetic of rank_of, on the maxima)
-  float U[2], L[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    float lp[kFusedG];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < kFusedG; ++g)
-      if (g < G) {
-        lp[g] = (s == 0 ? gm[g].x : gm[g].y) - lse2[g];
-        mx = fmaxf(mx, lp[g]);
-      }
-    float sum = 0.0f;
-#pragma unroll
-    for (int g = 0; g < kFusedG; ++g)
-      if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
-    U[s] = (mx + __builtin_amdgcn_logf(sum)) * kLn2 + kBoundMargin;
-    L[s] = mx * kLn2 + 0.0f;
-  }
-  const bool gv0 = 2 * t < ngrp, gv1 = 2 * t + 1 < ngrp;
-
-  // tau_lo: below the k-th largest L (the lower edge of the coarse bin holding it, one bin down)
-  float tau_lo = -INFINITY;
-  if (k <= ngrp) {
-    if (gv0) atomicAdd(&sm.hist[coarse_bin(L[0], r_lo)], 1u);
-    if (gv1) atomicAdd(&sm.hist[coarse_bin(L[1], r_lo)], 1u);
-    __syncthreads();
-    uint32_t bin, above;
-    pick_digit(sm, kBins, (uint32_t)k, bin, above);
-    if (bin > 0u) tau_lo = r_lo + (float)(bin - 1u) / kBinScale;
-    sm.hist[t] = 0u;
-    sm.hist[t + kSelThreads] = 0u;
-  }
-  // candidate groups, compacted in ascending order
-  const bool c0 = gv0 && U[0] >= tau_lo, c1 = gv1 && U[1] >= tau_lo;
-  {
-    uint32_t tot;
-    uint32_t off = block_exclusive_scan((c0 ? 1u : 0u) + (c1 ? 1u : 0u), sm.scan_scratch, tot);
-    if (c0) sm.grp[off++] = (uint16_t)(2 * t);
-    if (c1) sm.grp[off] = (uint16_t)(2 * t + 1);
-    if (t == 0) sm.n_grp = tot;
-  }
-  __syncthreads();
-  const uint32_t n_grp = sm.n_grp;
-
-  // r of the candidates' positions, four lanes per group (lane quad q = t % 4 holds positions
-  // 4q .. 4q + 3 of the group, so that the four lanes read each head's 64 bytes of the group
-  // together): pass s covers candidates 256 s .. 256 s + 255, candidate 256 s + t / 4 in
-  // v[4s .. 4s + 3]; -inf where there is none.  Passes then threads then lanes run in position order.
-  const float* lg = pr.logits + slice * G * N;
-  const int q4 = t & 3, gj = t >> 2;
-  const int n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
-  float v[4 * kMaxPasses];
-  int grp_of[kMaxPasses];
-  uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
-#pragma unroll
-  for (int s0 = 0; s0 < kMaxPasses; s0 += 2) {
-    if (s0 >= n_pass) {  // uniform: no candidates from here on
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        grp_of[s0 + u] = -1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * (s0 + u) + e] = -INFINITY;
-      }
-      continue;
-    }
-    float4 x[2][kFusedG];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t j = (uint32_t)((s0 + u) * kPassGroups + gj);
-      grp_of[s0 + u] = j < n_grp ? (int)sm.grp[j] : -1;
-      const int c = grp_of[s0 + u] >= 0 ? grp_of[s0 + u] : 0;  // a valid address, unused
-#pragma unroll
-      for (int g = 0; g < kFusedG; ++g)
-        x[u][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + kGrp * c + 4 * q4);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float r = -INFINITY;
-        if (grp_of[s0 + u] >= 0) {
-          r = rank_of<kFusedG>(x[u], e, lse2, G);
-          const uint32_t b = coarse_bin(r, r_lo);
-          if (cur_cnt != 0u && b != cur_bin) atomicAdd(&sm.hist[cur_bin], cur_cnt), cur_cnt = 0u;
-          cur_bin = b;
-          ++cur_cnt;
-        }
-        v[4 * (s0 + u) + e] = r;
-      }
-  }
-  if (cur_cnt) atomicAdd(&sm.hist[cur_bin], cur_cnt);
-  __syncthreads();
-
-  // the exact threshold among the candidates, as the resident selection finds it
-  uint32_t bin, above, in_bin;
-  threshold_bin(sm, (uint32_t)k, bin, above, in_bin);
-  select_in_groups(sm, v, grp_of, n_pass, k, r_lo, bin, above, in_bin, slice, idx_out);
-}
-
-// ---- rank_select for slices longer than one selection workgroup holds, from rank_keys' keys and
-// their maxima over every 16 positions.  The global histogram gives the coarse bin of the k-th
-// largest key; every key in that bin or a higher one lies in a group whose maximum is in such a
-// bin (the bins are non-decreasing in the key), so only those groups' keys are read (about k of
-// them), into registers, and the selection among them is the pruned kernel's.  More than
-// kMaxGroups such groups (a crowded threshold bin, or k near kMaxGroups): the sweeps over every
-// key instead.
-struct GroupedSmem {
-  uint32_t hist[kBins];
-  uint32_t scan_scratch[2 * kSelWaves];
-  uint32_t sel_digit, sel_above, n_cand;
-  uint32_t grp[kMaxGroups];  // candidate groups, ascending
-  uint32_t cand[kCand];
-};
-constexpr int kKmaxPre = 8;  // group maxima a thread loads before the histogram is read (128K: all)
-
-template <int D>
-__global__ __launch_bounds__(kSelThreads) void rank_select_grouped_kernel(const float* __restrict__ rkey,
-                                                                          const float* __restrict__ kmax,
-                                                                          const uint32_t* __restrict__ ghist,
-                                                                          int64_t N, int k, float r_lo,
-                                                                          int32_t* __restrict__ idx_out,
-                                                                          unsigned n_sel, MergeJob mj) {
-  if (blockIdx.x >= n_sel) {  // a merge workgroup: one query row per wave
-    const int64_t row = (int64_t)(blockIdx.x - n_sel) * kSelWaves + (threadIdx.x >> 6);
-    if (row < mj.rows) merge_row_wave<D>(mj.part_ml, mj.part_acc, mj.S, mj.out16, row);
-    return;
-  }
-  __shared__ union {
-    GroupedSmem g;
-    SelectSmem s;  // the sweeps' layout, after the grouped form has given up
-  } smu;
-  __shared__ float sweep_vals[2];
-  GroupedSmem& sm = smu.g;
-  const int t = threadIdx.x;
-  const int64_t slice = blockIdx.x;
-  // thread t looks at groups [g0, g1) = [t per, (t + 1) per); their maxima are loaded together
-  // with the histogram when they fit in registers
-  const int64_t ngrp = N / kGrp;
-  const float* gx = kmax + slice * ngrp;
-  const int64_t per = (ngrp + kSelThreads - 1) / kSelThreads;
-  const int64_t g0 = (int64_t)t * per, g1 = g0 + per < ngrp ? g0 + per : ngrp;
-  const bool pre = per <= kKmaxPre;  // uniform
-  float gk[kKmaxPre];
-#pragma unroll
-  for (int i = 0; i < kKmaxPre; ++i) gk[i] = pre && g0 + i < g1 ? gx[g0 + i] : 0.0f;
-  const uint32_t* gh = ghist + slice * kBins;
-  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
-  if (t == 0) sm.n_cand = 0u;
-  __syncthreads();
-  uint32_t bin, above, in_bin;
-  threshold_bin(sm, (uint32_t)k, bin, above, in_bin);
-
-  // candidate groups, compacted in ascending order
-  auto reaches = [&](float m) { return coarse_bin(m, r_lo) >= bin; };
-  uint32_t mine = 0u;
-  if (pre) {
-#pragma unroll
-    for (int i = 0; i < kKmaxPre; ++i) mine += g0 + i < g1 && reaches(gk[i]) ? 1u : 0u;
-  } else {
-    for (int64_t g = g0; g < g1; ++g) mine += reaches(gx[g]) ? 1u : 0u;
-  }
-  uint32_t n_grp;
-  uint32_t off = block_exclusive_scan(mine, sm.scan_scratch, n_grp);
-  if (n_grp <= (uint32_t)kMaxGroups && mine != 0u) {
-    if (pre) {
-#pragma unroll
-      for (int i = 0; i < kKmaxPre; ++i)
-        if (g0 + i < g1 && reaches(gk[i])) sm.grp[off++] = (uint32_t)(g0 + i);
-    } else {
-      for (int64_t g = g0; g < g1; ++g)
-        if (reaches(gx[g])) sm.grp[off++] = (uint32_t)g;
-    }
-  }
-  if (n_grp > (uint32_t)kMaxGroups) {  // uniform
-    __syncthreads();  // the grouped form's LDS becomes the sweeps'
-    select_by_sweeps(smu.s, sweep_vals, rkey, ghist, N, k, r_lo, idx_out, slice);
-    return;
-  }
-  __syncthreads();
-
-  // the candidates' keys, four lanes a group: pass s covers candidates kPassGroups s .. + 255
-  const float* ky = rkey + slice * N;
-  const int q4 = t & 3, gj = t >> 2;
-  const int n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
-  float v[4 * kMaxPasses];
-  int grp_of[kMaxPasses];
-#pragma unroll
-  for (int s = 0; s < kMaxPasses; ++s) {
-    const uint32_t j = (uint32_t)(s * kPassGroups + gj);
-    grp_of[s] = s < n_pass && j < n_grp ? (int)sm.grp[j] : -1;
-    float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (grp_of[s] >= 0) x = *reinterpret_cast<const float4*>(ky + (int64_t)kGrp * grp_of[s] + 4 * q4);
-    v[4 * s] = x.x;
-    v[4 * s + 1] = x.y;
-    v[4 * s + 2] = x.z;
-    v[4 * s + 3] = x.w;
-  }
-  select_in_groups(sm, v, grp_of, n_pass, k, r_lo, bin, above, in_bin, slice, idx_out);
-}
-
 template <int GM>
 void launch_keys(const Dims& d, int S, const float* logits, const float* part_m, const float* part_l, float r_lo,
                  float* keys, uint32_t* hist, float* kmax, hipStream_t s) {
@@ -1267,7 +1245,8 @@ void launch_select(const Dims& d, int k, float r_lo, const float* keys, const ui
     rank_select_resident_kernel<D, false><<<grid, kSelThreads, 0, s>>>(keys, hist, d.N, k, r_lo, idx_out, n_sel,
                                                                        mj, none);
   else
-    rank_select_grouped_kernel<D><<<grid, kSelThreads, 0, s>>>(keys, kmax, hist, d.N, k, r_lo, idx_out, n_sel, mj);
+    rank_select_pruned_kernel<D, true><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, PrunedRank{},
+                                                                   KeyGroups{keys, kmax, hist});
 }
 
 }  // namespace
@@ -1288,9 +1267,10 @@ hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const f
     const unsigned n_sel = (unsigned)d.slices();
     const unsigned grid = n_sel + (unsigned)ceil_div(mj.rows, kSelWaves);
     if (d.D == 64)
-      rank_select_pruned_kernel<64><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, pr);
+      rank_select_pruned_kernel<64, false><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, pr, KeyGroups{});
     else
-      rank_select_pruned_kernel<128><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, pr);
+      rank_select_pruned_kernel<128, false><<<grid, kSelThreads, 0, s>>>(d.N, k, r_lo, idx_out, n_sel, mj, pr,
+                                                                         KeyGroups{});
     return hipGetLastError();
   }
   if (d.N <= kResidentN && d.G <= kFusedG) {  // one launch: the selection forms r(p) itself
