@@ -17,22 +17,27 @@ __global__ __launch_bounds__(64) void flag_set_kernel(uint32_t* flag, uint32_t v
   if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Lane 0 polls the flag (acquire at device scope) until it has reached `value` (wrap-around
-// safe: value - flag taken as a signed distance) or `max_ticks` of the 100 MHz real-time
-// counter have passed; a wait that ends on the time limit adds one to *timeouts, so every call
-// ends and the caller can tell.
+// Lane 0 polls the flag until it has reached `value` (wrap-around safe: value - flag taken as a
+// signed distance) or `max_ticks` of the 100 MHz real-time counter have passed; a wait that ends
+// on the time limit adds one to *timeouts, so every call ends and the caller can tell.  The polls
+// are relaxed loads at device scope (they read past the non-coherent caches) about every 0.5 µs,
+// and the acquire is one fence once the value is there: an acquire at device scope on every poll
+// would invalidate caches that the kernels running beside the wait are using.
 __global__ __launch_bounds__(64) void flag_wait_kernel(const uint32_t* flag, uint32_t value, uint64_t max_ticks,
                                                        uint32_t* timeouts) {
   if (threadIdx.x != 0) return;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
-    const uint32_t v = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    if ((int32_t)(v - value) >= 0) return;
+    const uint32_t v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((int32_t)(v - value) >= 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      return;
+    }
     if (__builtin_amdgcn_s_memrealtime() - t0 > max_ticks) {
       atomicAdd(timeouts, 1u);
       return;
     }
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(16);
   }
 }
 
