@@ -237,7 +237,7 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
                               sm_scale, logits, part_m, part_l, hist, s);
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
   e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, rank_key_out != nullptr, hist, idx_out,
-                         nullptr, s, nullptr, reinterpret_cast<float*>(base + ws.kmax));
+                         nullptr, s, nullptr, nullptr, 0, reinterpret_cast<float*>(base + ws.kmax));
   return hip_status(e);
 }
 
@@ -458,17 +458,17 @@ int decode_step_impl(const specache_shape* shape, const void* q16, int n_tokens,
   a.rank_l = reinterpret_cast<float*>(base + ws.rank_l);
   a.rank_hist = reinterpret_cast<uint32_t*>(base + ws.hist);
   float* keys = rank_key_out ? rank_key_out : reinterpret_cast<float*>(base + ws.keys);
-  // bounds for the pruned selection: ranking against C' (the mixed-cache ranking replaces the
-  // fetched rows' logits after they are written), no key output, one bound group per selected
-  // position at most (G * T <= 8 follows from G <= 4)
-  if (!rank_mixed && !rank_key_out && rank_select_prunable(d, k_next))
-    a.rank_gmax = reinterpret_cast<float*>(base + ws.gmax);
+  // bounds for the pruned selection: no key output, one bound group per selected position at
+  // most (G * T <= 8 follows from G <= 4).  Ranking by the mixed cache replaces the fetched rows'
+  // logits after the bounds are taken: the selection then reads their groups whatever the bounds.
+  if (!rank_key_out && rank_select_prunable(d, k_next)) a.rank_gmax = reinterpret_cast<float*>(base + ws.gmax);
   // the split merge runs inside the selection's launch, on the compute units it leaves idle
   if (launch_attn_split(d, plan, a, s) != hipSuccess) return SPECACHE_ERR_HIP;
   const MergeJob merge{a.part_ml, a.part_acc, plan.S, (int64_t)d.B * d.Hq * n_tokens, a.out16};
   return hip_status(launch_rank_select(d, plan.S, a.rank_logits, a.rank_m, a.rank_l, k_next, keys,
                                        rank_key_out != nullptr, a.rank_hist, idx_next_out, &merge, s,
-                                       a.rank_gmax, reinterpret_cast<float*>(base + ws.gmax)));
+                                       a.rank_gmax, rank_mixed ? idx : nullptr, rank_mixed ? k : 0,
+                                       reinterpret_cast<float*>(base + ws.gmax)));
 }
 
 // The no-allocation decode step's scratch: one array per GPU, in the library's code object, held

@@ -145,14 +145,16 @@ struct MergeJob {
 // registers uses between its two kernels).
 // gmax: null, or the per-16-position logit maxima the split kernel wrote (rank_gmax); with them,
 // and no keys wanted, a slice of at most 32768 positions is selected from the logits of the
-// position groups whose bound reaches the k-th rank only.
+// position groups whose bound reaches the k-th rank only.  kappa / n_kappa: for the ranking by the
+// mixed cache, the fetched positions ([slices][n_kappa]) whose 16-bit logits replaced the
+// low-bit ones after the maxima were taken (their groups are always read); else null / 0.
 // kmax: [slices][N / 16] floats of workspace for the maxima of r(p) over every 16 positions,
 // written by the two-launch form (rank_keys) for its selection to read only the groups that
 // reach the threshold bin.
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, bool keys_wanted, uint32_t* hist,
                               int32_t* idx_out, const MergeJob* merge, hipStream_t s, const float* gmax,
-                              float* kmax);
+                              const int32_t* kappa, int n_kappa, float* kmax);
 
 // Whether the pruned selection (per-16-position bounds) serves this problem: slices of at most
 // 32768 positions, at most 4 heads per KV head, k at most one per group.

@@ -827,6 +827,7 @@ struct PrunedSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
   uint32_t sel_digit, sel_above, n_cand;
+  uint32_t kgrp[kMaxGroups / 32];  // mixed-cache ranking: the groups holding a fetched position
   float lse2[kFusedG];
   uint32_t n_grp;
   uint16_t grp[kMaxGroups];  // candidate groups, ascending
@@ -839,6 +840,10 @@ struct PrunedRank {
   const float* part_l;
   const float* gmax;    // [slices][G][N / 16], log2 units
   int G, S;
+  // Ranking by the mixed cache: the fetched positions ([slices][n_kappa]), whose logits are the
+  // 16-bit ones written after the bounds were taken from the low-bit ones; null otherwise.
+  const int32_t* kappa;
+  int n_kappa;
 };
 
 // The long-slice form (KEYS): slices longer than one selection workgroup holds, from rank_keys'
@@ -909,9 +914,15 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     const int64_t sb = (slice * G + hw) * S;
     const int j0 = lane < S ? lane : 0;
     const float m_first = pr.part_m[sb + j0], l_first = pr.part_l[sb + j0];
+    // ranking by the mixed cache: a group that holds a fetched position is a candidate whatever
+    // its bounds say (its logit there is a 16-bit one, taken after them), and gives no L
+    const bool mixed = pr.kappa != nullptr;  // uniform
+    const int32_t* kp = mixed ? pr.kappa + slice * pr.n_kappa : nullptr;
+    const int32_t kp0 = mixed && t < pr.n_kappa ? kp[t] : -1;
     asm volatile("" ::: "memory");
     sm.hist[t] = 0u;
     sm.hist[t + kSelThreads] = 0u;
+    if (t < kMaxGroups / 32) sm.kgrp[t] = 0u;
     if (wave < kFusedG) {
       const float l2 = head_lse2<64>(pr.part_m + sb, pr.part_l + sb, S, lane, m_first, l_first);
       if (wave < G && lane == 0) sm.lse2[wave] = l2;
@@ -920,6 +931,14 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       sm.n_cand = 0u;
     }
     __syncthreads();
+    if (mixed) {
+      auto mark = [&](int32_t p) {
+        if (p >= 0 && p < N) atomicOr(&sm.kgrp[p >> 9], 1u << ((p >> 4) & 31));
+      };
+      mark(kp0);
+      for (int i = t + kSelThreads; i < pr.n_kappa; i += kSelThreads) mark(kp[i]);
+      __syncthreads();
+    }
     float lse2[kFusedG];
 #pragma unroll
     for (int g = 0; g < kFusedG; ++g) lse2[g] = g < G ? sm.lse2[g] : 0.0f;
@@ -944,12 +963,15 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       L[s] = mx * kLn2 + 0.0f;
     }
     const bool gv0 = 2 * t < ngrp, gv1 = 2 * t + 1 < ngrp;
+    const uint32_t kw = mixed ? sm.kgrp[t >> 4] >> ((2 * t) & 31) : 0u;  // groups 2t, 2t + 1
+    const bool kg0 = kw & 1u, kg1 = (kw >> 1) & 1u;
 
-    // tau_lo: below the k-th largest L (the lower edge of the coarse bin holding it, one bin down)
+    // tau_lo: below the k-th largest L (the lower edge of the coarse bin holding it, one bin down);
+    // with fewer than k groups giving an L, no bound (bin 0)
     float tau_lo = -INFINITY;
     if (k <= ngrp) {
-      if (gv0) atomicAdd(&sm.hist[coarse_bin(L[0], r_lo)], 1u);
-      if (gv1) atomicAdd(&sm.hist[coarse_bin(L[1], r_lo)], 1u);
+      if (gv0 && !kg0) atomicAdd(&sm.hist[coarse_bin(L[0], r_lo)], 1u);
+      if (gv1 && !kg1) atomicAdd(&sm.hist[coarse_bin(L[1], r_lo)], 1u);
       __syncthreads();
       uint32_t bin, above;
       pick_digit(sm, kBins, (uint32_t)k, bin, above);
@@ -958,7 +980,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       sm.hist[t + kSelThreads] = 0u;
     }
     // candidate groups, compacted in ascending order
-    const bool c0 = gv0 && U[0] >= tau_lo, c1 = gv1 && U[1] >= tau_lo;
+    const bool c0 = gv0 && (U[0] >= tau_lo || kg0), c1 = gv1 && (U[1] >= tau_lo || kg1);
     {
       uint32_t tot;
       uint32_t off = block_exclusive_scan((c0 ? 1u : 0u) + (c1 ? 1u : 0u), sm.scan_scratch, tot);
@@ -1258,12 +1280,12 @@ bool rank_select_prunable(const Dims& d, int k) {
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,
                               const float* part_l, int k, float* keys, bool keys_wanted, uint32_t* hist,
                               int32_t* idx_out, const MergeJob* merge, hipStream_t s, const float* gmax,
-                              float* kmax) {
+                              const int32_t* kappa, int n_kappa, float* kmax) {
   const float r_lo = logf((float)d.G) - kBinSpan;  // the same value for both kernels
   const MergeJob none{nullptr, nullptr, 0, 0, nullptr};
   const MergeJob& mj = merge ? *merge : none;
   if (gmax && !keys_wanted && rank_select_prunable(d, k)) {
-    const PrunedRank pr{logits, part_m, part_l, gmax, d.G, S};
+    const PrunedRank pr{logits, part_m, part_l, gmax, d.G, S, n_kappa > 0 ? kappa : nullptr, n_kappa};
     const unsigned n_sel = (unsigned)d.slices();
     const unsigned grid = n_sel + (unsigned)ceil_div(mj.rows, kSelWaves);
     if (d.D == 64)

@@ -844,14 +844,18 @@ def test_overlapped_streams_match_serial(gpu, compute):
     ("llama8k", dict(seq_len=20480, top_k=300, seed=3), 0.0),           # every rank equal
     ("llama8k", dict(seq_len=20480, top_k=300, seed=3), 1e-3),          # a crowded threshold bin
     ("llama8k", dict(n_tokens=1, top_k=40), 1.0),          # pre-decoding shape, row 0
+    ("llama8k", dict(seq_len=8192 + 96, seed=6, tail_len=3), 1.0),   # a visible tail (mixed: in the LSE)
 ])
-def test_fused_step_selection_from_bounds(gpu, name, over, qscale):
+@pytest.mark.parametrize("mixed", [False, True])
+def test_fused_step_selection_from_bounds(gpu, name, over, qscale, mixed):
     """Without a key output the fused step selects from per-16-position logit maxima: groups
-    whose upper bound cannot reach the k-th rank are never read.  The set must be the oracle's
-    (tie band) and the one the unpruned selection makes from the same logits (which runs when
-    the keys are asked for)."""
+    whose upper bound cannot reach the k-th rank are never read.  Ranking by the mixed cache
+    (Algorithm 3's reading), the fetched rows' 16-bit logits replace the low-bit ones after the
+    maxima are taken, so the groups holding them are always read and give no lower bound.  The
+    set must be the oracle's (tie band) and the one the unpruned selection makes from the same
+    logits (which runs when the keys are asked for)."""
     cfg = get_config(name).with_(**over)
-    K, V, Q, _, _, _ = generate_all(cfg)
+    K, V, Q, _, KT, VT = generate_all(cfg)
     Q = (Q.astype(np.float32) * qscale).astype(np.float16)
     B, Hkv, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
     cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
@@ -859,7 +863,9 @@ def test_fused_step_selection_from_bounds(gpu, name, over, qscale):
     idx = _random_idx(rng, B, Hkv, N, cfg.top_k)
     ks, vs = oracle.gather_rows(K, V, idx)
     row = 1 if cfg.n_tokens == 2 else 0
-    args = dict(rank_row=row, idx=_dev(idx), k_sel=_dev(ks), v_sel=_dev(vs))
+    args = dict(rank_row=row, rank_mixed=mixed, idx=_dev(idx), k_sel=_dev(ks), v_sel=_dev(vs))
+    if KT is not None:
+        args.update(k_tail=_dev(KT), v_tail=_dev(VT))
     o1, pruned = decode_step(_dev(Q), cache, cfg.top_k, **args)
     rk = torch.empty((B, Hkv, N), dtype=torch.float32, device="cuda")
     o2, full = decode_step(_dev(Q), cache, cfg.top_k, rank_key_out=rk, **args)
@@ -867,8 +873,11 @@ def test_fused_step_selection_from_bounds(gpu, name, over, qscale):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(pruned, full)
     _, kh, _ = _reference_cache(K, V, cfg.bits)
-    r_ref = oracle.rank_scores(Q, kh, row, cfg.sm_scale)
-    if qscale == 0.0:
+    if mixed:
+        r_ref = oracle.rank_scores_mixed(Q, kh, row, cfg.sm_scale, idx=idx, k_sel=ks, k_tail=KT)
+    else:
+        r_ref = oracle.rank_scores(Q, kh, row, cfg.sm_scale)
+    if qscale == 0.0 and not mixed:
         assert np.array_equal(_np(pruned), np.broadcast_to(np.arange(cfg.top_k, dtype=np.int32), pruned.shape))
     _assert_topk(_np(pruned), r_ref, cfg.top_k, [(b, h) for b in range(B) for h in range(Hkv)],
-                 f"{name} {over} q x{qscale} bounds")
+                 f"{name} {over} q x{qscale} {'mixed' if mixed else 'lowbit'} bounds")
