@@ -195,7 +195,7 @@ def write_traffic_record(root: str, workload: str = "mistral32k"):
                 kind = fused.group(0)
                 after_split[queue] = True
             elif after_split.get(queue) and ("rank_keys" in name or "rank_select" in name):
-                kind = "rank_keys_kernel" if "rank_keys" in name else "rank_select_kernel (with the split merge)"
+                kind = "rank_keys_kernel" if "rank_keys" in name else "rank_select (with the split merge)"
                 if "rank_select" in name:
                     after_split[queue] = False
             else:

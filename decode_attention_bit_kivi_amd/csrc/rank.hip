@@ -6,31 +6,32 @@
 // SpeCache summary, §7 Algorithms 2 and 3 (ArgTopK of the attention row), and
 // §2 "attention sparsity" (a position is worth the attention mass it holds).
 //
-// Two kernels:
+// Kernels:
 //   rank_keys    (grid: position chunks x slices) computes r(p) for every
-//                position, writes it, and adds a coarse histogram of r into a
-//                per-slice global histogram (zeroed by the kernel that wrote
-//                the logits).  The coarse bins are linear in r over a window of
-//                32 below log G (r <= log G always): 64 bins per unit of r.
+//                position, writes it and its maximum over every 16 positions,
+//                and adds a coarse histogram of r into a per-slice global
+//                histogram (zeroed by the kernel that wrote the logits).  The
+//                coarse bins are linear in r over a window of 32 below log G
+//                (r <= log G always): 64 bins per unit of r.
 //   rank_select  (one 1024-thread workgroup per slice) finds the coarse bin
 //                that holds the k-th largest r, gathers that bin's keys into
-//                LDS in one sweep, finds the exact k-th largest key there by a
-//                three-digit radix select, and in a second sweep marks the
-//                selected positions in LDS bitmaps (128K positions at a time),
-//                whose set bits one prefix sum turns into the ascending output.
-//                A bin too large for LDS falls back to the radix select over
-//                all keys (three sweeps).  Every sweep reads 4096 consecutive
-//                values per step, a float4 per thread.  A slice of at most
-//                32768 positions is read once and kept in registers (32 keys
-//                a thread) for every step, and a bin of at most 64 keys is
-//                resolved by one wave counting, without the radix passes.
-//                The bin's value interval comes from a 64-way search by one
-//                wave.
-//   For a slice of at most 32768 positions and at most 4 heads per KV head
-//   there is one launch: the register-resident rank_select forms r(p) and the
-//   coarse histogram itself, with the arithmetic of rank_keys (shared
-//   functions, so the keys are the same bits), and no key buffer is written
-//   unless the caller asks for r.
+//                LDS, finds the exact k-th largest key there (one wave counting
+//                for at most 64 keys, else a three-digit radix select), and
+//                marks the selected positions for one prefix sum that turns
+//                them into the ascending output.  Its forms:
+//                - resident: a slice of at most 32768 positions read once into
+//                  registers (32 keys a thread), from rank_keys' keys or, with
+//                  at most 4 heads per KV head, forming r(p) and the histogram
+//                  itself from the logits (the arithmetic of rank_keys through
+//                  shared functions, so the keys are the same bits; no key
+//                  buffer unless the caller asks for r);
+//                - pruned (the fused step): bounds of every 16 positions from
+//                  the split kernel's per-head logit maxima; only the groups
+//                  whose upper bound reaches the k-th lower bound are read;
+//                - keys (longer slices): from rank_keys' keys, reading only the
+//                  groups whose maximum reaches the threshold bin, or sweeping
+//                  every key (bitmaps of 128K positions at a time) when too
+//                  many do.
 //   The exact selection compares order-preserving 32-bit integer keys of the
 //   float r.
 #include "merge.h"
