@@ -72,25 +72,34 @@ struct StreamSmem {
   } u;
 };
 
+// Ranking by the mixed cache with at most kStashFloats fetched-row logits per slice (rows x G):
+// the fetched rows' 16-bit logits wait in LDS until the low-bit loop has stored every position's
+// logit, then overwrite those of their positions.
+constexpr int kStashFloats = 2048;
+struct StreamSmemStash : StreamSmem {
+  float kst[kStashFloats];  // [fetched row of the split][head]
+};
+
 __device__ __forceinline__ void st_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int R>
 using IC = std::integral_constant<int, R>;
 
 // MODE 0: attention only; 1: with the rank row's logits, bounds and statistics against C';
-// 2: with the ranking by the mixed-cache attention row.
+// 2: with the ranking by the mixed-cache attention row; 3: the same with the fetched rows' logits
+// held in LDS until the end (the loop then stores like form 1).
 template <int MODE>
 __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L, int S) {
   // Only the explicit fmaf calls fuse: the compiler may not contract a product and a sum on its own,
   // which it could do differently in the two instantiations and so make the attention of the fused
   // step differ from decode_attn's in the last bit.
 #pragma clang fp contract(off)
-  constexpr bool RANK = MODE != 0, MIXED = MODE == 2;
+  constexpr bool RANK = MODE != 0, MIXED = MODE >= 2, STASH = MODE == 3;
   constexpr int D = kStD, W = kStW, CPL = kStCPL, P = kStreamAhead;
   constexpr int U = P % 2 == 0 ? P : 2 * P;  // unroll: the stage buffers and the two score sets
   constexpr float hK = 0.5f, hV = 0.5f;    // 1-bit codes: the operand is the sign of s around z + s/2
   static_assert(U == 2 || U == 4, "the remainder steps below are written out for U <= 4");
-  __shared__ StreamSmem sm;
+  __shared__ std::conditional_t<STASH, StreamSmemStash, StreamSmem> sm;
 
   const int tid = threadIdx.x;
   // the wave index as a wave-uniform (scalar) value: block indices and LDS bases derived from it
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
       const f4_t v = {xa[0], xa[1], xa[2], xa[3]};
       const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)((blk0 + jj) * 32 * 4));
       const uint32_t voff = rl_lane + 4 * (16 * (n16 >> 3) + 4 * g);
-      if constexpr (MIXED) {
+      if constexpr (MIXED && !STASH) {
         // the kappa positions are written by the 16-bit blocks instead
         if (rank_lane && kmw) {
           float* dst = a.rank_logits + (slice * G + arow / T) * N + (blk0 + jj) * 32;
@@ -355,6 +364,8 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
         // store is dropped): with no branch around it the compiler counts it, and the waits for
         // the staged loads stay exact.  Non-temporal: the selection reads back only the groups
         // its bounds keep (about a fifth), so the logits need not displace C' in the caches.
+        // (Form 3 stores the kappa positions' low-bit logits too; the end of the kernel writes
+        // their 16-bit ones over them.)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
                                                (int)(rank_lane ? voff : kStDropped), (int)soff, kStNonTemporal);
       }
@@ -525,8 +536,12 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
       if constexpr (RANK) {
         // ranking by the mixed cache: a fetched row's logit replaces its low-bit one
         if (MIXED && rank_lane && !tail && ok) {
-          const int64_t pos = a.idx[slice * a.k + base + tok];
-          a.rank_logits[(slice * G + arow / T) * N + pos] = v;
+          if constexpr (STASH) {
+            sm.kst[(base - i0 + tok) * G + arow / T] = v;  // the split's fetched row base - i0 + tok
+          } else {
+            const int64_t pos = a.idx[slice * a.k + base + tok];
+            a.rank_logits[(slice * G + arow / T) * N + pos] = v;
+          }
         }
       }
       if (tail) ok = ok && (base + tok <= a.tail - T + tq);
@@ -643,6 +658,14 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
     }
   }
   __syncthreads();  // all waves are done with their tiles and slots; the LDS union becomes the combine buffer
+  if constexpr (STASH) {
+    // the fetched rows' 16-bit logits over the low-bit ones the loop stored at their positions
+    const int n_kst = (i1 - i0) * G;
+    for (int e = tid; e < n_kst; e += 256) {
+      const int r = e / G, hh = e - r * G;
+      a.rank_logits[(slice * G + hh) * N + ix[i0 + r]] = sm.kst[e];
+    }
+  }
   if constexpr (RANK) {
     // one thread per head: combine the four waves and write this split's statistics over C'
     if (!MIXED && tid < G) {
@@ -736,6 +759,8 @@ hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArg
     attn_stream_kernel<0><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   else if (!a.rank_mixed)
     attn_stream_kernel<1><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  else if ((int64_t)a.k * d.G <= kStashFloats)
+    attn_stream_kernel<3><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   else
     attn_stream_kernel<2><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
   return hipGetLastError();

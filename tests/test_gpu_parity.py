@@ -594,13 +594,16 @@ def test_fused_step_mixed_cache_rank(gpu, name, over, mode):
 
 @pytest.mark.parametrize("seq_len", [32, 96, 32 * 7, 32 * 29, 8192 + 96])
 @pytest.mark.parametrize("cus", [8, None])
-def test_streamed_split_block_counts(gpu, seq_len, cus):
+@pytest.mark.parametrize("top_k", [64, 600])
+def test_streamed_split_block_counts(gpu, seq_len, cus, top_k):
     """The LDS-streamed split kernel (head_dim 128, 1-bit codes, G * T = 8) with every count of
     low-bit blocks per wave it meets: none, fewer than its loads ahead, and each remainder of its
     four-step loop.  On 8 compute units the plan takes few, long splits; on the device many short
     ones.  decode_attn against the oracle; the fused step (ranking against C', and by the mixed
-    cache) bit for bit against it, with its next selection against the oracle's ranking."""
-    cfg = get_config("llama8k").with_(bits=1, seq_len=seq_len, top_k=min(64, seq_len), tail_len=3, seed=7)
+    cache) bit for bit against it, with its next selection against the oracle's ranking.  Ranking
+    by the mixed cache, up to 512 fetched rows (4 heads) wait in LDS and overwrite their low-bit
+    logits at the end; more (600) are stored position by position as they come."""
+    cfg = get_config("llama8k").with_(bits=1, seq_len=seq_len, top_k=min(top_k, seq_len), tail_len=3, seed=7)
     K, V, Q, _, KT, VT = generate_all(cfg)
     B, Hkv, N = cfg.batch, cfg.n_kv_heads, cfg.seq_len
     rng = np.random.default_rng(seq_len)
@@ -623,7 +626,7 @@ def test_streamed_split_block_counts(gpu, seq_len, cus):
     assert torch.equal(o_c.view(torch.int16), o_sep.view(torch.int16))
     assert torch.equal(o_m.view(torch.int16), o_sep.view(torch.int16))
     _, kh, vh = _reference_cache(K, V, cfg.bits)
-    what = f"seq {seq_len} cus {cus}"
+    what = f"seq {seq_len} cus {cus} k {cfg.top_k}"
     ref = oracle.mixed_attention(Q, kh, vh, idx, ks, vs, KT, VT, sm_scale=cfg.sm_scale)
     _check_attn(_np(o_sep), ref, what)
     slices = [(b, h) for b in range(B) for h in range(Hkv)]
