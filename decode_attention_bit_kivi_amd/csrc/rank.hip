@@ -814,6 +814,9 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
 // at least k positions therefore have r >= the k-th largest L, and only a group whose U reaches
 // that value can hold a selected position.  The kernel reads the bounds, the logits of those
 // groups only, and selects among their positions exactly as the resident selection does.
+// Ranking by the mixed cache, the fetched positions' logits are 16-bit ones written after the
+// bounds were taken: the groups that hold them are always read and give no L.  The same kernel,
+// in its KEYS form (below), serves slices longer than kResidentN from rank_keys' keys.
 constexpr int kGrp = 16;                            // positions per bound group
 constexpr int kMaxGroups = (int)(kResidentN / kGrp);  // 2048: two groups per thread
 constexpr float kBoundMargin = 1e-3f;               // slack on U for the rounding of its arithmetic
