@@ -2,6 +2,7 @@
 // workspace carving, and dispatch to the kernel launchers.  Nothing here
 // allocates memory; the only state is the per-device address of the
 // no-allocation decode step's static scratch array.
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -58,14 +59,17 @@ struct ScoreWs {
   size_t logits, part_m, part_l, keys, hist, kmax, total;
 };
 
+// Split statistics sized for the score kernel's plan or the streamed kernel's, whichever has more
+// splits (score_topk runs the streamed kernel's score pass where it serves).
 ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
   ScoreWs w;
+  const size_t S = (size_t)std::max<int64_t>(p.S, attn_max_splits(d));
   w.logits = 0;
   size_t off = align256(sizeof(float) * (size_t)d.slices() * d.G * d.N);
   w.part_m = off;
-  off += align256(sizeof(float) * (size_t)d.slices() * d.G * p.S);
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * S);
   w.part_l = off;
-  off += align256(sizeof(float) * (size_t)d.slices() * d.G * p.S);
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * S);
   w.keys = off;
   off += align256(sizeof(float) * (size_t)d.slices() * d.N);
   w.hist = off;
@@ -135,6 +139,10 @@ const void* device_view(const void* p) {
   return nullptr;
 }
 
+}  // namespace
+
+namespace {
+int stream_cus(hipStream_t s);  // the compute units a stream's kernels may use (below)
 }  // namespace
 
 extern "C" {
@@ -232,11 +240,37 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
   float* keys = rank_key_out ? rank_key_out : reinterpret_cast<float*>(base + ws.keys);
   uint32_t* hist = reinterpret_cast<uint32_t*>(base + ws.hist);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_score(d, plan, static_cast<const _Float16*>(q16), n_tokens, rank_row,
-                              static_cast<const uint32_t*>(cache->k_codes), static_cast<const _Float16*>(cache->k_meta),
-                              sm_scale, logits, part_m, part_l, hist, s);
+  // the streamed kernel's score pass where it serves (head_dim 128, 1-bit codes, G * T <= 8),
+  // else the score kernel
+  AttnArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.q16 = static_cast<const _Float16*>(q16);
+  sa.T = n_tokens;
+  sa.k_codes = static_cast<const uint32_t*>(cache->k_codes);
+  sa.k_meta = static_cast<const _Float16*>(cache->k_meta);
+  sa.v_codes = static_cast<const uint32_t*>(cache->v_codes);
+  sa.v_meta = static_cast<const _Float16*>(cache->v_meta);
+  sa.seq_stride = d.Ns;
+  sa.group = d.group;
+  sa.sm_scale = sm_scale;
+  sa.rank_row = rank_row;
+  sa.rank_logits = logits;
+  sa.rank_m = part_m;
+  sa.rank_l = part_l;
+  sa.rank_hist = hist;
+  int S = plan.S;
+  hipError_t e;
+  if (attn_stream_serves(d, sa)) {
+    const AttnPlan ap = attn_plan(d, stream_cus(s), kStreamWGsPerCU);
+    S = ap.S;
+    e = launch_score_stream(d, ap, sa, s);
+  } else {
+    e = launch_score(d, plan, static_cast<const _Float16*>(q16), n_tokens, rank_row,
+                     static_cast<const uint32_t*>(cache->k_codes), static_cast<const _Float16*>(cache->k_meta),
+                     sm_scale, logits, part_m, part_l, hist, s);
+  }
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
-  e = launch_rank_select(d, plan.S, logits, part_m, part_l, k, keys, rank_key_out != nullptr, hist, idx_out,
+  e = launch_rank_select(d, S, logits, part_m, part_l, k, keys, rank_key_out != nullptr, hist, idx_out,
                          nullptr, s, nullptr, nullptr, 0, reinterpret_cast<float*>(base + ws.kmax));
   return hip_status(e);
 }

@@ -87,14 +87,15 @@ using IC = std::integral_constant<int, R>;
 
 // MODE 0: attention only; 1: with the rank row's logits, bounds and statistics against C';
 // 2: with the ranking by the mixed-cache attention row; 3: the same with the fetched rows' logits
-// held in LDS until the end (the loop then stores like form 1).
+// held in LDS until the end (the loop then stores like form 1); 4: the rank row's logits and
+// statistics against C' alone (score_topk: no values, no fetched rows, no tail, no output).
 template <int MODE>
 __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv, int G, int64_t N, int64_t L, int S) {
   // Only the explicit fmaf calls fuse: the compiler may not contract a product and a sum on its own,
   // which it could do differently in the two instantiations and so make the attention of the fused
   // step differ from decode_attn's in the last bit.
 #pragma clang fp contract(off)
-  constexpr bool RANK = MODE != 0, MIXED = MODE >= 2, STASH = MODE == 3;
+  constexpr bool RANK = MODE != 0, MIXED = MODE == 2 || MODE == 3, STASH = MODE == 3, SCORE = MODE == 4;
   constexpr int D = kStD, W = kStW, CPL = kStCPL, P = kStreamAhead;
   constexpr int U = P % 2 == 0 ? P : 2 * P;  // unroll: the stage buffers and the two score sets
   constexpr float hK = 0.5f, hV = 0.5f;    // 1-bit codes: the operand is the sign of s around z + s/2
@@ -240,11 +241,15 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
     const uint32_t blk = (uint32_t)(blk0 + jj);
     const auto kc = __builtin_amdgcn_raw_buffer_load_b64(kc_buf, (int)off_stage, (int)(blk * 512u), 0);
     const auto km = __builtin_amdgcn_raw_buffer_load_b64(km_buf, (int)off_stage, (int)((blk >> gshift) * 512u), 0);
-    const auto vc = __builtin_amdgcn_raw_buffer_load_b64(vc_buf, (int)off_stage, (int)(blk * 512u), 0);
-    const auto vm = __builtin_amdgcn_raw_buffer_load_b64(vm_buf, (int)off_stage_vm, (int)(blk * vm_bytes), 0);
     Staged st;
     st.kc_km = u32x4_t{kc[0], kc[1], km[0], km[1]};
-    st.vc_vm = u32x4_t{vc[0], vc[1], vm[0], vm[1]};
+    if constexpr (SCORE) {  // keys only
+      st.vc_vm = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+      const auto vc = __builtin_amdgcn_raw_buffer_load_b64(vc_buf, (int)off_stage, (int)(blk * 512u), 0);
+      const auto vm = __builtin_amdgcn_raw_buffer_load_b64(vm_buf, (int)off_stage_vm, (int)(blk * vm_bytes), 0);
+      st.vc_vm = u32x4_t{vc[0], vc[1], vm[0], vm[1]};
+    }
     return st;
   };
   auto stage_ptr = [&](int slot) { return sm.u.w[wave].stage[slot]; };
@@ -252,8 +257,10 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
     unsigned char* p = stage_ptr(slot);
     *reinterpret_cast<uint2*>(p + s_kc) = make_uint2(st.kc_km[0], st.kc_km[1]);
     *reinterpret_cast<uint2*>(p + s_km) = make_uint2(st.kc_km[2], st.kc_km[3]);
-    *reinterpret_cast<uint2*>(p + s_vc) = make_uint2(st.vc_vm[0], st.vc_vm[1]);
-    *reinterpret_cast<uint2*>(p + s_vm) = make_uint2(st.vc_vm[2], st.vc_vm[3]);
+    if constexpr (!SCORE) {
+      *reinterpret_cast<uint2*>(p + s_vc) = make_uint2(st.vc_vm[0], st.vc_vm[1]);
+      *reinterpret_cast<uint2*>(p + s_vm) = make_uint2(st.vc_vm[2], st.vc_vm[3]);
+    }
   };
 
   // Scores of the staged block in `slot`: the key codes expanded against the queries (chunks w and
@@ -406,6 +413,7 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
         for (int i = 0; i < 4; ++i) l_corr += __builtin_amdgcn_exp2f(xc[i] - mn);
       }
     }
+    if constexpr (SCORE) return;  // the statistics are all a score pass keeps
     const Frag Ap = make_p(p, 1.0f);
 
     // values: the value codes expanded against P, plus one MFMA whose columns are the per-token
@@ -680,6 +688,7 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
       a.rank_l[(slice * G + tid) * S + split] = Ls;
     }
   }
+  if constexpr (SCORE) return;  // a score pass writes no attention output (every thread leaves here)
   if (g == 0 && n16 < 8) {
     sm.u.comb.m[wave][n16] = mm;
     sm.u.comb.l[wave][n16] = f_self * l_row + f_other * l2;
@@ -751,6 +760,12 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
 
 bool attn_stream_serves(const Dims& d, const AttnArgs& a) {
   return d.D == kStD && d.bits == 1 && d.vbits == 1 && d.G * a.T <= 8;
+}
+
+hipError_t launch_score_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)plan.S, (unsigned)d.slices());
+  attn_stream_kernel<4><<<grid, 256, 0, s>>>(a, d.Hkv, d.G, d.N, plan.L, plan.S);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s) {

@@ -220,6 +220,10 @@ inline int attn_split_wgs_per_cu(const Dims& d, const AttnArgs& a) {
   return attn_stream_serves(d, a) ? kStreamWGsPerCU : kAttnWGsPerCU;
 }
 hipError_t launch_attn_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
+// The same kernel as a score pass (score_topk): the rank row's logits against C' into
+// a.rank_logits, its per-split statistics into a.rank_m / a.rank_l and the zeroed histogram
+// (a.rank_hist); a.k = 0, a.tail = 0, no attention output.  Serves what attn_stream_serves does.
+hipError_t launch_score_stream(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
 // The 16-bit comparator's split kernel: a.k_sel / a.v_sel are the whole 16-bit cache, a.k its
 // positions per slice; partials as launch_attn_split's, merged by launch_attn_merge.
 hipError_t launch_attn16_split(const Dims& d, const AttnPlan& plan, const AttnArgs& a, hipStream_t s);
