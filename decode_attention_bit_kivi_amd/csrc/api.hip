@@ -56,7 +56,7 @@ bool make_dims(const specache_shape* s, Dims* d, int* err) {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct ScoreWs {
-  size_t logits, part_m, part_l, keys, hist, kmax, total;
+  size_t logits, part_m, part_l, keys, hist, kmax, gmax, total;
 };
 
 // Split statistics sized for the score kernel's plan or the streamed kernel's, whichever has more
@@ -76,6 +76,8 @@ ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
   off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
   w.kmax = off;  // per-16-position maxima of r(p) (the two-launch selection)
   off += align256(sizeof(float) * (size_t)d.slices() * (d.N / 16));
+  w.gmax = off;  // per-16-position logit maxima of each head (the streamed score pass's bounds)
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / 16));
   w.total = off;
   return w;
 }
@@ -263,6 +265,8 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
   if (attn_stream_serves(d, sa)) {
     const AttnPlan ap = attn_plan(d, stream_cus(s), kStreamWGsPerCU);
     S = ap.S;
+    // with no keys asked for, the bounds for the pruned selection (as in the fused step)
+    if (!rank_key_out && rank_select_prunable(d, k)) sa.rank_gmax = reinterpret_cast<float*>(base + ws.gmax);
     e = launch_score_stream(d, ap, sa, s);
   } else {
     e = launch_score(d, plan, static_cast<const _Float16*>(q16), n_tokens, rank_row,
@@ -271,7 +275,7 @@ int specache_score_topk(const specache_shape* shape, const void* q16, int n_toke
   }
   if (e != hipSuccess) return SPECACHE_ERR_HIP;
   e = launch_rank_select(d, S, logits, part_m, part_l, k, keys, rank_key_out != nullptr, hist, idx_out,
-                         nullptr, s, nullptr, nullptr, 0, reinterpret_cast<float*>(base + ws.kmax));
+                         nullptr, s, sa.rank_gmax, nullptr, 0, reinterpret_cast<float*>(base + ws.kmax));
   return hip_status(e);
 }
 
