@@ -9,7 +9,11 @@
 // one workgroup of four waves per (split, KV head), wave w taking the split's 32-position blocks
 // w, w + 4, ...; its outputs are the split partials and, in the RANK form, the rank row's logits
 // and statistics (over C', or those of the attention itself when ranking by the mixed cache) and
-// the 16-position maxima.
+// the 16-position maxima.  One difference in the softmax: the running maximum of a row here also
+// covers the low-bit logits of the kappa positions, whose exponentials, dropped from the
+// attention, are the kappa terms of the ranking statistics over C' (attn_split_kernel keeps
+// those terms apart, with a maximum of their own).  The results agree to rounding; both forms of
+// this kernel (with and without the ranking outputs) compute the same attention bit for bit.
 //
 // What differs is how a block's bytes reach the matrix-core operands.  The operand layout holds
 // each code word and value-metadata entry in 4 lanes and each key scale in 16, so loading it
@@ -149,7 +153,8 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
   float m_used = kMergeEmpty;  // running max (log2 units) of accumulator row n16
   float l_part = 0.0f;         // this lane's share of that row's sum of exponentials (low-bit positions)
   float l16 = 0.0f;            // the same over the 16-bit rows (fetched and tail)
-  float m_corr = kMergeEmpty, l_corr = 0.0f;  // C' terms of kappa positions (ranking statistics)
+  // the C' exponentials of the kappa positions, relative to m_used (ranking statistics over C')
+  float l_kappa = 0.0f;
   f32x4 Oacc[CPL];
 #pragma unroll
   for (int ct = 0; ct < CPL; ++ct) Oacc[ct] = zero4();
@@ -175,6 +180,7 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
       m_used = mn;
       l_part *= alpha;
       l16 *= alpha;
+      l_kappa *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) xr[i] = xa[i] - mn;
       // whole-accumulator products: the accumulators then keep their registers through this
@@ -383,36 +389,25 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gm), gm_buf,
                                             (int)(rank_lane && g == 0 ? goff : kStDropped), 0, 0);
     }
-    float xc[4];  // C' logits of masked positions, for the ranking statistics
+    // The running maximum covers every C' logit, kappa positions included: their exponentials
+    // are then the ranking statistics' terms over C' as they stand, and the attention drops them
+    // (their 16-bit rows take their place).
+    online_update(xr, xa);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(xr[i]);
     if (kmw) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = 16 * (n16 >> 3) + 4 * g + i;
-        xc[i] = -INFINITY;
         if ((kmw >> tok) & 1u) {
-          xc[i] = xa[i];
-          xr[i] = -INFINITY;
-          xa[i] = -INFINITY;
+          if constexpr (RANK && !MIXED) l_kappa += p[i];
+          p[i] = 0.0f;
         }
       }
     }
-    online_update(xr, xa);
-    float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = __builtin_amdgcn_exp2f(xr[i]);
-      l_part += p[i];
-    }
-    if constexpr (RANK) {
-      if (kmw) {
-        const float cm = fmaxf(fmaxf(xc[0], xc[1]), fmaxf(xc[2], xc[3]));
-        const float mn = fmaxf(m_corr, cm);
-        l_corr *= __builtin_amdgcn_exp2f(m_corr - mn);
-        m_corr = mn;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) l_corr += __builtin_amdgcn_exp2f(xc[i] - mn);
-      }
-    }
+    for (int i = 0; i < 4; ++i) l_part += p[i];
     if constexpr (SCORE) return;  // the statistics are all a score pass keeps
     const Frag Ap = make_p(p, 1.0f);
 
@@ -635,13 +630,9 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
 
   __builtin_amdgcn_s_setprio(3);  // the rest of the workgroup is a chain of latencies: let it through
 
-  // ranking statistics over C' = the low-bit positions, kappa positions included
-  float rank_m_lane = m_used, rank_l_lane = l_part;
-  if constexpr (RANK) {
-    rank_m_lane = max_over_groups(fmaxf(m_used, m_corr));  // the same for the four lanes of a row
-    rank_l_lane = l_part * __builtin_amdgcn_exp2f(m_used - rank_m_lane) +
-                  l_corr * __builtin_amdgcn_exp2f(m_corr - rank_m_lane);
-  }
+  // ranking statistics over C' = the low-bit positions, kappa positions included (the same
+  // maximum in the four lanes of a row)
+  const float rank_m_lane = m_used, rank_l_lane = l_part + l_kappa;
 
   // ================= 16-bit rows of the tail (the fetched rows went first) =================
   for (int q = first_tail_q; q < n_sel_blk + n_tail_blk; q += 4) f16_block(q);
@@ -655,7 +646,7 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
   const float mm = fmaxf(m_used, m2);
   const float f_self = __builtin_amdgcn_exp2f(m_used - mm);
   const float f_other = __builtin_amdgcn_exp2f(m2 - mm);
-  if constexpr (RANK) {
+  if constexpr (RANK && !MIXED) {  // (the mixed ranking takes the attention's own statistics)
     float rl = sum_over_groups(rank_l_lane), rm = rank_m_lane;
     const float rm2 = __shfl_xor(rm, 8), rl2 = __shfl_xor(rl, 8);
     const float rmm = fmaxf(rm, rm2);
