@@ -76,8 +76,8 @@ ScoreWs score_ws(const Dims& d, const ScorePlan& p) {
   off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
   w.kmax = off;  // per-16-position maxima of r(p) (the two-launch selection)
   off += align256(sizeof(float) * (size_t)d.slices() * (d.N / 16));
-  w.gmax = off;  // per-16-position logit maxima of each head (the streamed score pass's bounds)
-  off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / 16));
+  w.gmax = off;  // per-group logit maxima of each head (the streamed score pass's bounds)
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / kBoundGroup));
   w.total = off;
   return w;
 }
@@ -107,9 +107,9 @@ AttnWs attn_ws(const Dims& d, int T) {
   off += align256(sizeof(float) * (size_t)d.slices() * d.N);
   w.hist = off;
   off += align256(sizeof(uint32_t) * (size_t)d.slices() * 2048);
-  w.gmax = off;  // per-16-position logit maxima of the pruned selection, or (two-launch form)
-                 // those of r(p)
-  off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / 16));
+  w.gmax = off;  // per-group logit maxima of the pruned selection, or (two-launch form) the
+                 // per-16-position maxima of r(p)
+  off += align256(sizeof(float) * (size_t)d.slices() * d.G * (d.N / kBoundGroup));
   w.total_step = off;
   return w;
 }

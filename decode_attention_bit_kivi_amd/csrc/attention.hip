@@ -367,12 +367,12 @@ __global__ __launch_bounds__(256, 2) void attn_split_kernel(AttnArgs a, int Hkv,
       }
     }
     if constexpr (RANK && PACK == 2) {
-      // the bound of each 16-position group for the pruned selection: this lane's four logits
-      // are tokens 4g .. 4g + 3 of tile n16 >> 3 for row arow, the four lanes g of n16 the tile
+      // the bound of each 8-position group for the pruned selection: this lane's four logits
+      // are tokens 4g .. 4g + 3 of tile n16 >> 3 for row arow, lanes g and g ^ 1 of n16 a group
       if (a.rank_gmax) {
-        const float gm = max_over_groups(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
-        if (rank_lane && g == 0)
-          a.rank_gmax[(slice * G + arow / T) * (N >> 4) + (blk0 + jj) * 2 + (n16 >> 3)] = gm;
+        const float gm = max_over_group_pairs(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
+        if (rank_lane && (g & 1) == 0)
+          a.rank_gmax[(slice * G + arow / T) * (N / kBoundGroup) + (blk0 + jj) * 4 + 2 * (n16 >> 3) + (g >> 1)] = gm;
       }
     }
     float xc[NX];  // C' logits of masked positions, for the ranking statistics

@@ -9,7 +9,7 @@
 // one workgroup of four waves per (split, KV head), wave w taking the split's 32-position blocks
 // w, w + 4, ...; its outputs are the split partials and, in the RANK form, the rank row's logits
 // and statistics (over C', or those of the attention itself when ranking by the mixed cache) and
-// the 16-position maxima.  One difference in the softmax: the running maximum of a row here also
+// the maxima of every 8 positions.  One difference in the softmax: the running maximum of a row here also
 // covers the low-bit logits of the kappa positions, whose exponentials, dropped from the
 // attention, are the kappa terms of the ranking statistics over C' (attn_split_kernel keeps
 // those terms apart, with a maximum of their own).  The results agree to rounding; both forms of
@@ -228,9 +228,9 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
                 RANK && a.rank_logits ? (uint32_t)(G * N * 4) : 0u);
   const uint32_t rl_lane = (uint32_t)((arow / T) * N * 4);
   const __amdgpu_buffer_rsrc_t gm_buf =
-      make_rsrc(RANK && a.rank_gmax ? static_cast<const void*>(a.rank_gmax + slice * G * (N >> 4))
+      make_rsrc(RANK && a.rank_gmax ? static_cast<const void*>(a.rank_gmax + slice * G * (N / kBoundGroup))
                                     : static_cast<const void*>(a.q16),
-                RANK && a.rank_gmax ? (uint32_t)(G * (N >> 4) * 4) : 0u);
+                RANK && a.rank_gmax ? (uint32_t)(G * (N / kBoundGroup) * 4) : 0u);
   // LDS byte offsets of this lane's operands in a staged block
   const int zrow = n16 < 2 * Wg ? n16 : 0;  // value-metadata row of the zero-point / scale column
   const uint32_t l_kc = (uint32_t)(kStKC + 16 * n16);                         // + 256: tile 1
@@ -382,12 +382,14 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
                                                (int)(rank_lane ? voff : kStDropped), (int)soff, kStNonTemporal);
       }
-      // the bound of each 16-position group for the pruned selection (a buffer of size 0 when it
-      // is not wanted): the four lanes g of n16 hold tile n16 >> 3 of row arow
-      const float gm = max_over_groups(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
-      const uint32_t goff = 4u * (uint32_t)((arow / T) * (N >> 4) + (blk0 + jj) * 2 + (n16 >> 3));
+      // the bound of each 8-position group for the pruned selection (a buffer of size 0 when it
+      // is not wanted): lanes g and g ^ 1 of n16 hold the eight logits of row arow at positions
+      // 16 (n16 >> 3) + 8 (g >> 1) .. of the block
+      const float gm = max_over_group_pairs(fmaxf(fmaxf(xa[0], xa[1]), fmaxf(xa[2], xa[3])));
+      const uint32_t goff =
+          4u * (uint32_t)((arow / T) * (N / kBoundGroup) + (blk0 + jj) * 4 + 2 * (n16 >> 3) + (g >> 1));
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gm), gm_buf,
-                                            (int)(rank_lane && g == 0 ? goff : kStDropped), 0, 0);
+                                            (int)(rank_lane && (g & 1) == 0 ? goff : kStDropped), 0, 0);
     }
     // The running maximum covers every C' logit, kappa positions included: their exponentials
     // are then the ranking statistics' terms over C' as they stand, and the attention drops them

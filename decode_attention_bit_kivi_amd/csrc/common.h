@@ -148,7 +148,7 @@ struct MergeJob {
 // merge: null, or the attention merge to run alongside the selection.  keys: where r(p) goes
 // (the caller's output when keys_wanted, else workspace a slice too large for one workgroup's
 // registers uses between its two kernels).
-// gmax: null, or the per-16-position logit maxima the split kernel wrote (rank_gmax); with them,
+// gmax: null, or the per-group logit maxima the split kernel wrote (rank_gmax); with them,
 // and no keys wanted, a slice of at most 32768 positions is selected from the logits of the
 // position groups whose bound reaches the k-th rank only.  kappa / n_kappa: for the ranking by the
 // mixed cache, the fetched positions ([slices][n_kappa]) whose 16-bit logits replaced the
@@ -161,8 +161,12 @@ hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const f
                               int32_t* idx_out, const MergeJob* merge, hipStream_t s, const float* gmax,
                               const int32_t* kappa, int n_kappa, float* kmax);
 
-// Whether the pruned selection (per-16-position bounds) serves this problem: slices of at most
-// 32768 positions, at most 4 heads per KV head, k at most one per group.
+// Positions per bound group: rank_gmax holds, per head, the maximum of the rank row's logits over
+// every kBoundGroup consecutive positions, which the pruned selection reads.
+constexpr int kBoundGroup = 8;
+
+// Whether the pruned selection (per-group bounds) serves this problem: slices of at most 32768
+// positions, at most 4 heads per KV head, k at most one per group.
 bool rank_select_prunable(const Dims& d, int k);
 
 // skip_negative: rows with a negative index are left untouched (resident-set reuse).
@@ -201,8 +205,9 @@ struct AttnArgs {
   float* rank_m;         // [slices][G][S]: per-split max of its softmax (log2 units)
   float* rank_l;         // [slices][G][S]: per-split sum of 2^(x - max)
   uint32_t* rank_hist;   // [slices][2048]: zeroed by the split kernel for the rank kernels
-  // optional (null: not written; only with rank_mixed = 0 and G * T <= 8): per head, the maximum
-  // of the rank row's logits over every 16 consecutive positions, [slices][G][N / 16], log2 units
+  // optional (null: not written; only with G * T <= 8): per head, the maximum of the rank row's
+  // logits over every kBoundGroup consecutive positions, [slices][G][N / kBoundGroup], log2 units
+  // (ranking by the mixed cache: the low-bit logits, before the fetched rows' replace them)
   float* rank_gmax;
 };
 

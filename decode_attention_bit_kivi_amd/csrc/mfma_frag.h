@@ -127,6 +127,12 @@ __device__ __forceinline__ float max_over_groups(float x) {
   asm(SPECACHE_SWAP_OP("v_permlane32_swap_b32", "v_max_f32") : "+v"(x), "+v"(y));
   return x;
 }
+// The maximum over k-groups g and g ^ 1 (lanes l and l ^ 16) only.
+__device__ __forceinline__ float max_over_group_pairs(float x) {
+  float y = x;
+  asm(SPECACHE_SWAP_OP("v_permlane16_swap_b32", "v_max_f32") : "+v"(x), "+v"(y));
+  return x;
+}
 __device__ __forceinline__ float sum_over_groups(float x) {
   float y = x;
   asm(SPECACHE_SWAP_OP("v_permlane16_swap_b32", "v_add_f32") : "+v"(x), "+v"(y));

@@ -25,7 +25,7 @@
 //                  itself from the logits (the arithmetic of rank_keys through
 //                  shared functions, so the keys are the same bits; no key
 //                  buffer unless the caller asks for r);
-//                - pruned (the fused step): bounds of every 16 positions from
+//                - pruned (the fused step): bounds of every 8 positions from
 //                  the split kernel's per-head logit maxima; only the groups
 //                  whose upper bound reaches the k-th lower bound are read;
 //                - keys (longer slices): from rank_keys' keys, reading only the
@@ -84,20 +84,23 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   return (uint32_t)v;
 }
 
-// Exclusive prefix sum over the 1024-thread workgroup; returns the exclusive value, writes the total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+// Exclusive prefix sum over the 1024-thread workgroup; returns the exclusive value, writes the
+// total.  One barrier: each wave posts its total, then every wave scans the 16 totals itself.
+// scratch holds two sets of totals, used in turn (ph, uniform, flips at each call): a wave can only
+// come back to a set after the barrier of the call in between, which every wave reaches after
+// reading it.  Everything every thread does before the call precedes everything any thread does
+// after it.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total, int& ph) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  uint32_t* tot_w = scratch + ph * kSelWaves;
+  ph ^= 1;
   const uint32_t x = wave_inclusive_scan(v);
-  if (lane == 63) scratch[wv] = x;
+  if (lane == 63) tot_w[wv] = x;
   __syncthreads();
-  if (wv == 0) {
-    const uint32_t s = wave_inclusive_scan(lane < kSelWaves ? scratch[lane] : 0u);
-    if (lane < kSelWaves) scratch[kSelWaves + lane] = s;  // inclusive wave prefix
-  }
-  __syncthreads();
-  const uint32_t before = wv > 0 ? scratch[kSelWaves + wv - 1] : 0u;
-  total = scratch[2 * kSelWaves - 1];
-  __syncthreads();
+  const uint32_t s = wave_inclusive_scan(lane < kSelWaves ? tot_w[lane] : 0u);  // lanes 0-15: inclusive
+  const uint32_t before = wv > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)s, wv - 1) : 0u;
+  total = (uint32_t)__builtin_amdgcn_readlane((int)s, kSelWaves - 1);
   return before + x - v;
 }
 
@@ -290,30 +293,33 @@ __device__ __forceinline__ int64_t sweep_pos(int64_t base, int i) {
 
 // The digit of hist[0, nbins) holding the krem-th largest element, counted from the top, and the
 // number of elements in the digits above it.
+// With krem outside [1, total], digit 0 and 0 above it.  Exactly one thread writes the answer,
+// after the scan's barrier: the reads of the previous call's answer precede that barrier.
 template <typename Smem>
-__device__ __forceinline__ void pick_digit(Smem& sm, int nbins, uint32_t krem, uint32_t& digit, uint32_t& above) {
+__device__ __forceinline__ void pick_digit(Smem& sm, int& ph, int nbins, uint32_t krem, uint32_t& digit,
+                                           uint32_t& above) {
   const int t = threadIdx.x;
-  if (t == 0) {
-    sm.sel_digit = 0u;
-    sm.sel_above = 0u;
-  }
   // thread t covers digits nbins-1-2t and nbins-2-2t
   const int dhi = nbins - 1 - 2 * t, dlo = dhi - 1;
   const uint32_t hhi = dhi >= 0 ? sm.hist[dhi] : 0u;
   const uint32_t hlo = dlo >= 0 ? sm.hist[dlo] : 0u;
   uint32_t tot;
-  const uint32_t excl = block_exclusive_scan(hhi + hlo, sm.scan_scratch, tot);
-  if (dhi >= 0 && excl < krem && excl + hhi >= krem) {
-    sm.sel_digit = (uint32_t)dhi;
-    sm.sel_above = excl;
-  } else if (dlo >= 0 && excl + hhi < krem && excl + hhi + hlo >= krem) {
-    sm.sel_digit = (uint32_t)dlo;
-    sm.sel_above = excl + hhi;
+  const uint32_t excl = block_exclusive_scan(hhi + hlo, sm.scan_scratch, tot, ph);
+  if (krem >= 1u && krem <= tot) {
+    if (dhi >= 0 && excl < krem && excl + hhi >= krem) {
+      sm.sel_digit = (uint32_t)dhi;
+      sm.sel_above = excl;
+    } else if (dlo >= 0 && excl + hhi < krem && excl + hhi + hlo >= krem) {
+      sm.sel_digit = (uint32_t)dlo;
+      sm.sel_above = excl + hhi;
+    }
+  } else if (dlo == 0 || (dhi == 0 && dlo < 0)) {
+    sm.sel_digit = 0u;
+    sm.sel_above = 0u;
   }
   __syncthreads();
   digit = sm.sel_digit;
   above = sm.sel_above;
-  __syncthreads();
 }
 
 // Exact radix select: the krem-th largest key among those `count` feeds to the histogram, as
@@ -321,8 +327,8 @@ __device__ __forceinline__ void pick_digit(Smem& sm, int nbins, uint32_t krem, u
 // count(shift, nbins, prefix, mask) adds every key u with (u & mask) == prefix to
 // sm.hist[(u >> shift) & (nbins - 1)].
 template <typename Smem, typename Count>
-__device__ __forceinline__ void radix_select(Smem& sm, uint32_t krem, Count count, uint32_t& thr, uint32_t& need_eq,
-                                             uint32_t& n_eq) {
+__device__ __forceinline__ void radix_select(Smem& sm, int& ph, uint32_t krem, Count count, uint32_t& thr,
+                                             uint32_t& need_eq, uint32_t& n_eq) {
   const int t = threadIdx.x;
   uint32_t prefix = 0u, mask = 0u;
   for (int pass = 0; pass < 3; ++pass) {  // digits: bits 31..21, 20..10, 9..0
@@ -333,7 +339,7 @@ __device__ __forceinline__ void radix_select(Smem& sm, uint32_t krem, Count coun
     count(shift, nbins, prefix, mask);
     __syncthreads();
     uint32_t dg, ab;
-    pick_digit(sm, nbins, krem, dg, ab);
+    pick_digit(sm, ph, nbins, krem, dg, ab);
     prefix |= dg << shift;
     mask |= (uint32_t)(nbins - 1) << shift;
     krem -= ab;
@@ -385,6 +391,7 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
                                  const uint32_t* __restrict__ ghist, int64_t N, int k, float r_lo,
                                  int32_t* __restrict__ idx_out, int64_t slice) {
   const int t = threadIdx.x, lane = t & 63;
+  int ph = 0;  // the block scans' scratch set (the caller's scans ended before its barrier)
   const float* ky = rkey + slice * N;
   const uint32_t* gh = ghist + slice * kBins;
   for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
@@ -392,7 +399,7 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
   __syncthreads();
 
   uint32_t bin, above;
-  pick_digit(sm, kBins, (uint32_t)k, bin, above);
+  pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
   const uint32_t in_bin = sm.hist[bin];
   // the threshold bin as an interval of values [lo, hi) (the top bin runs to +inf), found by two
   // binary searches over the keys.  The ranks hold no -0 and no NaN, so comparing the floats
@@ -433,7 +440,7 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
     });
     __syncthreads();
     const uint32_t nc = sm.n_cand < (uint32_t)kCand ? sm.n_cand : (uint32_t)kCand;
-    radix_select(sm, (uint32_t)k - above,
+    radix_select(sm, ph, (uint32_t)k - above,
                  [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
                    for (uint32_t i = t; i < nc; i += kSelThreads) {
                      const uint32_t u = sm.u.cand[i];
@@ -442,7 +449,7 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
                  },
                  thr, need_eq, n_thr);
   } else {
-    radix_select(sm, (uint32_t)k,
+    radix_select(sm, ph, (uint32_t)k,
                  [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
                    sweep(ky, 0, N, [&](int64_t base, const float (&v)[4 * kSweepU]) {
 #pragma unroll
@@ -464,6 +471,9 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
   uint32_t out_base = 0u, eq_seen = 0u;
   for (int64_t c0 = 0; c0 < N; c0 += kChunk) {
     const int64_t c1 = c0 + kChunk < N ? c0 + kChunk : N;
+    // the previous chunk's bitmap words are read by the threads that own them (kWordsPerThread
+    // each) and cleared here by others: every read must come first
+    if (c0 > 0) __syncthreads();
     for (int i = t; i < kWords; i += kSelThreads) {
       sm.u.bm.gt[i] = 0u;
       sm.u.bm.eq[i] = 0u;
@@ -488,10 +498,10 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
     uint32_t eq_tot = 0u, take_tot;
     uint32_t eq_take = 0u;
     if (!all_eq) {
-      const uint32_t eq_before = eq_seen + block_exclusive_scan(neq, sm.scan_scratch, eq_tot);
+      const uint32_t eq_before = eq_seen + block_exclusive_scan(neq, sm.scan_scratch, eq_tot, ph);
       eq_take = eq_before >= need_eq ? 0u : (need_eq - eq_before < neq ? need_eq - eq_before : neq);
     }
-    uint32_t out = out_base + block_exclusive_scan(ngt + eq_take, sm.scan_scratch, take_tot);
+    uint32_t out = out_base + block_exclusive_scan(ngt + eq_take, sm.scan_scratch, take_tot, ph);
     uint32_t eq_left = eq_take;
 #pragma unroll
     for (int j = 0; j < kWordsPerThread; ++j) {
@@ -568,6 +578,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
   }
   __shared__ ResidentSmem sm;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int ph = 0;  // the block scans' scratch set
   const int64_t slice = blockIdx.x;
   // N <= kResidentN: positions fit 32 bits; a float4 is wholly in range or wholly past N
   auto in_range = [&](int u) { return 4 * (t + u * kSelThreads) < (int)N; };
@@ -670,7 +681,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
   }
 
   uint32_t bin, above;
-  pick_digit(sm, kBins, (uint32_t)k, bin, above);
+  pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
   const uint32_t in_bin = sm.hist[bin];
   if (wave == 0) {
     const uint32_t key = first_key_of_bin_wave(bin, r_lo);
@@ -734,7 +745,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
       need_eq = sm.res[1];
       n_thr = sm.res[2];
     } else {
-      radix_select(sm, krem,
+      radix_select(sm, ph, krem,
                    [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
                      for (uint32_t i = t; i < nc; i += kSelThreads) {
                        const uint32_t u = sm.cand[i];
@@ -744,7 +755,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
                    thr, need_eq, n_thr);
     }
   } else {
-    radix_select(sm, (uint32_t)k,
+    radix_select(sm, ph, (uint32_t)k,
                  [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
 #pragma unroll
                    for (int i = 0; i < 4 * kSweepU; ++i) {
@@ -787,7 +798,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
   uint32_t tot;
   if (!all_eq) {
     const uint32_t ne = __popc(e);
-    const uint32_t eq_before = block_exclusive_scan(ne, sm.scan_scratch, tot);
+    const uint32_t eq_before = block_exclusive_scan(ne, sm.scan_scratch, tot, ph);
     uint32_t eq_take = eq_before >= need_eq ? 0u : (need_eq - eq_before < ne ? need_eq - eq_before : ne);
     while (eq_take > 0u) {  // the lowest equal positions first
       const uint32_t low = e & (0u - e);
@@ -796,7 +807,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
       --eq_take;
     }
   }
-  uint32_t out = block_exclusive_scan(__popc(m), sm.scan_scratch, tot);
+  uint32_t out = block_exclusive_scan(__popc(m), sm.scan_scratch, tot, ph);
   while (m != 0u) {
     const int b = __builtin_ctz(m);
     m &= m - 1u;
@@ -805,9 +816,9 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
   }
 }
 
-// ---- rank_select from per-16-position bounds (the fused step, slices of at most kResidentN
-// positions, at most kFusedG heads).  r(p) is non-decreasing in every head's logit, so with M_g
-// the maximum of head g's logits over a group of 16 positions:
+// ---- rank_select from per-group bounds (the fused step, slices of at most kResidentN positions,
+// at most kFusedG heads).  r(p) is non-decreasing in every head's logit, so with M_g the maximum
+// of head g's logits over a group of kBoundGroup (8) positions:
 //   U = r(M_1, .., M_G)             bounds r from above over the group, and
 //   L = max_g (M_g - LSE_g)         from below at the position holding that maximum (r is at
 //                                   least any one head's log-probability);
@@ -817,24 +828,26 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
 // Ranking by the mixed cache, the fetched positions' logits are 16-bit ones written after the
 // bounds were taken: the groups that hold them are always read and give no L.  The same kernel,
 // in its KEYS form (below), serves slices longer than kResidentN from rank_keys' keys.
-constexpr int kGrp = 16;                            // positions per bound group
-constexpr int kMaxGroups = (int)(kResidentN / kGrp);  // 2048: two groups per thread
-constexpr float kBoundMargin = 1e-3f;               // slack on U for the rounding of its arithmetic
+constexpr int kMaxBoundGroups = (int)(kResidentN / kBoundGroup);  // 4096: four groups per thread
+constexpr float kBoundMargin = 1e-3f;  // slack on U for the rounding of its arithmetic
+// The long-slice form's groups: 16 positions, from rank_keys' maxima of r(p).
+constexpr int kGrp = 16;
+constexpr int kMaxGroups = (int)(kResidentN / kGrp);  // 2048
+constexpr int kMaxPasses = 8;  // candidate passes: a group's positions 4 to a lane, 32 keys a thread
 
-constexpr int kPassGroups = kSelThreads / 4;             // candidate groups per pass (four lanes each)
-constexpr int kMaxPasses = kMaxGroups / kPassGroups;    // 8
-
-static_assert(kMaxGroups == 2 * kSelThreads, "two bound groups per thread");
-static_assert(4 * kMaxPasses == 32, "32 keys per thread");
+static_assert(kMaxBoundGroups == 4 * kSelThreads, "four bound groups per thread");
+static_assert(kMaxBoundGroups / (kSelThreads / (kBoundGroup / 4)) == kMaxPasses &&
+                  kMaxGroups / (kSelThreads / (kGrp / 4)) == kMaxPasses,
+              "32 keys per thread");
 
 struct PrunedSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
   uint32_t sel_digit, sel_above, n_cand;
-  uint32_t kgrp[kMaxGroups / 32];  // mixed-cache ranking: the groups holding a fetched position
+  uint32_t kgrp[kMaxBoundGroups / 32];  // mixed-cache ranking: the groups holding a fetched position
   float lse2[kFusedG];
   uint32_t n_grp;
-  uint16_t grp[kMaxGroups];  // candidate groups, ascending
+  uint16_t grp[kMaxBoundGroups];  // candidate groups, ascending
   uint32_t cand[kCand];
 };
 
@@ -842,7 +855,7 @@ struct PrunedRank {
   const float* logits;  // [slices][G][N], log2 units
   const float* part_m;  // [slices][G][S]
   const float* part_l;
-  const float* gmax;    // [slices][G][N / 16], log2 units
+  const float* gmax;    // [slices][G][N / kBoundGroup], log2 units
   int G, S;
   // Ranking by the mixed cache: the fetched positions ([slices][n_kappa]), whose logits are the
   // 16-bit ones written after the bounds were taken from the low-bit ones; null otherwise.
@@ -892,27 +905,31 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     if constexpr (KEYS) return smem.g;
     else return smem;
   }();
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, q4 = t & 3;
+  // positions per group: 8 (the split kernels' bounds) or 16 (rank_keys' maxima); a group's
+  // positions are read 4 to a lane, LPG lanes a group, PASS groups a pass
+  constexpr int GS = KEYS ? kGrp : kBoundGroup, LPG = GS / 4, PASS = kSelThreads / LPG;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, ql = t % LPG, gj = t / LPG;
   const int64_t slice = blockIdx.x;
-  // the candidates' keys: pass s (kPassGroups groups, four lanes each; lane quad q4 holds
-  // positions 4 q4 .. 4 q4 + 3 of its group) in v[4s .. 4s + 3] for group grp_of[s] (-1 for
-  // none: keys -inf); passes then threads in position order
+  int ph = 0;  // the block scans' scratch set
+  // the candidates' keys: pass s (PASS groups; lane ql of a group holds its positions
+  // 4 ql .. 4 ql + 3) in v[4s .. 4s + 3] for group grp_of[s] (-1 for none: keys -inf); passes
+  // then threads in position order
   float v[4 * kMaxPasses];
   int grp_of[kMaxPasses];
   int n_pass;
   uint32_t bin, above, in_bin;  // the k-th key's coarse bin, the keys above it and in it
   if constexpr (!KEYS) {
     const int G = pr.G, S = pr.S;
-    const int ngrp = (int)(N / kGrp);  // N is a multiple of 32 and at most kResidentN
+    const int ngrp = (int)(N / GS);  // N is a multiple of 32 and at most kResidentN: ngrp % 4 == 0
 
-    // the bounds of groups 2t and 2t + 1 (a float2 per head) and the first split statistics are
+    // the bounds of groups 4t .. 4t + 3 (a float4 per head) and the first split statistics are
     // loaded before anything waits
-    float2 gm[kFusedG];
+    float4 gm[kFusedG];
     {
       const float* gp = pr.gmax + slice * G * ngrp;
-      const int i0 = 2 * t < ngrp ? 2 * t : 0;
+      const int i0 = 4 * t < ngrp ? 4 * t : 0;
 #pragma unroll
-      for (int g = 0; g < kFusedG; ++g) gm[g] = *reinterpret_cast<const float2*>(gp + (g < G ? g : 0) * ngrp + i0);
+      for (int g = 0; g < kFusedG; ++g) gm[g] = *reinterpret_cast<const float4*>(gp + (g < G ? g : 0) * ngrp + i0);
     }
     const int hw = wave < G ? wave : 0;
     const int64_t sb = (slice * G + hw) * S;
@@ -926,7 +943,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     asm volatile("" ::: "memory");
     sm.hist[t] = 0u;
     sm.hist[t + kSelThreads] = 0u;
-    if (t < kMaxGroups / 32) sm.kgrp[t] = 0u;
+    if (t < kMaxBoundGroups / 32) sm.kgrp[t] = 0u;
     if (wave < kFusedG) {
       const float l2 = head_lse2<64>(pr.part_m + sb, pr.part_l + sb, S, lane, m_first, l_first);
       if (wave < G && lane == 0) sm.lse2[wave] = l2;
@@ -937,7 +954,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     __syncthreads();
     if (mixed) {
       auto mark = [&](int32_t p) {
-        if (p >= 0 && p < N) atomicOr(&sm.kgrp[p >> 9], 1u << ((p >> 4) & 31));
+        if (p >= 0 && p < N) atomicOr(&sm.kgrp[p / (32 * GS)], 1u << ((p / GS) & 31));
       };
       mark(kp0);
       for (int i = t + kSelThreads; i < pr.n_kappa; i += kSelThreads) mark(kp[i]);
@@ -947,61 +964,71 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
 #pragma unroll
     for (int g = 0; g < kFusedG; ++g) lse2[g] = g < G ? sm.lse2[g] : 0.0f;
 
-    // U and L of the two groups (the arithmetic of rank_of, on the maxima)
-    float U[2], L[2];
+    // head g's log2-probability bound over group s, and L of the four groups (natural-log units)
+    auto lp_of = [&](int s, int g) {
+      return (s == 0 ? gm[g].x : (s == 1 ? gm[g].y : (s == 2 ? gm[g].z : gm[g].w))) - lse2[g];
+    };
+    float L[4], mx2[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float lp[kFusedG];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int g = 0; g < kFusedG; ++g)
-        if (g < G) {
-          lp[g] = (s == 0 ? gm[g].x : gm[g].y) - lse2[g];
-          mx = fmaxf(mx, lp[g]);
-        }
-      float sum = 0.0f;
+    for (int s = 0; s < 4; ++s) {
+      mx2[s] = -INFINITY;
 #pragma unroll
       for (int g = 0; g < kFusedG; ++g)
-        if (g < G) sum += __builtin_amdgcn_exp2f(lp[g] - mx);
-      U[s] = (mx + __builtin_amdgcn_logf(sum)) * kLn2 + kBoundMargin;
-      L[s] = mx * kLn2 + 0.0f;
+        if (g < G) mx2[s] = fmaxf(mx2[s], lp_of(s, g));
+      L[s] = mx2[s] * kLn2 + 0.0f;
     }
-    const bool gv0 = 2 * t < ngrp, gv1 = 2 * t + 1 < ngrp;
-    const uint32_t kw = mixed ? sm.kgrp[t >> 4] >> ((2 * t) & 31) : 0u;  // groups 2t, 2t + 1
-    const bool kg0 = kw & 1u, kg1 = (kw >> 1) & 1u;
+    const bool gv = 4 * t < ngrp;  // groups 4t .. 4t + 3, all or none
+    const uint32_t kw = mixed ? (sm.kgrp[t >> 3] >> ((4 * t) & 31)) & 15u : 0u;  // their fetched-row bits
 
     // tau_lo: below the k-th largest L (the lower edge of the coarse bin holding it, one bin down);
     // with fewer than k groups giving an L, no bound (bin 0)
     float tau_lo = -INFINITY;
     if (k <= ngrp) {
-      if (gv0 && !kg0) atomicAdd(&sm.hist[coarse_bin(L[0], r_lo)], 1u);
-      if (gv1 && !kg1) atomicAdd(&sm.hist[coarse_bin(L[1], r_lo)], 1u);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (gv && !((kw >> s) & 1u)) atomicAdd(&sm.hist[coarse_bin(L[s], r_lo)], 1u);
       __syncthreads();
       uint32_t bin, above;
-      pick_digit(sm, kBins, (uint32_t)k, bin, above);
+      pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
       if (bin > 0u) tau_lo = r_lo + (float)(bin - 1u) / kBinScale;
       sm.hist[t] = 0u;
       sm.hist[t + kSelThreads] = 0u;
     }
-    // candidate groups, compacted in ascending order
-    const bool c0 = gv0 && (U[0] >= tau_lo || kg0), c1 = gv1 && (U[1] >= tau_lo || kg1);
+    // candidate groups, compacted in ascending order.  U >= tau_lo is tested as
+    // sum_g 2^(lp_g - t2) >= 1 with t2 = tau_lo in log2 units less the margin: the logarithm and
+    // the maximum of U's own arithmetic are not needed for the comparison.  A group whose maxima
+    // are all -inf is never a candidate (U is not a number there).
+    const float t2 = tau_lo / kLn2 - kBoundMargin / kLn2;
+    uint32_t cm = 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bool reach = tau_lo == -INFINITY;
+      if (!reach) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int g = 0; g < kFusedG; ++g)
+          if (g < G) sum += __builtin_amdgcn_exp2f(lp_of(s, g) - t2);
+        reach = sum >= 1.0f;
+      }
+      cm |= (gv && ((reach && mx2[s] > -INFINITY) || ((kw >> s) & 1u))) ? (1u << s) : 0u;
+    }
     {
       uint32_t tot;
-      uint32_t off = block_exclusive_scan((c0 ? 1u : 0u) + (c1 ? 1u : 0u), sm.scan_scratch, tot);
-      if (c0) sm.grp[off++] = (uint16_t)(2 * t);
-      if (c1) sm.grp[off] = (uint16_t)(2 * t + 1);
+      uint32_t off = block_exclusive_scan((uint32_t)__popc(cm), sm.scan_scratch, tot, ph);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if ((cm >> s) & 1u) sm.grp[off++] = (uint16_t)(4 * t + s);
       if (t == 0) sm.n_grp = tot;
     }
     __syncthreads();
     const uint32_t n_grp = sm.n_grp;
 
-    // r of the candidates' positions, four lanes per group (lane quad q = t % 4 holds positions
-    // 4q .. 4q + 3 of the group, so that the four lanes read each head's 64 bytes of the group
-    // together): pass s covers candidates 256 s .. 256 s + 255, candidate 256 s + t / 4 in
+    // r of the candidates' positions, two lanes per group (lane ql = t % 2 holds positions
+    // 4 ql .. 4 ql + 3 of the group, so that the two lanes read each head's 32 bytes of the group
+    // together): pass s covers candidates PASS s .. PASS s + PASS - 1, candidate PASS s + t / 2 in
     // v[4s .. 4s + 3]; -inf where there is none.  Passes then threads then lanes run in position order.
     const float* lg = pr.logits + slice * G * N;
-    const int gj = t >> 2;
-    n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
+    n_pass = (int)((n_grp + PASS - 1) / PASS);  // <= kMaxPasses
     uint32_t cur_bin = 0u, cur_cnt = 0u;  // this thread's pending histogram increment
 #pragma unroll
     for (int s0 = 0; s0 < kMaxPasses; s0 += 2) {
@@ -1017,12 +1044,12 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       float4 x[2][kFusedG];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t j = (uint32_t)((s0 + u) * kPassGroups + gj);
+        const uint32_t j = (uint32_t)((s0 + u) * PASS + gj);
         grp_of[s0 + u] = j < n_grp ? (int)sm.grp[j] : -1;
         const int c = grp_of[s0 + u] >= 0 ? grp_of[s0 + u] : 0;  // a valid address, unused
 #pragma unroll
         for (int g = 0; g < kFusedG; ++g)
-          x[u][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + kGrp * c + 4 * q4);
+          x[u][g] = *reinterpret_cast<const float4*>(lg + (int64_t)(g < G ? g : 0) * N + GS * c + 4 * ql);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -1043,12 +1070,12 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     __syncthreads();
 
     // the exact threshold among the candidates, as the resident selection finds it
-    pick_digit(sm, kBins, (uint32_t)k, bin, above);
+    pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
     in_bin = sm.hist[bin];
   } else {
     // thread t looks at groups [g0, g1) = [t per, (t + 1) per); their maxima are loaded together
     // with the histogram when they fit in registers
-    const int64_t ngrp = N / kGrp;
+    const int64_t ngrp = N / GS;
     const float* gx = kg.kmax + slice * ngrp;
     const int64_t per = (ngrp + kSelThreads - 1) / kSelThreads;
     const int64_t g0 = (int64_t)t * per, g1 = g0 + per < ngrp ? g0 + per : ngrp;
@@ -1060,7 +1087,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
     if (t == 0) sm.n_cand = 0u;
     __syncthreads();
-    pick_digit(sm, kBins, (uint32_t)k, bin, above);
+    pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
     in_bin = sm.hist[bin];
 
     // candidate groups, compacted in ascending order: a key is in the threshold bin or a higher
@@ -1074,7 +1101,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       for (int64_t g = g0; g < g1; ++g) mine += reaches(gx[g]) ? 1u : 0u;
     }
     uint32_t n_grp;
-    uint32_t off = block_exclusive_scan(mine, sm.scan_scratch, n_grp);
+    uint32_t off = block_exclusive_scan(mine, sm.scan_scratch, n_grp, ph);
     if (n_grp <= (uint32_t)kMaxGroups && mine != 0u) {
       if (pre) {
 #pragma unroll
@@ -1092,16 +1119,15 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     }
     __syncthreads();
 
-    // the candidates' keys, four lanes a group: pass s covers candidates kPassGroups s .. + 255
+    // the candidates' keys, four lanes a group: pass s covers candidates PASS s .. PASS s + 255
     const float* ky = kg.rkey + slice * N;
-    const int gj = t >> 2;
-    n_pass = (int)((n_grp + kPassGroups - 1) / kPassGroups);  // <= kMaxPasses
+    n_pass = (int)((n_grp + PASS - 1) / PASS);  // <= kMaxPasses
 #pragma unroll
     for (int s = 0; s < kMaxPasses; ++s) {
-      const uint32_t j = (uint32_t)(s * kPassGroups + gj);
+      const uint32_t j = (uint32_t)(s * PASS + gj);
       grp_of[s] = s < n_pass && j < n_grp ? (int)sm.grp[j] : -1;
       float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (grp_of[s] >= 0) x = *reinterpret_cast<const float4*>(ky + (int64_t)kGrp * grp_of[s] + 4 * q4);
+      if (grp_of[s] >= 0) x = *reinterpret_cast<const float4*>(ky + (int64_t)GS * grp_of[s] + 4 * ql);
       v[4 * s] = x.x;
       v[4 * s + 1] = x.y;
       v[4 * s + 2] = x.z;
@@ -1162,7 +1188,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       }
     }
     if (!found) {
-      radix_select(sm, krem,
+      radix_select(sm, ph, krem,
                    [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
                      for (uint32_t i = t; i < nc; i += kSelThreads) {
                        const uint32_t u = sm.cand[i];
@@ -1172,7 +1198,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
                    thr, need_eq, n_thr);
     }
   } else {
-    radix_select(sm, (uint32_t)k,
+    radix_select(sm, ph, (uint32_t)k,
                  [&](int shift, int nbins, uint32_t prefix, uint32_t mask) {
 #pragma unroll
                    for (int i = 0; i < 4 * kMaxPasses; ++i) {
@@ -1214,7 +1240,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       }
       uint32_t tot;
       const uint32_t packed = (uint32_t)__popc(m[s]) | ((uint32_t)__popc(m[s + 1]) << 16);
-      const uint32_t ex = block_exclusive_scan(packed, sm.scan_scratch, tot);
+      const uint32_t ex = block_exclusive_scan(packed, sm.scan_scratch, tot, ph);
       before[s] = carried + (ex & 0xffffu);
       before[s + 1] = carried + (tot & 0xffffu) + (ex >> 16);
       carried += (tot & 0xffffu) + (tot >> 16);
@@ -1245,7 +1271,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     while (m != 0u) {
       const int b = __builtin_ctz(m);
       m &= m - 1u;
-      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(kGrp * grp_of[s] + 4 * q4 + b);
+      if (out < (uint32_t)k) idx_out[slice * k + out] = (int32_t)(GS * grp_of[s] + 4 * ql + b);
       ++out;
     }
   }
@@ -1278,7 +1304,7 @@ void launch_select(const Dims& d, int k, float r_lo, const float* keys, const ui
 }  // namespace
 
 bool rank_select_prunable(const Dims& d, int k) {
-  return d.N <= kResidentN && d.G <= kFusedG && k <= d.N / kGrp;
+  return d.N <= kResidentN && d.G <= kFusedG && k <= d.N / kBoundGroup;
 }
 
 hipError_t launch_rank_select(const Dims& d, int S, const float* logits, const float* part_m,

@@ -838,8 +838,8 @@ def test_overlapped_streams_match_serial(gpu, compute):
 
 @pytest.mark.parametrize("name,over,qscale", [
     ("tiny", {}, 1.0),
-    ("tiny", dict(top_k=32), 1.0),                         # k = N / 16: one position per bound group
-    ("tiny", dict(top_k=33), 1.0),                         # k > N / 16: the unpruned selection
+    ("tiny", dict(top_k=64), 1.0),                         # k = N / 8: one position per bound group
+    ("tiny", dict(top_k=65), 1.0),                         # k > N / 8: the unpruned selection
     ("llama8k", {}, 1.0),
     ("llama8k", dict(seq_len=8192 + 96, seed=5), 1.0),     # ragged last split
     ("llama8k", dict(seq_len=4096, top_k=256, bits=1), 1.0),
@@ -851,7 +851,7 @@ def test_overlapped_streams_match_serial(gpu, compute):
 ])
 @pytest.mark.parametrize("mixed", [False, True])
 def test_fused_step_selection_from_bounds(gpu, name, over, qscale, mixed):
-    """Without a key output the fused step selects from per-16-position logit maxima: groups
+    """Without a key output the fused step selects from per-8-position logit maxima: groups
     whose upper bound cannot reach the k-th rank are never read.  Ranking by the mixed cache
     (Algorithm 3's reading), the fetched rows' 16-bit logits replace the low-bit ones after the
     maxima are taken, so the groups holding them are always read and give no lower bound.  The
