@@ -138,6 +138,25 @@ __device__ __forceinline__ float head_lse2(const float* pm, const float* pl, int
   return M + log2f(L);
 }
 
+// The same from 16 lanes: lane j of each row of 16 takes splits j, j + 16, ... (its first pair,
+// m_first / l_first, already loaded), and the rows merge across their lanes with DPP moves (no
+// LDS round trip): swaps of neighbours, then of pairs, then the two halves of each half row and of
+// the row (mirrors).  Each merge is symmetric, so every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float head_lse2_row(const float* pm, const float* pl, int S, int j, float m_first,
+                                               float l_first) {
+  float M = -INFINITY, L = 0.0f;
+  for (int s = j; s < S; s += 16) merge_stat(M, L, s == j ? m_first : pm[s], s == j ? l_first : pl[s]);
+  merge_stat(M, L, dpp_move<0xB1>(M), dpp_move<0xB1>(L));    // quad_perm [1, 0, 3, 2]
+  merge_stat(M, L, dpp_move<0x4E>(M), dpp_move<0x4E>(L));    // quad_perm [2, 3, 0, 1]
+  merge_stat(M, L, dpp_move<0x141>(M), dpp_move<0x141>(L));  // row_half_mirror
+  merge_stat(M, L, dpp_move<0x140>(M), dpp_move<0x140>(L));  // row_mirror
+  return M + log2f(L);
+}
+
 // r of the position held in component e of x[g] (head g's logit, log2 units):
 // log sum_g exp(s_g - LSE_g), in natural-log units.
 template <int GM>
@@ -607,7 +626,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
     };
     const int hw = wave < G ? wave : 0;  // waves past G merge head 0 again, unused
     const int64_t sb = (slice * G + hw) * S;
-    const int j0 = lane < S ? lane : 0;
+    const int j0 = (lane & 15) < S ? (lane & 15) : 0;
     const float m_first = fr.part_m[sb + j0], l_first = fr.part_l[sb + j0];
     asm volatile("" ::: "memory");
 #pragma unroll
@@ -615,7 +634,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
     sm.hist[t] = 0u;
     sm.hist[t + kSelThreads] = 0u;
     if (wave < kFusedG) {
-      const float l2 = head_lse2<64>(fr.part_m + sb, fr.part_l + sb, S, lane, m_first, l_first);
+      const float l2 = head_lse2_row(fr.part_m + sb, fr.part_l + sb, S, lane & 15, m_first, l_first);
       if (wave < G && lane == 0) lse2[wave] = l2;
     }
     if (t == 0) {
@@ -933,7 +952,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     }
     const int hw = wave < G ? wave : 0;
     const int64_t sb = (slice * G + hw) * S;
-    const int j0 = lane < S ? lane : 0;
+    const int j0 = (lane & 15) < S ? (lane & 15) : 0;
     const float m_first = pr.part_m[sb + j0], l_first = pr.part_l[sb + j0];
     // ranking by the mixed cache: a group that holds a fetched position is a candidate whatever
     // its bounds say (its logit there is a 16-bit one, taken after them), and gives no L
@@ -945,7 +964,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     sm.hist[t + kSelThreads] = 0u;
     if (t < kMaxBoundGroups / 32) sm.kgrp[t] = 0u;
     if (wave < kFusedG) {
-      const float l2 = head_lse2<64>(pr.part_m + sb, pr.part_l + sb, S, lane, m_first, l_first);
+      const float l2 = head_lse2_row(pr.part_m + sb, pr.part_l + sb, S, lane & 15, m_first, l_first);
       if (wave < G && lane == 0) sm.lse2[wave] = l2;
     }
     if (t == 0) {
