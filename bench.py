@@ -678,8 +678,8 @@ def main():
         "roofline": {
             "kernel": "decode_step (the split kernel with ranking outputs: attn_stream_kernel<1> for 1-bit "
                       "codes at head_dim 128, attn_split_kernel otherwise; then " + (
-                "rank_select_pruned: r(p) of the position groups whose 16-position bound reaches the k-th "
-                "rank, the top-k and the merge of the splits)" if N <= 32768 and Hq // Hkv <= 4 and k <= N // 16 else
+                "rank_select_pruned: r(p) of the position groups whose 8-position bound reaches the k-th "
+                "rank, the top-k and the merge of the splits)" if N <= 32768 and Hq // Hkv <= 4 and k <= N // 8 else
                 "rank_select forming r(p), the top-k and the merge of the splits)" if N <= 32768 and Hq // Hkv <= 4
                 else "rank_keys + rank_select merging the splits)"),
             "bound": "hbm",
