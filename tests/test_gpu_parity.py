@@ -343,6 +343,28 @@ def test_topk_long_slices_grouped_and_swept(gpu, k, qscale):
         assert np.array_equal(a, lowest) and np.array_equal(nxt, lowest)
 
 
+def test_topk_sweeps_over_two_chunks(gpu):
+    """A crowded threshold bin on a slice longer than one compaction chunk (131072 positions):
+    the sweeps mark and compact the selected positions chunk by chunk, the second chunk's bitmaps
+    cleared by other threads than the ones that read the first's.  The selected positions fall in
+    both chunks; score_topk and the fused step's next selection against the oracle."""
+    k = 3000
+    cfg = get_config("llama8k").with_(seq_len=131072 + 8192 + 96, top_k=k, seed=11)
+    K, V, Q, _, _, _ = generate_all(cfg)
+    Q = (Q.astype(np.float32) * 1e-3).astype(np.float16)
+    cache = quantize_pack(_dev(K), _dev(V), cfg.bits)
+    q = _dev(Q)
+    a = _np(score_topk(q, cache, k))
+    _, nxt = decode_step(q, cache, k)
+    nxt = _np(nxt)
+    _, kh, _ = _reference_cache(K, V, cfg.bits)
+    r_ref = oracle.rank_scores(Q, kh, 1, cfg.sm_scale)
+    slices = [(0, h) for h in range(cfg.n_kv_heads)]
+    assert (a >= 131072).any() and (a < 131072).any(), "the selection should span both chunks"
+    _assert_topk(a, r_ref, k, slices, "score_topk two chunks")
+    _assert_topk(nxt, r_ref, k, slices, "decode_step two chunks")
+
+
 @pytest.mark.parametrize("name,rank_row", [("mistral32k", 1), ("long128k", 1), ("layers32", 1),
                                            ("mistral32k", 0)])   # row 0 of two: the serial comparator's ranking
 def test_score_topk_full_size_sampled(gpu, name, rank_row):
