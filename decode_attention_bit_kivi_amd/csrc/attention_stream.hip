@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
         // issued by every lane, the lanes without a rank row addressing past the buffer (such a
         // store is dropped): with no branch around it the compiler counts it, and the waits for
         // the staged loads stay exact.  Non-temporal: the selection reads back only the groups
-        // its bounds keep (about a fifth), so the logits need not displace C' in the caches.
+        // its bounds keep (about a tenth), so the logits need not displace C' in the caches.
         // (Form 3 stores the kappa positions' low-bit logits too; the end of the kernel writes
         // their 16-bit ones over them.)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,

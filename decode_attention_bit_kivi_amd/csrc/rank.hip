@@ -22,9 +22,10 @@
 //                - resident: a slice of at most 32768 positions read once into
 //                  registers (32 keys a thread), from rank_keys' keys or, with
 //                  at most 4 heads per KV head, forming r(p) and the histogram
-//                  itself from the logits (the arithmetic of rank_keys through
-//                  shared functions, so the keys are the same bits; no key
-//                  buffer unless the caller asks for r);
+//                  itself from the logits (r(p) through rank_keys' function,
+//                  each head's log-sum-exp merged over 16 lanes as the pruned
+//                  form merges it, so the two forms' keys are the same bits; no
+//                  key buffer unless the caller asks for r);
 //                - pruned (the fused step): bounds of every 8 positions from
 //                  the split kernel's per-head logit maxima; only the groups
 //                  whose upper bound reaches the k-th lower bound are read;
