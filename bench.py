@@ -119,8 +119,8 @@ def parse(argv=None):
     ap.add_argument("--mode", choices=("step", "copy", "traffic-record"), default="step",
                     help="copy: a plain 1 GiB device-to-device copy, the reference for scaling the "
                          "profiler's HBM byte counters; traffic-record: write the HBM traffic record "
-                         "from the four counter runs under --pmc-root (see TRAFFIC_COMMANDS)")
-    ap.add_argument("--pmc-root", default="gpurun_out", help="directory holding the counter runs")
+                         "from the four counter runs under --pmc-root (see traffic_commands)")
+    ap.add_argument("--pmc-root", default="counters", help="directory holding the counter runs")
     return ap.parse_args(argv)
 
 
@@ -146,15 +146,19 @@ def copy_reference(reps: int = 5):
 MODEL_SHAPE = {"tiny": "tiny", "llama8k": "Llama-3-8B-shaped", "mistral32k": "Mistral-7B-shaped",
                "layers32": "Llama-3-8B-shaped", "long128k": "long-context (Llama/Mistral-shaped heads)"}
 TRAFFIC_KERNELS = "attn_split|attn_stream|rank_keys|rank_select|attn_merge"
-TRAFFIC_COMMANDS = [
-    "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_copy_fetch -o run -- python -u bench.py --mode copy",
-    "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_copy_write -o run -- python -u bench.py --mode copy",
-    f"rocprofv3 --kernel-include-regex '{TRAFFIC_KERNELS}' --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch "
-    "-o run -- python -u bench.py --steps 4 --warmup 2 --no-cpu-baseline",
-    f"rocprofv3 --kernel-include-regex '{TRAFFIC_KERNELS}' --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write "
-    "-o run -- python -u bench.py --steps 4 --warmup 2 --no-cpu-baseline",
-    "python bench.py --mode traffic-record --pmc-root gpurun_out",
-]
+
+
+def traffic_commands(root: str):
+    """The runs a traffic record is made from, their counter output under `root`."""
+    return [
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -d {root}/pmc_copy_fetch -o run -- python -u bench.py --mode copy",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -d {root}/pmc_copy_write -o run -- python -u bench.py --mode copy",
+        f"rocprofv3 --kernel-include-regex '{TRAFFIC_KERNELS}' --pmc FETCH_SIZE -f csv -d {root}/pmc_fetch "
+        "-o run -- python -u bench.py --steps 4 --warmup 2 --no-cpu-baseline",
+        f"rocprofv3 --kernel-include-regex '{TRAFFIC_KERNELS}' --pmc WRITE_SIZE -f csv -d {root}/pmc_write "
+        "-o run -- python -u bench.py --steps 4 --warmup 2 --no-cpu-baseline",
+        f"python bench.py --mode traffic-record --pmc-root {root}",
+    ]
 
 
 def _counter_rows(root: str, run: str, counter: str):
@@ -220,7 +224,7 @@ def write_traffic_record(root: str, workload: str = "mistral32k"):
                 "selection workgroup holds), each dispatch taken right after a fused-step split dispatch on "
                 "its queue; rocprofv3 FETCH_SIZE and WRITE_SIZE "
                 "per dispatch, scaled by the same counters' reading for a plain 1 GiB device copy",
-        "commands": TRAFFIC_COMMANDS,
+        "commands": traffic_commands(root),
         "calibration": {"copy_bytes_read": n, "copy_bytes_written": n,
                         "FETCH_SIZE_kib": round(cal["FETCH_SIZE"]), "WRITE_SIZE_kib": round(cal["WRITE_SIZE"]),
                         "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4)},
