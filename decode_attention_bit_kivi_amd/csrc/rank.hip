@@ -274,7 +274,7 @@ constexpr int kWordsPerThread = kWords / kSelThreads;
 struct SelectSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
-  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t sel_digit, sel_above, sel_count, n_cand;
   union {
     uint32_t cand[kCand];  // keys of the threshold bin
     struct {
@@ -311,13 +311,14 @@ __device__ __forceinline__ int64_t sweep_pos(int64_t base, int i) {
   return base + 4 * ((int64_t)threadIdx.x + (i >> 2) * kSelThreads) + (i & 3);
 }
 
-// The digit of hist[0, nbins) holding the krem-th largest element, counted from the top, and the
-// number of elements in the digits above it.
+// The digit of hist[0, nbins) holding the krem-th largest element, counted from the top, the
+// number of elements in the digits above it and the number in the digit itself (so that no
+// thread reads hist after the call: a caller may clear it next without a barrier).
 // With krem outside [1, total], digit 0 and 0 above it.  Exactly one thread writes the answer,
 // after the scan's barrier: the reads of the previous call's answer precede that barrier.
 template <typename Smem>
 __device__ __forceinline__ void pick_digit(Smem& sm, int& ph, int nbins, uint32_t krem, uint32_t& digit,
-                                           uint32_t& above) {
+                                           uint32_t& above, uint32_t& count) {
   const int t = threadIdx.x;
   // thread t covers digits nbins-1-2t and nbins-2-2t
   const int dhi = nbins - 1 - 2 * t, dlo = dhi - 1;
@@ -329,17 +330,21 @@ __device__ __forceinline__ void pick_digit(Smem& sm, int& ph, int nbins, uint32_
     if (dhi >= 0 && excl < krem && excl + hhi >= krem) {
       sm.sel_digit = (uint32_t)dhi;
       sm.sel_above = excl;
+      sm.sel_count = hhi;
     } else if (dlo >= 0 && excl + hhi < krem && excl + hhi + hlo >= krem) {
       sm.sel_digit = (uint32_t)dlo;
       sm.sel_above = excl + hhi;
+      sm.sel_count = hlo;
     }
   } else if (dlo == 0 || (dhi == 0 && dlo < 0)) {
     sm.sel_digit = 0u;
     sm.sel_above = 0u;
+    sm.sel_count = dlo == 0 ? hlo : hhi;
   }
   __syncthreads();
   digit = sm.sel_digit;
   above = sm.sel_above;
+  count = sm.sel_count;
 }
 
 // Exact radix select: the krem-th largest key among those `count` feeds to the histogram, as
@@ -358,12 +363,12 @@ __device__ __forceinline__ void radix_select(Smem& sm, int& ph, uint32_t krem, C
     __syncthreads();
     count(shift, nbins, prefix, mask);
     __syncthreads();
-    uint32_t dg, ab;
-    pick_digit(sm, ph, nbins, krem, dg, ab);
+    uint32_t dg, ab, cnt;
+    pick_digit(sm, ph, nbins, krem, dg, ab, cnt);
     prefix |= dg << shift;
     mask |= (uint32_t)(nbins - 1) << shift;
     krem -= ab;
-    if (pass == 2) n_eq = sm.hist[dg];  // the last digit's bin holds exactly the keys equal to thr
+    if (pass == 2) n_eq = cnt;  // the last digit's bin holds exactly the keys equal to thr
   }
   thr = prefix;
   need_eq = krem;
@@ -418,9 +423,8 @@ __device__ void select_by_sweeps(SelectSmem& sm, float* bin_vals, const float* _
   if (t == 0) sm.n_cand = 0u;
   __syncthreads();
 
-  uint32_t bin, above;
-  pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
-  const uint32_t in_bin = sm.hist[bin];
+  uint32_t bin, above, in_bin;
+  pick_digit(sm, ph, kBins, (uint32_t)k, bin, above, in_bin);
   // the threshold bin as an interval of values [lo, hi) (the top bin runs to +inf), found by two
   // binary searches over the keys.  The ranks hold no -0 and no NaN, so comparing the floats
   // orders them as their keys do.
@@ -561,7 +565,7 @@ static_assert(kSweepU == 8, "eight mark bytes per bitmap word");
 struct ResidentSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
-  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t sel_digit, sel_above, sel_count, n_cand;
   uint32_t res[4];  // small-bin selection: thr, need_eq, n_eq, found
   float bin_vals[2];
   // marks of positions 4n .. 4n + 3: bit e selected (above the threshold, or equal to it when all
@@ -700,9 +704,8 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_resident_kernel(const
     __syncthreads();
   }
 
-  uint32_t bin, above;
-  pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
-  const uint32_t in_bin = sm.hist[bin];
+  uint32_t bin, above, in_bin;
+  pick_digit(sm, ph, kBins, (uint32_t)k, bin, above, in_bin);
   if (wave == 0) {
     const uint32_t key = first_key_of_bin_wave(bin, r_lo);
     if (lane == 0) sm.bin_vals[0] = key_value(key);
@@ -863,7 +866,7 @@ static_assert(kMaxBoundGroups / (kSelThreads / (kBoundGroup / 4)) == kMaxPasses 
 struct PrunedSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
-  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t sel_digit, sel_above, sel_count, n_cand;
   uint32_t kgrp[kMaxBoundGroups / 32];  // mixed-cache ranking: the groups holding a fetched position
   float lse2[kFusedG];
   uint32_t n_grp;
@@ -893,7 +896,7 @@ struct PrunedRank {
 struct GroupedSmem {
   uint32_t hist[kBins];
   uint32_t scan_scratch[2 * kSelWaves];
-  uint32_t sel_digit, sel_above, n_cand;
+  uint32_t sel_digit, sel_above, sel_count, n_cand;
   uint32_t grp[kMaxGroups];  // candidate groups, ascending (indices past 65535 at long slices)
   uint32_t cand[kCand];
 };
@@ -1008,8 +1011,8 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
       for (int s = 0; s < 4; ++s)
         if (gv && !((kw >> s) & 1u)) atomicAdd(&sm.hist[coarse_bin(L[s], r_lo)], 1u);
       __syncthreads();
-      uint32_t bin, above;
-      pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
+      uint32_t bin, above, in_lo;
+      pick_digit(sm, ph, kBins, (uint32_t)k, bin, above, in_lo);
       if (bin > 0u) tau_lo = r_lo + (float)(bin - 1u) / kBinScale;
       sm.hist[t] = 0u;
       sm.hist[t + kSelThreads] = 0u;
@@ -1090,8 +1093,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     __syncthreads();
 
     // the exact threshold among the candidates, as the resident selection finds it
-    pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
-    in_bin = sm.hist[bin];
+    pick_digit(sm, ph, kBins, (uint32_t)k, bin, above, in_bin);
   } else {
     // thread t looks at groups [g0, g1) = [t per, (t + 1) per); their maxima are loaded together
     // with the histogram when they fit in registers
@@ -1107,8 +1109,7 @@ __global__ __launch_bounds__(kSelThreads) void rank_select_pruned_kernel(int64_t
     for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = gh[i];
     if (t == 0) sm.n_cand = 0u;
     __syncthreads();
-    pick_digit(sm, ph, kBins, (uint32_t)k, bin, above);
-    in_bin = sm.hist[bin];
+    pick_digit(sm, ph, kBins, (uint32_t)k, bin, above, in_bin);
 
     // candidate groups, compacted in ascending order: a key is in the threshold bin or a higher
     // one exactly when its bin is, so a group that holds one has its maximum there too
