@@ -55,7 +55,6 @@ static_assert(kStSlot % 16 == 0 && kStKS % 16 == 0 && kStVC % 16 == 0 && kStVM %
 constexpr float kStLog2e = 1.4426950408889634f;
 constexpr float kStRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr uint32_t kStDropped = 0x80000000u;  // a buffer offset past every buffer here: the store is dropped
-constexpr int kStNonTemporal = 2;  // cache-policy operand of a buffer access: the nt bit
 
 struct StreamSmem {
   uint32_t kmask[kAttnMaxBlocks];
@@ -375,12 +374,12 @@ __global__ __launch_bounds__(256, 3) void attn_stream_kernel(AttnArgs a, int Hkv
       } else {
         // issued by every lane, the lanes without a rank row addressing past the buffer (such a
         // store is dropped): with no branch around it the compiler counts it, and the waits for
-        // the staged loads stay exact.  Non-temporal: the selection reads back only the groups
-        // its bounds keep (about a tenth), so the logits need not displace C' in the caches.
-        // (Form 3 stores the kappa positions' low-bit logits too; the end of the kernel writes
-        // their 16-bit ones over them.)
+        // the staged loads stay exact.  An ordinary (cached) store: the selection that follows
+        // reads the candidate groups' logits back sooner than with non-temporal stores.  (Form 3
+        // stores the kappa positions' low-bit logits too; the end of the kernel writes their
+        // 16-bit ones over them.)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rl_buf,
-                                               (int)(rank_lane ? voff : kStDropped), (int)soff, kStNonTemporal);
+                                               (int)(rank_lane ? voff : kStDropped), (int)soff, 0);
       }
       // the bound of each 8-position group for the pruned selection (a buffer of size 0 when it
       // is not wanted): lanes g and g ^ 1 of n16 hold the eight logits of row arow at positions
