@@ -23,7 +23,7 @@ SPECACHE_ERR_WORKSPACE = 3
 SPECACHE_ERR_NOT_PINNED = 4
 SPECACHE_ERR_HIP = 5
 SPECACHE_ERR_TOO_LARGE = 6
-NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024   # SPECACHE_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024  # SPECACHE_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "specache_lowbit_bytes",

@@ -398,14 +398,14 @@ int specache_decode_step(const specache_shape* shape, const void* q16, int n_tok
  *
  * The array holds SPECACHE_NOALLOC_SCRATCH_BYTES per GPU (every GPU the library runs on keeps its
  * own copy until the process ends); a problem whose specache_decode_step_workspace_size exceeds
- * it returns SPECACHE_ERR_TOO_LARGE before anything is enqueued (96 MiB holds, for example, the
+ * it returns SPECACHE_ERR_TOO_LARGE before anything is enqueued (128 MiB holds, for example, the
  * 32K-context step at batch 16 with 8 KV heads, 32 query heads and k = 328).  Every call on one
  * GPU shares that GPU's array, which keeps the last call's contents (no part of it needs to start
  * at zero: the kernels clear what they accumulate into).  Calls on one stream are ordered; calls
  * that overlap on one GPU (several streams, or several host threads) race on the array and give
  * undefined results.  Other arguments and errors as for specache_decode_step.
  */
-#define SPECACHE_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+#define SPECACHE_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
 int specache_decode_step_noalloc(const specache_shape* shape, const void* q16, int n_tokens, int rank_row,
                                  int rank_mixed, const specache_lowbit* cache, const int32_t* idx, int k,
                                  const void* k_sel, const void* v_sel, const void* k_tail, const void* v_tail,

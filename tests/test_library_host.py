@@ -244,3 +244,6 @@ def test_noalloc_step_refuses_sizes_beyond_its_scratch_before_any_hip_call(lib):
     assert call(small, k_next=0) == _lib.SPECACHE_ERR_INVALID        # k_next < 1: invalid, not "too large"
     assert call(small, T=3) == _lib.SPECACHE_ERR_INVALID
     assert lib.specache_decode_step_workspace_size(ctypes.byref(small), 2, 328, 0, 328) <= _lib.NOALLOC_SCRATCH_BYTES
+    # the header's example: the 32K step at batch 16 (the 32-layer workload's shape) fits
+    layers32 = _shape(batch=16, n_q_heads=32, n_kv_heads=8, seq_len=32768)
+    assert lib.specache_decode_step_workspace_size(ctypes.byref(layers32), 2, 328, 0, 328) <= _lib.NOALLOC_SCRATCH_BYTES
